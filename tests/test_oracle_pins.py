@@ -1,0 +1,389 @@
+"""Pins of the CPU oracle against facts fixed outside its own code.
+
+Every check here compares the oracle with something it cannot agree with by
+construction: a hand-derived worked example, a closed form (Lemma 5.1, the
+SimHash collision law), an independent library routine (torch's attention and
+bfloat16 conversion), or a brute-force search written differently from the
+oracle's bucketed one.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import HeadCache, TempCacheOracle, bf16_round, simhash
+from oracle import annca as oannca
+from synth import WORKLOADS, ClusterPrompt, DriftStream
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _cache_from(g):
+    return HeadCache(g["head_dim"], g["budget"], g["tables"], g["bits"], g["threshold"],
+                     "f32", np.array(g["planes"], dtype=np.float64))
+
+
+def _sdpa(q, k, v, scale=None, mask=None):
+    """torch's CPU attention in float64: an independent softmax-attention routine."""
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None]
+    kt = torch.from_numpy(np.asarray(k, np.float64))[None]
+    vt = torch.from_numpy(np.asarray(v, np.float64))[None]
+    m = None if mask is None else torch.from_numpy(mask)[None]
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    return out[0].numpy()
+
+
+# ---------------------------------------------------------------- bfloat16 RNE
+
+def test_bf16_round_hand_values():
+    cases = {
+        0x3F800000: 0x3F800000,   # 1.0
+        0x3F808000: 0x3F800000,   # tie, kept pattern even -> down
+        0x3F818000: 0x3F820000,   # tie, kept pattern odd -> up
+        0x3F808001: 0x3F810000,   # above the tie -> up
+        0x3F807FFF: 0x3F800000,   # below the tie -> down
+        0x7F7FFFFF: 0x7F800000,   # largest finite rounds to +inf
+        0x80000000: 0x80000000,   # -0.0 stays
+    }
+    src = np.array(list(cases), dtype=np.uint32).view(np.float32)
+    out = bf16_round(src).view(np.uint32)
+    assert [int(v) for v in out] == list(cases.values())
+
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+                        (rng.standard_normal(1000) * 1e-38).astype(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(bf16_round(x).view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- SimHash
+
+def test_simhash_basis_golden(golden_dir):
+    g = _load(golden_dir, "simhash_basis.json")
+    codes, _ = simhash(np.array(g["inputs"]), np.array(g["planes"], dtype=np.float64))
+    assert codes.tolist() == g["expected_codes"]
+
+
+@pytest.mark.parametrize("bits", [8, 16, 32])
+@pytest.mark.parametrize("theta", [0.05, 0.3, 1.0, 2.0])
+def test_simhash_collision_law(bits, theta):
+    """Per table, P[codes equal] = (1 - theta/pi)^bits for random hyperplanes."""
+    d, L = 24, 40000
+    rng = np.random.default_rng(int(1000 * theta) + bits)
+    x = rng.standard_normal(d)
+    x /= np.linalg.norm(x)
+    u = rng.standard_normal(d)
+    u -= (u @ x) * x
+    u /= np.linalg.norm(u)
+    y = math.cos(theta) * x + math.sin(theta) * u
+    planes = rng.standard_normal((L, bits, d))
+    codes, _ = simhash(np.stack([x, y]), planes)
+    rate = float(np.mean(codes[0] == codes[1]))
+    p = (1.0 - theta / math.pi) ** bits
+    sigma = math.sqrt(max(p * (1 - p), 1e-12) / L)
+    assert abs(rate - p) <= 4 * sigma + 1e-9, (rate, p, sigma)
+
+
+# ---------------------------------------------------------------- worked examples
+
+def test_lemma_two_slots_golden(golden_dir):
+    g = _load(golden_dir, "lemma_two_slots.json")
+    hc = _cache_from(g)
+    for fr in g["frames"]:
+        hc.process_frame(np.array(fr["keys"]), np.array(fr["values"]))
+    assert hc.count[:hc.n_live].tolist() == g["expected_count"]
+    np.testing.assert_allclose(hc.V_m[:hc.n_live], g["expected_value_slots"], rtol=0, atol=0)
+    O, lse = hc.attend(np.array(g["queries"]))
+    np.testing.assert_allclose(O, g["expected_output"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, g["expected_lse"], rtol=0, atol=1e-12)
+
+
+def test_running_mean_golden(golden_dir):
+    g = _load(golden_dir, "running_mean.json")
+    hc = _cache_from(g)
+    for fr in g["frames"]:
+        hc.process_frame(np.array(fr["keys"]), np.array(fr["values"]))
+    e = g["expected"]
+    assert hc.n_live == e["n_live"] and hc.evicted_tokens == e["evicted_tokens"]
+    assert hc.K_m[0].tolist() == e["K_m"] and hc.V_m[0].tolist() == e["V_m"]
+    assert int(hc.count[0]) == e["count"] and int(hc.last[0]) == e["last"]
+
+
+def test_threshold_and_ties_golden(golden_dir):
+    g = _load(golden_dir, "threshold_and_ties.json")
+    hc = _cache_from(g)
+    res = [hc.process_frame(np.array(fr["keys"]), np.array(fr["values"])) for fr in g["frames"]]
+    e = g["expected"]
+    assert res[1].best_slot.tolist() == e["best_slot_frame1"]
+    assert res[1].merged.tolist() == e["merged_frame1"]
+    assert hc.count[:hc.n_live].tolist() == e["count"] and hc.n_live == e["n_live"]
+    assert hc.K_m[0].tolist() == e["K_m_slot0"] and hc.V_m[0].tolist() == e["V_m_slot0"]
+
+
+def test_lru_eviction_golden(golden_dir):
+    g = _load(golden_dir, "lru_eviction.json")
+    hc = _cache_from(g)
+    res = [hc.process_frame(np.array(fr["keys"]), np.array(fr["values"])) for fr in g["frames"]]
+    e = g["expected"]
+    assert res[2].slot.tolist() == e["slot_frame2"]
+    assert res[2].merged.tolist() == e["merged_frame2"]
+    assert res[2].evicted == e["evicted_frame2"]
+    assert hc.count[:3].tolist() == e["count"] and hc.last[:3].tolist() == e["last"]
+    assert hc.evicted_tokens == e["evicted_tokens"] and hc.n_live == e["n_live"]
+
+
+# ---------------------------------------------------------------- Lemma 5.1
+
+def _run_stream(w, frames, heads=None):
+    st = DriftStream(w)
+    orc = TempCacheOracle.for_workload(w, st.planes(), heads=heads)
+    raw_k, raw_v, last_q = [], [], None
+    for _ in range(frames):
+        K, V, Q, _ = st.next_frame()
+        if heads is not None:
+            K, V, Q = K[:heads], V[:heads], Q[:heads]
+        orc.process_frame(K, V)
+        raw_k.append(K)
+        raw_v.append(V)
+        last_q = Q
+    return orc, np.concatenate(raw_k, axis=1), np.concatenate(raw_v, axis=1), last_q
+
+
+def test_lemma51_tiny_variant():
+    """Exact copies merged with mean values + ln(count) = dense attention (1e-5)."""
+    w = WORKLOADS["tiny_lemma"]
+    orc, Kr, Vr, Q = _run_stream(w, 5)
+    hc = orc.heads[0]
+    assert hc.count[:hc.n_live].max() >= 4          # merges really happened
+    assert hc.n_live < Kr.shape[1]
+    O, _ = hc.attend(Q[0])
+    dense = _sdpa(Q[0], Kr[0], Vr[0], scale=1 / math.sqrt(w.head_dim))
+    assert np.abs(O - dense).max() < 1e-5
+
+
+def test_lemma51_two_heads_d128_variant():
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=256, dtype="f32", p_exact=0.6,
+                                  p_pert=0.0, budget=2048, seed=1101)
+    orc, Kr, Vr, Q = _run_stream(w, 6)
+    for h in range(2):
+        hc = orc.heads[h]
+        assert hc.count[:hc.n_live].max() >= 5
+        O, _ = hc.attend(Q[h])
+        dense = _sdpa(Q[h], Kr[h], Vr[h], scale=1 / math.sqrt(128))
+        assert np.abs(O - dense).max() < 1e-5
+
+
+def test_lemma_fails_without_log_count_bias():
+    """Sanity of the pin itself: dropping the bias moves the output well past 1e-5."""
+    w = WORKLOADS["tiny_lemma"]
+    orc, Kr, Vr, Q = _run_stream(w, 5)
+    hc = orc.heads[0]
+    S = hc.n_live
+    nobias = _sdpa(Q[0], hc.k_hat[:S], hc.v_hat[:S], scale=1 / math.sqrt(w.head_dim))
+    dense = _sdpa(Q[0], Kr[0], Vr[0], scale=1 / math.sqrt(w.head_dim))
+    assert np.abs(nobias - dense).max() > 1e-3
+
+
+# ---------------------------------------------------------------- attention special cases
+
+def test_no_merge_is_plain_attention():
+    """Threshold above 1: nothing merges, every count is 1, attend = plain softmax."""
+    w = WORKLOADS["tiny"].with_(threshold=1.5)
+    orc, Kr, Vr, Q = _run_stream(w, 3)
+    hc = orc.heads[0]
+    assert hc.n_live == Kr.shape[1] and (hc.count[:hc.n_live] == 1).all()
+    O, _ = hc.attend(Q[0])
+    ref = _sdpa(Q[0], Kr[0], Vr[0], scale=1 / math.sqrt(w.head_dim))
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one():
+    w = WORKLOADS["tiny"]
+    orc, Kr, Vr, Q = _run_stream(w, 5)
+    hc = orc.heads[0]
+    O, lse, P = hc.attend(Q[0], return_probs=True)
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)
+    hc.v_hat[:hc.n_live] = 1.0
+    O1, _ = hc.attend(Q[0])
+    np.testing.assert_allclose(O1, 1.0, atol=1e-12)
+    # lse is the log of the shifted partition function
+    S = hc.n_live
+    z = Q[0].astype(np.float64) @ hc.k_hat[:S].astype(np.float64).T / 8.0 + np.log(hc.count[:S])
+    np.testing.assert_allclose(lse, np.log(np.exp(z).sum(axis=1)), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- matching
+
+def _snapshot(hc):
+    S = hc.n_live
+    return hc.k_hat[:S].astype(np.float64).copy(), hc.codes[:S].copy()
+
+
+def _bruteforce_best(x, keys, allowed):
+    """argmax of cosine over allowed rows, computed on normalised matrices."""
+    idx = np.flatnonzero(allowed)
+    if idx.size == 0:
+        return -1, None
+    kn = keys[idx] / np.maximum(np.linalg.norm(keys[idx], axis=1, keepdims=True), 1e-300)
+    c = kn @ (x / np.linalg.norm(x))
+    top = c.max()
+    # lowest id among (numerically) equal maxima
+    return int(idx[np.flatnonzero(c >= top - 1e-12)[0]]), top
+
+
+def test_zero_bits_is_bruteforce_top1():
+    """b = 0: every live slot shares the single bucket, so match = global top-1."""
+    w = WORKLOADS["tiny"].with_(bits=0)
+    st = DriftStream(w)
+    hc = TempCacheOracle.for_workload(w, st.planes()).heads[0]
+    checked = 0
+    for _ in range(4):
+        K, V, _, _ = st.next_frame()
+        keys, _ = _snapshot(hc)
+        allowed = np.ones(keys.shape[0], dtype=bool)
+        res = hc.process_frame(K[0], V[0])
+        for i in range(K.shape[1]):
+            b, _ = _bruteforce_best(K[0, i].astype(np.float64), keys, allowed)
+            assert res.best_slot[i] == b
+            checked += keys.shape[0] > 0
+    assert checked > 0
+
+
+def test_bucketed_match_is_restricted_bruteforce():
+    """Match = brute-force top-1 over slots sharing a code in any table."""
+    w = WORKLOADS["tiny"].with_(tables=3, bits=6)
+    st = DriftStream(w)
+    hc = TempCacheOracle.for_workload(w, st.planes()).heads[0]
+    found_global = 0
+    for _ in range(5):
+        K, V, _, cat = st.next_frame()
+        keys, codes = _snapshot(hc)
+        res = hc.process_frame(K[0], V[0])
+        for i in range(K.shape[1]):
+            allowed = (codes == res.codes[i][None, :]).any(axis=1)
+            assert res.n_candidates[i] == allowed.sum()
+            b, _ = _bruteforce_best(K[0, i].astype(np.float64), keys, allowed)
+            assert res.best_slot[i] == b
+            if keys.shape[0]:
+                g, _ = _bruteforce_best(K[0, i].astype(np.float64), keys,
+                                        np.ones(keys.shape[0], dtype=bool))
+                if allowed[g]:
+                    assert res.best_slot[i] == g
+                    found_global += 1
+    assert found_global > 100
+
+
+def test_exact_copies_merge():
+    w = WORKLOADS["tiny"]
+    st = DriftStream(w)
+    hc = TempCacheOracle.for_workload(w, st.planes()).heads[0]
+    for f in range(5):
+        K, V, _, cat = st.next_frame()
+        res = hc.process_frame(K[0], V[0])
+        if f:
+            # an exact copy always finds the slot its source went to (same key
+            # bits, so the same codes) and is similar enough to merge
+            assert res.merged[cat == 0].all()
+            assert (res.best_cos[cat == 0] >= w.threshold).all()
+
+
+# ---------------------------------------------------------------- merge / evict invariants
+
+def test_conservation_and_contiguity_under_eviction():
+    w = WORKLOADS["tiny"].with_(budget=100)
+    st = DriftStream(w)
+    hc = TempCacheOracle.for_workload(w, st.planes()).heads[0]
+    total_evicted = 0
+    for f in range(12):
+        K, V, _, _ = st.next_frame()
+        before_last = hc.last.copy()
+        res = hc.process_frame(K[0], V[0])
+        assert hc.count[:hc.n_live].sum() + hc.evicted_tokens == hc.tokens_seen
+        assert hc.n_live <= hc.B
+        assert (hc.count[:hc.n_live] >= 1).all()
+        if res.evicted:
+            total_evicted += len(res.evicted)
+            merged_slots = set(res.best_slot[res.merged].tolist())
+            assert not merged_slots & set(res.evicted)
+            # evicted = the smallest (last, id) among slots not merged this frame
+            elig = sorted((int(before_last[s]), s) for s in range(hc.B) if s not in merged_slots)
+            assert sorted(res.evicted) == sorted(s for _, s in elig[:len(res.evicted)])
+    assert total_evicted > 0 and hc.n_live == hc.B
+
+
+def test_member_means_match_masters():
+    """fp64 mean over each slot's members equals the fp32 running mean (1e-5 rel)."""
+    w = WORKLOADS["tiny"].with_(budget=120)
+    st = DriftStream(w)
+    hc = TempCacheOracle.for_workload(w, st.planes()).heads[0]
+    frames_k, frames_v = [], []
+    for _ in range(8):
+        K, V, _, _ = st.next_frame()
+        frames_k.append(K[0])
+        frames_v.append(V[0])
+        hc.process_frame(K[0], V[0])
+    multi = 0
+    for s in range(hc.n_live):
+        mem = hc.members[s]
+        assert len(mem) == hc.count[s]
+        mk = np.mean([frames_k[f][i].astype(np.float64) for f, i in mem], axis=0)
+        mv = np.mean([frames_v[f][i].astype(np.float64) for f, i in mem], axis=0)
+        scale_k = max(1.0, np.abs(mk).max())
+        scale_v = max(1.0, np.abs(mv).max())
+        assert np.abs(hc.K_m[s] - mk).max() <= 1e-5 * scale_k
+        assert np.abs(hc.V_m[s] - mv).max() <= 1e-5 * scale_v
+        multi += len(mem) > 1
+    assert multi > 20
+
+
+def test_bf16_mirror_is_rounded_master():
+    w = WORKLOADS["dit1.3b"].with_(heads=1, tokens_per_frame=128, budget=512)
+    orc, _, _, _ = _run_stream(w, 4)
+    hc = orc.heads[0]
+    S = hc.n_live
+    ref = torch.from_numpy(hc.K_m[:S]).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(hc.k_hat[:S], ref)
+
+
+# ---------------------------------------------------------------- AnnCA
+
+def test_annca_selection_bruteforce_pairs():
+    rng = np.random.default_rng(3)
+    cq = rng.integers(0, 6, size=(40, 3)).astype(np.uint32)
+    cp = rng.integers(0, 6, size=(30, 3)).astype(np.uint32)
+    sel = oannca.select(cq, cp)
+    ref = [j for j in range(30) if any(cp[j, t] == cq[i, t] for i in range(40) for t in range(3))]
+    assert sel.tolist() == ref
+
+
+def test_annca_zero_bits_selects_all_and_equals_dense():
+    cp = ClusterPrompt(heads=1, queries_per_frame=64, frames=1, bits=0)
+    r = oannca.annca_frame(cp.Q[0], cp.Kp[0], cp.Vp[0], cp.planes())
+    assert r["sel"].size == cp.prompt_tokens
+    np.testing.assert_array_equal(r["o_sparse"], r["o_dense"])
+    ref = _sdpa(cp.Q[0], cp.Kp[0], cp.Vp[0], scale=1 / math.sqrt(128))
+    np.testing.assert_allclose(r["o_dense"], ref, atol=1e-12)
+
+
+def test_annca_sparse_is_masked_dense_and_bounded():
+    cp = ClusterPrompt(heads=1, queries_per_frame=200, frames=1)
+    r = oannca.annca_frame(cp.Q[0], cp.Kp[0], cp.Vp[0], cp.planes())
+    keep = np.zeros(cp.prompt_tokens, dtype=bool)
+    keep[r["sel"]] = True
+    assert 0 < keep.sum() < cp.prompt_tokens
+    mask = np.where(keep, 0.0, -np.inf)[None, :].repeat(200, axis=0)
+    ref = _sdpa(cp.Q[0], cp.Kp[0], cp.Vp[0], scale=1 / math.sqrt(128), mask=mask)
+    np.testing.assert_allclose(r["o_sparse"], ref, atol=1e-12)
+    vmax = np.abs(cp.Vp[0]).max()
+    err = np.abs(r["o_sparse"] - r["o_dense"]).max(axis=1)
+    assert (err <= 2 * r["delta"] * vmax + 1e-12).all()
