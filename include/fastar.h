@@ -1,0 +1,220 @@
+/*
+ * fastar.h -- C ABI of the TempCache compressed-KV attention step on gfx950.
+ *
+ * The operation (FAST-AR technical summary, gist.science, Portuguese page and
+ * its French twin, section "2. Componentes Principais / A. TempCache"): each
+ * new token's key is matched top-1 against the cached keys through a
+ * locality-sensitive hash instead of full attention matrices; a match above a
+ * similarity threshold is merged into the cached slot, which keeps the mean of
+ * the merged values and the group size; attention then shifts each slot's logit
+ * by the log of its group size, which Lemma 5.1 shows is exact for identical
+ * keys; the cache is bounded so memory and latency stay constant.  AnnCA
+ * (section "2. Componentes Principais / B. AnnCA") keeps, per frame, only the
+ * prompt tokens that share a hash bucket with at least one query of the frame.
+ *
+ * Readings of what the pages leave open, fixed by this library:
+ *   - hash: SimHash, L tables of b random hyperplanes; bit j of table t is
+ *     [<r_tj, x> > 0], stored as (1u << j) of one uint32 per table;
+ *   - candidates: live slots whose code equals the token's code in any table;
+ *     top-1 by cosine against the slot's stored key, ties to the lowest slot;
+ *   - merge iff cosine >= cos_threshold; merged key and value are running means
+ *     kept in binary32 (m += (x - m) / (count + 1), one rounded op at a time,
+ *     tokens of a frame in ascending order), mirrored in the storage dtype;
+ *   - eviction when a frame's inserts exceed the free slots: exactly the missing
+ *     number of slots not merged into in this frame, smallest
+ *     (last updated frame, slot id) first; inserts take the freed and then the
+ *     never-used ids in ascending order, so the live slots are always
+ *     [0, n_live);
+ *   - merged slots are re-hashed from their new stored key after each frame;
+ *   - attention: logit = <q, k_s> * scale + ln(count_s), softmax over the live
+ *     slots, output = sum_s p_s v_s.
+ *
+ * Conventions for every call:
+ *   - Pointers named *_dev are device memory owned by the caller; pointers
+ *     named *_host are host memory owned by the caller.  The library never
+ *     frees caller memory and never allocates device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; pointers must stay valid until
+ *     that work has completed.  Calls that read results back to the host say
+ *     so and synchronise the stream.
+ *   - Tensors are row-major with the last (feature) dimension contiguous;
+ *     strides are in elements.  Storage dtype FASTAR_BF16 means raw bfloat16
+ *     (16-bit) elements, FASTAR_F32 binary32.
+ *   - Every call returns a status.  Argument errors are detected on the host
+ *     before anything is enqueued and leave all state unchanged.  A HIP launch
+ *     error returns FASTAR_ERR_HIP; a device fault surfaces at the next
+ *     synchronising call.  fastar_last_error() gives a thread-local message.
+ *   - One cache handle must not be used from two streams at once.
+ */
+#ifndef FASTAR_H
+#define FASTAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FASTAR_OK = 0,
+  FASTAR_ERR_INVALID_ARGUMENT = 1,
+  FASTAR_ERR_WORKSPACE_TOO_SMALL = 2,
+  FASTAR_ERR_CAPACITY = 3,
+  FASTAR_ERR_HIP = 4,
+  FASTAR_ERR_UNSUPPORTED = 5
+} fastar_status;
+
+typedef enum { FASTAR_F32 = 0, FASTAR_BF16 = 1 } fastar_dtype;
+
+/* Limits checked by every call. */
+#define FASTAR_MAX_TABLES 8
+#define FASTAR_MAX_BITS 32
+#define FASTAR_MAX_BUDGET 32768
+#define FASTAR_MAX_TOKENS_PER_FRAME 8192
+#define FASTAR_MAX_ANNCA_QUERIES_PER_FRAME 4096
+#define FASTAR_MAX_ANNCA_PROMPT 16384
+
+typedef struct {
+  int32_t num_heads;     /* H >= 1; heads never interact                      */
+  int32_t head_dim;      /* d: 64 or 128                                       */
+  int32_t budget_slots;  /* B: slots per head, 1..FASTAR_MAX_BUDGET            */
+  int32_t num_tables;    /* L: 1..FASTAR_MAX_TABLES                            */
+  int32_t num_bits;      /* b: 0..FASTAR_MAX_BITS (0 = one bucket per table)    */
+  float cos_threshold;   /* merge iff cosine >= this (any finite value)         */
+  fastar_dtype dtype;    /* storage dtype of keys, values, queries, outputs    */
+} fastar_config;
+
+typedef struct fastar_cache_s* fastar_cache_t;
+
+/* Totals over all heads since create/reset (or as imported). */
+typedef struct {
+  int64_t frame;           /* frames merged so far                            */
+  int64_t tokens_seen;     /* tokens passed to fastar_match_merge             */
+  int64_t live_slots;      /* sum of n_live                                   */
+  int64_t merged_tokens;   /* tokens merged into an existing slot             */
+  int64_t inserted_tokens; /* tokens that took a new slot                     */
+  int64_t evicted_slots;   /* slots evicted to make room                      */
+  int64_t evicted_tokens;  /* tokens those slots held (sum of their counts)   */
+  int32_t max_live;        /* largest n_live over heads                       */
+  int32_t reserved;
+} fastar_stats;
+
+/* Host-side image of a cache's state; any pointer may be NULL to skip it.
+ * Shapes: k/v_master float [H][B][d]; k/v_mirror dtype [H][B][d];
+ * count, last int32 [H][B]; codes uint32 [H][L][B]; n_live int32 [H];
+ * evicted_tokens int64 [H]. */
+typedef struct {
+  float* k_master;
+  float* v_master;
+  void* k_mirror;
+  void* v_mirror;
+  int32_t* count;
+  int32_t* last;
+  uint32_t* codes;
+  int32_t* n_live;
+  int64_t* evicted_tokens;
+  int64_t frame;
+} fastar_cache_state;
+
+/* Thread-local text of the last error (empty string if none). */
+const char* fastar_last_error(void);
+
+/* Bytes of device workspace a cache with this configuration needs (host only). */
+fastar_status fastar_cache_workspace_bytes(const fastar_config* cfg, size_t* bytes);
+
+/* Create a cache in caller-provided device memory.
+ * planes_host: the SimHash hyperplanes, [L][b][d] in cfg->dtype, copied into
+ * the workspace.  workspace_dev: at least fastar_cache_workspace_bytes bytes,
+ * 256-byte aligned, kept alive by the caller until fastar_cache_destroy.
+ * The cache starts empty (n_live = 0, frame = 0).  Returns
+ * FASTAR_ERR_UNSUPPORTED if the current device is not gfx950.  On success
+ * *out is a host handle owned by the library. */
+fastar_status fastar_cache_create(const fastar_config* cfg, const void* planes_host,
+                                  void* workspace_dev, size_t workspace_bytes, void* stream,
+                                  fastar_cache_t* out);
+
+/* Free the host handle (the workspace stays the caller's). */
+fastar_status fastar_cache_destroy(fastar_cache_t cache);
+
+/* Empty the cache (state zeroed, frame = 0) on `stream`. */
+fastar_status fastar_cache_reset(fastar_cache_t cache, void* stream);
+
+/* Device pointer of the cache's hyperplanes ([L][b][d], cfg dtype). */
+fastar_status fastar_cache_planes(fastar_cache_t cache, const void** planes_dev);
+
+/* SimHash codes of H x N vectors (section 2A "Mecanismo": LSH as the ANN).
+ * x_dev: element (h, n, k) at x_dev[h*stride_h + n*stride_n + k], d in {64,128}.
+ * planes_dev: [L][b][d], same dtype as x.  codes_dev: uint32 [H][L][N]
+ * (bits above b are 0; b = 0 gives all-zero codes).  Stateless. */
+fastar_status fastar_hash(const void* x_dev, fastar_dtype dtype, int32_t H, int32_t N, int32_t d,
+                          int64_t stride_h, int64_t stride_n, const void* planes_dev, int32_t L,
+                          int32_t b, uint32_t* codes_dev, void* stream);
+
+/* Match, merge, evict, insert and re-hash `num_frames` frames of new tokens
+ * (section 2A: top-1 match against previous frames, merge above a threshold,
+ * bounded cache).  Frames are processed in order; frame f sees the state left
+ * by frame f-1 (including earlier frames of the same call), never its own
+ * tokens.  Token i of frame f of head h is k_dev/v_dev[h*stride_h +
+ * (f*tokens_per_frame + i)*stride_n + k] (cfg dtype).  codes_dev: uint32
+ * [H][L][num_frames*tokens_per_frame] codes of those keys, or NULL to hash them
+ * here with the cache's hyperplanes.  Optional outputs, [H][num_frames *
+ * tokens_per_frame]: slot_out_dev (slot each token ended in), merged_out_dev (1
+ * if merged into an existing slot).  Requires tokens_per_frame <= budget and
+ * <= FASTAR_MAX_TOKENS_PER_FRAME (then eviction always finds room). */
+fastar_status fastar_match_merge(fastar_cache_t cache, const void* k_dev, const void* v_dev,
+                                 int64_t stride_h, int64_t stride_n, const uint32_t* codes_dev,
+                                 int32_t tokens_per_frame, int32_t num_frames,
+                                 int32_t* slot_out_dev, uint8_t* merged_out_dev, void* stream);
+
+/* Attention of Nq queries per head over the live slots (section 2A, Lemma 5.1:
+ * logits shifted by the group size).  q_dev: (h, n, k) at q_dev[h*stride_h +
+ * n*stride_n + k]; o_dev likewise with o_stride_h, o_stride_n (cfg dtype);
+ * scale: logit scale, 0 means 1/sqrt(d); lse_dev: optional float [H][Nq],
+ * natural-log partition function.  An empty cache gives zero outputs and
+ * lse = -inf. */
+fastar_status fastar_attend(fastar_cache_t cache, const void* q_dev, int64_t stride_h,
+                            int64_t stride_n, int32_t Nq, float scale, void* o_dev,
+                            int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream);
+
+/* Totals over heads.  Synchronises `stream`. */
+fastar_status fastar_cache_stats(fastar_cache_t cache, void* stream, fastar_stats* out);
+
+/* Copy the state to host buffers.  Synchronises `stream`. */
+fastar_status fastar_cache_export(fastar_cache_t cache, void* stream, fastar_cache_state* out);
+
+/* Overwrite the state from host buffers (NULL members keep the current
+ * contents), then rebuild the bucket index.  Synchronises `stream`. */
+fastar_status fastar_cache_import(fastar_cache_t cache, const fastar_cache_state* in, void* stream);
+
+/* AnnCA selection (section 2B: keep the prompt tokens that share a bucket with
+ * at least one query of the frame).  q_codes_dev: uint32 [H][L][F*Nf] codes of
+ * the queries, frame g = columns [g*Nf, (g+1)*Nf); p_codes_dev: uint32
+ * [H][L][Np] codes of the prompt keys.  Outputs: sel_idx_dev int32
+ * [H][F][Np], the kept prompt ids of (h, g) in ascending order in the first
+ * sel_count_dev[h*F + g] entries (the rest unspecified).  Requires
+ * Nf <= FASTAR_MAX_ANNCA_QUERIES_PER_FRAME, Np <= FASTAR_MAX_ANNCA_PROMPT. */
+fastar_status fastar_annca_select(const uint32_t* q_codes_dev, int32_t Nf, int32_t F,
+                                  const uint32_t* p_codes_dev, int32_t Np, int32_t H, int32_t L,
+                                  int32_t* sel_idx_dev, int32_t* sel_count_dev, void* stream);
+
+/* Softmax attention of each frame's queries over a per-frame subset of keys
+ * (section 2B: attention over the kept prompt tokens only; no logit bias).
+ * q_dev (h, g*Nf + i, k); k_dev, v_dev (h, j, k) for j < Np with strides
+ * kv_stride_h, kv_stride_n; sel_idx_dev / sel_count_dev as produced by
+ * fastar_annca_select, or both NULL to attend over all Np keys (dense);
+ * o_dev like q_dev with o strides.  A frame with an empty subset gets zero
+ * outputs.  scale 0 means 1/sqrt(d). */
+fastar_status fastar_attend_subset(const void* q_dev, int64_t q_stride_h, int64_t q_stride_n,
+                                   const void* k_dev, const void* v_dev, int64_t kv_stride_h,
+                                   int64_t kv_stride_n, const int32_t* sel_idx_dev,
+                                   const int32_t* sel_count_dev, int32_t Nf, int32_t F, int32_t Np,
+                                   int32_t H, int32_t d, fastar_dtype dtype, float scale,
+                                   void* o_dev, int64_t o_stride_h, int64_t o_stride_n,
+                                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FASTAR_H */

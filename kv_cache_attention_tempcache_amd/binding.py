@@ -1,0 +1,367 @@
+"""ctypes binding of libfastar.so: argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI (include/fastar.h).
+torch supplies device memory and streams; this module checks tensor shapes,
+dtypes and devices, passes raw pointers and the current stream, and turns
+non-zero status codes into exceptions.  If the library is not built, every
+entry point raises: there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch  # imported before the library so both share torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfastar.so")
+
+F32, BF16 = 0, 1
+_DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16)}
+
+STATUS = {
+    0: "FASTAR_OK",
+    1: "FASTAR_ERR_INVALID_ARGUMENT",
+    2: "FASTAR_ERR_WORKSPACE_TOO_SMALL",
+    3: "FASTAR_ERR_CAPACITY",
+    4: "FASTAR_ERR_HIP",
+    5: "FASTAR_ERR_UNSUPPORTED",
+}
+
+
+class FastarError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("budget_slots", ctypes.c_int32), ("num_tables", ctypes.c_int32),
+                ("num_bits", ctypes.c_int32), ("cos_threshold", ctypes.c_float),
+                ("dtype", ctypes.c_int)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("frame", ctypes.c_int64), ("tokens_seen", ctypes.c_int64),
+                ("live_slots", ctypes.c_int64), ("merged_tokens", ctypes.c_int64),
+                ("inserted_tokens", ctypes.c_int64), ("evicted_slots", ctypes.c_int64),
+                ("evicted_tokens", ctypes.c_int64), ("max_live", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class State(ctypes.Structure):
+    _fields_ = [("k_master", ctypes.c_void_p), ("v_master", ctypes.c_void_p),
+                ("k_mirror", ctypes.c_void_p), ("v_mirror", ctypes.c_void_p),
+                ("count", ctypes.c_void_p), ("last", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("n_live", ctypes.c_void_p),
+                ("evicted_tokens", ctypes.c_void_p), ("frame", ctypes.c_int64)]
+
+
+# name -> (restype, argtypes); the C ABI of include/fastar.h
+_VP, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "fastar_last_error": (ctypes.c_char_p, []),
+    "fastar_cache_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(_SZ)]),
+    "fastar_cache_create": (ctypes.c_int, [ctypes.POINTER(Config), _VP, _VP, _SZ, _VP,
+                                           ctypes.POINTER(_VP)]),
+    "fastar_cache_destroy": (ctypes.c_int, [_VP]),
+    "fastar_cache_reset": (ctypes.c_int, [_VP, _VP]),
+    "fastar_cache_planes": (ctypes.c_int, [_VP, ctypes.POINTER(_VP)]),
+    "fastar_hash": (ctypes.c_int, [_VP, ctypes.c_int, _I32, _I32, _I32, _I64, _I64, _VP, _I32,
+                                   _I32, _VP, _VP]),
+    "fastar_match_merge": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _VP, _I32, _I32, _VP, _VP,
+                                          _VP]),
+    "fastar_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _F, _VP, _I64, _I64, _VP, _VP]),
+    "fastar_cache_stats": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(Stats)]),
+    "fastar_cache_export": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(State)]),
+    "fastar_cache_import": (ctypes.c_int, [_VP, ctypes.POINTER(State), _VP]),
+    "fastar_annca_select": (ctypes.c_int, [_VP, _I32, _I32, _VP, _I32, _I32, _I32, _VP, _VP,
+                                           _VP]),
+    "fastar_attend_subset": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _I64, _I64, _VP, _VP,
+                                            _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _F, _VP,
+                                            _I64, _I64, _VP]),
+}
+
+_lib = None
+
+
+def library():
+    """Load libfastar.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m kv_cache_attention_tempcache_amd.build)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = library().fastar_last_error().decode(errors="replace")
+        raise FastarError(status, msg)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() >= 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+
+
+def storage_dtype(dtype: str):
+    return _DTYPES[dtype]
+
+
+def planes_to_host(planes, dtype: str) -> np.ndarray:
+    """Hyperplanes as a contiguous host array in the storage format."""
+    p = torch.as_tensor(np.asarray(planes, dtype=np.float32))
+    if dtype == "bf16":
+        return p.to(torch.bfloat16).view(torch.int16).numpy().copy()
+    return p.numpy().astype(np.float32, copy=True)
+
+
+def hash_codes(x: torch.Tensor, planes: torch.Tensor, tables: int, bits: int,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """SimHash codes [H][L][N] (uint32 bit patterns in an int32 tensor) of x [H][N][d]."""
+    _require(x, "x")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _require(planes, "planes", x.dtype)
+    H, N, d = x.shape
+    if not planes.is_contiguous() or planes.numel() != tables * bits * d:
+        raise ValueError("planes must be contiguous [L][b][d]")
+    if out is None:
+        out = torch.empty((H, tables, N), dtype=torch.int32, device=x.device)
+    _require(out, "out", torch.int32)
+    dt = BF16 if x.dtype == torch.bfloat16 else F32
+    _check(library().fastar_hash(_ptr(x), dt, H, N, d, x.stride(0), x.stride(1), _ptr(planes),
+                                 tables, bits, _ptr(out), _stream(stream)))
+    return out
+
+
+@dataclass
+class CacheConfig:
+    heads: int
+    head_dim: int
+    budget: int
+    tables: int
+    bits: int
+    threshold: float
+    dtype: str = "bf16"
+
+    def c(self) -> Config:
+        return Config(self.heads, self.head_dim, self.budget, self.tables, self.bits,
+                      float(self.threshold), _DTYPES[self.dtype][0])
+
+
+def workspace_bytes(cfg: CacheConfig) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(library().fastar_cache_workspace_bytes(ctypes.byref(c), ctypes.byref(n)))
+    return n.value
+
+
+class Cache:
+    """A TempCache over a caller-owned device workspace (a torch uint8 tensor)."""
+
+    def __init__(self, cfg: CacheConfig, planes, device="cuda", stream=None):
+        self.cfg = cfg
+        self.torch_dtype = _DTYPES[cfg.dtype][1]
+        nbytes = workspace_bytes(cfg)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        host = planes_to_host(planes, cfg.dtype)
+        if host.size != cfg.tables * cfg.bits * cfg.head_dim:
+            raise ValueError("planes must have tables*bits*head_dim elements")
+        c = cfg.c()
+        h = ctypes.c_void_p(0)
+        _check(library().fastar_cache_create(ctypes.byref(c), host.ctypes.data,
+                                             _ptr(self.workspace), nbytes, _stream(stream),
+                                             ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            library().fastar_cache_destroy(self._h)
+            self._h = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    def planes_device(self) -> int:
+        p = ctypes.c_void_p(0)
+        _check(library().fastar_cache_planes(self._h, ctypes.byref(p)))
+        return p.value
+
+    def reset(self, stream=None):
+        _check(library().fastar_cache_reset(self._h, _stream(stream)))
+
+    def match_merge(self, k: torch.Tensor, v: torch.Tensor, tokens_per_frame: int,
+                    num_frames: int = 1, codes: torch.Tensor | None = None,
+                    slot_out: torch.Tensor | None = None, merged_out: torch.Tensor | None = None,
+                    stream=None):
+        """Merge num_frames frames of new keys/values [H][F*T][d] into the cache."""
+        _require(k, "k", self.torch_dtype)
+        _require(v, "v", self.torch_dtype)
+        if k.shape != v.shape or k.stride() != v.stride():
+            raise ValueError("k and v must have the same shape and strides")
+        H, N, d = k.shape
+        if H != self.cfg.heads or d != self.cfg.head_dim or N != tokens_per_frame * num_frames:
+            raise ValueError("k must be [heads][tokens_per_frame*num_frames][head_dim]")
+        if codes is not None:
+            _require(codes, "codes", torch.int32)
+            if tuple(codes.shape) != (H, self.cfg.tables, N) or not codes.is_contiguous():
+                raise ValueError("codes must be contiguous [H][L][N]")
+        for t, name, dt in ((slot_out, "slot_out", torch.int32), (merged_out, "merged_out", torch.uint8)):
+            if t is not None:
+                _require(t, name, dt)
+                if tuple(t.shape) != (H, N) or not t.is_contiguous():
+                    raise ValueError(f"{name} must be contiguous [H][N]")
+        _check(library().fastar_match_merge(self._h, _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+                                            _ptr(codes), tokens_per_frame, num_frames,
+                                            _ptr(slot_out), _ptr(merged_out), _stream(stream)))
+
+    def attend(self, q: torch.Tensor, scale: float = 0.0, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Attention of q [H][Nq][d] over the live slots with the ln(count) bias."""
+        _require(q, "q", self.torch_dtype)
+        H, Nq, d = q.shape
+        if H != self.cfg.heads or d != self.cfg.head_dim:
+            raise ValueError("q must be [heads][Nq][head_dim]")
+        if out is None:
+            out = torch.empty((H, Nq, d), dtype=self.torch_dtype, device=q.device)
+        _require(out, "out", self.torch_dtype)
+        if lse is not None:
+            _require(lse, "lse", torch.float32)
+            if tuple(lse.shape) != (H, Nq) or not lse.is_contiguous():
+                raise ValueError("lse must be contiguous [H][Nq]")
+        _check(library().fastar_attend(self._h, _ptr(q), q.stride(0), q.stride(1), Nq,
+                                       float(scale), _ptr(out), out.stride(0), out.stride(1),
+                                       _ptr(lse), _stream(stream)))
+        return out
+
+    def stats(self, stream=None) -> dict:
+        st = Stats()
+        _check(library().fastar_cache_stats(self._h, _stream(stream), ctypes.byref(st)))
+        return {name: getattr(st, name) for name, _ in Stats._fields_ if name != "reserved"}
+
+    def export_state(self, stream=None) -> dict:
+        c = self.cfg
+        H, B, d, L = c.heads, c.budget, c.head_dim, c.tables
+        mir = np.uint16 if c.dtype == "bf16" else np.float32
+        out = {
+            "k_master": np.empty((H, B, d), np.float32), "v_master": np.empty((H, B, d), np.float32),
+            "k_mirror": np.empty((H, B, d), mir), "v_mirror": np.empty((H, B, d), mir),
+            "count": np.empty((H, B), np.int32), "last": np.empty((H, B), np.int32),
+            "codes": np.empty((H, L, B), np.uint32), "n_live": np.empty(H, np.int32),
+            "evicted_tokens": np.empty(H, np.int64),
+        }
+        st = State(*[out[name].ctypes.data for name, _ in State._fields_[:-1]], 0)
+        _check(library().fastar_cache_export(self._h, _stream(stream), ctypes.byref(st)))
+        out["frame"] = int(st.frame)
+        return out
+
+    def import_state(self, state: dict, stream=None):
+        c = self.cfg
+        H, B, d, L = c.heads, c.budget, c.head_dim, c.tables
+        mir = np.uint16 if c.dtype == "bf16" else np.float32
+        spec = {"k_master": ((H, B, d), np.float32), "v_master": ((H, B, d), np.float32),
+                "k_mirror": ((H, B, d), mir), "v_mirror": ((H, B, d), mir),
+                "count": ((H, B), np.int32), "last": ((H, B), np.int32),
+                "codes": ((H, L, B), np.uint32), "n_live": ((H,), np.int32),
+                "evicted_tokens": ((H,), np.int64)}
+        keep = {}
+        ptrs = []
+        for name, _ in State._fields_[:-1]:
+            arr = state.get(name)
+            if arr is None:
+                ptrs.append(None)
+                continue
+            shape, dt = spec[name]
+            a = np.ascontiguousarray(arr, dtype=dt)
+            if a.shape != shape:
+                raise ValueError(f"{name} must have shape {shape}, got {a.shape}")
+            keep[name] = a
+            ptrs.append(a.ctypes.data)
+        st = State(*ptrs, int(state.get("frame", 0)))
+        _check(library().fastar_cache_import(self._h, ctypes.byref(st), _stream(stream)))
+
+
+def annca_select(q_codes: torch.Tensor, p_codes: torch.Tensor, frames: int,
+                 sel_idx: torch.Tensor | None = None, sel_count: torch.Tensor | None = None,
+                 stream=None):
+    """Per-frame kept prompt ids: (sel_idx [H][F][Np], sel_count [H][F])."""
+    _require(q_codes, "q_codes", torch.int32)
+    _require(p_codes, "p_codes", torch.int32)
+    H, L, NQ = q_codes.shape
+    Hp, Lp, Np = p_codes.shape
+    if (Hp, Lp) != (H, L) or NQ % frames:
+        raise ValueError("q_codes [H][L][F*Nf] and p_codes [H][L][Np] disagree")
+    if not (q_codes.is_contiguous() and p_codes.is_contiguous()):
+        raise ValueError("codes must be contiguous")
+    if sel_idx is None:
+        sel_idx = torch.empty((H, frames, Np), dtype=torch.int32, device=q_codes.device)
+    if sel_count is None:
+        sel_count = torch.empty((H, frames), dtype=torch.int32, device=q_codes.device)
+    _check(library().fastar_annca_select(_ptr(q_codes), NQ // frames, frames, _ptr(p_codes), Np,
+                                         H, L, _ptr(sel_idx), _ptr(sel_count), _stream(stream)))
+    return sel_idx, sel_count
+
+
+def attend_subset(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, frames: int,
+                  sel_idx: torch.Tensor | None = None, sel_count: torch.Tensor | None = None,
+                  scale: float = 0.0, out: torch.Tensor | None = None, stream=None):
+    """Each frame's queries attend over its kept prompt keys (or all, if no selection)."""
+    _require(q, "q")
+    _require(k, "k", q.dtype)
+    _require(v, "v", q.dtype)
+    H, NQ, d = q.shape
+    Np = k.shape[1]
+    if k.shape != v.shape or k.stride() != v.stride() or NQ % frames:
+        raise ValueError("bad shapes")
+    if (sel_idx is None) != (sel_count is None):
+        raise ValueError("sel_idx and sel_count go together")
+    if sel_idx is not None:
+        _require(sel_idx, "sel_idx", torch.int32)
+        _require(sel_count, "sel_count", torch.int32)
+        if tuple(sel_idx.shape) != (H, frames, Np) or tuple(sel_count.shape) != (H, frames):
+            raise ValueError("selection shapes disagree with q/k")
+    if out is None:
+        out = torch.empty_like(q)
+    dt = BF16 if q.dtype == torch.bfloat16 else F32
+    _check(library().fastar_attend_subset(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+        _ptr(sel_idx), _ptr(sel_count), NQ // frames, frames, Np, H, d, dt, float(scale),
+        _ptr(out), out.stride(0), out.stride(1), _stream(stream)))
+    return out

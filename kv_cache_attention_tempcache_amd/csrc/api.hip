@@ -1,0 +1,560 @@
+// Host side of the C ABI declared in fastar.h: argument validation, the
+// workspace layout of a cache, and the launch sequence of one chunk step.
+// Nothing here allocates device memory; every launch goes on the caller's
+// stream and nothing synchronises except create, stats, export and import.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "common.hpp"
+#include "fastar.h"
+
+using namespace fastar;
+
+struct fastar_cache_s {
+  fastar_config cfg;
+  Dims dm;
+  CacheDev dev;
+  Layout lay;
+  void* ws;
+  size_t ws_bytes;
+  int device;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+fastar_status fail(fastar_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+fastar_status ok() {
+  g_err.clear();
+  return FASTAR_OK;
+}
+
+#define FASTAR_HIP(expr)                                                              \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(FASTAR_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+#define FASTAR_REQUIRE(cond, msg) \
+  do {                            \
+    if (!(cond)) return fail(FASTAR_ERR_INVALID_ARGUMENT, msg); \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(fastar_dtype dt) { return dt == FASTAR_BF16 ? 2 : 4; }
+
+bool valid_dtype(fastar_dtype dt) { return dt == FASTAR_F32 || dt == FASTAR_BF16; }
+
+fastar_status make_dims(const fastar_config* cfg, Dims* dm) {
+  FASTAR_REQUIRE(cfg != nullptr, "config is NULL");
+  FASTAR_REQUIRE(cfg->num_heads >= 1, "num_heads must be >= 1");
+  FASTAR_REQUIRE(cfg->head_dim == 64 || cfg->head_dim == 128, "head_dim must be 64 or 128");
+  FASTAR_REQUIRE(cfg->budget_slots >= 1 && cfg->budget_slots <= FASTAR_MAX_BUDGET,
+                 "budget_slots out of range");
+  FASTAR_REQUIRE(cfg->num_tables >= 1 && cfg->num_tables <= FASTAR_MAX_TABLES,
+                 "num_tables out of range");
+  FASTAR_REQUIRE(cfg->num_bits >= 0 && cfg->num_bits <= FASTAR_MAX_BITS, "num_bits out of range");
+  FASTAR_REQUIRE(std::isfinite(cfg->cos_threshold), "cos_threshold must be finite");
+  FASTAR_REQUIRE(valid_dtype(cfg->dtype), "unknown dtype");
+  dm->H = cfg->num_heads;
+  dm->d = cfg->head_dim;
+  dm->B = cfg->budget_slots;
+  dm->L = cfg->num_tables;
+  dm->b = cfg->num_bits;
+  dm->elem = elem_bytes(cfg->dtype);
+  int nb = 6;  // at least 64 buckets
+  while ((1 << nb) < dm->B) ++nb;
+  dm->nb_bits = nb;
+  dm->NB = 1 << nb;
+  dm->Ppad = (dm->L * dm->b + 31) & ~31;
+  return FASTAR_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+enum Region {
+  kPlanes, kKMaster, kVMaster, kKMirror, kVMirror, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
+  kNLive, kEvicted, kCounters, kFrame, kStateEnd = kFrame,
+  kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupStart, kGroupSlot, kInsTok, kInsSlot,
+  kPlan, kNumRegions
+};
+
+fastar_status check_device_gfx950(int* device) {
+  FASTAR_HIP(hipGetDevice(device));
+  hipDeviceProp_t prop;
+  FASTAR_HIP(hipGetDeviceProperties(&prop, *device));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(FASTAR_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName +
+                                            ", this library is built for gfx950");
+  return FASTAR_OK;
+}
+
+__global__ void zero_kernel(uint4* p, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Zero [ptr, ptr+bytes) with a kernel (bytes and ptr are 256-byte aligned).
+hipError_t zero_bytes(void* ptr, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<uint4*>(ptr), n16);
+  return hipGetLastError();
+}
+
+fastar_status check_handle(fastar_cache_t c) {
+  if (c == nullptr) return fail(FASTAR_ERR_INVALID_ARGUMENT, "cache handle is NULL");
+  return FASTAR_OK;
+}
+
+}  // namespace
+
+namespace fastar {
+
+Layout make_layout(const Dims& dm) {
+  Layout L{};
+  const size_t H = dm.H, B = dm.B, d = dm.d, Lt = dm.L, e = dm.elem;
+  size_t sizes[kNumRegions] = {};
+  sizes[kPlanes] = (size_t)(dm.L * dm.b > 0 ? dm.L * dm.b : 1) * d * e;
+  sizes[kKMaster] = H * B * d * 4;
+  sizes[kVMaster] = H * B * d * 4;
+  sizes[kKMirror] = H * B * d * e;
+  sizes[kVMirror] = H * B * d * e;
+  sizes[kCount] = H * B * 4;
+  sizes[kLast] = H * B * 4;
+  sizes[kCodes] = H * Lt * B * 4;
+  sizes[kIdxOff] = H * Lt * ((size_t)dm.NB + 1) * 4;
+  sizes[kIdxSlot] = H * Lt * B * 4;
+  sizes[kNLive] = H * 4;
+  sizes[kEvicted] = H * 8;
+  sizes[kCounters] = H * kNumCounters * 8;
+  sizes[kFrame] = 4;
+  sizes[kBestSlot] = H * B * 4;
+  sizes[kBestCos] = H * B * 4;
+  sizes[kDec] = H * B * 4;
+  sizes[kFrameCodes] = H * Lt * B * 4;
+  sizes[kGroupTok] = H * B * 4;
+  sizes[kGroupStart] = H * (B + 1) * 4;
+  sizes[kGroupSlot] = H * B * 4;
+  sizes[kInsTok] = H * B * 4;
+  sizes[kInsSlot] = H * B * 4;
+  sizes[kPlan] = H * kPlanStride * 4;
+  size_t off = 0;
+  for (int r = 0; r < kNumRegions; ++r) {
+    L.off[r] = off;
+    off = align256(off + sizes[r]);
+  }
+  L.off[kNumRegions] = off;
+  L.total = off;
+  return L;
+}
+
+CacheDev carve(void* base, const Dims& dm) {
+  const Layout L = make_layout(dm);
+  uint8_t* b = static_cast<uint8_t*>(base);
+  CacheDev c{};
+  c.planes = b + L.off[kPlanes];
+  c.k_master = reinterpret_cast<float*>(b + L.off[kKMaster]);
+  c.v_master = reinterpret_cast<float*>(b + L.off[kVMaster]);
+  c.k_mirror = b + L.off[kKMirror];
+  c.v_mirror = b + L.off[kVMirror];
+  c.count = reinterpret_cast<int32_t*>(b + L.off[kCount]);
+  c.last = reinterpret_cast<int32_t*>(b + L.off[kLast]);
+  c.codes = reinterpret_cast<uint32_t*>(b + L.off[kCodes]);
+  c.idx_off = reinterpret_cast<int32_t*>(b + L.off[kIdxOff]);
+  c.idx_slot = reinterpret_cast<int32_t*>(b + L.off[kIdxSlot]);
+  c.n_live = reinterpret_cast<int32_t*>(b + L.off[kNLive]);
+  c.evicted_tokens = reinterpret_cast<int64_t*>(b + L.off[kEvicted]);
+  c.counters = reinterpret_cast<int64_t*>(b + L.off[kCounters]);
+  c.frame = reinterpret_cast<int32_t*>(b + L.off[kFrame]);
+  c.best_slot = reinterpret_cast<int32_t*>(b + L.off[kBestSlot]);
+  c.best_cos = reinterpret_cast<float*>(b + L.off[kBestCos]);
+  c.dec = reinterpret_cast<int32_t*>(b + L.off[kDec]);
+  c.frame_codes = reinterpret_cast<uint32_t*>(b + L.off[kFrameCodes]);
+  c.group_tok = reinterpret_cast<int32_t*>(b + L.off[kGroupTok]);
+  c.group_start = reinterpret_cast<int32_t*>(b + L.off[kGroupStart]);
+  c.group_slot = reinterpret_cast<int32_t*>(b + L.off[kGroupSlot]);
+  c.ins_tok = reinterpret_cast<int32_t*>(b + L.off[kInsTok]);
+  c.ins_slot = reinterpret_cast<int32_t*>(b + L.off[kInsSlot]);
+  c.plan = reinterpret_cast<int32_t*>(b + L.off[kPlan]);
+  return c;
+}
+
+}  // namespace fastar
+
+extern "C" {
+
+const char* fastar_last_error(void) { return g_err.c_str(); }
+
+fastar_status fastar_cache_workspace_bytes(const fastar_config* cfg, size_t* bytes) {
+  Dims dm;
+  fastar_status st = make_dims(cfg, &dm);
+  if (st != FASTAR_OK) return st;
+  FASTAR_REQUIRE(bytes != nullptr, "bytes is NULL");
+  *bytes = make_layout(dm).total;
+  return ok();
+}
+
+fastar_status fastar_cache_create(const fastar_config* cfg, const void* planes_host,
+                                  void* workspace_dev, size_t workspace_bytes, void* stream,
+                                  fastar_cache_t* out) {
+  Dims dm;
+  fastar_status st = make_dims(cfg, &dm);
+  if (st != FASTAR_OK) return st;
+  FASTAR_REQUIRE(out != nullptr, "out is NULL");
+  FASTAR_REQUIRE(workspace_dev != nullptr, "workspace is NULL");
+  FASTAR_REQUIRE(aligned(workspace_dev, 256), "workspace must be 256-byte aligned");
+  FASTAR_REQUIRE(planes_host != nullptr || dm.L * dm.b == 0, "planes_host is NULL");
+  const Layout lay = make_layout(dm);
+  if (workspace_bytes < lay.total)
+    return fail(FASTAR_ERR_WORKSPACE_TOO_SMALL,
+                "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                    std::to_string(lay.total));
+  int device = 0;
+  st = check_device_gfx950(&device);
+  if (st != FASTAR_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CacheDev dev = carve(workspace_dev, dm);
+  FASTAR_HIP(zero_bytes(workspace_dev, lay.off[kStateEnd + 1], s));
+  const size_t plane_bytes = (size_t)dm.L * dm.b * dm.d * dm.elem;
+  if (plane_bytes) FASTAR_HIP(hipMemcpyAsync(dev.planes, planes_host, plane_bytes,
+                                             hipMemcpyHostToDevice, s));
+  FASTAR_HIP(hipStreamSynchronize(s));
+  fastar_cache_s* c = new fastar_cache_s;
+  c->cfg = *cfg;
+  c->dm = dm;
+  c->dev = dev;
+  c->lay = lay;
+  c->ws = workspace_dev;
+  c->ws_bytes = workspace_bytes;
+  c->device = device;
+  *out = c;
+  return ok();
+}
+
+fastar_status fastar_cache_destroy(fastar_cache_t cache) {
+  delete cache;
+  return ok();
+}
+
+fastar_status fastar_cache_reset(fastar_cache_t c, void* stream) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  uint8_t* b = static_cast<uint8_t*>(c->ws);
+  const size_t lo = c->lay.off[kKMaster], hi = c->lay.off[kStateEnd + 1];
+  FASTAR_HIP(zero_bytes(b + lo, hi - lo, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+fastar_status fastar_cache_planes(fastar_cache_t c, const void** planes_dev) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  FASTAR_REQUIRE(planes_dev != nullptr, "planes_dev is NULL");
+  *planes_dev = c->dev.planes;
+  return ok();
+}
+
+fastar_status fastar_hash(const void* x_dev, fastar_dtype dtype, int32_t H, int32_t N, int32_t d,
+                          int64_t stride_h, int64_t stride_n, const void* planes_dev, int32_t L,
+                          int32_t b, uint32_t* codes_dev, void* stream) {
+  FASTAR_REQUIRE(valid_dtype(dtype), "unknown dtype");
+  FASTAR_REQUIRE(H >= 0 && N >= 0, "H and N must be >= 0");
+  FASTAR_REQUIRE(d == 64 || d == 128, "d must be 64 or 128");
+  FASTAR_REQUIRE(L >= 1 && L <= FASTAR_MAX_TABLES, "L out of range");
+  FASTAR_REQUIRE(b >= 0 && b <= FASTAR_MAX_BITS, "b out of range");
+  if ((int64_t)H * N == 0) return ok();
+  FASTAR_REQUIRE(x_dev && codes_dev, "NULL pointer");
+  FASTAR_REQUIRE(planes_dev != nullptr || b == 0, "planes_dev is NULL");
+  const int vec = dtype == FASTAR_BF16 ? 8 : 4;
+  FASTAR_REQUIRE(aligned(x_dev, 16) && aligned(planes_dev, 16) && aligned(codes_dev, 4),
+                 "x and planes must be 16-byte aligned");
+  FASTAR_REQUIRE(stride_h % vec == 0 && stride_n % vec == 0 && stride_n >= d,
+                 "strides must be multiples of 16 bytes and rows must not overlap");
+  HashArgs a{};
+  a.x = x_dev;
+  a.sx_h = stride_h;
+  a.sx_n = stride_n;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.L = L;
+  a.b = b;
+  a.planes = planes_dev;
+  a.codes = codes_dev;
+  a.codes_ld = N;
+  a.codes_col0 = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FASTAR_HIP(dtype == FASTAR_BF16 ? launch_hash_bf16(a, s) : launch_hash_f32(a, s));
+  return ok();
+}
+
+fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void* v_dev,
+                                 int64_t stride_h, int64_t stride_n, const uint32_t* codes_dev,
+                                 int32_t tokens_per_frame, int32_t num_frames,
+                                 int32_t* slot_out_dev, uint8_t* merged_out_dev, void* stream) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  const Dims& dm = c->dm;
+  const int T = tokens_per_frame, F = num_frames;
+  FASTAR_REQUIRE(T >= 1 && F >= 1, "tokens_per_frame and num_frames must be >= 1");
+  if (T > dm.B || T > FASTAR_MAX_TOKENS_PER_FRAME)
+    return fail(FASTAR_ERR_CAPACITY, "tokens_per_frame " + std::to_string(T) +
+                                         " exceeds the budget or the per-frame limit");
+  FASTAR_REQUIRE(k_dev && v_dev, "k or v is NULL");
+  const int vec = dm.elem == 2 ? 8 : 4;
+  FASTAR_REQUIRE(aligned(k_dev, 16) && aligned(v_dev, 16), "k and v must be 16-byte aligned");
+  FASTAR_REQUIRE(stride_h % vec == 0 && stride_n % vec == 0 && stride_n >= dm.d,
+                 "strides must be multiples of 16 bytes and rows must not overlap");
+  FASTAR_REQUIRE(codes_dev == nullptr || aligned(codes_dev, 4), "codes misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const CacheDev& dev = c->dev;
+  const int64_t N = (int64_t)T * F;
+  for (int f = 0; f < F; ++f) {
+    const int64_t tok0 = (int64_t)f * T;
+    const uint8_t* kf = static_cast<const uint8_t*>(k_dev) + tok0 * stride_n * dm.elem;
+    const uint8_t* vf = static_cast<const uint8_t*>(v_dev) + tok0 * stride_n * dm.elem;
+    const uint32_t* codes = codes_dev;
+    int64_t codes_ld = N, codes_col0 = tok0;
+    if (codes == nullptr) {
+      HashArgs ha{};
+      ha.x = kf;
+      ha.sx_h = stride_h;
+      ha.sx_n = stride_n;
+      ha.H = dm.H;
+      ha.N = T;
+      ha.d = dm.d;
+      ha.L = dm.L;
+      ha.b = dm.b;
+      ha.planes = dev.planes;
+      ha.codes = dev.frame_codes;
+      ha.codes_ld = dm.B;
+      ha.codes_col0 = 0;
+      FASTAR_HIP(dm.elem == 2 ? launch_hash_bf16(ha, s) : launch_hash_f32(ha, s));
+      codes = dev.frame_codes;
+      codes_ld = dm.B;
+      codes_col0 = 0;
+    }
+    MatchArgs ma{kf, stride_h, stride_n, codes, codes_ld, codes_col0, T, c->cfg.cos_threshold};
+    FASTAR_HIP(launch_match(dm, dev, ma, s));
+    MergeArgs ga{kf, vf, stride_h, stride_n, codes, codes_ld, codes_col0, T,
+                 slot_out_dev, merged_out_dev, N, tok0};
+    FASTAR_HIP(launch_plan(dm, dev, ga, s));
+    FASTAR_HIP(launch_apply(dm, dev, ga, s));
+    FASTAR_HIP(launch_rehash(dm, dev, T, s));
+    FASTAR_HIP(launch_index(dm, dev, true, s));
+  }
+  return ok();
+}
+
+fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_h,
+                            int64_t stride_n, int32_t Nq, float scale, void* o_dev,
+                            int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  const Dims& dm = c->dm;
+  FASTAR_REQUIRE(Nq >= 0, "Nq must be >= 0");
+  if (Nq == 0) return ok();
+  FASTAR_REQUIRE(q_dev && o_dev, "q or o is NULL");
+  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  const int vec = dm.elem == 2 ? 8 : 4;
+  FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(o_dev, 16), "q and o must be 16-byte aligned");
+  FASTAR_REQUIRE(stride_h % vec == 0 && stride_n % vec == 0 && stride_n >= dm.d,
+                 "q strides must be multiples of 16 bytes");
+  FASTAR_REQUIRE(o_stride_h % vec == 0 && o_stride_n % vec == 0 && o_stride_n >= dm.d,
+                 "o strides must be multiples of 16 bytes");
+  FASTAR_REQUIRE(lse_dev == nullptr || aligned(lse_dev, 4), "lse misaligned");
+  AttendArgs a{};
+  a.q = q_dev;
+  a.sq_h = stride_h;
+  a.sq_n = stride_n;
+  a.k = c->dev.k_mirror;
+  a.v = c->dev.v_mirror;
+  a.sk_h = (int64_t)dm.B * dm.d;
+  a.sk_n = dm.d;
+  a.count = c->dev.count;
+  a.count_ld = dm.B;
+  a.n_keys = c->dev.n_live;
+  a.n_keys_const = 0;
+  a.sel = nullptr;
+  a.sel_ld = 0;
+  a.o = o_dev;
+  a.so_h = o_stride_h;
+  a.so_n = o_stride_n;
+  a.lse = lse_dev;
+  a.H = dm.H;
+  a.d = dm.d;
+  a.Nseg = Nq;
+  a.F = 1;
+  a.scale = scale == 0.0f ? 1.0f / std::sqrt((float)dm.d) : scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FASTAR_HIP(dm.elem == 2 ? launch_attend_bf16(a, s) : launch_attend_f32(a, s));
+  return ok();
+}
+
+fastar_status fastar_cache_stats(fastar_cache_t c, void* stream, fastar_stats* out) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  FASTAR_REQUIRE(out != nullptr, "out is NULL");
+  const Dims& dm = c->dm;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lo = c->lay.off[kNLive], hi = c->lay.off[kStateEnd + 1];
+  std::string buf(hi - lo, '\0');
+  FASTAR_HIP(hipMemcpyAsync(&buf[0], static_cast<uint8_t*>(c->ws) + lo, hi - lo,
+                            hipMemcpyDeviceToHost, s));
+  FASTAR_HIP(hipStreamSynchronize(s));
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(buf.data());
+  const int32_t* n_live = reinterpret_cast<const int32_t*>(base);
+  const int64_t* ev = reinterpret_cast<const int64_t*>(base + (c->lay.off[kEvicted] - lo));
+  const int64_t* cn = reinterpret_cast<const int64_t*>(base + (c->lay.off[kCounters] - lo));
+  const int32_t* fr = reinterpret_cast<const int32_t*>(base + (c->lay.off[kFrame] - lo));
+  fastar_stats r{};
+  r.frame = *fr;
+  for (int h = 0; h < dm.H; ++h) {
+    r.live_slots += n_live[h];
+    if (n_live[h] > r.max_live) r.max_live = n_live[h];
+    r.evicted_tokens += ev[h];
+    r.tokens_seen += cn[h * kNumCounters + kCntTokens];
+    r.merged_tokens += cn[h * kNumCounters + kCntMerged];
+    r.inserted_tokens += cn[h * kNumCounters + kCntInserted];
+    r.evicted_slots += cn[h * kNumCounters + kCntEvictedSlots];
+  }
+  *out = r;
+  return ok();
+}
+
+fastar_status fastar_cache_export(fastar_cache_t c, void* stream, fastar_cache_state* out) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  FASTAR_REQUIRE(out != nullptr, "out is NULL");
+  const Dims& dm = c->dm;
+  const CacheDev& d = c->dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t HBd = (size_t)dm.H * dm.B * dm.d, HB = (size_t)dm.H * dm.B;
+  auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
+    return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s) : hipSuccess;
+  };
+  FASTAR_HIP(cp(out->k_master, d.k_master, HBd * 4));
+  FASTAR_HIP(cp(out->v_master, d.v_master, HBd * 4));
+  FASTAR_HIP(cp(out->k_mirror, d.k_mirror, HBd * dm.elem));
+  FASTAR_HIP(cp(out->v_mirror, d.v_mirror, HBd * dm.elem));
+  FASTAR_HIP(cp(out->count, d.count, HB * 4));
+  FASTAR_HIP(cp(out->last, d.last, HB * 4));
+  FASTAR_HIP(cp(out->codes, d.codes, HB * dm.L * 4));
+  FASTAR_HIP(cp(out->n_live, d.n_live, (size_t)dm.H * 4));
+  FASTAR_HIP(cp(out->evicted_tokens, d.evicted_tokens, (size_t)dm.H * 8));
+  int32_t frame = 0;
+  FASTAR_HIP(hipMemcpyAsync(&frame, d.frame, 4, hipMemcpyDeviceToHost, s));
+  FASTAR_HIP(hipStreamSynchronize(s));
+  out->frame = frame;
+  return ok();
+}
+
+fastar_status fastar_cache_import(fastar_cache_t c, const fastar_cache_state* in, void* stream) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  FASTAR_REQUIRE(in != nullptr, "in is NULL");
+  FASTAR_REQUIRE(in->frame >= 0 && in->frame < INT32_MAX, "frame out of range");
+  const Dims& dm = c->dm;
+  if (in->n_live) {
+    for (int h = 0; h < dm.H; ++h)
+      FASTAR_REQUIRE(in->n_live[h] >= 0 && in->n_live[h] <= dm.B, "n_live out of range");
+  }
+  const CacheDev& d = c->dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t HBd = (size_t)dm.H * dm.B * dm.d, HB = (size_t)dm.H * dm.B;
+  auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
+    return src ? hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s) : hipSuccess;
+  };
+  FASTAR_HIP(cp(d.k_master, in->k_master, HBd * 4));
+  FASTAR_HIP(cp(d.v_master, in->v_master, HBd * 4));
+  FASTAR_HIP(cp(d.k_mirror, in->k_mirror, HBd * dm.elem));
+  FASTAR_HIP(cp(d.v_mirror, in->v_mirror, HBd * dm.elem));
+  FASTAR_HIP(cp(d.count, in->count, HB * 4));
+  FASTAR_HIP(cp(d.last, in->last, HB * 4));
+  FASTAR_HIP(cp(d.codes, in->codes, HB * dm.L * 4));
+  FASTAR_HIP(cp(d.n_live, in->n_live, (size_t)dm.H * 4));
+  FASTAR_HIP(cp(d.evicted_tokens, in->evicted_tokens, (size_t)dm.H * 8));
+  const int32_t frame = (int32_t)in->frame;
+  FASTAR_HIP(hipMemcpyAsync(d.frame, &frame, 4, hipMemcpyHostToDevice, s));
+  FASTAR_HIP(launch_index(dm, d, false, s));
+  FASTAR_HIP(hipStreamSynchronize(s));
+  return ok();
+}
+
+fastar_status fastar_annca_select(const uint32_t* q_codes_dev, int32_t Nf, int32_t F,
+                                  const uint32_t* p_codes_dev, int32_t Np, int32_t H, int32_t L,
+                                  int32_t* sel_idx_dev, int32_t* sel_count_dev, void* stream) {
+  FASTAR_REQUIRE(H >= 1 && F >= 1 && L >= 1 && L <= FASTAR_MAX_TABLES, "H, F, L out of range");
+  FASTAR_REQUIRE(Nf >= 1 && Nf <= FASTAR_MAX_ANNCA_QUERIES_PER_FRAME, "Nf out of range");
+  FASTAR_REQUIRE(Np >= 1 && Np <= FASTAR_MAX_ANNCA_PROMPT, "Np out of range");
+  FASTAR_REQUIRE(q_codes_dev && p_codes_dev && sel_idx_dev && sel_count_dev, "NULL pointer");
+  SelectArgs a{q_codes_dev, p_codes_dev, Nf, F, Np, H, L, sel_idx_dev, sel_count_dev};
+  FASTAR_HIP(launch_annca_select(a, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+fastar_status fastar_attend_subset(const void* q_dev, int64_t q_stride_h, int64_t q_stride_n,
+                                   const void* k_dev, const void* v_dev, int64_t kv_stride_h,
+                                   int64_t kv_stride_n, const int32_t* sel_idx_dev,
+                                   const int32_t* sel_count_dev, int32_t Nf, int32_t F, int32_t Np,
+                                   int32_t H, int32_t d, fastar_dtype dtype, float scale,
+                                   void* o_dev, int64_t o_stride_h, int64_t o_stride_n,
+                                   void* stream) {
+  FASTAR_REQUIRE(valid_dtype(dtype), "unknown dtype");
+  FASTAR_REQUIRE(d == 64 || d == 128, "d must be 64 or 128");
+  FASTAR_REQUIRE(H >= 1 && F >= 1 && Nf >= 0 && Np >= 0, "sizes out of range");
+  FASTAR_REQUIRE((sel_idx_dev == nullptr) == (sel_count_dev == nullptr),
+                 "sel_idx and sel_count must both be given or both be NULL");
+  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  if (Nf == 0) return ok();
+  FASTAR_REQUIRE(q_dev && k_dev && v_dev && o_dev, "NULL pointer");
+  const int vec = dtype == FASTAR_BF16 ? 8 : 4;
+  FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(k_dev, 16) && aligned(v_dev, 16) &&
+                     aligned(o_dev, 16),
+                 "q, k, v, o must be 16-byte aligned");
+  FASTAR_REQUIRE(q_stride_h % vec == 0 && q_stride_n % vec == 0 && kv_stride_h % vec == 0 &&
+                     kv_stride_n % vec == 0 && o_stride_h % vec == 0 && o_stride_n % vec == 0,
+                 "strides must be multiples of 16 bytes");
+  AttendArgs a{};
+  a.q = q_dev;
+  a.sq_h = q_stride_h;
+  a.sq_n = q_stride_n;
+  a.k = k_dev;
+  a.v = v_dev;
+  a.sk_h = kv_stride_h;
+  a.sk_n = kv_stride_n;
+  a.count = nullptr;
+  a.count_ld = 0;
+  a.n_keys = sel_count_dev;
+  a.n_keys_const = Np;
+  a.sel = sel_idx_dev;
+  a.sel_ld = Np;
+  a.o = o_dev;
+  a.so_h = o_stride_h;
+  a.so_n = o_stride_n;
+  a.lse = nullptr;
+  a.H = H;
+  a.d = d;
+  a.Nseg = Nf;
+  a.F = F;
+  a.scale = scale == 0.0f ? 1.0f / std::sqrt((float)d) : scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FASTAR_HIP(dtype == FASTAR_BF16 ? launch_attend_bf16(a, s) : launch_attend_f32(a, s));
+  return ok();
+}
+
+}  // extern "C"

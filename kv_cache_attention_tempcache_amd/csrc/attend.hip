@@ -1,0 +1,423 @@
+// Attention over the merged cache with the group-size logit shift (FAST-AR
+// summary, section 2A, Lemma 5.1: merging identical keys is exact when values
+// are averaged and each logit is shifted by its group size), and the same
+// kernel over a per-frame subset of prompt keys for AnnCA (section 2B).
+//
+// bf16 path, per workgroup of 4 waves; each wave owns QB blocks of 32 queries:
+//   S^T = K Q^T on the 32x32x16 bf16 MFMA: A = a K tile row block from LDS,
+//     B = the wave's queries, held in registers for the whole key loop.  The
+//     accumulator gives each lane one query column and 16 key rows, so the
+//     running max and sum stay in the lane (plus one exchange with lane^32).
+//   logits in log2 units: t = s * scale * log2(e) + log2(count).  The running
+//     max is refreshed lazily (only when a tile's max exceeds it by more than
+//     8), which keeps every weight <= 2^8 and skips most rescales of O.
+//   O^T += V^T P^T: B = the probabilities, converted to bf16 in registers in
+//     exactly the k-order the accumulator produced them; A = V^T, read from an
+//     LDS copy of the V tile that is transposed while it is written.
+//   K and V tiles (BN keys) are double-buffered in LDS: the next tile's global
+//     loads are in flight while the current one is multiplied.
+//   Blocks are renumbered so each XCD (blocks are dealt round-robin over the 8
+//     XCDs) gets a contiguous range of (head, query tile) and shares its L2.
+// f32 path (small fp32 workloads): one thread per query, fp32 online softmax.
+#include "common.hpp"
+
+namespace fastar {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = bid & 7, k = bid >> 3;
+  return x * q + min(x, r) + k;
+}
+
+template <int D, int QB, int BN>
+struct Cfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 256;
+  static constexpr int BM = kWaves * QB * 32;
+  static constexpr int KP = D * 2 + 16;   // bytes per K row in LDS
+  static constexpr int VP = BN * 2 + 8;   // bytes per V^T row in LDS
+  static constexpr int kKBytes = BN * KP;
+  static constexpr int kVBytes = D * VP;
+  static constexpr int kBufBytes = kKBytes + kVBytes + BN * 4;
+  static constexpr int kKPer = (BN * D / 8) / kThreads;         // 16-byte K chunks per thread
+  static constexpr int kVPer = ((BN / 2) * (D / 8)) / kThreads;  // (key pair, chunk) per thread
+  static_assert((BN * D / 8) % kThreads == 0, "K tile split");
+  static_assert(((BN / 2) * (D / 8)) % kThreads == 0, "V tile split");
+  static_assert(kBufBytes % 16 == 0, "buffer alignment");
+};
+
+template <int D, int QB, int BN, bool GATHER>
+__global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a, int qtiles) {
+  using C = Cfg<D, QB, BN>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int total = gridDim.x;
+  const int lb_id = xcd_remap(blockIdx.x, total);
+  const int per_head = a.F * qtiles;
+  const int h = lb_id / per_head;
+  const int g = (lb_id - h * per_head) / qtiles;
+  const int qt = lb_id - h * per_head - g * qtiles;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 31, hf = lane >> 5;
+  const int nkeys = a.n_keys ? a.n_keys[h * a.F + g] : a.n_keys_const;
+  const float cscale = a.scale * kLog2e;
+
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.sq_h;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + (int64_t)h * a.sk_h;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + (int64_t)h * a.sk_h;
+  const int32_t* cnt = a.count ? a.count + (int64_t)h * a.count_ld : nullptr;
+  const int32_t* sel = GATHER ? a.sel + (int64_t)(h * a.F + g) * a.sel_ld : nullptr;
+  uint16_t* obase = static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h;
+
+  // queries of this wave: segment-local index qi = qt*BM + wave*QB*32 + qb*32 + m
+  bf16x8_t Qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qt * C::BM + wave * QB * 32 + qb * 32 + m;
+    const bool ok = qi < a.Nseg;
+    const uint16_t* qp = qbase + (int64_t)(g * a.Nseg + (ok ? qi : 0)) * a.sq_n + hf * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
+      if (!ok) v = bf16x8_t{};
+      Qf[qb][ks] = v;
+    }
+  }
+
+  f32x16_t O[D / 32][QB];
+  float mrun[QB], lrun[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mrun[qb] = -__builtin_huge_valf();
+    lrun[qb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) O[db][qb] = f32x16_t{};
+  }
+
+  const int nt = (nkeys + BN - 1) / BN;
+  uint4 kreg[C::kKPer];
+  uint4 vreg[2 * C::kVPer];
+  float lbreg = 0.0f;
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < C::kKPer; ++i) {
+      const int chunk = tid + i * C::kThreads;
+      const int row = chunk / (D / 8), ch = chunk % (D / 8);
+      const int key = k0 + row;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (key < nkeys) {
+        const int src = GATHER ? sel[key] : key;
+        v = *reinterpret_cast<const uint4*>(kbase + (int64_t)src * a.sk_n + ch * 8);
+      }
+      kreg[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < C::kVPer; ++i) {
+      const int unit = tid + i * C::kThreads;
+      const int p = unit % (BN / 2), ch = unit / (BN / 2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = k0 + 2 * p + u;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (key < nkeys) {
+          const int src = GATHER ? sel[key] : key;
+          v = *reinterpret_cast<const uint4*>(vbase + (int64_t)src * a.sk_n + ch * 8);
+        }
+        vreg[2 * i + u] = v;
+      }
+    }
+    if (tid < BN) {
+      const int key = k0 + tid;
+      float lbv = -__builtin_huge_valf();
+      if (key < nkeys) {
+        const int src = GATHER ? sel[key] : key;
+        lbv = cnt ? __log2f((float)cnt[src]) : 0.0f;
+      }
+      lbreg = lbv;
+    }
+  };
+
+  auto store_tile = [&](uint8_t* buf) {
+#pragma unroll
+    for (int i = 0; i < C::kKPer; ++i) {
+      const int chunk = tid + i * C::kThreads;
+      const int row = chunk / (D / 8), ch = chunk % (D / 8);
+      *reinterpret_cast<uint4*>(buf + row * C::KP + ch * 16) = kreg[i];
+    }
+    uint8_t* vt = buf + C::kKBytes;
+#pragma unroll
+    for (int i = 0; i < C::kVPer; ++i) {
+      const int unit = tid + i * C::kThreads;
+      const int p = unit % (BN / 2), ch = unit / (BN / 2);
+      const uint32_t a0[4] = {vreg[2 * i].x, vreg[2 * i].y, vreg[2 * i].z, vreg[2 * i].w};
+      const uint32_t a1[4] = {vreg[2 * i + 1].x, vreg[2 * i + 1].y, vreg[2 * i + 1].z,
+                              vreg[2 * i + 1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (e & 1) ? (a0[e >> 1] >> 16) : (a0[e >> 1] & 0xffffu);
+        const uint32_t hi = (e & 1) ? (a1[e >> 1] & 0xffff0000u) : (a1[e >> 1] << 16);
+        *reinterpret_cast<uint32_t*>(vt + (ch * 8 + e) * C::VP + p * 4) = lo | hi;
+      }
+    }
+    if (tid < BN) reinterpret_cast<float*>(buf + C::kKBytes + C::kVBytes)[tid] = lbreg;
+  };
+
+  if (nt > 0) {
+    load_tile(0);
+    store_tile(smem);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < nt; ++it) {
+    const bool has_next = it + 1 < nt;
+    if (has_next) load_tile((it + 1) * BN);
+    const uint8_t* buf = smem + (it & 1) * C::kBufBytes;
+    const uint8_t* ks_lds = buf;
+    const uint8_t* vt_lds = buf + C::kKBytes;
+    const float* lb_lds = reinterpret_cast<const float*>(buf + C::kKBytes + C::kVBytes);
+
+    // S^T = K Q^T
+    f32x16_t S[BN / 32][QB];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            ks_lds + (kb * 32 + m) * C::KP + (hf * (D / 2) + ks * 8) * 2);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[qb][ks], S[kb][qb], 0, 0, 0);
+      }
+    }
+
+    // logits, lazy running max, probabilities
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const float4 b4 = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            S[kb][qb][4 * jg + r] = __builtin_fmaf(S[kb][qb][4 * jg + r], cscale, bb[r]);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, S[kb][qb][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > mrun[qb] + 8.0f;
+      if (__ballot(need)) {
+        const float mnew = need ? mx : mrun[qb];
+        const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
+        lrun[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) O[db][qb][j] *= alpha;
+        mrun[qb] = mnew;
+      }
+      float ls = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float p = __builtin_amdgcn_exp2f(S[kb][qb][j] - mrun[qb]);
+          S[kb][qb][j] = p;
+          ls += p;
+        }
+      lrun[qb] += ls;
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t pf[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pf[qb][i] = (__bf16)S[kb][qb][8 * kk + i];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const uint8_t* vp = vt_lds + (db * 32 + m) * C::VP + (kb * 32 + kk * 16 + 4 * hf) * 2;
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vp);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vp + 16);
+          const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
+          const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&vv);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);
+        }
+      }
+    }
+
+    if (has_next) store_tile(smem + ((it + 1) & 1) * C::kBufBytes);
+    __syncthreads();
+  }
+
+  // normalise and store: lane holds O^T rows d = db*32 + 8*(j/4) + 4*hf + j%4
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qt * C::BM + wave * QB * 32 + qb * 32 + m;
+    const float lt = lrun[qb] + __shfl_xor(lrun[qb], 32);
+    if (qi >= a.Nseg) continue;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    uint16_t* op = obase + (int64_t)(g * a.Nseg + qi) * a.so_n;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        uint32_t w0 = f32_to_bf16_bits(O[db][qb][4 * jg + 0] * inv) |
+                      (f32_to_bf16_bits(O[db][qb][4 * jg + 1] * inv) << 16);
+        uint32_t w1 = f32_to_bf16_bits(O[db][qb][4 * jg + 2] * inv) |
+                      (f32_to_bf16_bits(O[db][qb][4 * jg + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + db * 32 + 8 * jg + 4 * hf) = make_uint2(w0, w1);
+      }
+    if (a.lse && hf == 0)
+      a.lse[(int64_t)h * a.F * a.Nseg + (int64_t)g * a.Nseg + qi] =
+          lt > 0.0f ? (mrun[qb] + __log2f(lt)) * kLn2 : -__builtin_huge_valf();
+  }
+}
+
+template <int D, bool GATHER>
+__global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles) {
+  constexpr int KT = 32;
+  __shared__ float Ks[KT][D];
+  __shared__ float Vs[KT][D];
+  __shared__ float lbs[KT];
+  const int per_head = a.F * qtiles;
+  const int h = blockIdx.x / per_head;
+  const int g = (blockIdx.x - h * per_head) / qtiles;
+  const int qt = blockIdx.x - h * per_head - g * qtiles;
+  const int tid = threadIdx.x;
+  const int qi = qt * 64 + tid;
+  const bool ok = qi < a.Nseg;
+  const int nkeys = a.n_keys ? a.n_keys[h * a.F + g] : a.n_keys_const;
+  const float cscale = a.scale * kLog2e;
+  const float* qp = static_cast<const float*>(a.q) + (int64_t)h * a.sq_h +
+                    (int64_t)(g * a.Nseg + (ok ? qi : 0)) * a.sq_n;
+  const float* kbase = static_cast<const float*>(a.k) + (int64_t)h * a.sk_h;
+  const float* vbase = static_cast<const float*>(a.v) + (int64_t)h * a.sk_h;
+  const int32_t* cnt = a.count ? a.count + (int64_t)h * a.count_ld : nullptr;
+  const int32_t* sel = GATHER ? a.sel + (int64_t)(h * a.F + g) * a.sel_ld : nullptr;
+
+  float qv[D], o[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qv[e] = ok ? qp[e] : 0.0f;
+    o[e] = 0.0f;
+  }
+  float mrun = -__builtin_huge_valf(), l = 0.0f;
+  for (int k0 = 0; k0 < nkeys; k0 += KT) {
+    for (int idx = tid; idx < KT * D; idx += 64) {
+      const int r = idx / D, e = idx % D;
+      const int key = k0 + r;
+      float kx = 0.0f, vx = 0.0f;
+      if (key < nkeys) {
+        const int src = GATHER ? sel[key] : key;
+        kx = kbase[(int64_t)src * a.sk_n + e];
+        vx = vbase[(int64_t)src * a.sk_n + e];
+      }
+      Ks[r][e] = kx;
+      Vs[r][e] = vx;
+    }
+    if (tid < KT) {
+      const int key = k0 + tid;
+      float lbv = -__builtin_huge_valf();
+      if (key < nkeys) {
+        const int src = GATHER ? sel[key] : key;
+        lbv = cnt ? log2f((float)cnt[src]) : 0.0f;
+      }
+      lbs[tid] = lbv;
+    }
+    __syncthreads();
+    const int nr = min(KT, nkeys - k0);
+    for (int r = 0; r < nr; ++r) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qv[e], Ks[r][e], dot);
+      const float t = dot * cscale + lbs[r];
+      if (t > mrun) {
+        const float alpha = exp2f(mrun - t);
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < D; ++e) o[e] *= alpha;
+        mrun = t;
+      }
+      const float p = exp2f(t - mrun);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) o[e] = __builtin_fmaf(p, Vs[r][e], o[e]);
+    }
+    __syncthreads();
+  }
+  if (!ok) return;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float* op = static_cast<float*>(a.o) + (int64_t)h * a.so_h + (int64_t)(g * a.Nseg + qi) * a.so_n;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[e] = o[e] * inv;
+  if (a.lse)
+    a.lse[(int64_t)h * a.F * a.Nseg + (int64_t)g * a.Nseg + qi] =
+        l > 0.0f ? (mrun + log2f(l)) * kLn2 : -__builtin_huge_valf();
+}
+
+template <int D, int QB, int BN, bool GATHER>
+hipError_t launch_bf16_cfg(const AttendArgs& a, hipStream_t s) {
+  using C = Cfg<D, QB, BN>;
+  const int qtiles = (a.Nseg + C::BM - 1) / C::BM;
+  const int blocks = a.H * a.F * qtiles;
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = 2 * (size_t)C::kBufBytes;
+  auto kern = attend_bf16_kernel<D, QB, BN, GATHER>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(C::kThreads), lds, s, a, qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
+  const bool gather = a.sel != nullptr;
+  if (a.d == 128)
+    return gather ? launch_bf16_cfg<128, 1, 64, true>(a, s) : launch_bf16_cfg<128, 1, 64, false>(a, s);
+  return gather ? launch_bf16_cfg<64, 2, 64, true>(a, s) : launch_bf16_cfg<64, 2, 64, false>(a, s);
+}
+
+hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s) {
+  const int qtiles = (a.Nseg + 63) / 64;
+  const int blocks = a.H * a.F * qtiles;
+  if (blocks == 0) return hipSuccess;
+  const bool gather = a.sel != nullptr;
+  if (a.d == 128) {
+    if (gather) hipLaunchKernelGGL((attend_f32_kernel<128, true>), dim3(blocks), dim3(64), 0, s, a, qtiles);
+    else hipLaunchKernelGGL((attend_f32_kernel<128, false>), dim3(blocks), dim3(64), 0, s, a, qtiles);
+  } else {
+    if (gather) hipLaunchKernelGGL((attend_f32_kernel<64, true>), dim3(blocks), dim3(64), 0, s, a, qtiles);
+    else hipLaunchKernelGGL((attend_f32_kernel<64, false>), dim3(blocks), dim3(64), 0, s, a, qtiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fastar

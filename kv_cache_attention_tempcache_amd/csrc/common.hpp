@@ -1,0 +1,177 @@
+// Shared definitions of the gfx950 TempCache library: storage types, the
+// workspace layout of a cache, and the internal launcher interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fastar.h"
+
+#define FASTAR_MAX_TABLES_DEV FASTAR_MAX_TABLES
+
+namespace fastar {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bfloat16
+// bfloat16 values travel as raw 16-bit patterns.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// binary32 -> bfloat16, round to nearest, ties to even (the format definition:
+// keep the upper 16 bits, decide the rounding from the lower 16).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN -> quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Load/store one element of storage type T (float or uint16_t bf16 bits) as float.
+template <typename T> __device__ __forceinline__ float load_f32(const T* p);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p) {
+  return bf16_bits_to_f32(*p);
+}
+
+// Bucket of a code in a table of 2^nb_bits buckets (multiplicative hashing;
+// the bucket only narrows the search, equality of codes is checked exactly).
+__device__ __forceinline__ uint32_t bucket_of(uint32_t code, int nb_bits) {
+  return nb_bits == 0 ? 0u : (code * 0x9E3779B1u) >> (32 - nb_bits);
+}
+
+// ---------------------------------------------------------------- cache layout
+// Per-head counters (int64): tokens seen, merged tokens, inserted tokens,
+// evicted slots.
+enum { kCntTokens = 0, kCntMerged = 1, kCntInserted = 2, kCntEvictedSlots = 3, kNumCounters = 4 };
+// Per-head plan summary written by the planning kernel of each frame (int32).
+enum { kPlanGroups = 0, kPlanInserts = 1, kPlanMergeTokens = 2, kPlanEvict = 3, kPlanStride = 8 };
+
+struct Dims {
+  int H, d, B, L, b;
+  int elem;      // storage bytes per element (2 or 4)
+  int nb_bits;   // log2 of buckets per (head, table)
+  int NB;        // buckets per (head, table)
+  int Ppad;      // L*b rounded up to a multiple of 32
+};
+
+// Device pointers into one cache's workspace.
+struct CacheDev {
+  void* planes;        // [L*b][d] storage dtype
+  float* k_master;     // [H][B][d]
+  float* v_master;     // [H][B][d]
+  void* k_mirror;      // [H][B][d] storage dtype
+  void* v_mirror;      // [H][B][d] storage dtype
+  int32_t* count;      // [H][B]
+  int32_t* last;       // [H][B]
+  uint32_t* codes;     // [H][L][B]
+  int32_t* idx_off;    // [H][L][NB+1]
+  int32_t* idx_slot;   // [H][L][B]
+  int32_t* n_live;     // [H]
+  int64_t* evicted_tokens;  // [H]
+  int64_t* counters;   // [H][kNumCounters]
+  int32_t* frame;      // [1]
+  // per-frame scratch (a frame has at most B tokens)
+  int32_t* best_slot;  // [H][B] top-1 candidate or -1
+  float* best_cos;     // [H][B]
+  int32_t* dec;        // [H][B] merge target or -1 (insert)
+  uint32_t* frame_codes;  // [H][L][B] codes of the frame when hashed here
+  int32_t* group_tok;  // [H][B] merging tokens sorted by (slot, token)
+  int32_t* group_start;   // [H][B+1]
+  int32_t* group_slot; // [H][B]
+  int32_t* ins_tok;    // [H][B]
+  int32_t* ins_slot;   // [H][B]
+  int32_t* plan;       // [H][kPlanStride]
+};
+
+struct Layout {
+  size_t off[32];
+  size_t total;
+};
+
+// Computes the byte offsets of every CacheDev member for these dimensions.
+Layout make_layout(const Dims& dm);
+CacheDev carve(void* base, const Dims& dm);
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `stream` and return the launch status.
+
+// SimHash.  Row n of head h is x + h*sx_h + n*sx_n (or row rows[h*rows_ld+n]
+// when rows != nullptr, for n < n_rows[h]).  Codes go to
+// codes[(h*L + t)*codes_ld + codes_col0 + n] (or column rows[...] when gathering).
+struct HashArgs {
+  const void* x;
+  int64_t sx_h, sx_n;
+  int H, N, d, L, b;
+  const void* planes;
+  uint32_t* codes;
+  int64_t codes_ld, codes_col0;
+  const int32_t* rows;      // optional gather list
+  int64_t rows_ld;
+  const int32_t* n_rows;    // per-head row count when gathering (device)
+  int n_rows_stride;        // int32 stride between heads in n_rows
+};
+hipError_t launch_hash_bf16(const HashArgs& a, hipStream_t s);
+hipError_t launch_hash_f32(const HashArgs& a, hipStream_t s);
+
+// One frame of matching.
+struct MatchArgs {
+  const void* x;            // keys of the frame: head h, token i at x + h*sx_h + i*sx_n
+  int64_t sx_h, sx_n;
+  const uint32_t* codes;    // codes[(h*L + t)*codes_ld + codes_col0 + i]
+  int64_t codes_ld, codes_col0;
+  int T;
+  float tau;
+};
+hipError_t launch_match(const Dims& dm, const CacheDev& c, const MatchArgs& a, hipStream_t s);
+
+// One frame of planning + applying (merge, evict, insert).
+struct MergeArgs {
+  const void* k;            // token i of the frame at k + h*sx_h + i*sx_n
+  const void* v;
+  int64_t sx_h, sx_n;
+  const uint32_t* codes;    // as MatchArgs
+  int64_t codes_ld, codes_col0;
+  int T;
+  int32_t* slot_out;        // optional, slot_out[h*out_ld + out_col0 + i]
+  uint8_t* merged_out;      // optional
+  int64_t out_ld, out_col0;
+};
+hipError_t launch_plan(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s);
+hipError_t launch_apply(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s);
+hipError_t launch_rehash(const Dims& dm, const CacheDev& c, int T, hipStream_t s);
+hipError_t launch_index(const Dims& dm, const CacheDev& c, bool bump_frame, hipStream_t s);
+
+// Attention (TempCache over the live slots, or AnnCA over a per-frame subset).
+struct AttendArgs {
+  const void* q;
+  int64_t sq_h, sq_n;
+  const void* k;            // key j of head h at k + h*sk_h + j*sk_n
+  const void* v;
+  int64_t sk_h, sk_n;
+  const int32_t* count;     // optional [H][count_ld] group sizes (ln-count bias)
+  int64_t count_ld;
+  const int32_t* n_keys;    // per (head, segment) key count (device), or nullptr
+  int n_keys_const;         // used when n_keys == nullptr
+  const int32_t* sel;       // optional gather list: sel[(h*F + g)*sel_ld + j]
+  int64_t sel_ld;
+  void* o;
+  int64_t so_h, so_n;
+  float* lse;               // optional [H][F*Nseg]
+  int H, d, Nseg, F;        // F segments (frames) of Nseg queries each
+  float scale;              // logit scale
+};
+hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s);
+
+// AnnCA per-frame selection.
+struct SelectArgs {
+  const uint32_t* q_codes;  // [H][L][F*Nf]
+  const uint32_t* p_codes;  // [H][L][Np]
+  int Nf, F, Np, H, L;
+  int32_t* sel_idx;         // [H][F][Np]
+  int32_t* sel_count;       // [H][F]
+};
+hipError_t launch_annca_select(const SelectArgs& a, hipStream_t s);
+
+}  // namespace fastar

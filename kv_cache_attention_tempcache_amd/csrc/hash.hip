@@ -1,0 +1,172 @@
+// SimHash on gfx950 (FAST-AR summary, section 2A "Mecanismo": the nearest-
+// neighbour search runs on locality-sensitive hashes).  Bit j of table t is
+// [<r_tj, x> > 0], stored as 1u << j.
+//
+// bf16 path: the projection is a small GEMM (rows x d) * (d x L*b) on the
+// 32x32x16 bf16 MFMA.  A wave owns 32 rows; the hyperplanes sit in LDS.  The
+// accumulator layout puts one hyperplane per lane column and rows in
+// registers, so one wave ballot over a register yields two complete 32-bit
+// words of sign bits (rows r and r+4), already in LSB-first plane order.
+//
+// f32 path: one thread per (row, table), products and sums in float64.
+#include "common.hpp"
+
+namespace fastar {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+constexpr int kHashWaves = 4;
+
+__device__ __forceinline__ uint32_t extract_code(const uint32_t (&w)[9], int off, int b) {
+  if (b == 0) return 0u;
+  const int wi = off >> 5, sh = off & 31;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k == wi) lo = w[k];
+    if (k == wi + 1) hi = w[k];
+  }
+  uint64_t both = ((uint64_t)hi << 32) | lo;
+  uint32_t code = (uint32_t)(both >> sh);
+  return b == 32 ? code : (code & ((1u << b) - 1u));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void hash_bf16_kernel(HashArgs a, int tiles_per_head,
+                                                        int total_tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int kPitch = D * 2 + 16;  // bytes per LDS hyperplane row (padding avoids conflicts)
+  const int P = a.L * a.b;
+  const int Ppad = (P + 31) & ~31;
+  const uint16_t* planes = static_cast<const uint16_t*>(a.planes);
+  for (int idx = threadIdx.x; idx < Ppad * (D / 8); idx += blockDim.x) {
+    const int row = idx / (D / 8), ch = idx % (D / 8);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < P) v = reinterpret_cast<const uint4*>(planes + (size_t)row * D)[ch];
+    *reinterpret_cast<uint4*>(smem + row * kPitch + ch * 16) = v;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 31, hf = lane >> 5;
+  // Row owned by this lane in the ballot words: register j = 4*(m/8) + m%4,
+  // low half of the ballot if (m/4) is even, high half otherwise.
+  const int my_j = 4 * (m >> 3) + (m & 3);
+  const bool my_hi = ((m >> 2) & 1) != 0;
+  const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
+
+  for (int tile = blockIdx.x * kHashWaves + wave; tile < total_tiles;
+       tile += gridDim.x * kHashWaves) {
+    const int h = tile / tiles_per_head;
+    const int r0 = (tile - h * tiles_per_head) * 32;
+    const int nrows = a.rows ? a.n_rows[(int64_t)h * a.n_rows_stride] : a.N;
+    if (r0 >= nrows) continue;
+    const int r = r0 + m;
+    const bool valid = r < nrows;
+    int64_t xrow = r;
+    if (a.rows) xrow = valid ? a.rows[(int64_t)h * a.rows_ld + r] : 0;
+    else if (!valid) xrow = 0;
+
+    // A operand: row m, features hf*D/2 + ks*8 .. +7 for k-step ks (the same
+    // feature permutation is applied to the hyperplanes below).
+    bf16x8_t A[D / 16];
+    const uint16_t* xp = xbase + (int64_t)h * a.sx_h + xrow * a.sx_n + hf * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(xp + ks * 8);
+      if (!valid) v = bf16x8_t{};
+      A[ks] = v;
+    }
+
+    uint32_t words[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) words[k] = 0u;
+#pragma unroll
+    for (int pb = 0; pb < 8; ++pb) {
+      if (pb * 32 >= Ppad) break;
+      f32x16_t acc = {};
+      const uint8_t* bp = smem + (pb * 32 + m) * kPitch + (hf * (D / 2)) * 2;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(bp + ks * 16);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks], B, acc, 0, 0, 0);
+      }
+      uint32_t w = 0u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint64_t bal = __ballot(acc[j] > 0.0f);
+        const uint32_t pick = my_hi ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+        if (my_j == j) w = pick;
+      }
+      words[pb] = w;
+    }
+
+    if (hf == 0 && valid) {
+      const int64_t col = a.rows ? xrow : (int64_t)r;
+      for (int t = 0; t < a.L; ++t) {
+        a.codes[((int64_t)h * a.L + t) * a.codes_ld + a.codes_col0 + col] =
+            extract_code(words, t * a.b, a.b);
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void hash_f32_kernel(HashArgs a, int64_t total) {
+  const float* planes = static_cast<const float*>(a.planes);
+  const float* xbase = static_cast<const float*>(a.x);
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(idx % a.L);
+    const int64_t rest = idx / a.L;
+    const int r = (int)(rest % a.N);
+    const int h = (int)(rest / a.N);
+    const int nrows = a.rows ? a.n_rows[(int64_t)h * a.n_rows_stride] : a.N;
+    if (r >= nrows) continue;
+    const int64_t xrow = a.rows ? (int64_t)a.rows[(int64_t)h * a.rows_ld + r] : (int64_t)r;
+    const float* xp = xbase + (int64_t)h * a.sx_h + xrow * a.sx_n;
+    uint32_t code = 0u;
+    for (int j = 0; j < a.b; ++j) {
+      const float* rp = planes + ((int64_t)t * a.b + j) * D;
+      double acc = 0.0;
+      for (int k = 0; k < D; ++k) acc += (double)xp[k] * (double)rp[k];
+      if (acc > 0.0) code |= 1u << j;
+    }
+    a.codes[((int64_t)h * a.L + t) * a.codes_ld + a.codes_col0 + xrow] = code;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hash_bf16(const HashArgs& a, hipStream_t s) {
+  const int tiles_per_head = (a.N + 31) / 32;
+  const int total = a.H * tiles_per_head;
+  if (total == 0) return hipSuccess;
+  int blocks = (total + kHashWaves - 1) / kHashWaves;
+  if (blocks > 4096) blocks = 4096;
+  const int Ppad = (a.L * a.b + 31) & ~31;
+  const size_t lds = (size_t)Ppad * (a.d * 2 + 16) + 16;
+  if (a.d == 128)
+    hipLaunchKernelGGL(hash_bf16_kernel<128>, dim3(blocks), dim3(256), lds, s, a, tiles_per_head,
+                       total);
+  else
+    hipLaunchKernelGGL(hash_bf16_kernel<64>, dim3(blocks), dim3(256), lds, s, a, tiles_per_head,
+                       total);
+  return hipGetLastError();
+}
+
+hipError_t launch_hash_f32(const HashArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.H * a.N * a.L;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (a.d == 128)
+    hipLaunchKernelGGL(hash_f32_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a, total);
+  else
+    hipLaunchKernelGGL(hash_f32_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a, total);
+  return hipGetLastError();
+}
+
+}  // namespace fastar

@@ -1,0 +1,81 @@
+// Bucket index over the live slots, rebuilt after every frame (the candidate
+// sets of the next frame's match must reflect merged and inserted slots).
+//
+// One workgroup per (head, table): an LDS histogram of bucket sizes, an
+// exclusive scan into CSR offsets, then a scatter of slot ids.  The order of
+// slots inside a bucket depends on atomic timing, which does not matter: the
+// match reads every slot of a bucket and breaks ties on the slot id.
+#include "common.hpp"
+
+namespace fastar {
+namespace {
+
+constexpr int kIdxThreads = 1024;
+constexpr int kIdxWaves = kIdxThreads / kWave;
+
+__global__ __launch_bounds__(kIdxThreads) void index_kernel(Dims dm, CacheDev c, int bump_frame) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t cnt[];  // [NB] then [kIdxWaves]
+  uint32_t* s_scan = cnt + dm.NB;
+  const int ht = blockIdx.x;
+  const int h = ht / dm.L;
+  const int n = c.n_live[h];
+  const int NB = dm.NB, B = dm.B;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t* codes = c.codes + (int64_t)ht * B;
+  int32_t* off = c.idx_off + (int64_t)ht * (NB + 1);
+  int32_t* slots = c.idx_slot + (int64_t)ht * B;
+
+  for (int i = tid; i < NB; i += kIdxThreads) cnt[i] = 0u;
+  __syncthreads();
+  for (int s = tid; s < n; s += kIdxThreads) atomicAdd(&cnt[bucket_of(codes[s], dm.nb_bits)], 1u);
+  __syncthreads();
+
+  // exclusive scan of cnt: each thread owns a contiguous run of buckets
+  const int per = (NB + kIdxThreads - 1) / kIdxThreads;
+  const int lo = min(NB, tid * per), hi = min(NB, lo + per);
+  uint32_t sum = 0u;
+  for (int i = lo; i < hi; ++i) sum += cnt[i];
+  uint32_t x = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_scan[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t sv = lane < kIdxWaves ? s_scan[lane] : 0u;
+#pragma unroll
+    for (int o = 1; o < kIdxWaves; o <<= 1) {
+      const uint32_t y = __shfl_up(sv, o, 64);
+      if (lane >= o) sv += y;
+    }
+    if (lane < kIdxWaves) s_scan[lane] = sv;
+  }
+  __syncthreads();
+  uint32_t run = (w ? s_scan[w - 1] : 0u) + x - sum;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t cc = cnt[i];
+    off[i] = (int32_t)run;
+    cnt[i] = run;
+    run += cc;
+  }
+  if (tid == 0) off[NB] = n;
+  __syncthreads();
+  for (int s = tid; s < n; s += kIdxThreads) {
+    const uint32_t pos = atomicAdd(&cnt[bucket_of(codes[s], dm.nb_bits)], 1u);
+    slots[pos] = s;
+  }
+  if (bump_frame && ht == 0 && tid == 0) *c.frame += 1;
+}
+
+}  // namespace
+
+hipError_t launch_index(const Dims& dm, const CacheDev& c, bool bump_frame, hipStream_t s) {
+  const size_t lds = (size_t)dm.NB * 4 + kIdxWaves * 4;
+  hipLaunchKernelGGL(index_kernel, dim3(dm.H * dm.L), dim3(kIdxThreads), lds, s, dm, c,
+                     bump_frame ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace fastar

@@ -1,0 +1,141 @@
+// Top-1 match of a frame's new keys against the cached slot keys (FAST-AR
+// summary, section 2A "Mecanismo": find each current-frame token's nearest
+// neighbour among earlier frames through LSH, without full attention matrices).
+//
+// A group of 16 lanes owns one token.  For every table it reads the token's
+// bucket from the CSR index, keeps the slots whose code equals the token's code
+// (a bucket may hold several codes), skips slots already seen through an
+// earlier table, and scores each candidate by the cosine of the token key and
+// the slot's stored key.  Products and sums are float64, so the decision agrees
+// with an exact evaluation except within ~1e-15 of a tie.  Ties go to the
+// lowest slot id; the token merges iff its best cosine >= the threshold.
+//
+// The traffic is a gather of a handful of random 128- or 256-byte slot rows per
+// token: there is no reuse between lanes to stage through LDS, so rows go
+// straight from L2/HBM into registers with 8- or 16-byte loads per lane.
+#include "common.hpp"
+
+namespace fastar {
+namespace {
+
+constexpr int kGroup = 16;  // lanes per token
+
+template <typename T, int E>
+__device__ __forceinline__ void load_row(const T* p, float (&v)[E]) {
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (E == 8) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      v[0] = __uint_as_float(u.x << 16);
+      v[1] = __uint_as_float(u.x & 0xffff0000u);
+      v[2] = __uint_as_float(u.y << 16);
+      v[3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < E; k += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(p + k);
+      v[k] = f.x;
+      v[k + 1] = f.y;
+      v[k + 2] = f.z;
+      v[k + 3] = f.w;
+    }
+  }
+}
+
+__device__ __forceinline__ double group_sum(double x) {
+#pragma unroll
+  for (int off = kGroup / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kGroup);
+  return x;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchArgs a) {
+  constexpr int E = D / kGroup;
+  const int h = blockIdx.y;
+  const int i = blockIdx.x * (256 / kGroup) + (threadIdx.x / kGroup);
+  const int gl = threadIdx.x & (kGroup - 1);
+  if (i >= a.T) return;  // all 16 lanes of a group leave together
+  const int L = dm.L, B = dm.B, NB = dm.NB, nb_bits = dm.nb_bits;
+
+  float xv[E];
+  load_row<T, E>(static_cast<const T*>(a.x) + (int64_t)h * a.sx_h + (int64_t)i * a.sx_n + gl * E,
+                 xv);
+  double nx2 = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) nx2 += (double)xv[e] * (double)xv[e];
+  nx2 = group_sum(nx2);
+
+  uint32_t qc[FASTAR_MAX_TABLES_DEV];
+#pragma unroll
+  for (int t = 0; t < FASTAR_MAX_TABLES_DEV; ++t)
+    qc[t] = t < L ? a.codes[((int64_t)h * L + t) * a.codes_ld + a.codes_col0 + i] : 0u;
+
+  const T* keys = static_cast<const T*>(c.k_mirror) + (int64_t)h * B * D;
+  const uint32_t* scodes = c.codes + (int64_t)h * L * B;
+  double best = -__builtin_huge_val();
+  int best_s = -1;
+#pragma unroll
+  for (int t = 0; t < FASTAR_MAX_TABLES_DEV; ++t) {
+    if (t >= L) break;
+    const uint32_t code = qc[t];
+    const int64_t ht = (int64_t)h * L + t;
+    const uint32_t bk = bucket_of(code, nb_bits);
+    const int beg = c.idx_off[ht * (NB + 1) + bk];
+    const int end = c.idx_off[ht * (NB + 1) + bk + 1];
+    for (int p = beg; p < end; ++p) {
+      const int s = c.idx_slot[ht * B + p];
+      if (scodes[(int64_t)t * B + s] != code) continue;
+      bool seen = false;
+#pragma unroll
+      for (int t2 = 0; t2 < FASTAR_MAX_TABLES_DEV; ++t2)
+        if (t2 < t && scodes[(int64_t)t2 * B + s] == qc[t2]) seen = true;
+      if (seen) continue;
+      float kv[E];
+      load_row<T, E>(keys + (int64_t)s * D + gl * E, kv);
+      double dot = 0.0, nk2 = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dot += (double)xv[e] * (double)kv[e];
+        nk2 += (double)kv[e] * (double)kv[e];
+      }
+      dot = group_sum(dot);
+      nk2 = group_sum(nk2);
+      const double cs = (nx2 == 0.0 || nk2 == 0.0) ? 0.0 : dot / (sqrt(nx2) * sqrt(nk2));
+      if (cs > best || (cs == best && s < best_s)) {
+        best = cs;
+        best_s = s;
+      }
+    }
+  }
+  if (gl == 0) {
+    const int64_t o = (int64_t)h * B + i;
+    c.best_slot[o] = best_s;
+    c.best_cos[o] = best_s >= 0 ? (float)best : 0.0f;
+    c.dec[o] = (best_s >= 0 && best >= (double)a.tau) ? best_s : -1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_match(const Dims& dm, const CacheDev& c, const MatchArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const dim3 grid((a.T + 15) / 16, dm.H);
+  if (dm.elem == 2) {
+    if (dm.d == 128) hipLaunchKernelGGL((match_kernel<uint16_t, 128>), grid, dim3(256), 0, s, dm, c, a);
+    else hipLaunchKernelGGL((match_kernel<uint16_t, 64>), grid, dim3(256), 0, s, dm, c, a);
+  } else {
+    if (dm.d == 128) hipLaunchKernelGGL((match_kernel<float, 128>), grid, dim3(256), 0, s, dm, c, a);
+    else hipLaunchKernelGGL((match_kernel<float, 64>), grid, dim3(256), 0, s, dm, c, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fastar

@@ -1,0 +1,397 @@
+// Merge, evict and insert one frame of tokens into the bounded slot store
+// (FAST-AR summary, section 2A: merged tokens keep the mean of their values and
+// their group size; the cache growth is limited so memory stays constant).
+//
+// plan_kernel (one workgroup per head) decides everything that needs a view of
+// the whole frame:
+//   - groups the merging tokens by target slot, tokens ascending, by sorting the
+//     unique keys slot*T + token in LDS (bitonic): each group then has exactly
+//     one owner in the apply step, so slot state is never updated atomically;
+//   - ranks the inserting tokens in ascending order (block scan);
+//   - when the inserts exceed the free slots, selects exactly the missing
+//     number of slots not merged into in this frame, smallest
+//     (last updated frame, slot id) first: an 8-bit radix select on `last`
+//     finds the cut-off frame, a block scan breaks the tie on slot id;
+//   - gives the inserts the evicted ids, then the never-used ids, ascending.
+// apply_kernel: one wave per merge group or insert.  A merge group replays
+// m += (x - m) / (count + 1) in binary32, one correctly rounded op at a time,
+// token by token, for the key and the value master, then refreshes the
+// storage-dtype mirrors.  Integer counters in LDS use atomics only where the
+// result does not depend on their order (histograms, bit sets, sums).
+#include "common.hpp"
+
+namespace fastar {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+
+// Exclusive scan over the block; `total` receives the block sum.  Uses
+// s_scan[0..kPlanWaves) and leaves it reusable on return.
+__device__ int block_excl_scan(int v, int* s_scan, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_scan[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int sv = lane < kPlanWaves ? s_scan[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < kPlanWaves; o <<= 1) {
+      const int y = __shfl_up(sv, o, 64);
+      if (lane >= o) sv += y;
+    }
+    if (lane < kPlanWaves) s_scan[lane] = sv;
+  }
+  __syncthreads();
+  const int base = w ? s_scan[w - 1] : 0;
+  total = s_scan[kPlanWaves - 1];
+  __syncthreads();
+  return base + x - v;
+}
+
+struct PlanShared {
+  int digit, krem, n_groups;
+  unsigned long long evicted_count;
+};
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c, MergeArgs a,
+                                                            int Tp) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t sm[];
+  const int T = a.T, B = dm.B;
+  uint32_t* keys = sm;                         // [Tp]
+  int32_t* ins_list = (int32_t*)(keys + Tp);   // [T] inserting tokens, ascending
+  int32_t* ev_list = ins_list + T;             // [T] evicted slots, ascending
+  uint32_t* merged_bits = (uint32_t*)(ev_list + T);  // [(B+31)/32]
+  int* s_scan = (int*)(merged_bits + ((B + 31) >> 5));  // [kPlanWaves]
+  int* hist = s_scan + kPlanWaves;              // [256]
+  __shared__ PlanShared ps;
+
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int f = *c.frame;
+  const int n_live = c.n_live[h];
+  const int32_t* dec = c.dec + (int64_t)h * B;
+  const int per_t = (T + kPlanThreads - 1) / kPlanThreads;
+  const int t_lo = min(T, tid * per_t), t_hi = min(T, t_lo + per_t);
+
+  // 1. rank the inserting tokens (ascending token order)
+  int cnt = 0;
+  for (int i = t_lo; i < t_hi; ++i) cnt += dec[i] < 0;
+  int m = 0;
+  int r = block_excl_scan(cnt, s_scan, m);
+  for (int i = t_lo; i < t_hi; ++i)
+    if (dec[i] < 0) ins_list[r++] = i;
+
+  // 2. sort the merging tokens by (slot, token)
+  for (int i = tid; i < Tp; i += kPlanThreads) {
+    const int dv = i < T ? dec[i] : -1;
+    keys[i] = dv >= 0 ? (uint32_t)dv * (uint32_t)T + (uint32_t)i : 0xffffffffu;
+  }
+  __syncthreads();
+  for (int k = 2; k <= Tp; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < Tp; i += kPlanThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint32_t x = keys[i], y = keys[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // 3. groups of equal slot among the M merging tokens
+  const int M = T - m;
+  int32_t* g_tok = c.group_tok + (int64_t)h * B;
+  int32_t* g_start = c.group_start + (int64_t)h * (B + 1);
+  int32_t* g_slot = c.group_slot + (int64_t)h * B;
+  const int k_lo = min(M, tid * per_t), k_hi = min(M, k_lo + per_t);
+  cnt = 0;
+  for (int k = k_lo; k < k_hi; ++k)
+    cnt += (k == 0) || (keys[k] / (uint32_t)T != keys[k - 1] / (uint32_t)T);
+  int n_groups = 0;
+  int g = block_excl_scan(cnt, s_scan, n_groups);
+  for (int k = k_lo; k < k_hi; ++k) {
+    const uint32_t slot = keys[k] / (uint32_t)T;
+    g_tok[k] = (int32_t)(keys[k] % (uint32_t)T);
+    if (k == 0 || slot != keys[k - 1] / (uint32_t)T) {
+      g_start[g] = k;
+      g_slot[g] = (int32_t)slot;
+      ++g;
+    }
+  }
+  if (tid == 0) g_start[n_groups] = M;
+
+  // 4. eviction, only if the inserts do not fit
+  const int need = max(0, m - (B - n_live));
+  if (need > 0) {
+    for (int w = tid; w < ((B + 31) >> 5); w += kPlanThreads) merged_bits[w] = 0u;
+    if (tid == 0) {
+      ps.krem = need;
+      ps.evicted_count = 0ull;
+    }
+    __syncthreads();
+    for (int k = tid; k < M; k += kPlanThreads) {
+      const uint32_t slot = keys[k] / (uint32_t)T;
+      atomicOr(&merged_bits[slot >> 5], 1u << (slot & 31));
+    }
+    __syncthreads();
+    const int32_t* last = c.last + (int64_t)h * B;
+    auto eligible = [&](int s) { return ((merged_bits[s >> 5] >> (s & 31)) & 1u) == 0u; };
+    // radix select of the need-th smallest `last` among eligible live slots
+    // (every eligible slot was last updated before frame f, so last <= f-1)
+    uint32_t prefix = 0u;
+    const uint32_t maxv = (uint32_t)(f - 1);
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (shift > 0 && (maxv >> shift) == 0u) continue;
+      for (int q = tid; q < 256; q += kPlanThreads) hist[q] = 0;
+      __syncthreads();
+      const uint64_t hi_mask = ~((1ull << (shift + 8)) - 1ull);
+      for (int s = tid; s < n_live; s += kPlanThreads) {
+        if (!eligible(s)) continue;
+        const uint32_t lv = (uint32_t)last[s];
+        if (((uint64_t)lv & hi_mask) != ((uint64_t)prefix & hi_mask)) continue;
+        atomicAdd(&hist[(lv >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0, dg = 0;
+        const int kr = ps.krem;
+        for (dg = 0; dg < 256; ++dg) {
+          if (cum + hist[dg] >= kr) break;
+          cum += hist[dg];
+        }
+        ps.digit = dg;
+        ps.krem = kr - cum;
+      }
+      __syncthreads();
+      prefix |= (uint32_t)ps.digit << shift;
+      __syncthreads();
+    }
+    const uint32_t cut = prefix;      // the need-th smallest `last`
+    const int take_eq = ps.krem;      // how many slots with last == cut to evict
+    const int per_s = (n_live + kPlanThreads - 1) / kPlanThreads;
+    const int s_lo = min(n_live, tid * per_s), s_hi = min(n_live, s_lo + per_s);
+    // rank of each slot among the eligible ones with last == cut
+    int eq = 0;
+    for (int s = s_lo; s < s_hi; ++s) eq += eligible(s) && (uint32_t)last[s] == cut;
+    int eq_total = 0;
+    const int eq_base = block_excl_scan(eq, s_scan, eq_total);
+    int evc = 0;
+    {
+      int er = eq_base;
+      for (int s = s_lo; s < s_hi; ++s) {
+        if (!eligible(s)) continue;
+        const uint32_t lv = (uint32_t)last[s];
+        if (lv < cut) ++evc;
+        else if (lv == cut) evc += (er++ < take_eq);
+      }
+    }
+    int ev_total = 0;
+    int ep = block_excl_scan(evc, s_scan, ev_total);
+    {
+      int er = eq_base;
+      unsigned long long tok = 0ull;
+      const int32_t* count = c.count + (int64_t)h * B;
+      for (int s = s_lo; s < s_hi; ++s) {
+        if (!eligible(s)) continue;
+        const uint32_t lv = (uint32_t)last[s];
+        bool ev = false;
+        if (lv < cut) ev = true;
+        else if (lv == cut) ev = (er++ < take_eq);
+        if (ev) {
+          ev_list[ep++] = s;
+          tok += (unsigned long long)count[s];
+        }
+      }
+      if (tok) atomicAdd(&ps.evicted_count, tok);
+    }
+  }
+  __syncthreads();
+
+  // 5. slots for the inserts: evicted ids first, then never-used ids, ascending
+  int32_t* i_tok = c.ins_tok + (int64_t)h * B;
+  int32_t* i_slot = c.ins_slot + (int64_t)h * B;
+  const bool want_out = a.slot_out != nullptr || a.merged_out != nullptr;
+  for (int q = tid; q < m; q += kPlanThreads) {
+    const int tok = ins_list[q];
+    const int slot = q < need ? ev_list[q] : n_live + (q - need);
+    i_tok[q] = tok;
+    i_slot[q] = slot;
+    if (want_out) {
+      const int64_t o = (int64_t)h * a.out_ld + a.out_col0 + tok;
+      if (a.slot_out) a.slot_out[o] = slot;
+      if (a.merged_out) a.merged_out[o] = 0;
+    }
+  }
+  if (want_out) {
+    for (int i = tid; i < T; i += kPlanThreads) {
+      const int dv = dec[i];
+      if (dv < 0) continue;
+      const int64_t o = (int64_t)h * a.out_ld + a.out_col0 + i;
+      if (a.slot_out) a.slot_out[o] = dv;
+      if (a.merged_out) a.merged_out[o] = 1;
+    }
+  }
+  if (tid == 0) {
+    c.n_live[h] = n_live + m - need;
+    if (need > 0) c.evicted_tokens[h] += (int64_t)ps.evicted_count;
+    int64_t* cn = c.counters + (int64_t)h * kNumCounters;
+    cn[kCntTokens] += T;
+    cn[kCntMerged] += M;
+    cn[kCntInserted] += m;
+    cn[kCntEvictedSlots] += need;
+    int32_t* pl = c.plan + (int64_t)h * kPlanStride;
+    pl[kPlanGroups] = n_groups;
+    pl[kPlanInserts] = m;
+    pl[kPlanMergeTokens] = M;
+    pl[kPlanEvict] = need;
+  }
+}
+
+template <typename T> __device__ __forceinline__ void store_mirror(T* p, float v);
+template <> __device__ __forceinline__ void store_mirror<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_mirror<uint16_t>(uint16_t* p, float v) {
+  *p = (uint16_t)f32_to_bf16_bits(v);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeArgs a) {
+#pragma clang fp contract(off)
+  constexpr int E = D / kWave;  // features per lane
+  const int h = blockIdx.y;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int B = dm.B, L = dm.L;
+  const int32_t* pl = c.plan + (int64_t)h * kPlanStride;
+  const int ng = pl[kPlanGroups], nins = pl[kPlanInserts];
+  if (w >= ng + nins) return;
+  const int f = *c.frame;
+  const T* kin = static_cast<const T*>(a.k) + (int64_t)h * a.sx_h;
+  const T* vin = static_cast<const T*>(a.v) + (int64_t)h * a.sx_h;
+  T* kmir = static_cast<T*>(c.k_mirror);
+  T* vmir = static_cast<T*>(c.v_mirror);
+
+  if (w < ng) {
+    const int s = c.group_slot[(int64_t)h * B + w];
+    const int k0 = c.group_start[(int64_t)h * (B + 1) + w];
+    const int k1 = c.group_start[(int64_t)h * (B + 1) + w + 1];
+    const int64_t row = ((int64_t)h * B + s) * D + lane * E;
+    const int c0 = c.count[(int64_t)h * B + s];
+    float km[E], vm[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      km[e] = c.k_master[row + e];
+      vm[e] = c.v_master[row + e];
+    }
+    for (int k = k0; k < k1; ++k) {
+      const int tok = c.group_tok[(int64_t)h * B + k];
+      const float div = (float)(c0 + (k - k0) + 1);
+      const T* kp = kin + (int64_t)tok * a.sx_n + lane * E;
+      const T* vp = vin + (int64_t)tok * a.sx_n + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float dk = load_f32<T>(kp + e) - km[e];
+        const float dv = load_f32<T>(vp + e) - vm[e];
+        const float qk = dk / div;
+        const float qv = dv / div;
+        km[e] = km[e] + qk;
+        vm[e] = vm[e] + qv;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      c.k_master[row + e] = km[e];
+      c.v_master[row + e] = vm[e];
+      store_mirror<T>(kmir + row + e, km[e]);
+      store_mirror<T>(vmir + row + e, vm[e]);
+    }
+    if (lane == 0) {
+      c.count[(int64_t)h * B + s] = c0 + (k1 - k0);
+      c.last[(int64_t)h * B + s] = f;
+    }
+  } else {
+    const int q = w - ng;
+    const int tok = c.ins_tok[(int64_t)h * B + q];
+    const int s = c.ins_slot[(int64_t)h * B + q];
+    const int64_t row = ((int64_t)h * B + s) * D + lane * E;
+    const T* kp = kin + (int64_t)tok * a.sx_n + lane * E;
+    const T* vp = vin + (int64_t)tok * a.sx_n + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const T kr = kp[e], vr = vp[e];
+      c.k_master[row + e] = load_f32<T>(&kr);
+      c.v_master[row + e] = load_f32<T>(&vr);
+      kmir[row + e] = kr;
+      vmir[row + e] = vr;
+    }
+    if (lane == 0) {
+      c.count[(int64_t)h * B + s] = 1;
+      c.last[(int64_t)h * B + s] = f;
+    }
+    if (lane < L)
+      c.codes[((int64_t)h * L + lane) * B + s] =
+          a.codes[((int64_t)h * L + lane) * a.codes_ld + a.codes_col0 + tok];
+  }
+}
+
+}  // namespace
+
+static int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+hipError_t launch_plan(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s) {
+  const int Tp = next_pow2(a.T < 2 ? 2 : a.T);
+  const size_t lds = (size_t)Tp * 4 + (size_t)a.T * 8 + (size_t)((dm.B + 31) / 32) * 4 +
+                     (size_t)(kPlanWaves + 256) * 4;
+  hipLaunchKernelGGL(plan_kernel, dim3(dm.H), dim3(kPlanThreads), lds, s, dm, c, a, Tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const dim3 grid((a.T + 3) / 4, dm.H);
+  if (dm.elem == 2) {
+    if (dm.d == 128) hipLaunchKernelGGL((apply_kernel<uint16_t, 128>), grid, dim3(256), 0, s, dm, c, a);
+    else hipLaunchKernelGGL((apply_kernel<uint16_t, 64>), grid, dim3(256), 0, s, dm, c, a);
+  } else {
+    if (dm.d == 128) hipLaunchKernelGGL((apply_kernel<float, 128>), grid, dim3(256), 0, s, dm, c, a);
+    else hipLaunchKernelGGL((apply_kernel<float, 64>), grid, dim3(256), 0, s, dm, c, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rehash(const Dims& dm, const CacheDev& c, int T, hipStream_t s) {
+  HashArgs h{};
+  h.x = c.k_mirror;
+  h.sx_h = (int64_t)dm.B * dm.d;
+  h.sx_n = dm.d;
+  h.H = dm.H;
+  h.N = T;
+  h.d = dm.d;
+  h.L = dm.L;
+  h.b = dm.b;
+  h.planes = c.planes;
+  h.codes = c.codes;
+  h.codes_ld = dm.B;
+  h.codes_col0 = 0;
+  h.rows = c.group_slot;
+  h.rows_ld = dm.B;
+  h.n_rows = c.plan + kPlanGroups;
+  h.n_rows_stride = kPlanStride;
+  return dm.elem == 2 ? launch_hash_bf16(h, s) : launch_hash_f32(h, s);
+}
+
+}  // namespace fastar

@@ -1,0 +1,327 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Tolerances: hash bits identical except where the float64 projection has
+|proj| < 1e-4 (counted); match indices, decisions, counts and the binary32
+slot state bit-exact given identical codes; attention outputs within max-abs
+2e-2 (bf16) or 1e-4 (fp32); Lemma 5.1 within 1e-5 (fp32).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_attention_tempcache_amd as fa
+from oracle import TempCacheOracle, simhash
+from oracle import annca as oannca
+from synth import WORKLOADS, ClusterPrompt, DriftStream
+from tests.helpers import (ambiguous_bit_mask, compare_codes, compare_state, mirror_to_f32,
+                           oracle_codes_for_device, oracle_state_for_import, to_device)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _cache_for(w, planes):
+    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+    return fa.Cache(cfg, planes)
+
+
+def _planes_dev(planes, dtype):
+    return to_device(planes, dtype).contiguous()
+
+
+# ------------------------------------------------------------------ hash
+
+@pytest.mark.parametrize("dtype,H,N,d,L,b", [
+    ("bf16", 3, 200, 128, 4, 32),
+    ("bf16", 2, 97, 64, 4, 16),
+    ("bf16", 1, 33, 128, 3, 20),
+    ("bf16", 2, 64, 128, 8, 32),
+    ("f32", 1, 64, 64, 1, 16),
+    ("f32", 2, 50, 128, 4, 32),
+])
+def test_hash_matches_oracle(dtype, H, N, d, L, b):
+    rng = np.random.default_rng(11 + N)
+    from synth import round_to_storage
+    x = round_to_storage(rng.standard_normal((H, N, d)).astype(np.float32), dtype)
+    planes = round_to_storage(rng.standard_normal((L, b, d)).astype(np.float32), dtype)
+    codes = fa.hash_codes(to_device(x, dtype), _planes_dev(planes, dtype), L, b)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy().view(np.uint32)
+    bad = amb = 0
+    for h in range(H):
+        ref, _ = simhash(x[h], planes)
+        mask = ambiguous_bit_mask(x[h], planes)
+        nb, na = compare_codes(got[h].T, ref, mask)
+        bad += nb
+        amb += na
+    print(f"hash {dtype} H={H} N={N} d={d} L={L} b={b}: ambiguous differing bits={amb}")
+    assert bad == 0
+
+
+def test_hash_zero_bits_gives_zero_codes():
+    x = torch.randn(2, 40, 128, device="cuda").to(torch.bfloat16)
+    planes = torch.zeros(0, dtype=torch.bfloat16, device="cuda")
+    codes = fa.hash_codes(x, planes, 3, 0)
+    torch.cuda.synchronize()
+    assert (codes == 0).all()
+
+
+# ------------------------------------------------------------------ match / merge
+
+def _run_frames(w, frames, check_every=True, use_gpu_hash=False):
+    st = DriftStream(w)
+    planes = st.planes()
+    orc = TempCacheOracle.for_workload(w, planes)
+    cache = _cache_for(w, planes)
+    H, T = w.heads, w.tokens_per_frame
+    amb_total = 0
+    last_q = None
+    for f in range(frames):
+        K, V, Q, _ = st.next_frame()
+        res = orc.process_frame(K, V)
+        near = sum(int(r.near_tie.sum()) for r in res)
+        assert near == 0, f"frame {f}: {near} near-ties"
+        codes = None if use_gpu_hash else oracle_codes_for_device([r.codes for r in res])
+        slot_out = torch.full((H, T), -7, dtype=torch.int32, device="cuda")
+        merged_out = torch.full((H, T), 7, dtype=torch.uint8, device="cuda")
+        cache.match_merge(to_device(K, w.dtype), to_device(V, w.dtype), T, 1, codes=codes,
+                          slot_out=slot_out, merged_out=merged_out)
+        torch.cuda.synchronize()
+        so = slot_out.cpu().numpy()
+        mo = merged_out.cpu().numpy()
+        for h in range(H):
+            np.testing.assert_array_equal(mo[h].astype(bool), res[h].merged, err_msg=f"frame {f} head {h}")
+            np.testing.assert_array_equal(so[h], res[h].slot, err_msg=f"frame {f} head {h}")
+        if check_every or f == frames - 1:
+            gst = cache.export_state()
+            compare_state(gst, orc, w.dtype)
+            # slot codes: identical except ambiguous bits; re-sync those
+            ost = orc.state()
+            resync = False
+            for h in range(H):
+                n = int(ost["n_live"][h])
+                mask = ambiguous_bit_mask(ost["k_hat"][h, :n], planes)
+                nb, na = compare_codes(gst["codes"][h][:, :n].T, ost["codes"][h, :n], mask)
+                assert nb == 0, f"frame {f} head {h}: {nb} non-ambiguous code bits differ"
+                amb_total += na
+                resync |= na > 0
+            if resync:
+                cache.import_state({"codes": np.ascontiguousarray(ost["codes"].transpose(0, 2, 1)),
+                                    "frame": ost["frame"]})
+        last_q = Q
+    return orc, cache, amb_total, last_q
+
+
+@pytest.mark.parametrize("name,overrides,frames", [
+    ("tiny", {}, 5),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048), 6),
+    ("dit1.3b", dict(heads=3, tokens_per_frame=129, budget=180, seed=77), 8),   # eviction
+    ("dit14b", dict(heads=2, tokens_per_frame=250, budget=300, head_dim=64, seed=78), 7),  # eviction
+])
+def test_match_merge_matches_oracle_given_codes(name, overrides, frames):
+    w = WORKLOADS[name].with_(**overrides)
+    print(f"match_merge parity: {w.name} {overrides} frames={frames}", flush=True)
+    orc, cache, amb, _ = _run_frames(w, frames)
+    ev = sum(h.evicted_tokens for h in orc.heads)
+    print(f"  ambiguous slot-code bits re-synced: {amb}; evicted tokens: {ev}")
+
+
+def test_eviction_really_happens_in_the_small_budget_case():
+    w = WORKLOADS["dit1.3b"].with_(heads=3, tokens_per_frame=129, budget=180, seed=77)
+    orc, cache, _, _ = _run_frames(w, 8, check_every=False)
+    assert cache.stats()["evicted_slots"] > 0
+    assert sum(h.evicted_tokens for h in orc.heads) > 0
+
+
+def test_gpu_hashing_end_to_end_matches_oracle():
+    """Library hashes the keys itself (bf16 MFMA); decisions still match the oracle."""
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=256, budget=1024, seed=91)
+    _run_frames(w, 5, check_every=False, use_gpu_hash=True)
+
+
+def test_frame_split_invariance():
+    """One call with 3 frames == three calls with one frame each (bit-identical state)."""
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=200, budget=900, seed=5)
+    st = DriftStream(w)
+    planes = st.planes()
+    K, V, _ = st.frames(6)
+    a, b = _cache_for(w, planes), _cache_for(w, planes)
+    T = w.tokens_per_frame
+    kd, vd = to_device(K, w.dtype), to_device(V, w.dtype)
+    a.match_merge(kd[:, :3 * T], vd[:, :3 * T], T, 3)
+    a.match_merge(kd[:, 3 * T:], vd[:, 3 * T:], T, 3)
+    for f in range(6):
+        b.match_merge(kd[:, f * T:(f + 1) * T], vd[:, f * T:(f + 1) * T], T, 1)
+    torch.cuda.synchronize()
+    sa, sb = a.export_state(), b.export_state()
+    for key in ("k_master", "v_master", "k_mirror", "v_mirror", "count", "last", "codes",
+                "n_live", "evicted_tokens"):
+        np.testing.assert_array_equal(sa[key], sb[key], err_msg=key)
+    assert sa["frame"] == sb["frame"] == 6
+
+
+def test_determinism_two_runs():
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=300, budget=700, seed=6)
+    outs = []
+    for _ in range(2):
+        st = DriftStream(w)
+        planes = st.planes()
+        K, V, _ = st.frames(5)
+        c = _cache_for(w, planes)
+        c.match_merge(to_device(K, w.dtype), to_device(V, w.dtype), w.tokens_per_frame, 5)
+        torch.cuda.synchronize()
+        outs.append(c.export_state())
+    for key in outs[0]:
+        np.testing.assert_array_equal(np.asarray(outs[0][key]), np.asarray(outs[1][key]), err_msg=key)
+
+
+def test_conservation_on_device():
+    w = WORKLOADS["dit1.3b"].with_(heads=3, tokens_per_frame=129, budget=170, seed=8)
+    st = DriftStream(w)
+    planes = st.planes()
+    K, V, _ = st.frames(9)
+    c = _cache_for(w, planes)
+    c.match_merge(to_device(K, w.dtype), to_device(V, w.dtype), w.tokens_per_frame, 9)
+    torch.cuda.synchronize()
+    s = c.export_state()
+    stats = c.stats()
+    for h in range(w.heads):
+        n = int(s["n_live"][h])
+        assert n <= w.budget
+        assert (s["count"][h, :n] >= 1).all()
+        assert int(s["count"][h, :n].sum()) + int(s["evicted_tokens"][h]) == 9 * w.tokens_per_frame
+    assert stats["tokens_seen"] == 9 * w.tokens_per_frame * w.heads
+    assert stats["merged_tokens"] + stats["inserted_tokens"] == stats["tokens_seen"]
+
+
+# ------------------------------------------------------------------ attend
+
+@pytest.mark.parametrize("name,overrides,frames", [
+    ("tiny", {}, 5),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048), 6),
+    ("dit1.3b", dict(heads=3, tokens_per_frame=131, budget=1024, head_dim=64, seed=3), 4),
+    ("dit14b", dict(heads=2, tokens_per_frame=333, budget=4096, seed=4), 5),
+])
+def test_attend_matches_oracle(name, overrides, frames):
+    w = WORKLOADS[name].with_(**overrides)
+    st = DriftStream(w)
+    planes = st.planes()
+    orc = TempCacheOracle.for_workload(w, planes)
+    Q = None
+    for _ in range(frames):
+        K, V, Q, _ = st.next_frame()
+        orc.process_frame(K, V)
+    cache = _cache_for(w, planes)
+    cache.import_state(oracle_state_for_import(orc, w.dtype))
+    lse = torch.empty((w.heads, Q.shape[1]), dtype=torch.float32, device="cuda")
+    out = cache.attend(to_device(Q, w.dtype), lse=lse)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = orc.attend(Q)
+    got = out.float().cpu().numpy()
+    err = np.abs(got - O_ref).max()
+    lerr = np.abs(lse.cpu().numpy() - lse_ref).max()
+    print(f"attend {w.name} {overrides}: n_live={[h.n_live for h in orc.heads]} max-abs={err:.3e} lse={lerr:.3e}")
+    assert err <= TOL[w.dtype]
+    assert lerr <= (1e-3 if w.dtype == "bf16" else 1e-5) * max(1.0, np.abs(lse_ref).max())
+
+
+def test_attend_values_one_give_one():
+    """Softmax rows sum to one: with every stored value 1 the output is 1."""
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=300, budget=2048, seed=12)
+    st = DriftStream(w)
+    planes = st.planes()
+    orc = TempCacheOracle.for_workload(w, planes)
+    for _ in range(4):
+        K, V, Q, _ = st.next_frame()
+        orc.process_frame(K, V)
+    s = oracle_state_for_import(orc, w.dtype)
+    s["v_mirror"] = np.full_like(s["v_mirror"], 0x3F80)  # bf16 1.0
+    cache = _cache_for(w, planes)
+    cache.import_state(s)
+    out = cache.attend(to_device(Q, w.dtype))
+    torch.cuda.synchronize()
+    assert np.abs(out.float().cpu().numpy() - 1.0).max() <= 1e-2
+
+
+def test_attend_empty_cache_gives_zeros():
+    w = WORKLOADS["dit1.3b"].with_(heads=2, budget=256)
+    cache = _cache_for(w, DriftStream(w).planes())
+    q = torch.randn(2, 70, 128, device="cuda").to(torch.bfloat16)
+    lse = torch.zeros(2, 70, device="cuda")
+    out = cache.attend(q, lse=lse)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isinf(lse).all()
+
+
+def test_lemma51_on_gpu_fp32():
+    """Full GPU path (hash, match, merge, attend) on exact duplicates = dense attention."""
+    w = WORKLOADS["tiny_lemma"]
+    st = DriftStream(w)
+    planes = st.planes()
+    cache = _cache_for(w, planes)
+    ks, vs = [], []
+    Q = None
+    for _ in range(5):
+        K, V, Q, _ = st.next_frame()
+        cache.match_merge(to_device(K, "f32"), to_device(V, "f32"), w.tokens_per_frame, 1)
+        ks.append(K)
+        vs.append(V)
+    out = cache.attend(to_device(Q, "f32"))
+    torch.cuda.synchronize()
+    Kr = np.concatenate(ks, axis=1)[0].astype(np.float64)
+    Vr = np.concatenate(vs, axis=1)[0].astype(np.float64)
+    q = Q[0].astype(np.float64)
+    z = q @ Kr.T / math.sqrt(w.head_dim)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    dense = (p / p.sum(axis=1, keepdims=True)) @ Vr
+    stats = cache.stats()
+    assert stats["live_slots"] < Kr.shape[0]
+    err = np.abs(out.cpu().numpy()[0] - dense).max()
+    print(f"Lemma 5.1 on GPU: slots={stats['live_slots']} raw={Kr.shape[0]} max-abs={err:.2e}")
+    assert err < 1e-5
+
+
+# ------------------------------------------------------------------ AnnCA
+
+def test_annca_select_and_sparse_attend_match_oracle():
+    cp = ClusterPrompt(heads=2, queries_per_frame=300, frames=3)
+    H, F, Nf, Np = 2, 3, 300, cp.prompt_tokens
+    planes = cp.planes()
+    q_dev = to_device(cp.Q, "bf16")
+    kp_dev, vp_dev = to_device(cp.Kp, "bf16"), to_device(cp.Vp, "bf16")
+    pl_dev = _planes_dev(planes, "bf16")
+    qc = fa.hash_codes(q_dev, pl_dev, cp.tables, cp.bits)
+    pc = fa.hash_codes(kp_dev, pl_dev, cp.tables, cp.bits)
+    torch.cuda.synchronize()
+    # device codes vs oracle codes (ambiguity-tolerant)
+    for h in range(H):
+        for x, got in ((cp.Q[h], qc[h]), (cp.Kp[h], pc[h])):
+            ref, _ = simhash(x, planes)
+            nb, _ = compare_codes(got.cpu().numpy().view(np.uint32).T, ref,
+                                  ambiguous_bit_mask(x, planes))
+            assert nb == 0
+    # selection given identical (oracle) codes: exact
+    oq = [simhash(cp.Q[h], planes)[0] for h in range(H)]
+    op = [simhash(cp.Kp[h], planes)[0] for h in range(H)]
+    sel, cnt = fa.annca_select(oracle_codes_for_device(oq), oracle_codes_for_device(op), F)
+    out = fa.attend_subset(q_dev, kp_dev, vp_dev, F, sel, cnt)
+    dense = fa.attend_subset(q_dev, kp_dev, vp_dev, F)
+    torch.cuda.synchronize()
+    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    got = out.float().cpu().numpy()
+    got_dense = dense.float().cpu().numpy()
+    for h in range(H):
+        for g in range(F):
+            rows = slice(g * Nf, (g + 1) * Nf)
+            r = oannca.annca_frame(cp.Q[h, rows], cp.Kp[h], cp.Vp[h], planes,
+                                   codes_q=oq[h][rows], codes_p=op[h])
+            n = int(cnt_h[h, g])
+            assert n == r["sel"].size
+            np.testing.assert_array_equal(sel_h[h, g, :n], r["sel"])
+            assert np.abs(got[h, rows] - r["o_sparse"]).max() <= 2e-2
+            assert np.abs(got_dense[h, rows] - r["o_dense"]).max() <= 2e-2
+    print(f"AnnCA kept per frame: {cnt_h.tolist()} of {Np}")
