@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "common.hpp"
 #include "fastar.h"
@@ -77,13 +78,14 @@ fastar_status make_dims(const fastar_config* cfg, Dims* dm) {
   dm->nb_bits = nb;
   dm->NB = 1 << nb;
   dm->Ppad = (dm->L * dm->b + 31) & ~31;
+  dm->Bp = (dm->B + kSlotPad - 1) / kSlotPad * kSlotPad;
   return FASTAR_OK;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 enum Region {
-  kPlanes, kKMaster, kVMaster, kKMirror, kVMirror, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
+  kPlanes, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
   kNLive, kEvicted, kCounters, kFrame, kStateEnd = kFrame,
   kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupStart, kGroupSlot, kInsTok, kInsSlot,
   kPlan, kNumRegions
@@ -132,8 +134,10 @@ Layout make_layout(const Dims& dm) {
   sizes[kPlanes] = (size_t)(dm.L * dm.b > 0 ? dm.L * dm.b : 1) * d * e;
   sizes[kKMaster] = H * B * d * 4;
   sizes[kVMaster] = H * B * d * 4;
-  sizes[kKMirror] = H * B * d * e;
-  sizes[kVMirror] = H * B * d * e;
+  const size_t Bp = dm.Bp;
+  sizes[kKMirror] = H * Bp * d * e;
+  sizes[kVMirror] = H * Bp * d * e;
+  sizes[kLb] = H * Bp * 4;
   sizes[kCount] = H * B * 4;
   sizes[kLast] = H * B * 4;
   sizes[kCodes] = H * Lt * B * 4;
@@ -172,6 +176,7 @@ CacheDev carve(void* base, const Dims& dm) {
   c.v_master = reinterpret_cast<float*>(b + L.off[kVMaster]);
   c.k_mirror = b + L.off[kKMirror];
   c.v_mirror = b + L.off[kVMirror];
+  c.lb = reinterpret_cast<float*>(b + L.off[kLb]);
   c.count = reinterpret_cast<int32_t*>(b + L.off[kCount]);
   c.last = reinterpret_cast<int32_t*>(b + L.off[kLast]);
   c.codes = reinterpret_cast<uint32_t*>(b + L.off[kCodes]);
@@ -233,6 +238,7 @@ fastar_status fastar_cache_create(const fastar_config* cfg, const void* planes_h
   const size_t plane_bytes = (size_t)dm.L * dm.b * dm.d * dm.elem;
   if (plane_bytes) FASTAR_HIP(hipMemcpyAsync(dev.planes, planes_host, plane_bytes,
                                              hipMemcpyHostToDevice, s));
+  FASTAR_HIP(launch_finalize_state(dm, dev, s));
   FASTAR_HIP(hipStreamSynchronize(s));
   fastar_cache_s* c = new fastar_cache_s;
   c->cfg = *cfg;
@@ -257,6 +263,7 @@ fastar_status fastar_cache_reset(fastar_cache_t c, void* stream) {
   uint8_t* b = static_cast<uint8_t*>(c->ws);
   const size_t lo = c->lay.off[kKMaster], hi = c->lay.off[kStateEnd + 1];
   FASTAR_HIP(zero_bytes(b + lo, hi - lo, static_cast<hipStream_t>(stream)));
+  FASTAR_HIP(launch_finalize_state(c->dm, c->dev, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -377,13 +384,20 @@ fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_
   FASTAR_REQUIRE(o_stride_h % vec == 0 && o_stride_n % vec == 0 && o_stride_n >= dm.d,
                  "o strides must be multiples of 16 bytes");
   FASTAR_REQUIRE(lse_dev == nullptr || aligned(lse_dev, 4), "lse misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float sc = scale == 0.0f ? 1.0f / std::sqrt((float)dm.d) : scale;
+  if (dm.elem == 2) {
+    CacheAttendArgs ca{q_dev, stride_h, stride_n, o_dev, o_stride_h, o_stride_n, lse_dev, Nq, sc};
+    FASTAR_HIP(launch_attend_cache_bf16(dm, c->dev, ca, s));
+    return ok();
+  }
   AttendArgs a{};
   a.q = q_dev;
   a.sq_h = stride_h;
   a.sq_n = stride_n;
   a.k = c->dev.k_mirror;
   a.v = c->dev.v_mirror;
-  a.sk_h = (int64_t)dm.B * dm.d;
+  a.sk_h = (int64_t)dm.Bp * dm.d;
   a.sk_n = dm.d;
   a.count = c->dev.count;
   a.count_ld = dm.B;
@@ -399,9 +413,8 @@ fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_
   a.d = dm.d;
   a.Nseg = Nq;
   a.F = 1;
-  a.scale = scale == 0.0f ? 1.0f / std::sqrt((float)dm.d) : scale;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  FASTAR_HIP(dm.elem == 2 ? launch_attend_bf16(a, s) : launch_attend_f32(a, s));
+  a.scale = sc;
+  FASTAR_HIP(launch_attend_f32(a, s));
   return ok();
 }
 
@@ -449,8 +462,22 @@ fastar_status fastar_cache_export(fastar_cache_t c, void* stream, fastar_cache_s
   };
   FASTAR_HIP(cp(out->k_master, d.k_master, HBd * 4));
   FASTAR_HIP(cp(out->v_master, d.v_master, HBd * 4));
-  FASTAR_HIP(cp(out->k_mirror, d.k_mirror, HBd * dm.elem));
-  FASTAR_HIP(cp(out->v_mirror, d.v_mirror, HBd * dm.elem));
+  const size_t row = (size_t)dm.d * dm.elem;
+  if (out->k_mirror)
+    FASTAR_HIP(hipMemcpy2DAsync(out->k_mirror, (size_t)dm.B * row, d.k_mirror, (size_t)dm.Bp * row,
+                                (size_t)dm.B * row, dm.H, hipMemcpyDeviceToHost, s));
+  std::vector<uint16_t> vgrp;
+  const bool grouped = dm.elem == 2;
+  if (out->v_mirror) {
+    if (grouped) {
+      vgrp.resize((size_t)dm.H * dm.Bp * dm.d);
+      FASTAR_HIP(hipMemcpyAsync(vgrp.data(), d.v_mirror, vgrp.size() * 2, hipMemcpyDeviceToHost, s));
+    } else {
+      FASTAR_HIP(hipMemcpy2DAsync(out->v_mirror, (size_t)dm.B * row, d.v_mirror,
+                                  (size_t)dm.Bp * row, (size_t)dm.B * row, dm.H,
+                                  hipMemcpyDeviceToHost, s));
+    }
+  }
   FASTAR_HIP(cp(out->count, d.count, HB * 4));
   FASTAR_HIP(cp(out->last, d.last, HB * 4));
   FASTAR_HIP(cp(out->codes, d.codes, HB * dm.L * 4));
@@ -459,6 +486,13 @@ fastar_status fastar_cache_export(fastar_cache_t c, void* stream, fastar_cache_s
   int32_t frame = 0;
   FASTAR_HIP(hipMemcpyAsync(&frame, d.frame, 4, hipMemcpyDeviceToHost, s));
   FASTAR_HIP(hipStreamSynchronize(s));
+  if (out->v_mirror && grouped) {
+    uint16_t* dst = static_cast<uint16_t*>(out->v_mirror);
+    for (int h = 0; h < dm.H; ++h)
+      for (int sl = 0; sl < dm.B; ++sl)
+        for (int e = 0; e < dm.d; ++e)
+          dst[((size_t)h * dm.B + sl) * dm.d + e] = vgrp[vmirror_index(h, sl, e, dm.Bp, dm.d, true)];
+  }
   out->frame = frame;
   return ok();
 }
@@ -481,8 +515,26 @@ fastar_status fastar_cache_import(fastar_cache_t c, const fastar_cache_state* in
   };
   FASTAR_HIP(cp(d.k_master, in->k_master, HBd * 4));
   FASTAR_HIP(cp(d.v_master, in->v_master, HBd * 4));
-  FASTAR_HIP(cp(d.k_mirror, in->k_mirror, HBd * dm.elem));
-  FASTAR_HIP(cp(d.v_mirror, in->v_mirror, HBd * dm.elem));
+  const size_t row = (size_t)dm.d * dm.elem;
+  if (in->k_mirror)
+    FASTAR_HIP(hipMemcpy2DAsync(d.k_mirror, (size_t)dm.Bp * row, in->k_mirror, (size_t)dm.B * row,
+                                (size_t)dm.B * row, dm.H, hipMemcpyHostToDevice, s));
+  std::vector<uint16_t> vgrp;
+  if (in->v_mirror) {
+    if (dm.elem == 2) {
+      vgrp.assign((size_t)dm.H * dm.Bp * dm.d, 0);
+      const uint16_t* src = static_cast<const uint16_t*>(in->v_mirror);
+      for (int h = 0; h < dm.H; ++h)
+        for (int sl = 0; sl < dm.B; ++sl)
+          for (int e = 0; e < dm.d; ++e)
+            vgrp[vmirror_index(h, sl, e, dm.Bp, dm.d, true)] = src[((size_t)h * dm.B + sl) * dm.d + e];
+      FASTAR_HIP(hipMemcpyAsync(d.v_mirror, vgrp.data(), vgrp.size() * 2, hipMemcpyHostToDevice, s));
+    } else {
+      FASTAR_HIP(hipMemcpy2DAsync(d.v_mirror, (size_t)dm.Bp * row, in->v_mirror,
+                                  (size_t)dm.B * row, (size_t)dm.B * row, dm.H,
+                                  hipMemcpyHostToDevice, s));
+    }
+  }
   FASTAR_HIP(cp(d.count, in->count, HB * 4));
   FASTAR_HIP(cp(d.last, in->last, HB * 4));
   FASTAR_HIP(cp(d.codes, in->codes, HB * dm.L * 4));
@@ -490,6 +542,7 @@ fastar_status fastar_cache_import(fastar_cache_t c, const fastar_cache_state* in
   FASTAR_HIP(cp(d.evicted_tokens, in->evicted_tokens, (size_t)dm.H * 8));
   const int32_t frame = (int32_t)in->frame;
   FASTAR_HIP(hipMemcpyAsync(d.frame, &frame, 4, hipMemcpyHostToDevice, s));
+  FASTAR_HIP(launch_finalize_state(dm, d, s));
   FASTAR_HIP(launch_index(dm, d, false, s));
   FASTAR_HIP(hipStreamSynchronize(s));
   return ok();

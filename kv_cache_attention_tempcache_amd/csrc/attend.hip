@@ -381,6 +381,212 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles
         l > 0.0f ? (mrun + log2f(l)) * kLn2 : -__builtin_huge_valf();
 }
 
+// ---------------------------------------------------------------------------
+// Attention over a bf16 cache in its own layout: K mirror rows [H][Bp][D], the
+// V mirror grouped by 4 slots ([H][Bp/4][D][4], see vmirror_index) and
+// lb = log2(count) per slot with -inf past n_live.  Tiles of BN slots are
+// copied HBM -> LDS with direct-to-LDS loads (no registers in between): K rows
+// with their 16-byte chunks XOR-swizzled by row so the MFMA operand reads are
+// bank-conflict free, V and lb verbatim.  The grouped V layout makes the P*V
+// operand (4 consecutive keys of one feature) one aligned 8-byte LDS read, so
+// no transpose is needed anywhere.  Slots past n_live inside the last tile have
+// zero rows and lb = -inf, so they need no masking.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+template <int D, int BN, int WAVES>
+struct CCfg {
+  static constexpr int kThreads = WAVES * 64;
+  static constexpr int BM = WAVES * 32;
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kRowChunks = D / 8;
+  static constexpr int kKBytes = BN * D * 2;
+  static constexpr int kVBytes = BN * D * 2;
+  static constexpr int kBuf = kKBytes + kVBytes + BN * 4;
+  static constexpr int kKInstr = kKBytes / 1024;  // wave-wide 1 KiB direct loads per tile
+  static_assert(kKBytes % 1024 == 0 && kBuf % 16 == 0, "tile shape");
+};
+
+template <int D, int BN, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 2) void attend_cache_kernel(Dims dm, CacheDev c,
+                                                                     CacheAttendArgs a, int qtiles) {
+  using C = CCfg<D, BN, WAVES>;
+  // Two distinct LDS objects: the compiler can then tell the buffer being read
+  // from the one the next tile's copy writes, and does not wait for the copy.
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[C::kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kBuf];
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lid / qtiles, qt = lid - h * qtiles;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 31, hf = lane >> 5;
+  const int Bp = dm.Bp;
+  const int nkeys = c.n_live[h];
+  const float cscale = a.scale * kLog2e;
+  const uint16_t* kg = static_cast<const uint16_t*>(c.k_mirror) + (int64_t)h * Bp * D;
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(c.v_mirror) +
+                                                       (int64_t)h * Bp * D);
+  const float* lbg = c.lb + (int64_t)h * Bp;
+
+  auto issue = [&](int k0, uint8_t* buf) {
+    for (int i = wave; i < C::kKInstr; i += WAVES) {
+      const int off = i * 1024 + lane * 16;
+      const int row = off / C::kRowBytes;
+      const int slot = (off - row * C::kRowBytes) >> 4;
+      const int chunk = slot ^ (row & (C::kRowChunks - 1));
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(kg + (int64_t)(k0 + row) * D + chunk * 8),
+                                       (lds_void_t*)(buf + i * 1024), 16, 0, 0);
+    }
+    const uint8_t* vt = vg + (int64_t)k0 * D * 2;
+    for (int i = wave; i < C::kKInstr; i += WAVES)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + i * 1024 + lane * 16),
+                                       (lds_void_t*)(buf + C::kKBytes + i * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < (BN + 63) / 64; ++i) {
+      if (wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(lbg + k0 + i * 64 + lane),
+                                         (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256),
+                                         4, 0, 0);
+    }
+  };
+
+  const int qi = qt * C::BM + wave * 32 + m;
+  const bool qok = qi < a.Nq;
+  bf16x8_t Qf[D / 16];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.sq_h +
+                         (int64_t)(qok ? qi : 0) * a.sq_n + hf * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
+      if (!qok) v = bf16x8_t{};
+      Qf[ks] = v;
+    }
+  }
+  f32x16_t O[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) O[db] = f32x16_t{};
+  float mrun = -__builtin_huge_valf(), lrun = 0.0f;
+
+  // One key tile: read `cur`, while the copy of tile it+1 fills `nxt`.
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int it, int nt) {
+    const uint8_t* vt_lds = cur + C::kKBytes;
+    const float* lb_lds = reinterpret_cast<const float*>(cur + C::kKBytes + C::kVBytes);
+    float4 lbr[BN / 32][4];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg)
+        lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
+    if (it + 1 < nt) issue((it + 1) * BN, nxt);
+
+    f32x16_t S[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) S[kb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        const int row = kb * 32 + m;
+        const int chunk = hf * (D / 16) + ks;
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            cur + row * C::kRowBytes + ((chunk ^ (row & (C::kRowChunks - 1))) << 4));
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[ks], S[kb], 0, 0, 0);
+      }
+    }
+    float mx = -__builtin_huge_valf();
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const float bb[4] = {lbr[kb][jg].x, lbr[kb][jg].y, lbr[kb][jg].z, lbr[kb][jg].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float t = __builtin_fmaf(S[kb][4 * jg + r], cscale, bb[r]);
+          S[kb][4 * jg + r] = t;
+          mx = fmaxf(mx, t);
+        }
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = mx > mrun + 8.0f;
+    if (__ballot(need)) {
+      const float mnew = need ? mx : mrun;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      lrun *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) O[db][j] *= alpha;
+      mrun = mnew;
+    }
+    float ls = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t pf;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = __builtin_amdgcn_exp2f(S[kb][8 * kk + i] - mrun);
+          ls += p;
+          pf[i] = (__bf16)p;
+        }
+        const int g0 = kb * 8 + kk * 4 + hf;  // group of keys kb*32 + kk*16 + 4*hf .. +3
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const uint8_t* vp = vt_lds + ((g0 * D + db * 32 + m) << 3);
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vp);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vp + 2 * D * 8);
+          const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
+          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *reinterpret_cast<const bf16x8_t*>(&vv), pf, O[db], 0, 0, 0);
+        }
+      }
+    }
+    lrun += ls;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  const int nt = (nkeys + BN - 1) / BN;
+  if (nt > 0) issue(0, buf0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < nt; it += 2) {
+    step(buf0, buf1, it, nt);
+    if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
+  }
+
+  const float lt = lrun + __shfl_xor(lrun, 32);
+  if (!qok) return;
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h + (int64_t)qi * a.so_n;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const uint32_t w0 = f32_to_bf16_bits(O[db][4 * jg + 0] * inv) |
+                          (f32_to_bf16_bits(O[db][4 * jg + 1] * inv) << 16);
+      const uint32_t w1 = f32_to_bf16_bits(O[db][4 * jg + 2] * inv) |
+                          (f32_to_bf16_bits(O[db][4 * jg + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + db * 32 + 8 * jg + 4 * hf) = make_uint2(w0, w1);
+    }
+  if (a.lse && hf == 0)
+    a.lse[(int64_t)h * a.Nq + qi] = lt > 0.0f ? (mrun + __log2f(lt)) * kLn2 : -__builtin_huge_valf();
+}
+
+template <int D, int BN, int WAVES>
+hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
+                            hipStream_t s) {
+  using C = CCfg<D, BN, WAVES>;
+  const int qtiles = (a.Nq + C::BM - 1) / C::BM;
+  const int blocks = dm.H * qtiles;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES>), dim3(blocks), dim3(C::kThreads), 0, s,
+                     dm, c, a, qtiles);
+  return hipGetLastError();
+}
+
 template <int D, int QB, int BN, bool GATHER>
 hipError_t launch_bf16_cfg(const AttendArgs& a, hipStream_t s) {
   using C = Cfg<D, QB, BN>;
@@ -398,11 +604,34 @@ hipError_t launch_bf16_cfg(const AttendArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Tile shape: 32-query blocks per wave and keys per LDS tile.
+#ifndef FASTAR_ATTN_QB128
+#define FASTAR_ATTN_QB128 1
+#endif
+#ifndef FASTAR_ATTN_BN
+#define FASTAR_ATTN_BN 64
+#endif
+
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
   const bool gather = a.sel != nullptr;
+  constexpr int QB = FASTAR_ATTN_QB128, BN = FASTAR_ATTN_BN;
   if (a.d == 128)
-    return gather ? launch_bf16_cfg<128, 1, 64, true>(a, s) : launch_bf16_cfg<128, 1, 64, false>(a, s);
+    return gather ? launch_bf16_cfg<128, QB, BN, true>(a, s) : launch_bf16_cfg<128, QB, BN, false>(a, s);
   return gather ? launch_bf16_cfg<64, 2, 64, true>(a, s) : launch_bf16_cfg<64, 2, 64, false>(a, s);
+}
+
+#ifndef FASTAR_CACHE_BN
+#define FASTAR_CACHE_BN 64
+#endif
+#ifndef FASTAR_CACHE_WAVES
+#define FASTAR_CACHE_WAVES 8
+#endif
+
+hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
+                                    hipStream_t s) {
+  constexpr int BN = FASTAR_CACHE_BN, W = FASTAR_CACHE_WAVES;
+  if (dm.d == 128) return launch_cache_cfg<128, BN, W>(dm, c, a, s);
+  return launch_cache_cfg<64, BN, W>(dm, c, a, s);
 }
 
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s) {

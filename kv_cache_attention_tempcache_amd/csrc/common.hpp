@@ -13,6 +13,18 @@
 namespace fastar {
 
 constexpr int kWave = 64;
+constexpr int kSlotPad = 128;  // mirror rows per head are padded to a multiple of this
+
+// Element offset of feature e of slot s of head h in the value mirror.  For
+// bf16 storage the mirror groups 4 consecutive slots per feature
+// ([H][Bp/4][d][4]) so attention reads 4 consecutive keys of one feature as a
+// single 8-byte word (the k-contiguous operand the P*V product needs); fp32
+// storage keeps plain rows ([H][Bp][d]).
+__host__ __device__ __forceinline__ int64_t vmirror_index(int h, int s, int e, int Bp, int d,
+                                                          bool grouped) {
+  return grouped ? (int64_t)h * Bp * d + (int64_t)(s >> 2) * d * 4 + e * 4 + (s & 3)
+                 : ((int64_t)h * Bp + s) * d + e;
+}
 
 // ---------------------------------------------------------------- bfloat16
 // bfloat16 values travel as raw 16-bit patterns.
@@ -49,6 +61,7 @@ enum { kPlanGroups = 0, kPlanInserts = 1, kPlanMergeTokens = 2, kPlanEvict = 3, 
 
 struct Dims {
   int H, d, B, L, b;
+  int Bp;        // B rounded up to a multiple of kSlotPad (mirror rows per head)
   int elem;      // storage bytes per element (2 or 4)
   int nb_bits;   // log2 of buckets per (head, table)
   int NB;        // buckets per (head, table)
@@ -60,8 +73,9 @@ struct CacheDev {
   void* planes;        // [L*b][d] storage dtype
   float* k_master;     // [H][B][d]
   float* v_master;     // [H][B][d]
-  void* k_mirror;      // [H][B][d] storage dtype
-  void* v_mirror;      // [H][B][d] storage dtype
+  void* k_mirror;      // [H][Bp][d] storage dtype
+  void* v_mirror;      // storage dtype, see vmirror_index
+  float* lb;           // [H][Bp] log2(count) of live slots, -inf elsewhere
   int32_t* count;      // [H][B]
   int32_t* last;       // [H][B]
   uint32_t* codes;     // [H][L][B]
@@ -141,6 +155,21 @@ hipError_t launch_plan(const Dims& dm, const CacheDev& c, const MergeArgs& a, hi
 hipError_t launch_apply(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s);
 hipError_t launch_rehash(const Dims& dm, const CacheDev& c, int T, hipStream_t s);
 hipError_t launch_index(const Dims& dm, const CacheDev& c, bool bump_frame, hipStream_t s);
+// Recompute lb from count/n_live and zero the mirrors of slots >= n_live.
+hipError_t launch_finalize_state(const Dims& dm, const CacheDev& c, hipStream_t s);
+
+// Attention of queries over the live slots of a bf16 cache.
+struct CacheAttendArgs {
+  const void* q;
+  int64_t sq_h, sq_n;
+  void* o;
+  int64_t so_h, so_n;
+  float* lse;               // optional [H][Nq]
+  int Nq;
+  float scale;
+};
+hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
+                                    hipStream_t s);
 
 // Attention (TempCache over the live slots, or AnnCA over a per-frame subset).
 struct AttendArgs {

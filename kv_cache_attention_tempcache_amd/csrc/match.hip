@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
   for (int t = 0; t < FASTAR_MAX_TABLES_DEV; ++t)
     qc[t] = t < L ? a.codes[((int64_t)h * L + t) * a.codes_ld + a.codes_col0 + i] : 0u;
 
-  const T* keys = static_cast<const T*>(c.k_mirror) + (int64_t)h * B * D;
+  const T* keys = static_cast<const T*>(c.k_mirror) + (int64_t)h * dm.Bp * D;
   const uint32_t* scodes = c.codes + (int64_t)h * L * B;
   double best = -__builtin_huge_val();
   int best_s = -1;

@@ -276,16 +276,19 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
   const int ng = pl[kPlanGroups], nins = pl[kPlanInserts];
   if (w >= ng + nins) return;
   const int f = *c.frame;
-  const T* kin = static_cast<const T*>(a.k) + (int64_t)h * a.sx_h;
+  const T* kin = static_cast<const T*>(a.k) + (int64_t)h * a.sx_h;  // frame base, head h
   const T* vin = static_cast<const T*>(a.v) + (int64_t)h * a.sx_h;
   T* kmir = static_cast<T*>(c.k_mirror);
   T* vmir = static_cast<T*>(c.v_mirror);
 
+  constexpr bool kGrouped = sizeof(T) == 2;
+  const int Bp = dm.Bp;
   if (w < ng) {
     const int s = c.group_slot[(int64_t)h * B + w];
     const int k0 = c.group_start[(int64_t)h * (B + 1) + w];
     const int k1 = c.group_start[(int64_t)h * (B + 1) + w + 1];
     const int64_t row = ((int64_t)h * B + s) * D + lane * E;
+    const int64_t mrow = ((int64_t)h * Bp + s) * D + lane * E;
     const int c0 = c.count[(int64_t)h * B + s];
     float km[E], vm[E];
 #pragma unroll
@@ -312,18 +315,21 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
     for (int e = 0; e < E; ++e) {
       c.k_master[row + e] = km[e];
       c.v_master[row + e] = vm[e];
-      store_mirror<T>(kmir + row + e, km[e]);
-      store_mirror<T>(vmir + row + e, vm[e]);
+      store_mirror<T>(kmir + mrow + e, km[e]);
+      store_mirror<T>(vmir + vmirror_index(h, s, lane * E + e, Bp, D, kGrouped), vm[e]);
     }
     if (lane == 0) {
-      c.count[(int64_t)h * B + s] = c0 + (k1 - k0);
+      const int cnt = c0 + (k1 - k0);
+      c.count[(int64_t)h * B + s] = cnt;
       c.last[(int64_t)h * B + s] = f;
+      c.lb[(int64_t)h * Bp + s] = __log2f((float)cnt);
     }
   } else {
     const int q = w - ng;
     const int tok = c.ins_tok[(int64_t)h * B + q];
     const int s = c.ins_slot[(int64_t)h * B + q];
     const int64_t row = ((int64_t)h * B + s) * D + lane * E;
+    const int64_t mrow = ((int64_t)h * Bp + s) * D + lane * E;
     const T* kp = kin + (int64_t)tok * a.sx_n + lane * E;
     const T* vp = vin + (int64_t)tok * a.sx_n + lane * E;
 #pragma unroll
@@ -331,16 +337,39 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
       const T kr = kp[e], vr = vp[e];
       c.k_master[row + e] = load_f32<T>(&kr);
       c.v_master[row + e] = load_f32<T>(&vr);
-      kmir[row + e] = kr;
-      vmir[row + e] = vr;
+      kmir[mrow + e] = kr;
+      vmir[vmirror_index(h, s, lane * E + e, Bp, D, kGrouped)] = vr;
     }
     if (lane == 0) {
       c.count[(int64_t)h * B + s] = 1;
       c.last[(int64_t)h * B + s] = f;
+      c.lb[(int64_t)h * Bp + s] = 0.0f;
     }
     if (lane < L)
       c.codes[((int64_t)h * L + lane) * B + s] =
           a.codes[((int64_t)h * L + lane) * a.codes_ld + a.codes_col0 + tok];
+  }
+}
+
+// lb[s] = log2(count[s]) for live slots, -inf for the rest, whose mirror rows
+// are zeroed (attention tiles may cover them; they must contribute nothing).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void finalize_kernel(Dims dm, CacheDev c) {
+  const int h = blockIdx.y;
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (s >= dm.Bp) return;
+  const int n = c.n_live[h];
+  if (s < n) {
+    if (lane == 0) c.lb[(int64_t)h * dm.Bp + s] = __log2f((float)c.count[(int64_t)h * dm.B + s]);
+    return;
+  }
+  if (lane == 0) c.lb[(int64_t)h * dm.Bp + s] = -__builtin_huge_valf();
+  T* kmir = static_cast<T*>(c.k_mirror);
+  T* vmir = static_cast<T*>(c.v_mirror);
+  for (int e = lane; e < D; e += kWave) {
+    kmir[((int64_t)h * dm.Bp + s) * D + e] = T(0);
+    vmir[vmirror_index(h, s, e, dm.Bp, D, sizeof(T) == 2)] = T(0);
   }
 }
 
@@ -373,10 +402,22 @@ hipError_t launch_apply(const Dims& dm, const CacheDev& c, const MergeArgs& a, h
   return hipGetLastError();
 }
 
+hipError_t launch_finalize_state(const Dims& dm, const CacheDev& c, hipStream_t s) {
+  const dim3 grid((dm.Bp + 3) / 4, dm.H);
+  if (dm.elem == 2) {
+    if (dm.d == 128) hipLaunchKernelGGL((finalize_kernel<uint16_t, 128>), grid, dim3(256), 0, s, dm, c);
+    else hipLaunchKernelGGL((finalize_kernel<uint16_t, 64>), grid, dim3(256), 0, s, dm, c);
+  } else {
+    if (dm.d == 128) hipLaunchKernelGGL((finalize_kernel<float, 128>), grid, dim3(256), 0, s, dm, c);
+    else hipLaunchKernelGGL((finalize_kernel<float, 64>), grid, dim3(256), 0, s, dm, c);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_rehash(const Dims& dm, const CacheDev& c, int T, hipStream_t s) {
   HashArgs h{};
   h.x = c.k_mirror;
-  h.sx_h = (int64_t)dm.B * dm.d;
+  h.sx_h = (int64_t)dm.Bp * dm.d;
   h.sx_n = dm.d;
   h.H = dm.H;
   h.N = T;
