@@ -26,9 +26,11 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
   const int q = total >> 3, r = total & 7;
@@ -394,10 +396,10 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
-template <int D, int BN, int WAVES>
+template <int D, int BN, int WAVES, int QB>
 struct CCfg {
   static constexpr int kThreads = WAVES * 64;
-  static constexpr int BM = WAVES * 32;
+  static constexpr int BM = WAVES * 32 * QB;
   static constexpr int kRowBytes = D * 2;
   static constexpr int kRowChunks = D / 8;
   static constexpr int kKBytes = BN * D * 2;
@@ -405,16 +407,22 @@ struct CCfg {
   static constexpr int kBuf = kKBytes + kVBytes + BN * 4;
   static constexpr int kKInstr = kKBytes / 1024;  // wave-wide 1 KiB direct loads per tile
   static_assert(kKBytes % 1024 == 0 && kBuf % 16 == 0, "tile shape");
+  static_assert((2 * kKInstr) % WAVES == 0, "every wave issues the same number of copies");
 };
 
-template <int D, int BN, int WAVES>
-__global__ __launch_bounds__(WAVES * 64, 2) void attend_cache_kernel(Dims dm, CacheDev c,
-                                                                     CacheAttendArgs a, int qtiles) {
-  using C = CCfg<D, BN, WAVES>;
-  // Two distinct LDS objects: the compiler can then tell the buffer being read
-  // from the one the next tile's copy writes, and does not wait for the copy.
+// QB blocks of 32 queries per wave: every K or V fragment read from LDS feeds
+// QB MFMAs, which is what keeps the kernel below the LDS bandwidth (one 1 KiB
+// operand per 32x32x16 MFMA would need all 128 B/clk of a CU's LDS).
+template <int D, int BN, int WAVES, int QB>
+__global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kernel(
+    Dims dm, CacheDev c, CacheAttendArgs a, int qtiles) {
+  using C = CCfg<D, BN, WAVES, QB>;
+  // Three distinct LDS objects: tile it is read from one while the copies of
+  // tiles it+1 and it+2 are in flight into the others.  Distinct objects let
+  // the compiler see that the reads never alias the copies in flight.
   __shared__ __attribute__((aligned(16))) uint8_t buf0[C::kBuf];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t buf2[C::kBuf];
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lid / qtiles, qt = lid - h * qtiles;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -449,39 +457,47 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attend_cache_kernel(Dims dm, Ca
     }
   };
 
-  const int qi = qt * C::BM + wave * 32 + m;
-  const bool qok = qi < a.Nq;
-  bf16x8_t Qf[D / 16];
-  {
+  // queries of this wave: qi = qt*BM + wave*32*QB + qb*32 + m
+  bf16x8_t Qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qt * C::BM + (wave * QB + qb) * 32 + m;
+    const bool qok = qi < a.Nq;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.sq_h +
                          (int64_t)(qok ? qi : 0) * a.sq_n + hf * (D / 2);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
       if (!qok) v = bf16x8_t{};
-      Qf[ks] = v;
+      Qf[qb][ks] = v;
     }
   }
-  f32x16_t O[D / 32];
+  f32x16_t O[D / 32][QB];
+  float mrun[QB], lrun[QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) O[db] = f32x16_t{};
-  float mrun = -__builtin_huge_valf(), lrun = 0.0f;
+  for (int qb = 0; qb < QB; ++qb) {
+    mrun[qb] = -__builtin_huge_valf();
+    lrun[qb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) O[db][qb] = f32x16_t{};
+  }
 
-  // One key tile: read `cur`, while the copy of tile it+1 fills `nxt`.
-  auto step = [&](const uint8_t* cur, uint8_t* nxt, int it, int nt) {
+  // Copies this wave issues per tile: K and V chunks, plus the bias row for
+  // the last wave(s).
+  constexpr int kCopies = 2 * C::kKInstr / WAVES;
+  const bool lb_wave = wave >= WAVES - (BN + 63) / 64;
+
+  // One key tile: read `cur`, issue the copy of tile it+2 into `nxt2`.
+  auto step = [&](const uint8_t* cur, uint8_t* nxt2, int it, int nt) {
     const uint8_t* vt_lds = cur + C::kKBytes;
     const float* lb_lds = reinterpret_cast<const float*>(cur + C::kKBytes + C::kVBytes);
-    float4 lbr[BN / 32][4];
+    if (it + 2 < nt) issue((it + 2) * BN, nxt2);
+
+    f32x16_t S[BN / 32][QB];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg)
-        lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
-    if (it + 1 < nt) issue((it + 1) * BN, nxt);
-
-    f32x16_t S[BN / 32];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) S[kb] = f32x16_t{};
+      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
@@ -490,100 +506,140 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attend_cache_kernel(Dims dm, Ca
         const int chunk = hf * (D / 16) + ks;
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
             cur + row * C::kRowBytes + ((chunk ^ (row & (C::kRowChunks - 1))) << 4));
-        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[ks], S[kb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[qb][ks], S[kb][qb], 0, 0, 0);
       }
     }
-    float mx = -__builtin_huge_valf();
+    float4 lbr[BN / 32][4];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
+    for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const float bb[4] = {lbr[kb][jg].x, lbr[kb][jg].y, lbr[kb][jg].z, lbr[kb][jg].w};
+      for (int jg = 0; jg < 4; ++jg)
+        lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float t = __builtin_fmaf(S[kb][4 * jg + r], cscale, bb[r]);
-          S[kb][4 * jg + r] = t;
-          mx = fmaxf(mx, t);
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const float bb[4] = {lbr[kb][jg].x, lbr[kb][jg].y, lbr[kb][jg].z, lbr[kb][jg].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float t = __builtin_fmaf(S[kb][qb][4 * jg + r], cscale, bb[r]);
+            S[kb][qb][4 * jg + r] = t;
+            mx = fmaxf(mx, t);
+          }
         }
       }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool need = mx > mrun + 8.0f;
-    if (__ballot(need)) {
-      const float mnew = need ? mx : mrun;
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-      lrun *= alpha;
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > mrun[qb] + 8.0f;
+      if (__ballot(need)) {
+        const float mnew = need ? mx : mrun[qb];
+        const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
+        lrun[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) O[db][j] *= alpha;
-      mrun = mnew;
+          for (int j = 0; j < 16; ++j) O[db][qb][j] *= alpha;
+        mrun[qb] = mnew;
+      }
     }
-    float ls = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t pf;
+        bf16x8_t pf[QB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p = __builtin_amdgcn_exp2f(S[kb][8 * kk + i] - mrun);
-          ls += p;
-          pf[i] = (__bf16)p;
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            pf[qb][i] = (__bf16)__builtin_amdgcn_exp2f(S[kb][qb][8 * kk + i] - mrun[qb]);
+          // row sum of the same bf16-rounded weights the MFMA multiplies
+          float ls = lrun[qb];
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            const bf16x2_t pp = {pf[qb][i], pf[qb][i + 1]};
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
+          }
+          lrun[qb] = ls;
         }
-        const int g0 = kb * 8 + kk * 4 + hf;  // group of keys kb*32 + kk*16 + 4*hf .. +3
+        // keys kb*32 + kk*16 + {4*hf..4*hf+3, 8+4*hf..8+4*hf+3}: one 16-byte word
+        const uint8_t* vbase = vt_lds + ((((kb * 2 + kk) * 2 + hf) * D + m) << 4);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const uint8_t* vp = vt_lds + ((g0 * D + db * 32 + m) << 3);
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vp);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vp + 2 * D * 8);
-          const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *reinterpret_cast<const bf16x8_t*>(&vv), pf, O[db], 0, 0, 0);
+          const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vbase + db * 32 * 16);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);
         }
       }
     }
-    lrun += ls;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // Tile it+1 must have landed in LDS (every wave waits for its own copies,
+    // then all meet at the barrier), and this tile's LDS reads must be done
+    // before its buffer is refilled; the copies of tile it+2 stay in flight.
+    // A plain barrier, not __syncthreads(): the latter's fence would also
+    // wait for the it+2 copies.
+    if (it + 2 < nt) {
+      if (lb_wave)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies + 1) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
   };
 
   const int nt = (nkeys + BN - 1) / BN;
   if (nt > 0) issue(0, buf0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int it = 0; it < nt; it += 2) {
-    step(buf0, buf1, it, nt);
+  if (nt > 1) issue(BN, buf1);
+  if (nt > 1) {
+    if (lb_wave)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies + 1) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  for (int it = 0; it < nt; it += 3) {
+    step(buf0, buf2, it, nt);
     if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
+    if (it + 2 < nt) step(buf2, buf1, it + 2, nt);
   }
 
-  const float lt = lrun + __shfl_xor(lrun, 32);
-  if (!qok) return;
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h + (int64_t)qi * a.so_n;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qt * C::BM + (wave * QB + qb) * 32 + m;
+    const float lt = lrun[qb] + __shfl_xor(lrun[qb], 32);
+    if (qi >= a.Nq) continue;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h + (int64_t)qi * a.so_n;
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg) {
-      const uint32_t w0 = f32_to_bf16_bits(O[db][4 * jg + 0] * inv) |
-                          (f32_to_bf16_bits(O[db][4 * jg + 1] * inv) << 16);
-      const uint32_t w1 = f32_to_bf16_bits(O[db][4 * jg + 2] * inv) |
-                          (f32_to_bf16_bits(O[db][4 * jg + 3] * inv) << 16);
-      *reinterpret_cast<uint2*>(op + db * 32 + 8 * jg + 4 * hf) = make_uint2(w0, w1);
-    }
-  if (a.lse && hf == 0)
-    a.lse[(int64_t)h * a.Nq + qi] = lt > 0.0f ? (mrun + __log2f(lt)) * kLn2 : -__builtin_huge_valf();
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const uint32_t w0 = f32_to_bf16_bits(O[db][qb][4 * jg + 0] * inv) |
+                            (f32_to_bf16_bits(O[db][qb][4 * jg + 1] * inv) << 16);
+        const uint32_t w1 = f32_to_bf16_bits(O[db][qb][4 * jg + 2] * inv) |
+                            (f32_to_bf16_bits(O[db][qb][4 * jg + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + db * 32 + 8 * jg + 4 * hf) = make_uint2(w0, w1);
+      }
+    if (a.lse && hf == 0)
+      a.lse[(int64_t)h * a.Nq + qi] =
+          lt > 0.0f ? (mrun[qb] + __log2f(lt)) * kLn2 : -__builtin_huge_valf();
+  }
 }
 
-template <int D, int BN, int WAVES>
+template <int D, int BN, int WAVES, int QB>
 hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                             hipStream_t s) {
-  using C = CCfg<D, BN, WAVES>;
+  using C = CCfg<D, BN, WAVES, QB>;
   const int qtiles = (a.Nq + C::BM - 1) / C::BM;
   const int blocks = dm.H * qtiles;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES>), dim3(blocks), dim3(C::kThreads), 0, s,
-                     dm, c, a, qtiles);
+  hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB>), dim3(blocks), dim3(C::kThreads), 0,
+                     s, dm, c, a, qtiles);
   return hipGetLastError();
 }
 
@@ -626,12 +682,15 @@ hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
 #ifndef FASTAR_CACHE_WAVES
 #define FASTAR_CACHE_WAVES 8
 #endif
+#ifndef FASTAR_CACHE_QB
+#define FASTAR_CACHE_QB 1
+#endif
 
 hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                                     hipStream_t s) {
-  constexpr int BN = FASTAR_CACHE_BN, W = FASTAR_CACHE_WAVES;
-  if (dm.d == 128) return launch_cache_cfg<128, BN, W>(dm, c, a, s);
-  return launch_cache_cfg<64, BN, W>(dm, c, a, s);
+  constexpr int BN = FASTAR_CACHE_BN, W = FASTAR_CACHE_WAVES, QB = FASTAR_CACHE_QB;
+  if (dm.d == 128) return launch_cache_cfg<128, BN, W, QB>(dm, c, a, s);
+  return launch_cache_cfg<64, 64, 4, 1>(dm, c, a, s);
 }
 
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s) {

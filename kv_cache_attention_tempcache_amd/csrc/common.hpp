@@ -16,14 +16,19 @@ constexpr int kWave = 64;
 constexpr int kSlotPad = 128;  // mirror rows per head are padded to a multiple of this
 
 // Element offset of feature e of slot s of head h in the value mirror.  For
-// bf16 storage the mirror groups 4 consecutive slots per feature
-// ([H][Bp/4][d][4]) so attention reads 4 consecutive keys of one feature as a
-// single 8-byte word (the k-contiguous operand the P*V product needs); fp32
-// storage keeps plain rows ([H][Bp][d]).
+// bf16 storage, each block of 16 consecutive slots is stored as two halves of
+// [d][8]: half 0 holds slots {0-3, 8-11} and half 1 slots {4-7, 12-15} of the
+// block, in that order.  That is exactly the set and order of keys one lane
+// supplies as the k-operand of a 32x32x16 MFMA (lane half h, k-slots 8h..8h+7)
+// in the P*V product, so attention reads each operand as one aligned 16-byte
+// word.  fp32 storage keeps plain rows ([H][Bp][d]).
 __host__ __device__ __forceinline__ int64_t vmirror_index(int h, int s, int e, int Bp, int d,
                                                           bool grouped) {
-  return grouped ? (int64_t)h * Bp * d + (int64_t)(s >> 2) * d * 4 + e * 4 + (s & 3)
-                 : ((int64_t)h * Bp + s) * d + e;
+  if (!grouped) return ((int64_t)h * Bp + s) * d + e;
+  const int r = s & 15;
+  const int half = (r >> 2) & 1;
+  const int pos = (r & 3) | ((r >> 3) << 2);
+  return (int64_t)h * Bp * d + ((int64_t)((s >> 4) * 2 + half) * d + e) * 8 + pos;
 }
 
 // ---------------------------------------------------------------- bfloat16
