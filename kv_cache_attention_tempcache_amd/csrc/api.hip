@@ -86,7 +86,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 enum Region {
   kPlanes, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
-  kNLive, kEvicted, kCounters, kFrame, kStateEnd = kFrame,
+  kNLive, kEvicted, kCounters, kOwner, kGsize, kFrame, kStateEnd = kFrame,
   kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupStart, kGroupSlot, kInsTok, kInsSlot,
   kPlan, kNumRegions
 };
@@ -146,6 +146,8 @@ Layout make_layout(const Dims& dm) {
   sizes[kNLive] = H * 4;
   sizes[kEvicted] = H * 8;
   sizes[kCounters] = H * kNumCounters * 8;
+  sizes[kOwner] = H * B * 4;
+  sizes[kGsize] = H * B * 4;
   sizes[kFrame] = 4;
   sizes[kBestSlot] = H * B * 4;
   sizes[kBestCos] = H * B * 4;
@@ -186,6 +188,8 @@ CacheDev carve(void* base, const Dims& dm) {
   c.evicted_tokens = reinterpret_cast<int64_t*>(b + L.off[kEvicted]);
   c.counters = reinterpret_cast<int64_t*>(b + L.off[kCounters]);
   c.frame = reinterpret_cast<int32_t*>(b + L.off[kFrame]);
+  c.owner = reinterpret_cast<int32_t*>(b + L.off[kOwner]);
+  c.gsize = reinterpret_cast<int32_t*>(b + L.off[kGsize]);
   c.best_slot = reinterpret_cast<int32_t*>(b + L.off[kBestSlot]);
   c.best_cos = reinterpret_cast<float*>(b + L.off[kBestCos]);
   c.dec = reinterpret_cast<int32_t*>(b + L.off[kDec]);

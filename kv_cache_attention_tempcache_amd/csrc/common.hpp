@@ -63,6 +63,7 @@ __device__ __forceinline__ uint32_t bucket_of(uint32_t code, int nb_bits) {
 enum { kCntTokens = 0, kCntMerged = 1, kCntInserted = 2, kCntEvictedSlots = 3, kNumCounters = 4 };
 // Per-head plan summary written by the planning kernel of each frame (int32).
 enum { kPlanGroups = 0, kPlanInserts = 1, kPlanMergeTokens = 2, kPlanEvict = 3, kPlanStride = 8 };
+constexpr int32_t kNoOwner = 0x7fffffff;
 
 struct Dims {
   int H, d, B, L, b;
@@ -90,6 +91,11 @@ struct CacheDev {
   int64_t* evicted_tokens;  // [H]
   int64_t* counters;   // [H][kNumCounters]
   int32_t* frame;      // [1]
+  // Per-slot merge bookkeeping of the frame being processed: the lowest token
+  // that merges into the slot (kNoOwner if none) and how many tokens do.  Set
+  // by the match step, consumed and reset by the planning step.
+  int32_t* owner;      // [H][B]
+  int32_t* gsize;      // [H][B]
   // per-frame scratch (a frame has at most B tokens)
   int32_t* best_slot;  // [H][B] top-1 candidate or -1
   float* best_cos;     // [H][B]

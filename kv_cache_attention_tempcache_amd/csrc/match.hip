@@ -119,7 +119,13 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
     const int64_t o = (int64_t)h * B + i;
     c.best_slot[o] = best_s;
     c.best_cos[o] = best_s >= 0 ? (float)best : 0.0f;
-    c.dec[o] = (best_s >= 0 && best >= (double)a.tau) ? best_s : -1;
+    const bool merge = best_s >= 0 && best >= (double)a.tau;
+    c.dec[o] = merge ? best_s : -1;
+    if (merge) {
+      // order-independent: the lowest merging token and the group size
+      atomicMin(&c.owner[(int64_t)h * B + best_s], i);
+      atomicAdd(&c.gsize[(int64_t)h * B + best_s], 1);
+    }
   }
 }
 

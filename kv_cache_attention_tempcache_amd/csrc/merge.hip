@@ -4,10 +4,12 @@
 //
 // plan_kernel (one workgroup per head) decides everything that needs a view of
 // the whole frame:
-//   - groups the merging tokens by target slot, tokens ascending, by sorting the
-//     unique keys slot*T + token in LDS (bitonic): each group then has exactly
+//   - groups the merging tokens by target slot, tokens ascending: the match
+//     step left, per slot, the lowest merging token (the group's leader) and
+//     the group size; one block scan gives every leader its group index and
+//     member offset and every insert its rank; a leader of a group of several
+//     tokens collects the others in token order.  Each group then has exactly
 //     one owner in the apply step, so slot state is never updated atomically;
-//   - ranks the inserting tokens in ascending order (block scan);
 //   - when the inserts exceed the free slots, selects exactly the missing
 //     number of slots not merged into in this frame, smallest
 //     (last updated frame, slot id) first: an 8-bit radix select on `last`
@@ -28,125 +30,116 @@ constexpr int kPlanWaves = kPlanThreads / kWave;
 
 // Exclusive scan over the block; `total` receives the block sum.  Uses
 // s_scan[0..kPlanWaves) and leaves it reusable on return.
-__device__ int block_excl_scan(int v, int* s_scan, int& total) {
+template <typename V>
+__device__ V block_excl_scan(V v, V* s_scan, V& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
+  V x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
+    const V y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
   if (lane == 63) s_scan[w] = x;
   __syncthreads();
   if (w == 0) {
-    int sv = lane < kPlanWaves ? s_scan[lane] : 0;
+    V sv = lane < kPlanWaves ? s_scan[lane] : V(0);
 #pragma unroll
     for (int o = 1; o < kPlanWaves; o <<= 1) {
-      const int y = __shfl_up(sv, o, 64);
+      const V y = __shfl_up(sv, o, 64);
       if (lane >= o) sv += y;
     }
     if (lane < kPlanWaves) s_scan[lane] = sv;
   }
   __syncthreads();
-  const int base = w ? s_scan[w - 1] : 0;
+  const V base = w ? s_scan[w - 1] : V(0);
   total = s_scan[kPlanWaves - 1];
   __syncthreads();
   return base + x - v;
 }
 
 struct PlanShared {
-  int digit, krem, n_groups;
+  int digit, krem;
   unsigned long long evicted_count;
 };
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c, MergeArgs a,
-                                                            int Tp) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t sm[];
+// Three counts per token packed in one 64-bit scan: group leaders (bits
+// 42..62), members of the groups they lead (bits 21..41), inserts (0..20).
+constexpr int kLeadShift = 42, kMemShift = 21;
+constexpr uint64_t kField = (1ull << 21) - 1;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c, MergeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) int32_t sm[];
   const int T = a.T, B = dm.B;
-  uint32_t* keys = sm;                         // [Tp]
-  int32_t* ins_list = (int32_t*)(keys + Tp);   // [T] inserting tokens, ascending
-  int32_t* ev_list = ins_list + T;             // [T] evicted slots, ascending
-  uint32_t* merged_bits = (uint32_t*)(ev_list + T);  // [(B+31)/32]
-  int* s_scan = (int*)(merged_bits + ((B + 31) >> 5));  // [kPlanWaves]
-  int* hist = s_scan + kPlanWaves;              // [256]
+  int32_t* dec_s = sm;                 // [T] merge target of each token, -1 = insert
+  int32_t* ins_list = dec_s + T;       // [T] inserting tokens, ascending
+  int32_t* ev_list = ins_list + T;     // [T] evicted slots, ascending
+  __shared__ uint64_t s_scan64[kPlanWaves];
+  __shared__ int s_scan[kPlanWaves];
+  __shared__ int hist[256];
   __shared__ PlanShared ps;
 
   const int h = blockIdx.x, tid = threadIdx.x;
   const int f = *c.frame;
   const int n_live = c.n_live[h];
-  const int32_t* dec = c.dec + (int64_t)h * B;
+  int32_t* owner = c.owner + (int64_t)h * B;
+  int32_t* gsize = c.gsize + (int64_t)h * B;
+  for (int i = tid; i < T; i += kPlanThreads) dec_s[i] = c.dec[(int64_t)h * B + i];
+  __syncthreads();
+
+  // 1. per token: leader of a merge group (its group size), or insert
   const int per_t = (T + kPlanThreads - 1) / kPlanThreads;
   const int t_lo = min(T, tid * per_t), t_hi = min(T, t_lo + per_t);
-
-  // 1. rank the inserting tokens (ascending token order)
-  int cnt = 0;
-  for (int i = t_lo; i < t_hi; ++i) cnt += dec[i] < 0;
-  int m = 0;
-  int r = block_excl_scan(cnt, s_scan, m);
-  for (int i = t_lo; i < t_hi; ++i)
-    if (dec[i] < 0) ins_list[r++] = i;
-
-  // 2. sort the merging tokens by (slot, token)
-  for (int i = tid; i < Tp; i += kPlanThreads) {
-    const int dv = i < T ? dec[i] : -1;
-    keys[i] = dv >= 0 ? (uint32_t)dv * (uint32_t)T + (uint32_t)i : 0xffffffffu;
-  }
-  __syncthreads();
-  for (int k = 2; k <= Tp; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < Tp; i += kPlanThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint32_t x = keys[i], y = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
+  uint64_t mine = 0;
+  for (int i = t_lo; i < t_hi; ++i) {
+    const int s = dec_s[i];
+    if (s < 0) {
+      mine += 1;
+    } else if (owner[s] == i) {
+      mine += (1ull << kLeadShift) | ((uint64_t)gsize[s] << kMemShift);
     }
   }
+  uint64_t tot = 0;
+  uint64_t run = block_excl_scan<uint64_t>(mine, s_scan64, tot);
+  const int n_groups = (int)(tot >> kLeadShift);
+  const int M = (int)((tot >> kMemShift) & kField);
+  const int m = (int)(tot & kField);
 
-  // 3. groups of equal slot among the M merging tokens
-  const int M = T - m;
+  // 2. group lists (members ascending) and the insert list
   int32_t* g_tok = c.group_tok + (int64_t)h * B;
   int32_t* g_start = c.group_start + (int64_t)h * (B + 1);
   int32_t* g_slot = c.group_slot + (int64_t)h * B;
-  const int k_lo = min(M, tid * per_t), k_hi = min(M, k_lo + per_t);
-  cnt = 0;
-  for (int k = k_lo; k < k_hi; ++k)
-    cnt += (k == 0) || (keys[k] / (uint32_t)T != keys[k - 1] / (uint32_t)T);
-  int n_groups = 0;
-  int g = block_excl_scan(cnt, s_scan, n_groups);
-  for (int k = k_lo; k < k_hi; ++k) {
-    const uint32_t slot = keys[k] / (uint32_t)T;
-    g_tok[k] = (int32_t)(keys[k] % (uint32_t)T);
-    if (k == 0 || slot != keys[k - 1] / (uint32_t)T) {
-      g_start[g] = k;
-      g_slot[g] = (int32_t)slot;
-      ++g;
+  for (int i = t_lo; i < t_hi; ++i) {
+    const int s = dec_s[i];
+    if (s < 0) {
+      ins_list[(int)(run & kField)] = i;
+      run += 1;
+      continue;
     }
+    if (owner[s] != i) continue;
+    const int g = (int)(run >> kLeadShift);
+    const int start = (int)((run >> kMemShift) & kField);
+    const int size = gsize[s];
+    g_slot[g] = s;
+    g_start[g] = start;
+    g_tok[start] = i;
+    // the other members follow the leader in token order
+    for (int j = i + 1, k = 1; k < size && j < T; ++j)
+      if (dec_s[j] == s) g_tok[start + k++] = j;
+    run += (1ull << kLeadShift) | ((uint64_t)size << kMemShift);
   }
   if (tid == 0) g_start[n_groups] = M;
 
-  // 4. eviction, only if the inserts do not fit
+  // 3. eviction, only if the inserts do not fit: exactly `need` slots not
+  //    merged into in this frame (owner unset), smallest (last, slot) first
   const int need = max(0, m - (B - n_live));
   if (need > 0) {
-    for (int w = tid; w < ((B + 31) >> 5); w += kPlanThreads) merged_bits[w] = 0u;
     if (tid == 0) {
       ps.krem = need;
       ps.evicted_count = 0ull;
     }
     __syncthreads();
-    for (int k = tid; k < M; k += kPlanThreads) {
-      const uint32_t slot = keys[k] / (uint32_t)T;
-      atomicOr(&merged_bits[slot >> 5], 1u << (slot & 31));
-    }
-    __syncthreads();
     const int32_t* last = c.last + (int64_t)h * B;
-    auto eligible = [&](int s) { return ((merged_bits[s >> 5] >> (s & 31)) & 1u) == 0u; };
+    auto eligible = [&](int s) { return owner[s] == kNoOwner; };
     // radix select of the need-th smallest `last` among eligible live slots
     // (every eligible slot was last updated before frame f, so last <= f-1)
     uint32_t prefix = 0u;
@@ -185,7 +178,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
     int eq = 0;
     for (int s = s_lo; s < s_hi; ++s) eq += eligible(s) && (uint32_t)last[s] == cut;
     int eq_total = 0;
-    const int eq_base = block_excl_scan(eq, s_scan, eq_total);
+    const int eq_base = block_excl_scan<int>(eq, s_scan, eq_total);
     int evc = 0;
     {
       int er = eq_base;
@@ -197,7 +190,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
       }
     }
     int ev_total = 0;
-    int ep = block_excl_scan(evc, s_scan, ev_total);
+    int ep = block_excl_scan<int>(evc, s_scan, ev_total);
     {
       int er = eq_base;
       unsigned long long tok = 0ull;
@@ -218,6 +211,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   }
   __syncthreads();
 
+  // 4. reset the per-slot bookkeeping for the next frame (leaders own it)
+  for (int i = t_lo; i < t_hi; ++i) {
+    const int s = dec_s[i];
+    if (s >= 0 && owner[s] == i) {
+      owner[s] = kNoOwner;
+      gsize[s] = 0;
+    }
+  }
+
   // 5. slots for the inserts: evicted ids first, then never-used ids, ascending
   int32_t* i_tok = c.ins_tok + (int64_t)h * B;
   int32_t* i_slot = c.ins_slot + (int64_t)h * B;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   }
   if (want_out) {
     for (int i = tid; i < T; i += kPlanThreads) {
-      const int dv = dec[i];
+      const int dv = dec_s[i];
       if (dv < 0) continue;
       const int64_t o = (int64_t)h * a.out_ld + a.out_col0 + i;
       if (a.slot_out) a.slot_out[o] = dv;
@@ -359,6 +361,10 @@ __global__ __launch_bounds__(256) void finalize_kernel(Dims dm, CacheDev c) {
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (s >= dm.Bp) return;
+  if (s < dm.B && lane == 0) {
+    c.owner[(int64_t)h * dm.B + s] = kNoOwner;
+    c.gsize[(int64_t)h * dm.B + s] = 0;
+  }
   const int n = c.n_live[h];
   if (s < n) {
     if (lane == 0) c.lb[(int64_t)h * dm.Bp + s] = __log2f((float)c.count[(int64_t)h * dm.B + s]);
@@ -375,17 +381,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(Dims dm, CacheDev c) {
 
 }  // namespace
 
-static int next_pow2(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
 hipError_t launch_plan(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s) {
-  const int Tp = next_pow2(a.T < 2 ? 2 : a.T);
-  const size_t lds = (size_t)Tp * 4 + (size_t)a.T * 8 + (size_t)((dm.B + 31) / 32) * 4 +
-                     (size_t)(kPlanWaves + 256) * 4;
-  hipLaunchKernelGGL(plan_kernel, dim3(dm.H), dim3(kPlanThreads), lds, s, dm, c, a, Tp);
+  const size_t lds = (size_t)a.T * 3 * 4;
+  hipLaunchKernelGGL(plan_kernel, dim3(dm.H), dim3(kPlanThreads), lds, s, dm, c, a);
   return hipGetLastError();
 }
 
