@@ -142,7 +142,7 @@ Layout make_layout(const Dims& dm) {
   sizes[kLast] = H * B * 4;
   sizes[kCodes] = H * Lt * B * 4;
   sizes[kIdxOff] = H * Lt * ((size_t)dm.NB + 1) * 4;
-  sizes[kIdxSlot] = H * Lt * B * 4;
+  sizes[kIdxSlot] = H * Lt * B * 8;
   sizes[kNLive] = H * 4;
   sizes[kEvicted] = H * 8;
   sizes[kCounters] = H * kNumCounters * 8;
@@ -183,7 +183,7 @@ CacheDev carve(void* base, const Dims& dm) {
   c.last = reinterpret_cast<int32_t*>(b + L.off[kLast]);
   c.codes = reinterpret_cast<uint32_t*>(b + L.off[kCodes]);
   c.idx_off = reinterpret_cast<int32_t*>(b + L.off[kIdxOff]);
-  c.idx_slot = reinterpret_cast<int32_t*>(b + L.off[kIdxSlot]);
+  c.idx_ent = reinterpret_cast<uint2*>(b + L.off[kIdxSlot]);
   c.n_live = reinterpret_cast<int32_t*>(b + L.off[kNLive]);
   c.evicted_tokens = reinterpret_cast<int64_t*>(b + L.off[kEvicted]);
   c.counters = reinterpret_cast<int64_t*>(b + L.off[kCounters]);

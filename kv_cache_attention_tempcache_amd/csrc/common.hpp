@@ -85,8 +85,8 @@ struct CacheDev {
   int32_t* count;      // [H][B]
   int32_t* last;       // [H][B]
   uint32_t* codes;     // [H][L][B]
-  int32_t* idx_off;    // [H][L][NB+1]
-  int32_t* idx_slot;   // [H][L][B]
+  int32_t* idx_off;    // [H][L][NB+1] CSR offsets of the buckets
+  uint2* idx_ent;      // [H][L][B] (slot, code) entries grouped by bucket
   int32_t* n_live;     // [H]
   int64_t* evicted_tokens;  // [H]
   int64_t* counters;   // [H][kNumCounters]

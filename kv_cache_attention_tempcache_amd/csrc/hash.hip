@@ -3,7 +3,9 @@
 // [<r_tj, x> > 0], stored as 1u << j.
 //
 // bf16 path: the projection is a small GEMM (rows x d) * (d x L*b) on the
-// 32x32x16 bf16 MFMA.  A wave owns 32 rows; the hyperplanes sit in LDS.  The
+// 32x32x16 bf16 MFMA.  A wave owns 32 rows and reads the hyperplane operands
+// straight from L2 (a few KiB shared by every wave), with no LDS staging and
+// no block barrier between the loads and the MFMAs.  The
 // accumulator layout puts one hyperplane per lane column and rows in
 // registers, so one wave ballot over a register yields two complete 32-bit
 // words of sign bits (rows r and r+4), already in LSB-first plane order.
@@ -36,19 +38,9 @@ __device__ __forceinline__ uint32_t extract_code(const uint32_t (&w)[9], int off
 template <int D>
 __global__ __launch_bounds__(256) void hash_bf16_kernel(HashArgs a, int tiles_per_head,
                                                         int total_tiles) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int kPitch = D * 2 + 16;  // bytes per LDS hyperplane row (padding avoids conflicts)
   const int P = a.L * a.b;
   const int Ppad = (P + 31) & ~31;
   const uint16_t* planes = static_cast<const uint16_t*>(a.planes);
-  for (int idx = threadIdx.x; idx < Ppad * (D / 8); idx += blockDim.x) {
-    const int row = idx / (D / 8), ch = idx % (D / 8);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < P) v = reinterpret_cast<const uint4*>(planes + (size_t)row * D)[ch];
-    *reinterpret_cast<uint4*>(smem + row * kPitch + ch * 16) = v;
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, hf = lane >> 5;
   // Row owned by this lane in the ballot words: register j = 4*(m/8) + m%4,
@@ -86,11 +78,14 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(HashArgs a, int tiles_pe
 #pragma unroll
     for (int pb = 0; pb < 8; ++pb) {
       if (pb * 32 >= Ppad) break;
+      // B operand straight from L2: hyperplane pb*32 + m (zero past L*b)
+      const int prow = pb * 32 + m;
+      const uint16_t* pp = planes + (int64_t)(prow < P ? prow : 0) * D + hf * (D / 2);
       f32x16_t acc = {};
-      const uint8_t* bp = smem + (pb * 32 + m) * kPitch + (hf * (D / 2)) * 2;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(bp + ks * 16);
+        bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(pp + ks * 8);
+        if (prow >= P) B = bf16x8_t{};
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks], B, acc, 0, 0, 0);
       }
       uint32_t w = 0u;
@@ -146,13 +141,11 @@ hipError_t launch_hash_bf16(const HashArgs& a, hipStream_t s) {
   if (total == 0) return hipSuccess;
   int blocks = (total + kHashWaves - 1) / kHashWaves;
   if (blocks > 4096) blocks = 4096;
-  const int Ppad = (a.L * a.b + 31) & ~31;
-  const size_t lds = (size_t)Ppad * (a.d * 2 + 16) + 16;
   if (a.d == 128)
-    hipLaunchKernelGGL(hash_bf16_kernel<128>, dim3(blocks), dim3(256), lds, s, a, tiles_per_head,
+    hipLaunchKernelGGL(hash_bf16_kernel<128>, dim3(blocks), dim3(256), 0, s, a, tiles_per_head,
                        total);
   else
-    hipLaunchKernelGGL(hash_bf16_kernel<64>, dim3(blocks), dim3(256), lds, s, a, tiles_per_head,
+    hipLaunchKernelGGL(hash_bf16_kernel<64>, dim3(blocks), dim3(256), 0, s, a, tiles_per_head,
                        total);
   return hipGetLastError();
 }

@@ -1,10 +1,11 @@
 // Bucket index over the live slots, rebuilt after every frame (the candidate
 // sets of the next frame's match must reflect merged and inserted slots).
 //
-// One workgroup per (head, table): an LDS histogram of bucket sizes, an
-// exclusive scan into CSR offsets, then a scatter of slot ids.  The order of
-// slots inside a bucket depends on atomic timing, which does not matter: the
-// match reads every slot of a bucket and breaks ties on the slot id.
+// One workgroup per (head, table): LDS atomics give the bucket sizes and each
+// slot's position inside its bucket in one pass; an exclusive scan turns the
+// sizes into CSR offsets; each slot then writes its (slot, code) entry.  The
+// order inside a bucket depends on atomic timing, which does not matter: the
+// match reads every entry of a bucket and breaks ties on the slot id.
 #include "common.hpp"
 
 namespace fastar {
@@ -12,6 +13,9 @@ namespace {
 
 constexpr int kIdxThreads = 1024;
 constexpr int kIdxWaves = kIdxThreads / kWave;
+
+// Slots handled per thread: B <= kIdxThreads * kIdxPer.
+constexpr int kIdxPer = (FASTAR_MAX_BUDGET + kIdxThreads - 1) / kIdxThreads;
 
 __global__ __launch_bounds__(kIdxThreads) void index_kernel(Dims dm, CacheDev c, int bump_frame) {
   extern __shared__ __attribute__((aligned(16))) uint32_t cnt[];  // [NB] then [kIdxWaves]
@@ -23,11 +27,22 @@ __global__ __launch_bounds__(kIdxThreads) void index_kernel(Dims dm, CacheDev c,
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t* codes = c.codes + (int64_t)ht * B;
   int32_t* off = c.idx_off + (int64_t)ht * (NB + 1);
-  int32_t* slots = c.idx_slot + (int64_t)ht * B;
+  uint2* ent = c.idx_ent + (int64_t)ht * B;
 
   for (int i = tid; i < NB; i += kIdxThreads) cnt[i] = 0u;
+  uint32_t code[kIdxPer], pos[kIdxPer];
+#pragma unroll
+  for (int k = 0; k < kIdxPer; ++k) {
+    const int s = tid + k * kIdxThreads;
+    code[k] = s < n ? codes[s] : 0u;
+  }
   __syncthreads();
-  for (int s = tid; s < n; s += kIdxThreads) atomicAdd(&cnt[bucket_of(codes[s], dm.nb_bits)], 1u);
+  // one atomic pass: bucket sizes and each slot's position inside its bucket
+#pragma unroll
+  for (int k = 0; k < kIdxPer; ++k) {
+    const int s = tid + k * kIdxThreads;
+    if (s < n) pos[k] = atomicAdd(&cnt[bucket_of(code[k], dm.nb_bits)], 1u);
+  }
   __syncthreads();
 
   // exclusive scan of cnt: each thread owns a contiguous run of buckets
@@ -62,9 +77,10 @@ __global__ __launch_bounds__(kIdxThreads) void index_kernel(Dims dm, CacheDev c,
   }
   if (tid == 0) off[NB] = n;
   __syncthreads();
-  for (int s = tid; s < n; s += kIdxThreads) {
-    const uint32_t pos = atomicAdd(&cnt[bucket_of(codes[s], dm.nb_bits)], 1u);
-    slots[pos] = s;
+#pragma unroll
+  for (int k = 0; k < kIdxPer; ++k) {
+    const int s = tid + k * kIdxThreads;
+    if (s < n) ent[cnt[bucket_of(code[k], dm.nb_bits)] + pos[k]] = make_uint2((uint32_t)s, code[k]);
   }
   if (bump_frame && ht == 0 && tid == 0) *c.frame += 1;
 }

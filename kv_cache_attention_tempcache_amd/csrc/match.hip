@@ -3,10 +3,11 @@
 // neighbour among earlier frames through LSH, without full attention matrices).
 //
 // A group of 16 lanes owns one token.  For every table it reads the token's
-// bucket from the CSR index, keeps the slots whose code equals the token's code
-// (a bucket may hold several codes), skips slots already seen through an
-// earlier table, and scores each candidate by the cosine of the token key and
-// the slot's stored key.  Products and sums are float64, so the decision agrees
+// bucket from the CSR index of (slot, code) entries, keeps the slots whose code
+// equals the token's code (a bucket may hold several codes), skips slots
+// already scored through an earlier table (a slot remembered in registers; a
+// slot scored twice past that list only costs time), and scores each candidate
+// by the cosine of the token key and the slot's stored key.  Products and sums are float64, so the decision agrees
 // with an exact evaluation except within ~1e-15 of a tie.  Ties go to the
 // lowest slot id; the token merges iff its best cosine >= the threshold.
 //
@@ -59,52 +60,73 @@ __device__ __forceinline__ double group_sum(double x) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchArgs a) {
   constexpr int E = D / kGroup;
+  constexpr int LT = FASTAR_MAX_TABLES_DEV;
+  constexpr int kSeen = 8;  // slots remembered for de-duplication across tables
   const int h = blockIdx.y;
   const int i = blockIdx.x * (256 / kGroup) + (threadIdx.x / kGroup);
   const int gl = threadIdx.x & (kGroup - 1);
   if (i >= a.T) return;  // all 16 lanes of a group leave together
   const int L = dm.L, B = dm.B, NB = dm.NB, nb_bits = dm.nb_bits;
 
+  // All independent loads first: the token's key, its codes, then every
+  // table's bucket bounds and first entry, so the dependent chain per token is
+  // codes -> bucket bounds -> entries -> candidate keys.
   float xv[E];
   load_row<T, E>(static_cast<const T*>(a.x) + (int64_t)h * a.sx_h + (int64_t)i * a.sx_n + gl * E,
                  xv);
+  uint32_t qc[LT];
+#pragma unroll
+  for (int t = 0; t < LT; ++t)
+    qc[t] = t < L ? a.codes[((int64_t)h * L + t) * a.codes_ld + a.codes_col0 + i] : 0u;
+  int beg[LT], end[LT];
+#pragma unroll
+  for (int t = 0; t < LT; ++t) {
+    beg[t] = end[t] = 0;
+    if (t < L) {
+      const int32_t* off = c.idx_off + ((int64_t)h * L + t) * (NB + 1) + bucket_of(qc[t], nb_bits);
+      beg[t] = off[0];
+      end[t] = off[1];
+    }
+  }
+  uint2 first[LT];
+#pragma unroll
+  for (int t = 0; t < LT; ++t)
+    first[t] = (t < L && beg[t] < end[t]) ? c.idx_ent[((int64_t)h * L + t) * B + beg[t]]
+                                            : make_uint2(0u, 0u);
+
   double nx2 = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) nx2 += (double)xv[e] * (double)xv[e];
   nx2 = group_sum(nx2);
 
-  uint32_t qc[FASTAR_MAX_TABLES_DEV];
-#pragma unroll
-  for (int t = 0; t < FASTAR_MAX_TABLES_DEV; ++t)
-    qc[t] = t < L ? a.codes[((int64_t)h * L + t) * a.codes_ld + a.codes_col0 + i] : 0u;
-
   const T* keys = static_cast<const T*>(c.k_mirror) + (int64_t)h * dm.Bp * D;
-  const uint32_t* scodes = c.codes + (int64_t)h * L * B;
   double best = -__builtin_huge_val();
   int best_s = -1;
+  int seen[kSeen];
+  int nseen = 0;
 #pragma unroll
-  for (int t = 0; t < FASTAR_MAX_TABLES_DEV; ++t) {
+  for (int t = 0; t < LT; ++t) {
     if (t >= L) break;
-    const uint32_t code = qc[t];
-    const int64_t ht = (int64_t)h * L + t;
-    const uint32_t bk = bucket_of(code, nb_bits);
-    const int beg = c.idx_off[ht * (NB + 1) + bk];
-    const int end = c.idx_off[ht * (NB + 1) + bk + 1];
-    for (int p = beg; p < end; ++p) {
-      const int s = c.idx_slot[ht * B + p];
-      if (scodes[(int64_t)t * B + s] != code) continue;
-      bool seen = false;
+    const uint2* ent = c.idx_ent + ((int64_t)h * L + t) * B;
+    for (int p = beg[t]; p < end[t]; ++p) {
+      const uint2 e = p == beg[t] ? first[t] : ent[p];
+      if (e.y != qc[t]) continue;  // same bucket, different code
+      const int s = (int)e.x;
+      bool dup = false;
 #pragma unroll
-      for (int t2 = 0; t2 < FASTAR_MAX_TABLES_DEV; ++t2)
-        if (t2 < t && scodes[(int64_t)t2 * B + s] == qc[t2]) seen = true;
-      if (seen) continue;
+      for (int k = 0; k < kSeen; ++k) dup |= (k < nseen) && seen[k] == s;
+      if (dup) continue;  // already scored through an earlier table
+#pragma unroll
+      for (int k = 0; k < kSeen; ++k)
+        if (k == nseen) seen[k] = s;
+      nseen = min(nseen + 1, kSeen);
       float kv[E];
       load_row<T, E>(keys + (int64_t)s * D + gl * E, kv);
       double dot = 0.0, nk2 = 0.0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        dot += (double)xv[e] * (double)kv[e];
-        nk2 += (double)kv[e] * (double)kv[e];
+      for (int q = 0; q < E; ++q) {
+        dot += (double)xv[q] * (double)kv[q];
+        nk2 += (double)kv[q] * (double)kv[q];
       }
       dot = group_sum(dot);
       nk2 = group_sum(nk2);

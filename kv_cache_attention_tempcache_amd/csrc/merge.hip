@@ -15,7 +15,7 @@
 //     (last updated frame, slot id) first: an 8-bit radix select on `last`
 //     finds the cut-off frame, a block scan breaks the tie on slot id;
 //   - gives the inserts the evicted ids, then the never-used ids, ascending.
-// apply_kernel: one wave per merge group or insert.  A merge group replays
+// apply_kernel: 16 lanes per merge group or insert.  A merge group replays
 // m += (x - m) / (count + 1) in binary32, one correctly rounded op at a time,
 // token by token, for the key and the value master, then refreshes the
 // storage-dtype mirrors.  Integer counters in LDS use atomics only where the
@@ -266,14 +266,73 @@ template <> __device__ __forceinline__ void store_mirror<uint16_t>(uint16_t* p, 
   *p = (uint16_t)f32_to_bf16_bits(v);
 }
 
+// Vector of E storage elements as floats (E = 4 or 8).
+template <typename T, int E>
+__device__ __forceinline__ void load_vec(const T* p, float (&v)[E]) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[E / 2];
+    if constexpr (E == 8) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      w[0] = u.x; w[1] = u.y;
+    }
+#pragma unroll
+    for (int k = 0; k < E / 2; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < E; k += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(p + k);
+      v[k] = f.x; v[k + 1] = f.y; v[k + 2] = f.z; v[k + 3] = f.w;
+    }
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void load_f32vec(const float* p, float (&v)[E]) {
+#pragma unroll
+  for (int k = 0; k < E; k += 4) {
+    const float4 f = *reinterpret_cast<const float4*>(p + k);
+    v[k] = f.x; v[k + 1] = f.y; v[k + 2] = f.z; v[k + 3] = f.w;
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void store_f32vec(float* p, const float (&v)[E]) {
+#pragma unroll
+  for (int k = 0; k < E; k += 4) *reinterpret_cast<float4*>(p + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+}
+
+constexpr int kApplyGroup = 16;  // lanes per merge group or insert
+
+// E consecutive mirror elements of one row, stored with one vector store.
+template <typename T, int E>
+__device__ __forceinline__ void store_mirror_vec(T* p, const float (&v)[E]) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[E / 2];
+#pragma unroll
+    for (int k = 0; k < E / 2; ++k)
+      w[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
+    if constexpr (E == 8) *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  } else {
+    store_f32vec<E>(reinterpret_cast<float*>(p), v);
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeArgs a) {
 #pragma clang fp contract(off)
-  constexpr int E = D / kWave;  // features per lane
+  constexpr int E = D / kApplyGroup;  // features per lane
+  constexpr bool kGrouped = sizeof(T) == 2;
   const int h = blockIdx.y;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int B = dm.B, L = dm.L;
+  const int w = blockIdx.x * (256 / kApplyGroup) + (threadIdx.x / kApplyGroup);
+  const int gl = threadIdx.x & (kApplyGroup - 1);
+  const int B = dm.B, L = dm.L, Bp = dm.Bp;
   const int32_t* pl = c.plan + (int64_t)h * kPlanStride;
   const int ng = pl[kPlanGroups], nins = pl[kPlanInserts];
   if (w >= ng + nins) return;
@@ -282,45 +341,41 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
   const T* vin = static_cast<const T*>(a.v) + (int64_t)h * a.sx_h;
   T* kmir = static_cast<T*>(c.k_mirror);
   T* vmir = static_cast<T*>(c.v_mirror);
+  const int e0 = gl * E;
 
-  constexpr bool kGrouped = sizeof(T) == 2;
-  const int Bp = dm.Bp;
   if (w < ng) {
     const int s = c.group_slot[(int64_t)h * B + w];
     const int k0 = c.group_start[(int64_t)h * (B + 1) + w];
     const int k1 = c.group_start[(int64_t)h * (B + 1) + w + 1];
-    const int64_t row = ((int64_t)h * B + s) * D + lane * E;
-    const int64_t mrow = ((int64_t)h * Bp + s) * D + lane * E;
+    const int64_t row = ((int64_t)h * B + s) * D + e0;
     const int c0 = c.count[(int64_t)h * B + s];
     float km[E], vm[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      km[e] = c.k_master[row + e];
-      vm[e] = c.v_master[row + e];
-    }
+    load_f32vec<E>(c.k_master + row, km);
+    load_f32vec<E>(c.v_master + row, vm);
     for (int k = k0; k < k1; ++k) {
       const int tok = c.group_tok[(int64_t)h * B + k];
       const float div = (float)(c0 + (k - k0) + 1);
-      const T* kp = kin + (int64_t)tok * a.sx_n + lane * E;
-      const T* vp = vin + (int64_t)tok * a.sx_n + lane * E;
+      float xk[E], xv[E];
+      load_vec<T, E>(kin + (int64_t)tok * a.sx_n + e0, xk);
+      load_vec<T, E>(vin + (int64_t)tok * a.sx_n + e0, xv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float dk = load_f32<T>(kp + e) - km[e];
-        const float dv = load_f32<T>(vp + e) - vm[e];
+        const float dk = xk[e] - km[e];
+        const float dv = xv[e] - vm[e];
         const float qk = dk / div;
         const float qv = dv / div;
         km[e] = km[e] + qk;
         vm[e] = vm[e] + qv;
       }
     }
+    store_f32vec<E>(c.k_master + row, km);
+    store_f32vec<E>(c.v_master + row, vm);
+    const int64_t mrow = ((int64_t)h * Bp + s) * D + e0;
+    store_mirror_vec<T, E>(kmir + mrow, km);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      c.k_master[row + e] = km[e];
-      c.v_master[row + e] = vm[e];
-      store_mirror<T>(kmir + mrow + e, km[e]);
-      store_mirror<T>(vmir + vmirror_index(h, s, lane * E + e, Bp, D, kGrouped), vm[e]);
-    }
-    if (lane == 0) {
+    for (int e = 0; e < E; ++e)
+      store_mirror<T>(vmir + vmirror_index(h, s, e0 + e, Bp, D, kGrouped), vm[e]);
+    if (gl == 0) {
       const int cnt = c0 + (k1 - k0);
       c.count[(int64_t)h * B + s] = cnt;
       c.last[(int64_t)h * B + s] = f;
@@ -330,26 +385,26 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
     const int q = w - ng;
     const int tok = c.ins_tok[(int64_t)h * B + q];
     const int s = c.ins_slot[(int64_t)h * B + q];
-    const int64_t row = ((int64_t)h * B + s) * D + lane * E;
-    const int64_t mrow = ((int64_t)h * Bp + s) * D + lane * E;
-    const T* kp = kin + (int64_t)tok * a.sx_n + lane * E;
-    const T* vp = vin + (int64_t)tok * a.sx_n + lane * E;
+    const int64_t row = ((int64_t)h * B + s) * D + e0;
+    const int64_t mrow = ((int64_t)h * Bp + s) * D + e0;
+    const T* kp = kin + (int64_t)tok * a.sx_n + e0;
+    const T* vp = vin + (int64_t)tok * a.sx_n + e0;
+    float xk[E], xv[E];
+    load_vec<T, E>(kp, xk);
+    load_vec<T, E>(vp, xv);
+    store_f32vec<E>(c.k_master + row, xk);
+    store_f32vec<E>(c.v_master + row, xv);
+    store_mirror_vec<T, E>(kmir + mrow, xk);  // inputs are storage-exact: copies
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const T kr = kp[e], vr = vp[e];
-      c.k_master[row + e] = load_f32<T>(&kr);
-      c.v_master[row + e] = load_f32<T>(&vr);
-      kmir[mrow + e] = kr;
-      vmir[vmirror_index(h, s, lane * E + e, Bp, D, kGrouped)] = vr;
-    }
-    if (lane == 0) {
+    for (int e = 0; e < E; ++e) vmir[vmirror_index(h, s, e0 + e, Bp, D, kGrouped)] = vp[e];
+    if (gl == 0) {
       c.count[(int64_t)h * B + s] = 1;
       c.last[(int64_t)h * B + s] = f;
       c.lb[(int64_t)h * Bp + s] = 0.0f;
     }
-    if (lane < L)
-      c.codes[((int64_t)h * L + lane) * B + s] =
-          a.codes[((int64_t)h * L + lane) * a.codes_ld + a.codes_col0 + tok];
+    if (gl < L)
+      c.codes[((int64_t)h * L + gl) * B + s] =
+          a.codes[((int64_t)h * L + gl) * a.codes_ld + a.codes_col0 + tok];
   }
 }
 
@@ -389,7 +444,8 @@ hipError_t launch_plan(const Dims& dm, const CacheDev& c, const MergeArgs& a, hi
 
 hipError_t launch_apply(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const dim3 grid((a.T + 3) / 4, dm.H);
+  constexpr int kItems = 256 / kApplyGroup;
+  const dim3 grid((a.T + kItems - 1) / kItems, dm.H);
   if (dm.elem == 2) {
     if (dm.d == 128) hipLaunchKernelGGL((apply_kernel<uint16_t, 128>), grid, dim3(256), 0, s, dm, c, a);
     else hipLaunchKernelGGL((apply_kernel<uint16_t, 64>), grid, dim3(256), 0, s, dm, c, a);
