@@ -47,6 +47,11 @@ def _parse():
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads the CPU oracle times (0 = all for dit1.3b, 2 for dit14b)")
     p.add_argument("--frames", type=int, default=240, help="rollout length")
+    p.add_argument("--measure-traffic", action="store_true",
+                   help="run rocprofv3 FETCH_SIZE / WRITE_SIZE passes and record them in profiles/")
+    p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"),
+                   help="where --measure-traffic writes its summary")
+    p.add_argument("--traffic-child", action="store_true", help=argparse.SUPPRESS)
     return p.parse_args()
 
 
@@ -111,8 +116,144 @@ def cpu_baseline(w, frames, planes, heads):
     }
 
 
+ATTEND_SRC = os.path.join(ROOT, "kv_cache_attention_tempcache_amd", "csrc", "attend.hip")
+CALIB_BYTES = 1 << 30   # plain device copy used to scale the HBM counters
+
+
+def _attend_src_hash() -> str:
+    import hashlib
+    with open(ATTEND_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic_path(workload: str, out_dir: str | None = None) -> str:
+    return os.path.join(out_dir or os.path.join(ROOT, "profiles"),
+                        f"attend_traffic_{workload}.txt")
+
+
+def _load_traffic(workload: str):
+    """Measured HBM bytes per attend launch, if taken on the current kernel."""
+    path = _traffic_path(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("RESULT "):
+                rec = json.loads(line[len("RESULT "):])
+                if rec.get("attend_src_sha256_16") == _attend_src_hash():
+                    return rec
+    return None
+
+
+def _build_step_caches(fa, torch, w, nrep):
+    """The prefilled cache, its copies, and the chunk inputs of the timed step."""
+    from synth import DriftStream
+    st = DriftStream(w)
+    planes = st.planes()
+    n_frames = w.prefill_frames + w.frames_per_chunk
+    frames = []
+    for _ in range(n_frames):
+        K, V, Q, _ = st.next_frame()
+        frames.append((K, V, Q))
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()  # noqa: E731
+    T, F = w.tokens_per_frame, w.frames_per_chunk
+    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+    base = fa.Cache(cfg, planes)
+    for c0 in range(0, w.prefill_frames, F):
+        n = min(F, w.prefill_frames - c0)
+        kd = dev(np.concatenate([frames[f][0] for f in range(c0, c0 + n)], axis=1))
+        vd = dev(np.concatenate([frames[f][1] for f in range(c0, c0 + n)], axis=1))
+        base.match_merge(kd, vd, T, n)
+    chunk = [dev(np.concatenate([frames[f][i] for f in range(w.prefill_frames, n_frames)], axis=1))
+             for i in range(3)]
+    torch.cuda.synchronize()
+    caches = []
+    for _ in range(nrep):
+        c = fa.Cache(cfg, planes)
+        c.workspace.copy_(base.workspace)
+        caches.append(c)
+    torch.cuda.synchronize()
+    return base, caches, chunk, frames, planes
+
+
+def traffic_child(args, fa, torch):
+    """Workload profiled by the counter passes: one plain copy, then steps."""
+    from synth import WORKLOADS
+    w = WORKLOADS[args.workload]
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    _, caches, (ck, cv, cq), _, _ = _build_step_caches(fa, torch, w, 3)
+    out = torch.empty_like(cq)
+    for c in caches:
+        c.match_merge(ck, cv, w.tokens_per_frame, w.frames_per_chunk)
+        c.attend(cq, out=out)
+    torch.cuda.synchronize()
+    print("traffic child done", flush=True)
+
+
+def measure_traffic(args):
+    """Two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) of traffic_child."""
+    import csv
+    import subprocess
+    import tempfile
+    out = {}
+    cmds = []
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = tempfile.mkdtemp(prefix="fastar_pmc_", dir=os.environ.get("TMPDIR", "/tmp"))
+        cmd = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", d, "-o", "pmc", "--",
+               sys.executable, os.path.abspath(__file__), "--traffic-child", "--workload",
+               args.workload]
+        cmds.append(" ".join(cmd[:6] + ["<dir>"] + cmd[7:]))
+        subprocess.run(["timeout", "-s", "KILL", "300"] + cmd, check=True, cwd=d)
+        rows = []
+        for root, _, files in os.walk(d):
+            for fn in files:
+                if fn.endswith("counter_collection.csv"):
+                    with open(os.path.join(root, fn)) as f:
+                        rows.extend(csv.DictReader(f))
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        att = [float(r["Counter_Value"]) for r in rows
+               if "attend_cache_kernel" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        if not copies or not att:
+            raise RuntimeError(f"{counter}: no copy or attend dispatches in the counter output")
+        kib_copy = max(copies)
+        out[counter] = {"copy_kib": kib_copy, "attend_kib_mean": float(np.mean(att)),
+                        "attend_dispatches": len(att),
+                        "scale": (CALIB_BYTES / 1024.0) / kib_copy}
+    fetch = out["FETCH_SIZE"]["attend_kib_mean"] * 1024 * out["FETCH_SIZE"]["scale"]
+    write = out["WRITE_SIZE"]["attend_kib_mean"] * 1024 * out["WRITE_SIZE"]["scale"]
+    rec = {"workload": args.workload, "attend_fetch_bytes": fetch, "attend_write_bytes": write,
+           "attend_bytes": fetch + write, "counters": out,
+           "attend_src_sha256_16": _attend_src_hash()}
+    write_traffic(rec, cmds, _traffic_path(args.workload, args.out_dir))
+    print(json.dumps(rec), flush=True)
+
+
+def write_traffic(rec, cmds, path):
+    """Summary of the two counter passes, with the RESULT line bench.py reads."""
+    out = rec["counters"]
+    fetch, write = rec["attend_fetch_bytes"], rec["attend_write_bytes"]
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of attend_cache_kernel, workload {rec['workload']}\n")
+        f.write("# commands (run from a scratch directory, one counter per pass):\n")
+        for c in cmds:
+            f.write(f"#   timeout -s KILL 300 {c}\n")
+        f.write(f"# produced by: python bench.py --measure-traffic --workload {rec['workload']}\n")
+        f.write(f"# scale = {CALIB_BYTES} B plain device copy / its counter reading\n")
+        for k, v in out.items():
+            f.write(f"# {k}: copy {v['copy_kib']:.0f} KiB, attend mean {v['attend_kib_mean']:.0f} KiB"
+                    f" over {v['attend_dispatches']} dispatches, scale {v['scale']:.4f}\n")
+        f.write(f"# attend HBM bytes per launch: fetch {fetch:.4g}, write {write:.4g}\n")
+        f.write("RESULT " + json.dumps(rec) + "\n")
+
+
 def main():
     args = _parse()
+    if args.measure_traffic:
+        return measure_traffic(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the TempCache step "
               "shards by head with no exchange inside the step, and multi-GPU runs are not "
@@ -130,39 +271,16 @@ def main():
     torch.cuda.init()
     fa.library()
 
+    if args.traffic_child:
+        return traffic_child(args, fa, torch)
     if args.workload == "rollout":
         return rollout(args, fa, torch)
 
     w = WORKLOADS[args.workload]
-    st = DriftStream(w)
-    planes = st.planes()
-    n_frames = w.prefill_frames + w.frames_per_chunk
-    frames = []
-    for _ in range(n_frames):
-        K, V, Q, _ = st.next_frame()
-        frames.append((K, V, Q))
-    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()  # noqa: E731
-    T, F, H = w.tokens_per_frame, w.frames_per_chunk, w.heads
-    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
-
-    base = fa.Cache(cfg, planes)
-    for c0 in range(0, w.prefill_frames, F):
-        n = min(F, w.prefill_frames - c0)
-        kd = dev(np.concatenate([frames[f][0] for f in range(c0, c0 + n)], axis=1))
-        vd = dev(np.concatenate([frames[f][1] for f in range(c0, c0 + n)], axis=1))
-        base.match_merge(kd, vd, T, n)
-    ck = dev(np.concatenate([frames[f][0] for f in range(w.prefill_frames, n_frames)], axis=1))
-    cv = dev(np.concatenate([frames[f][1] for f in range(w.prefill_frames, n_frames)], axis=1))
-    cq = dev(np.concatenate([frames[f][2] for f in range(w.prefill_frames, n_frames)], axis=1))
-    torch.cuda.synchronize()
-    pre = base.stats()
-
+    T, F = w.tokens_per_frame, w.frames_per_chunk
     nrep = args.warmup + args.steps
-    caches = []
-    for _ in range(nrep):
-        c = fa.Cache(cfg, planes)
-        c.workspace.copy_(base.workspace)
-        caches.append(c)
+    base, caches, (ck, cv, cq), frames, planes = _build_step_caches(fa, torch, w, nrep)
+    pre = base.stats()
     out = torch.empty_like(cq)
     torch.cuda.synchronize()
 
@@ -203,6 +321,10 @@ def main():
     attend_flops = float(4 * w.chunk_tokens * n_live.sum() * w.head_dim)
     attend_avg_s = float(np.mean(attend_ms)) / 1e3
     attend_tflops = attend_flops / attend_avg_s / 1e12
+    # algorithmic HBM bytes of one attend launch: Q and O once, every live
+    # slot's K and V rows and its log2-count once per head
+    attend_bytes = float(w.heads * w.chunk_tokens * w.head_dim * 2 * 2 +
+                         n_live.sum() * (w.head_dim * 2 * 2 + 4))
 
     res = {
         "metric": "query tokens/s per compressed-KV attention step",
@@ -220,12 +342,13 @@ def main():
         "config": _workload_desc(w),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attend_bf16_kernel",
+            "kernel": "attend_cache_kernel",
             "achieved": attend_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attend_tflops / PEAK_BF16_TFLOPS,
             "traffic": None,
+            "algorithmic_bytes": attend_bytes,
         },
         "detail": {
             "attend_ms_mean": float(np.mean(attend_ms)),
@@ -244,9 +367,12 @@ def main():
         "context": "pages report end-to-end only: FAST-AR 5-10x vs dense FlashAttention-3 with "
                    "constant memory; LIPAR 1.45x (NVIDIA A6000); not comparable to this step",
     }
+    tr = _load_traffic(args.workload)
+    if tr is not None:
+        res["roofline"]["traffic"] = tr["attend_bytes"]
     if not args.no_cpu_baseline:
         heads = args.cpu_heads or (w.heads if w.heads <= 12 else 2)
-        res["cpu_baseline"] = cpu_baseline(w, frames, planes, heads)
+        res["cpu_baseline"] = cpu_baseline(w, [(K, V, Q) for K, V, Q in frames], planes, heads)
     print(json.dumps(res), flush=True)
 
 
