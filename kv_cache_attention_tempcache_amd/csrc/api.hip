@@ -4,6 +4,7 @@
 // stream and nothing synchronises except create, stats, export and import.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -334,6 +335,10 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   const CacheDev& dev = c->dev;
   const int64_t N = (int64_t)T * F;
+  // Without caller codes, the new keys are hashed into frame_codes ([H][L][B])
+  // ahead of their frames, as many frames per launch as fit in B columns: the
+  // codes of new keys do not depend on the cache state.
+  const int hash_group = std::max(1, dm.B / T);
   for (int f = 0; f < F; ++f) {
     const int64_t tok0 = (int64_t)f * T;
     const uint8_t* kf = static_cast<const uint8_t*>(k_dev) + tok0 * stride_n * dm.elem;
@@ -341,23 +346,26 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
     const uint32_t* codes = codes_dev;
     int64_t codes_ld = N, codes_col0 = tok0;
     if (codes == nullptr) {
-      HashArgs ha{};
-      ha.x = kf;
-      ha.sx_h = stride_h;
-      ha.sx_n = stride_n;
-      ha.H = dm.H;
-      ha.N = T;
-      ha.d = dm.d;
-      ha.L = dm.L;
-      ha.b = dm.b;
-      ha.planes = dev.planes;
-      ha.codes = dev.frame_codes;
-      ha.codes_ld = dm.B;
-      ha.codes_col0 = 0;
-      FASTAR_HIP(dm.elem == 2 ? launch_hash_bf16(ha, s) : launch_hash_f32(ha, s));
+      const int g = f % hash_group;  // position of this frame in its hash group
+      if (g == 0) {
+        HashArgs ha{};
+        ha.x = kf;
+        ha.sx_h = stride_h;
+        ha.sx_n = stride_n;
+        ha.H = dm.H;
+        ha.N = T * std::min(hash_group, F - f);
+        ha.d = dm.d;
+        ha.L = dm.L;
+        ha.b = dm.b;
+        ha.planes = dev.planes;
+        ha.codes = dev.frame_codes;
+        ha.codes_ld = dm.B;
+        ha.codes_col0 = 0;
+        FASTAR_HIP(dm.elem == 2 ? launch_hash_bf16(ha, s) : launch_hash_f32(ha, s));
+      }
       codes = dev.frame_codes;
       codes_ld = dm.B;
-      codes_col0 = 0;
+      codes_col0 = (int64_t)g * T;
     }
     MatchArgs ma{kf, stride_h, stride_n, codes, codes_ld, codes_col0, T, c->cfg.cos_threshold};
     FASTAR_HIP(launch_match(dm, dev, ma, s));

@@ -407,25 +407,30 @@ struct CCfg {
   static constexpr int kBuf = kKBytes + kVBytes + BN * 4;
   static constexpr int kKInstr = kKBytes / 1024;  // wave-wide 1 KiB direct loads per tile
   static_assert(kKBytes % 1024 == 0 && kBuf % 16 == 0, "tile shape");
-  static_assert((2 * kKInstr) % WAVES == 0, "every wave issues the same number of copies");
+  static_assert(kKInstr % WAVES == 0, "every wave issues the same number of copies");
 };
 
 // QB blocks of 32 queries per wave: every K or V fragment read from LDS feeds
 // QB MFMAs, which is what keeps the kernel below the LDS bandwidth (one 1 KiB
 // operand per 32x32x16 MFMA would need all 128 B/clk of a CU's LDS).
-template <int D, int BN, int WAVES, int QB>
+template <int D, int BN, int WAVES, int QB, int NBUF>
 __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kernel(
     Dims dm, CacheDev c, CacheAttendArgs a, int qtiles) {
   using C = CCfg<D, BN, WAVES, QB>;
-  // Three distinct LDS objects: tile it is read from one while the copies of
-  // tiles it+1 and it+2 are in flight into the others.  Distinct objects let
-  // the compiler see that the reads never alias the copies in flight.
+  static_assert(NBUF == 3 || NBUF == 4, "ring depth");
+  // A ring of NBUF distinct LDS objects: tile it is read from one while the
+  // copies of tiles it+1 .. it+NBUF-1 are in flight into the others.  Distinct
+  // objects let the compiler see that the reads never alias the copies in
+  // flight.
   __shared__ __attribute__((aligned(16))) uint8_t buf0[C::kBuf];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kBuf];
   __shared__ __attribute__((aligned(16))) uint8_t buf2[C::kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t buf3[NBUF == 4 ? C::kBuf : 16];
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lid / qtiles, qt = lid - h * qtiles;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform by construction: keeps the barrier paths below scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31, hf = lane >> 5;
   const int Bp = dm.Bp;
   const int nkeys = c.n_live[h];
@@ -435,23 +440,34 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
                                                        (int64_t)h * Bp * D);
   const float* lbg = c.lb + (int64_t)h * Bp;
 
-  auto issue = [&](int k0, uint8_t* buf) {
-    for (int i = wave; i < C::kKInstr; i += WAVES) {
-      const int off = i * 1024 + lane * 16;
-      const int row = off / C::kRowBytes;
-      const int slot = (off - row * C::kRowBytes) >> 4;
-      const int chunk = slot ^ (row & (C::kRowChunks - 1));
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(kg + (int64_t)(k0 + row) * D + chunk * 8),
-                                       (lds_void_t*)(buf + i * 1024), 16, 0, 0);
-    }
-    const uint8_t* vt = vg + (int64_t)k0 * D * 2;
-    for (int i = wave; i < C::kKInstr; i += WAVES)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + i * 1024 + lane * 16),
+  // Copy addresses: a wave-uniform tile base plus per-lane byte offsets that
+  // do not change from tile to tile, so issuing a copy costs no vector math.
+  // Wave w copies the 1 KiB chunks w, w + WAVES, ... of the K and V tiles; K
+  // rows land XOR-swizzled by 16-byte chunk.
+  constexpr int kPerWave = C::kKInstr / WAVES;
+  uint32_t koff[kPerWave];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int off = (wave + j * WAVES) * 1024 + lane * 16;
+    const int row = off / C::kRowBytes;
+    const int slot = (off - row * C::kRowBytes) >> 4;
+    koff[j] = (uint32_t)(row * C::kRowBytes + ((slot ^ (row & (C::kRowChunks - 1))) << 4));
+  }
+  auto issue = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
+    const uint8_t* kt = reinterpret_cast<const uint8_t*>(kg) + (int64_t)k0 * C::kRowBytes;
+    const uint8_t* vt = vg + (int64_t)k0 * C::kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int i = wave + j * WAVES;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(kt + koff[j]), (lds_void_t*)(buf + i * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + i * 1024 + (uint32_t)lane * 16u),
                                        (lds_void_t*)(buf + C::kKBytes + i * 1024), 16, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < (BN + 63) / 64; ++i) {
       if (wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(lbg + k0 + i * 64 + lane),
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(lbg + k0 + i * 64 + (uint32_t)lane),
                                          (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256),
                                          4, 0, 0);
     }
@@ -487,11 +503,28 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   constexpr int kCopies = 2 * C::kKInstr / WAVES;
   const bool lb_wave = wave >= WAVES - (BN + 63) / 64;
 
-  // One key tile: read `cur`, issue the copy of tile it+2 into `nxt2`.
-  auto step = [&](const uint8_t* cur, uint8_t* nxt2, int it, int nt) {
+  // Wait until at most n tiles' copies issued by this wave are in flight
+  // (every older tile has landed), finish this wave's LDS reads, then meet
+  // the other waves.  A plain barrier, not __syncthreads(): the latter's
+  // fence would also wait for the copies that are meant to stay in flight.
+  auto wait_barrier = [&](int n) __attribute__((always_inline)) {
+    if (lb_wave) {
+      if (n >= 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kCopies + 1)) : "memory");
+      else if (n == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies + 1) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      if (n >= 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kCopies) : "memory");
+      else if (n == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
+
+  // One key tile: read `cur`, issue the copy of tile it+NBUF-1 into `nxt`
+  // (the buffer read in the previous step).
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int it, int nt) __attribute__((always_inline)) {
     const uint8_t* vt_lds = cur + C::kKBytes;
     const float* lb_lds = reinterpret_cast<const float*>(cur + C::kKBytes + C::kVBytes);
-    if (it + 2 < nt) issue((it + 2) * BN, nxt2);
+    if (it + NBUF - 1 < nt) issue((it + NBUF - 1) * BN, nxt);
 
     f32x16_t S[BN / 32][QB];
 #pragma unroll
@@ -576,36 +609,27 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
         }
       }
     }
-    // Tile it+1 must have landed in LDS (every wave waits for its own copies,
-    // then all meet at the barrier), and this tile's LDS reads must be done
-    // before its buffer is refilled; the copies of tile it+2 stay in flight.
-    // A plain barrier, not __syncthreads(): the latter's fence would also
-    // wait for the it+2 copies.
-    if (it + 2 < nt) {
-      if (lb_wave)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies + 1) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
+    // Tile it+1 must have landed; the copies of tiles it+2 .. it+NBUF-1
+    // stay in flight.
+    wait_barrier(min(nt - 1, it + NBUF - 1) - (it + 1));
   };
 
   const int nt = (nkeys + BN - 1) / BN;
-  if (nt > 0) issue(0, buf0);
-  if (nt > 1) issue(BN, buf1);
-  if (nt > 1) {
-    if (lb_wave)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies + 1) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kCopies) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-  for (int it = 0; it < nt; it += 3) {
-    step(buf0, buf2, it, nt);
-    if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
-    if (it + 2 < nt) step(buf2, buf1, it + 2, nt);
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u)
+    if (u < nt) issue(u * BN, u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : buf3);
+  wait_barrier(min(nt, NBUF - 1) - 1);
+  for (int it = 0; it < nt; it += NBUF) {
+    if (NBUF == 3) {
+      step(buf0, buf2, it, nt);
+      if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
+      if (it + 2 < nt) step(buf2, buf1, it + 2, nt);
+    } else {
+      step(buf0, buf3, it, nt);
+      if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
+      if (it + 2 < nt) step(buf2, buf1, it + 2, nt);
+      if (it + 3 < nt) step(buf3, buf2, it + 3, nt);
+    }
   }
 
 #pragma unroll
@@ -631,14 +655,14 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   }
 }
 
-template <int D, int BN, int WAVES, int QB>
+template <int D, int BN, int WAVES, int QB, int NBUF>
 hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                             hipStream_t s) {
   using C = CCfg<D, BN, WAVES, QB>;
   const int qtiles = (a.Nq + C::BM - 1) / C::BM;
   const int blocks = dm.H * qtiles;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB>), dim3(blocks), dim3(C::kThreads), 0,
+  hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF>), dim3(blocks), dim3(C::kThreads), 0,
                      s, dm, c, a, qtiles);
   return hipGetLastError();
 }
@@ -676,6 +700,9 @@ hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
   return gather ? launch_bf16_cfg<64, 2, 64, true>(a, s) : launch_bf16_cfg<64, 2, 64, false>(a, s);
 }
 
+#ifndef FASTAR_CACHE_NBUF
+#define FASTAR_CACHE_NBUF 4
+#endif
 #ifndef FASTAR_CACHE_BN
 #define FASTAR_CACHE_BN 64
 #endif
@@ -689,8 +716,8 @@ hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
 hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                                     hipStream_t s) {
   constexpr int BN = FASTAR_CACHE_BN, W = FASTAR_CACHE_WAVES, QB = FASTAR_CACHE_QB;
-  if (dm.d == 128) return launch_cache_cfg<128, BN, W, QB>(dm, c, a, s);
-  return launch_cache_cfg<64, 64, 4, 1>(dm, c, a, s);
+  if (dm.d == 128) return launch_cache_cfg<128, BN, W, QB, FASTAR_CACHE_NBUF>(dm, c, a, s);
+  return launch_cache_cfg<64, 64, 4, 1, FASTAR_CACHE_NBUF>(dm, c, a, s);
 }
 
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s) {

@@ -2,13 +2,13 @@
 // neighbour search runs on locality-sensitive hashes).  Bit j of table t is
 // [<r_tj, x> > 0], stored as 1u << j.
 //
-// bf16 path: the projection is a small GEMM (rows x d) * (d x L*b) on the
+// bf16 path: the projection is a small GEMM (L*b x d) * (d x rows) on the
 // 32x32x16 bf16 MFMA.  A wave owns 32 rows and reads the hyperplane operands
 // straight from L2 (a few KiB shared by every wave), with no LDS staging and
-// no block barrier between the loads and the MFMAs.  The
-// accumulator layout puts one hyperplane per lane column and rows in
-// registers, so one wave ballot over a register yields two complete 32-bit
-// words of sign bits (rows r and r+4), already in LSB-first plane order.
+// no block barrier between the loads and the MFMAs.  With hyperplanes as the
+// MFMA rows, each lane's accumulators hold 16 of the 32 projections of one
+// key row, so it packs 16 sign bits locally and one lane exchange with the
+// other half-wave completes the 32-bit word, in LSB-first plane order.
 //
 // f32 path: one thread per (row, table), products and sums in float64.
 #include "common.hpp"
@@ -43,10 +43,6 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(HashArgs a, int tiles_pe
   const uint16_t* planes = static_cast<const uint16_t*>(a.planes);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, hf = lane >> 5;
-  // Row owned by this lane in the ballot words: register j = 4*(m/8) + m%4,
-  // low half of the ballot if (m/4) is even, high half otherwise.
-  const int my_j = 4 * (m >> 3) + (m & 3);
-  const bool my_hi = ((m >> 2) & 1) != 0;
   const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
 
   for (int tile = blockIdx.x * kHashWaves + wave; tile < total_tiles;
@@ -75,27 +71,44 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(HashArgs a, int tiles_pe
     uint32_t words[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) words[k] = 0u;
-#pragma unroll
-    for (int pb = 0; pb < 8; ++pb) {
-      if (pb * 32 >= Ppad) break;
-      // B operand straight from L2: hyperplane pb*32 + m (zero past L*b)
+    // B operands straight from L2: hyperplane pb*32 + m (zero past L*b); the
+    // next block's operands are loaded while this block's MFMAs run
+    const int npb = Ppad / 32;
+    auto load_b = [&](int pb, bf16x8_t (&Bf)[D / 16]) __attribute__((always_inline)) {
       const int prow = pb * 32 + m;
       const uint16_t* pp = planes + (int64_t)(prow < P ? prow : 0) * D + hf * (D / 2);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) Bf[ks] = *reinterpret_cast<const bf16x8_t*>(pp + ks * 8);
+      if (pb * 32 + 32 > P) {  // only a last, partial block has padding planes
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          if (prow >= P) Bf[ks] = bf16x8_t{};
+      }
+    };
+    // hyperplanes as MFMA rows, keys as columns: register j of lane l holds
+    // plane 8*(j/4) + 4*(l/32) + j%4 of key row l%32
+    auto block = [&](int pb, const bf16x8_t (&Bf)[D / 16]) __attribute__((always_inline)) {
       f32x16_t acc = {};
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(pp + ks * 8);
-        if (prow >= P) B = bf16x8_t{};
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks], B, acc, 0, 0, 0);
-      }
-      uint32_t w = 0u;
+      for (int ks = 0; ks < D / 16; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bf[ks], A[ks], acc, 0, 0, 0);
+      uint32_t bits = 0u;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint64_t bal = __ballot(acc[j] > 0.0f);
-        const uint32_t pick = my_hi ? (uint32_t)(bal >> 32) : (uint32_t)bal;
-        if (my_j == j) w = pick;
-      }
-      words[pb] = w;
+      for (int j = 0; j < 16; ++j)
+        bits |= (acc[j] > 0.0f ? 1u : 0u) << (8 * (j >> 2) + (j & 3));
+      bits <<= 4 * hf;
+      words[pb] = bits | __shfl_xor(bits, 32);  // both halves: the word of row m
+    };
+    bf16x8_t B0[D / 16], B1[D / 16];
+    load_b(0, B0);
+#pragma unroll
+    for (int pb = 0; pb < 8; pb += 2) {
+      if (pb >= npb) break;
+      if (pb + 1 < npb) load_b(pb + 1, B1);
+      block(pb, B0);
+      if (pb + 1 >= npb) break;
+      if (pb + 2 < npb) load_b(pb + 2, B0);
+      block(pb + 1, B1);
     }
 
     if (hf == 0 && valid) {

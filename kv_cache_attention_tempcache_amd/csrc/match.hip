@@ -3,11 +3,12 @@
 // neighbour among earlier frames through LSH, without full attention matrices).
 //
 // A group of 16 lanes owns one token.  For every table it reads the token's
-// bucket from the CSR index of (slot, code) entries, keeps the slots whose code
-// equals the token's code (a bucket may hold several codes), skips slots
-// already scored through an earlier table (a slot remembered in registers; a
-// slot scored twice past that list only costs time), and scores each candidate
-// by the cosine of the token key and the slot's stored key.  Products and sums are float64, so the decision agrees
+// bucket from the CSR index of (slot, code) entries, 16 entries at a time,
+// keeps the slots whose code equals the token's code (a bucket may hold several
+// codes) and that no earlier table listed, and scores each candidate by the
+// cosine of the token key and the slot's stored key, a few candidate rows in
+// flight at a time.  A list that overflows is scored and restarted, so a slot
+// may then be scored twice, which only costs time.  Products and sums are float64, so the decision agrees
 // with an exact evaluation except within ~1e-15 of a tie.  Ties go to the
 // lowest slot id; the token merges iff its best cosine >= the threshold.
 //
@@ -61,7 +62,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchArgs a) {
   constexpr int E = D / kGroup;
   constexpr int LT = FASTAR_MAX_TABLES_DEV;
-  constexpr int kSeen = 8;  // slots remembered for de-duplication across tables
+  constexpr int kMaxCand = 16;  // candidates listed before scoring
+  constexpr int kBatch = 4;     // candidate rows in flight together
   const int h = blockIdx.y;
   const int i = blockIdx.x * (256 / kGroup) + (threadIdx.x / kGroup);
   const int gl = threadIdx.x & (kGroup - 1);
@@ -102,41 +104,76 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
   const T* keys = static_cast<const T*>(c.k_mirror) + (int64_t)h * dm.Bp * D;
   double best = -__builtin_huge_val();
   int best_s = -1;
-  int seen[kSeen];
-  int nseen = 0;
+  // score candidates cand[0..n): the row loads of a batch are issued before
+  // any of its arithmetic, so one memory round trip serves kBatch candidates
+  auto score = [&](const int (&cand)[kMaxCand], int n) __attribute__((always_inline)) {
+    for (int b0 = 0; b0 < n; b0 += kBatch) {
+      float kv[kBatch][E];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        load_row<T, E>(keys + (int64_t)cand[min(b0 + u, n - 1)] * D + gl * E, kv[u]);
+      double dot[kBatch], nk2[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        dot[u] = 0.0;
+        nk2[u] = 0.0;
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          dot[u] += (double)xv[q] * (double)kv[u][q];
+          nk2[u] += (double)kv[u][q] * (double)kv[u][q];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        dot[u] = group_sum(dot[u]);
+        nk2[u] = group_sum(nk2[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (b0 + u >= n) break;
+        const int s = cand[b0 + u];
+        const double cs =
+            (nx2 == 0.0 || nk2[u] == 0.0) ? 0.0 : dot[u] / (sqrt(nx2) * sqrt(nk2[u]));
+        if (cs > best || (cs == best && s < best_s)) {
+          best = cs;
+          best_s = s;
+        }
+      }
+    }
+  };
+
+  // Candidates: entries of the token's bucket in every table whose code equals
+  // the token's, each slot once.  The 16 lanes read 16 entries of a bucket at
+  // a time; a ballot over the group lists the matching ones.  The candidate
+  // list is identical in every lane of the group.
+  int cand[kMaxCand];
+  int nc = 0;
+  const int gbase = threadIdx.x & 63 & ~(kGroup - 1);
 #pragma unroll
   for (int t = 0; t < LT; ++t) {
     if (t >= L) break;
     const uint2* ent = c.idx_ent + ((int64_t)h * L + t) * B;
-    for (int p = beg[t]; p < end[t]; ++p) {
-      const uint2 e = p == beg[t] ? first[t] : ent[p];
-      if (e.y != qc[t]) continue;  // same bucket, different code
-      const int s = (int)e.x;
-      bool dup = false;
-#pragma unroll
-      for (int k = 0; k < kSeen; ++k) dup |= (k < nseen) && seen[k] == s;
-      if (dup) continue;  // already scored through an earlier table
-#pragma unroll
-      for (int k = 0; k < kSeen; ++k)
-        if (k == nseen) seen[k] = s;
-      nseen = min(nseen + 1, kSeen);
-      float kv[E];
-      load_row<T, E>(keys + (int64_t)s * D + gl * E, kv);
-      double dot = 0.0, nk2 = 0.0;
-#pragma unroll
-      for (int q = 0; q < E; ++q) {
-        dot += (double)xv[q] * (double)kv[q];
-        nk2 += (double)kv[q] * (double)kv[q];
-      }
-      dot = group_sum(dot);
-      nk2 = group_sum(nk2);
-      const double cs = (nx2 == 0.0 || nk2 == 0.0) ? 0.0 : dot / (sqrt(nx2) * sqrt(nk2));
-      if (cs > best || (cs == best && s < best_s)) {
-        best = cs;
-        best_s = s;
+    for (int p0 = beg[t]; p0 < end[t]; p0 += kGroup) {
+      const int p = p0 + gl;
+      const uint2 e = p < end[t] ? (p == beg[t] ? first[t] : ent[p]) : make_uint2(0u, 0u);
+      const bool ok = p < end[t] && e.y == qc[t];
+      uint32_t mask = (uint32_t)(__ballot(ok) >> gbase) & 0xffffu;
+      while (mask) {
+        const int j = __builtin_ctz(mask);
+        mask &= mask - 1;
+        const int s = __shfl((int)e.x, j, kGroup);
+        bool dup = false;
+        for (int k = 0; k < nc; ++k) dup |= cand[k] == s;
+        if (dup) continue;
+        if (nc == kMaxCand) {  // rare: a full list is scored and emptied
+          score(cand, nc);
+          nc = 0;
+        }
+        cand[nc++] = s;
       }
     }
   }
+  score(cand, nc);
   if (gl == 0) {
     const int64_t o = (int64_t)h * B + i;
     c.best_slot[o] = best_s;

@@ -352,20 +352,36 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
     float km[E], vm[E];
     load_f32vec<E>(c.k_master + row, km);
     load_f32vec<E>(c.v_master + row, vm);
-    for (int k = k0; k < k1; ++k) {
-      const int tok = c.group_tok[(int64_t)h * B + k];
-      const float div = (float)(c0 + (k - k0) + 1);
-      float xk[E], xv[E];
-      load_vec<T, E>(kin + (int64_t)tok * a.sx_n + e0, xk);
-      load_vec<T, E>(vin + (int64_t)tok * a.sx_n + e0, xv);
+    // The updates run strictly in token order; only the loads run ahead: the
+    // group's member ids are read kApplyGroup at a time (one per lane), and
+    // the inputs of kPrefetch members are in flight together.
+    constexpr int kPrefetch = 4;
+    const int32_t* gt = c.group_tok + (int64_t)h * B;
+    for (int b0 = k0; b0 < k1; b0 += kApplyGroup) {
+      const int nb = min(kApplyGroup, k1 - b0);
+      const int my_tok = gl < nb ? gt[b0 + gl] : 0;
+      for (int j = 0; j < nb; j += kPrefetch) {
+        float xk[kPrefetch][E], xv[kPrefetch][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float dk = xk[e] - km[e];
-        const float dv = xv[e] - vm[e];
-        const float qk = dk / div;
-        const float qv = dv / div;
-        km[e] = km[e] + qk;
-        vm[e] = vm[e] + qv;
+        for (int u = 0; u < kPrefetch; ++u) {
+          const int tok = __shfl(my_tok, min(j + u, nb - 1), kApplyGroup);
+          load_vec<T, E>(kin + (int64_t)tok * a.sx_n + e0, xk[u]);
+          load_vec<T, E>(vin + (int64_t)tok * a.sx_n + e0, xv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kPrefetch; ++u) {
+          if (j + u >= nb) break;
+          const float div = (float)(c0 + (b0 - k0) + j + u + 1);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float dk = xk[u][e] - km[e];
+            const float dv = xv[u][e] - vm[e];
+            const float qk = dk / div;
+            const float qv = dv / div;
+            km[e] = km[e] + qk;
+            vm[e] = vm[e] + qv;
+          }
+        }
       }
     }
     store_f32vec<E>(c.k_master + row, km);
