@@ -75,7 +75,7 @@ fastar_status make_dims(const fastar_config* cfg, Dims* dm) {
   dm->b = cfg->num_bits;
   dm->elem = elem_bytes(cfg->dtype);
   int nb = 6;  // at least 64 buckets
-  while ((1 << nb) < dm->B) ++nb;
+  while ((1 << nb) * kSlotsPerBucket < dm->B) ++nb;
   dm->nb_bits = nb;
   dm->NB = 1 << nb;
   dm->Ppad = (dm->L * dm->b + 31) & ~31;
@@ -478,18 +478,9 @@ fastar_status fastar_cache_export(fastar_cache_t c, void* stream, fastar_cache_s
   if (out->k_mirror)
     FASTAR_HIP(hipMemcpy2DAsync(out->k_mirror, (size_t)dm.B * row, d.k_mirror, (size_t)dm.Bp * row,
                                 (size_t)dm.B * row, dm.H, hipMemcpyDeviceToHost, s));
-  std::vector<uint16_t> vgrp;
-  const bool grouped = dm.elem == 2;
-  if (out->v_mirror) {
-    if (grouped) {
-      vgrp.resize((size_t)dm.H * dm.Bp * dm.d);
-      FASTAR_HIP(hipMemcpyAsync(vgrp.data(), d.v_mirror, vgrp.size() * 2, hipMemcpyDeviceToHost, s));
-    } else {
-      FASTAR_HIP(hipMemcpy2DAsync(out->v_mirror, (size_t)dm.B * row, d.v_mirror,
-                                  (size_t)dm.Bp * row, (size_t)dm.B * row, dm.H,
-                                  hipMemcpyDeviceToHost, s));
-    }
-  }
+  if (out->v_mirror)
+    FASTAR_HIP(hipMemcpy2DAsync(out->v_mirror, (size_t)dm.B * row, d.v_mirror, (size_t)dm.Bp * row,
+                                (size_t)dm.B * row, dm.H, hipMemcpyDeviceToHost, s));
   FASTAR_HIP(cp(out->count, d.count, HB * 4));
   FASTAR_HIP(cp(out->last, d.last, HB * 4));
   FASTAR_HIP(cp(out->codes, d.codes, HB * dm.L * 4));
@@ -498,13 +489,6 @@ fastar_status fastar_cache_export(fastar_cache_t c, void* stream, fastar_cache_s
   int32_t frame = 0;
   FASTAR_HIP(hipMemcpyAsync(&frame, d.frame, 4, hipMemcpyDeviceToHost, s));
   FASTAR_HIP(hipStreamSynchronize(s));
-  if (out->v_mirror && grouped) {
-    uint16_t* dst = static_cast<uint16_t*>(out->v_mirror);
-    for (int h = 0; h < dm.H; ++h)
-      for (int sl = 0; sl < dm.B; ++sl)
-        for (int e = 0; e < dm.d; ++e)
-          dst[((size_t)h * dm.B + sl) * dm.d + e] = vgrp[vmirror_index(h, sl, e, dm.Bp, dm.d, true)];
-  }
   out->frame = frame;
   return ok();
 }
@@ -531,22 +515,9 @@ fastar_status fastar_cache_import(fastar_cache_t c, const fastar_cache_state* in
   if (in->k_mirror)
     FASTAR_HIP(hipMemcpy2DAsync(d.k_mirror, (size_t)dm.Bp * row, in->k_mirror, (size_t)dm.B * row,
                                 (size_t)dm.B * row, dm.H, hipMemcpyHostToDevice, s));
-  std::vector<uint16_t> vgrp;
-  if (in->v_mirror) {
-    if (dm.elem == 2) {
-      vgrp.assign((size_t)dm.H * dm.Bp * dm.d, 0);
-      const uint16_t* src = static_cast<const uint16_t*>(in->v_mirror);
-      for (int h = 0; h < dm.H; ++h)
-        for (int sl = 0; sl < dm.B; ++sl)
-          for (int e = 0; e < dm.d; ++e)
-            vgrp[vmirror_index(h, sl, e, dm.Bp, dm.d, true)] = src[((size_t)h * dm.B + sl) * dm.d + e];
-      FASTAR_HIP(hipMemcpyAsync(d.v_mirror, vgrp.data(), vgrp.size() * 2, hipMemcpyHostToDevice, s));
-    } else {
-      FASTAR_HIP(hipMemcpy2DAsync(d.v_mirror, (size_t)dm.Bp * row, in->v_mirror,
-                                  (size_t)dm.B * row, (size_t)dm.B * row, dm.H,
-                                  hipMemcpyHostToDevice, s));
-    }
-  }
+  if (in->v_mirror)
+    FASTAR_HIP(hipMemcpy2DAsync(d.v_mirror, (size_t)dm.Bp * row, in->v_mirror, (size_t)dm.B * row,
+                                (size_t)dm.B * row, dm.H, hipMemcpyHostToDevice, s));
   FASTAR_HIP(cp(d.count, in->count, HB * 4));
   FASTAR_HIP(cp(d.last, in->last, HB * 4));
   FASTAR_HIP(cp(d.codes, in->codes, HB * dm.L * 4));

@@ -384,16 +384,19 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles
 }
 
 // ---------------------------------------------------------------------------
-// Attention over a bf16 cache in its own layout: K mirror rows [H][Bp][D], the
-// V mirror grouped by 4 slots ([H][Bp/4][D][4], see vmirror_index) and
-// lb = log2(count) per slot with -inf past n_live.  Tiles of BN slots are
-// copied HBM -> LDS with direct-to-LDS loads (no registers in between): K rows
-// with their 16-byte chunks XOR-swizzled by row so the MFMA operand reads are
-// bank-conflict free, V and lb verbatim.  The grouped V layout makes the P*V
-// operand (4 consecutive keys of one feature) one aligned 8-byte LDS read, so
-// no transpose is needed anywhere.  Slots past n_live inside the last tile have
-// zero rows and lb = -inf, so they need no masking.
+// Attention over a bf16 cache in its own layout: K and V mirror rows
+// [H][Bp][D] and lb = log2(count) per slot with -inf past n_live.  Tiles of BN
+// slots are copied HBM -> LDS with direct-to-LDS loads (no registers in
+// between), the 16-byte chunks of every K and V row permuted by row so that
+// the operand reads below are bank-conflict free.  K rows feed S^T = K Q^T
+// directly (a lane reads 8 consecutive features of one key).  For
+// O^T += V^T P^T a lane needs 8 keys of one feature: gfx950's transposing LDS
+// read (ds_read_b64_tr_b16) gathers them from row-major V, 4 keys per read.
+// Slots past n_live inside the last tile have zero rows and lb = -inf, so they
+// need no masking.
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
 template <int D, int BN, int WAVES, int QB>
@@ -408,6 +411,15 @@ struct CCfg {
   static constexpr int kKInstr = kKBytes / 1024;  // wave-wide 1 KiB direct loads per tile
   static_assert(kKBytes % 1024 == 0 && kBuf % 16 == 0, "tile shape");
   static_assert(kKInstr % WAVES == 0, "every wave issues the same number of copies");
+  // LDS chunk permutations (XOR on the 16-byte chunk index of a row).  K: a
+  // wave reads one chunk of 32 consecutive rows.  V: a half-wave reads 4
+  // chunks (32 features) of 4 consecutive rows, which this spreads over all
+  // 64 banks (D = 128: row r's chunks move by 4*(r%4); D = 64, two rows per
+  // 256 bytes: by 4*((r/2)%2)).
+  static __device__ __forceinline__ int kswz(int row) { return row & (kRowChunks - 1); }
+  static __device__ __forceinline__ int vswz(int row) {
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+  }
 };
 
 // QB blocks of 32 queries per wave: every K or V fragment read from LDS feeds
@@ -442,16 +454,17 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
 
   // Copy addresses: a wave-uniform tile base plus per-lane byte offsets that
   // do not change from tile to tile, so issuing a copy costs no vector math.
-  // Wave w copies the 1 KiB chunks w, w + WAVES, ... of the K and V tiles; K
-  // rows land XOR-swizzled by 16-byte chunk.
+  // Wave w copies the 1 KiB chunks w, w + WAVES, ... of the K and V tiles; LDS
+  // position (row, chunk) receives global chunk chunk ^ swz(row).
   constexpr int kPerWave = C::kKInstr / WAVES;
-  uint32_t koff[kPerWave];
+  uint32_t koff[kPerWave], voff[kPerWave];
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
     const int off = (wave + j * WAVES) * 1024 + lane * 16;
     const int row = off / C::kRowBytes;
     const int slot = (off - row * C::kRowBytes) >> 4;
-    koff[j] = (uint32_t)(row * C::kRowBytes + ((slot ^ (row & (C::kRowChunks - 1))) << 4));
+    koff[j] = (uint32_t)(row * C::kRowBytes + ((slot ^ C::kswz(row)) << 4));
+    voff[j] = (uint32_t)(row * C::kRowBytes + ((slot ^ C::vswz(row)) << 4));
   }
   auto issue = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
     const uint8_t* kt = reinterpret_cast<const uint8_t*>(kg) + (int64_t)k0 * C::kRowBytes;
@@ -461,7 +474,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
       const int i = wave + j * WAVES;
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(kt + koff[j]), (lds_void_t*)(buf + i * 1024),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + i * 1024 + (uint32_t)lane * 16u),
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + voff[j]),
                                        (lds_void_t*)(buf + C::kKBytes + i * 1024), 16, 0, 0);
     }
 #pragma unroll
@@ -486,6 +499,21 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
       bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
       if (!qok) v = bf16x8_t{};
       Qf[qb][ks] = v;
+    }
+  }
+  // Transposing V reads: within each 16-lane group, source lane j reads 4
+  // features (8 bytes) of key row 4*hf + j/4 at feature 16*(group%2) + 4*(j%4)
+  // of a 32-feature block; lane i then holds 4 consecutive keys of feature
+  // 16*(group%2) + i.  Offsets per feature block; the key offset of a tile
+  // (a multiple of 8 rows) leaves the chunk permutation unchanged.
+  uint32_t vtr[D / 32];
+  {
+    const int j = lane & 15;
+    const int row = 4 * hf + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      vtr[db] = (uint32_t)(row * C::kRowBytes + (((col >> 3) ^ C::vswz(row)) << 4) + (col & 7) * 2);
     }
   }
   f32x16_t O[D / 32][QB];
@@ -538,7 +566,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
         const int row = kb * 32 + m;
         const int chunk = hf * (D / 16) + ks;
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-            cur + row * C::kRowBytes + ((chunk ^ (row & (C::kRowChunks - 1))) << 4));
+            cur + row * C::kRowBytes + ((chunk ^ C::kswz(row)) << 4));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[qb][ks], S[kb][qb], 0, 0, 0);
@@ -598,11 +626,17 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
           }
           lrun[qb] = ls;
         }
-        // keys kb*32 + kk*16 + {4*hf..4*hf+3, 8+4*hf..8+4*hf+3}: one 16-byte word
-        const uint8_t* vbase = vt_lds + ((((kb * 2 + kk) * 2 + hf) * D + m) << 4);
+        // A operand: feature db*32 + m, keys kb*32 + kk*16 + {4*hf..4*hf+3}
+        // then {8+4*hf..8+4*hf+3}, the key order of the P fragment
+        const uint8_t* vrow = vt_lds + (kb * 32 + kk * 16) * C::kRowBytes;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vbase + db * 32 * 16);
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(vrow + vtr[db]));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(vrow + vtr[db] + 8 * C::kRowBytes));
+          const bf16x8_t vf = __builtin_bit_cast(
+              bf16x8_t, (v8i16_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);

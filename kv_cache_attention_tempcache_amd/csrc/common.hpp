@@ -14,22 +14,13 @@ namespace fastar {
 
 constexpr int kWave = 64;
 constexpr int kSlotPad = 128;  // mirror rows per head are padded to a multiple of this
-
-// Element offset of feature e of slot s of head h in the value mirror.  For
-// bf16 storage, each block of 16 consecutive slots is stored as two halves of
-// [d][8]: half 0 holds slots {0-3, 8-11} and half 1 slots {4-7, 12-15} of the
-// block, in that order.  That is exactly the set and order of keys one lane
-// supplies as the k-operand of a 32x32x16 MFMA (lane half h, k-slots 8h..8h+7)
-// in the P*V product, so attention reads each operand as one aligned 16-byte
-// word.  fp32 storage keeps plain rows ([H][Bp][d]).
-__host__ __device__ __forceinline__ int64_t vmirror_index(int h, int s, int e, int Bp, int d,
-                                                          bool grouped) {
-  if (!grouped) return ((int64_t)h * Bp + s) * d + e;
-  const int r = s & 15;
-  const int half = (r >> 2) & 1;
-  const int pos = (r & 3) | ((r >> 3) << 2);
-  return (int64_t)h * Bp * d + ((int64_t)((s >> 4) * 2 + half) * d + e) * 8 + pos;
-}
+#ifndef FASTAR_SLOTS_PER_BUCKET
+#define FASTAR_SLOTS_PER_BUCKET 4
+#endif
+// Buckets of the LSH index: about this many budget slots per bucket.  The
+// match reads a bucket 16 entries at a time and filters by code, so a few
+// slots per bucket cost it nothing while shrinking the index rebuild.
+constexpr int kSlotsPerBucket = FASTAR_SLOTS_PER_BUCKET;
 
 // ---------------------------------------------------------------- bfloat16
 // bfloat16 values travel as raw 16-bit patterns.
@@ -80,7 +71,7 @@ struct CacheDev {
   float* k_master;     // [H][B][d]
   float* v_master;     // [H][B][d]
   void* k_mirror;      // [H][Bp][d] storage dtype
-  void* v_mirror;      // storage dtype, see vmirror_index
+  void* v_mirror;      // [H][Bp][d] storage dtype
   float* lb;           // [H][Bp] log2(count) of live slots, -inf elsewhere
   int32_t* count;      // [H][B]
   int32_t* last;       // [H][B]

@@ -328,7 +328,6 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeArgs a) {
 #pragma clang fp contract(off)
   constexpr int E = D / kApplyGroup;  // features per lane
-  constexpr bool kGrouped = sizeof(T) == 2;
   const int h = blockIdx.y;
   const int w = blockIdx.x * (256 / kApplyGroup) + (threadIdx.x / kApplyGroup);
   const int gl = threadIdx.x & (kApplyGroup - 1);
@@ -388,9 +387,7 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
     store_f32vec<E>(c.v_master + row, vm);
     const int64_t mrow = ((int64_t)h * Bp + s) * D + e0;
     store_mirror_vec<T, E>(kmir + mrow, km);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      store_mirror<T>(vmir + vmirror_index(h, s, e0 + e, Bp, D, kGrouped), vm[e]);
+    store_mirror_vec<T, E>(vmir + mrow, vm);
     if (gl == 0) {
       const int cnt = c0 + (k1 - k0);
       c.count[(int64_t)h * B + s] = cnt;
@@ -411,8 +408,7 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
     store_f32vec<E>(c.k_master + row, xk);
     store_f32vec<E>(c.v_master + row, xv);
     store_mirror_vec<T, E>(kmir + mrow, xk);  // inputs are storage-exact: copies
-#pragma unroll
-    for (int e = 0; e < E; ++e) vmir[vmirror_index(h, s, e0 + e, Bp, D, kGrouped)] = vp[e];
+    store_mirror_vec<T, E>(vmir + mrow, xv);
     if (gl == 0) {
       c.count[(int64_t)h * B + s] = 1;
       c.last[(int64_t)h * B + s] = f;
@@ -446,7 +442,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(Dims dm, CacheDev c) {
   T* vmir = static_cast<T*>(c.v_mirror);
   for (int e = lane; e < D; e += kWave) {
     kmir[((int64_t)h * dm.Bp + s) * D + e] = T(0);
-    vmir[vmirror_index(h, s, e, dm.Bp, D, sizeof(T) == 2)] = T(0);
+    vmir[((int64_t)h * dm.Bp + s) * D + e] = T(0);
   }
 }
 
