@@ -373,7 +373,8 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
                  slot_out_dev, merged_out_dev, N, tok0};
     FASTAR_HIP(launch_plan(dm, dev, ga, s));
     FASTAR_HIP(launch_apply(dm, dev, ga, s));
-    FASTAR_HIP(launch_rehash(dm, dev, T, s));
+    // bf16 storage: the apply kernel already refreshed the merged slots' codes
+    if (dm.elem != 2) FASTAR_HIP(launch_rehash(dm, dev, T, s));
     FASTAR_HIP(launch_index(dm, dev, true, s));
   }
   return ok();

@@ -48,6 +48,22 @@ __device__ __forceinline__ uint32_t bucket_of(uint32_t code, int nb_bits) {
   return nb_bits == 0 ? 0u : (code * 0x9E3779B1u) >> (32 - nb_bits);
 }
 
+// Code of one table: bits [off, off+b) of the concatenated 32-bit words of
+// sign bits (word k holds planes 32k .. 32k+31, LSB first).
+__device__ __forceinline__ uint32_t extract_code(const uint32_t (&w)[9], int off, int b) {
+  if (b == 0) return 0u;
+  const int wi = off >> 5, sh = off & 31;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k == wi) lo = w[k];
+    if (k == wi + 1) hi = w[k];
+  }
+  uint64_t both = ((uint64_t)hi << 32) | lo;
+  uint32_t code = (uint32_t)(both >> sh);
+  return b == 32 ? code : (code & ((1u << b) - 1u));
+}
+
 // ---------------------------------------------------------------- cache layout
 // Per-head counters (int64): tokens seen, merged tokens, inserted tokens,
 // evicted slots.

@@ -21,20 +21,6 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 constexpr int kHashWaves = 4;
 
-__device__ __forceinline__ uint32_t extract_code(const uint32_t (&w)[9], int off, int b) {
-  if (b == 0) return 0u;
-  const int wi = off >> 5, sh = off & 31;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    if (k == wi) lo = w[k];
-    if (k == wi + 1) hi = w[k];
-  }
-  uint64_t both = ((uint64_t)hi << 32) | lo;
-  uint32_t code = (uint32_t)(both >> sh);
-  return b == 32 ? code : (code & ((1u << b) - 1u));
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void hash_bf16_kernel(HashArgs a, int tiles_per_head,
                                                         int total_tiles) {

@@ -52,9 +52,22 @@ __device__ __forceinline__ void load_row(const T* p, float (&v)[E]) {
   }
 }
 
+// Sum over the 16 lanes of a DPP row (a token's lane group): rotations by 8,
+// 4, 2, 1 within the row.  Every lane adds the same two partial sums (in
+// commuted order), so all 16 end with the identical value.
+template <int R>
+__device__ __forceinline__ double row_rotate(double x) {
+  const int l = __double2loint(x), h = __double2hiint(x);
+  const int lo = __builtin_amdgcn_update_dpp(l, l, 0x120 + R, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(h, h, 0x120 + R, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
 __device__ __forceinline__ double group_sum(double x) {
-#pragma unroll
-  for (int off = kGroup / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kGroup);
+  static_assert(kGroup == 16, "a token's lanes are one DPP row");
+  x += row_rotate<8>(x);
+  x += row_rotate<4>(x);
+  x += row_rotate<2>(x);
+  x += row_rotate<1>(x);
   return x;
 }
 
@@ -90,19 +103,30 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
       end[t] = off[1];
     }
   }
+  // the first 16 entries of every table's bucket, one per lane, all in flight
+  // together (buckets hold a few entries; longer ones are read on in the loop)
   uint2 first[LT];
 #pragma unroll
   for (int t = 0; t < LT; ++t)
-    first[t] = (t < L && beg[t] < end[t]) ? c.idx_ent[((int64_t)h * L + t) * B + beg[t]]
-                                            : make_uint2(0u, 0u);
+    first[t] = (t < L && beg[t] + gl < end[t])
+                   ? c.idx_ent[((int64_t)h * L + t) * B + beg[t] + gl]
+                   : make_uint2(0u, 0u);
 
+  double xd[E];
   double nx2 = 0.0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) nx2 += (double)xv[e] * (double)xv[e];
+  for (int e = 0; e < E; ++e) {
+    xd[e] = (double)xv[e];
+    nx2 = __builtin_fma(xd[e], xd[e], nx2);
+  }
   nx2 = group_sum(nx2);
 
   const T* keys = static_cast<const T*>(c.k_mirror) + (int64_t)h * dm.Bp * D;
-  double best = -__builtin_huge_val();
+  // Candidates are ranked by key = dot*|dot| / |k|^2, an increasing function
+  // of the cosine for a fixed token, compared by cross-multiplication (no
+  // division or square root per candidate); ties go to the lower slot.  A
+  // zero key row scores cosine 0, i.e. key 0/1.
+  double bnum = 0.0, bden = 1.0, bdot = 0.0, bnk2 = 0.0;
   int best_s = -1;
   // score candidates cand[0..n): the row loads of a batch are issued before
   // any of its arithmetic, so one memory round trip serves kBatch candidates
@@ -119,8 +143,9 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
         nk2[u] = 0.0;
 #pragma unroll
         for (int q = 0; q < E; ++q) {
-          dot[u] += (double)xv[q] * (double)kv[u][q];
-          nk2[u] += (double)kv[u][q] * (double)kv[u][q];
+          const double k = (double)kv[u][q];
+          dot[u] = __builtin_fma(xd[q], k, dot[u]);
+          nk2[u] = __builtin_fma(k, k, nk2[u]);
         }
       }
 #pragma unroll
@@ -132,10 +157,15 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
       for (int u = 0; u < kBatch; ++u) {
         if (b0 + u >= n) break;
         const int s = cand[b0 + u];
-        const double cs =
-            (nx2 == 0.0 || nk2[u] == 0.0) ? 0.0 : dot[u] / (sqrt(nx2) * sqrt(nk2[u]));
-        if (cs > best || (cs == best && s < best_s)) {
-          best = cs;
+        const bool zero = nx2 == 0.0 || nk2[u] == 0.0;
+        const double num = zero ? 0.0 : dot[u] * fabs(dot[u]);
+        const double den = zero ? 1.0 : nk2[u];
+        const double lhs = num * bden, rhs = bnum * den;
+        if (best_s < 0 || lhs > rhs || (lhs == rhs && s < best_s)) {
+          bnum = num;
+          bden = den;
+          bdot = zero ? 0.0 : dot[u];
+          bnk2 = nk2[u];
           best_s = s;
         }
       }
@@ -155,7 +185,7 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
     const uint2* ent = c.idx_ent + ((int64_t)h * L + t) * B;
     for (int p0 = beg[t]; p0 < end[t]; p0 += kGroup) {
       const int p = p0 + gl;
-      const uint2 e = p < end[t] ? (p == beg[t] ? first[t] : ent[p]) : make_uint2(0u, 0u);
+      const uint2 e = p < end[t] ? (p0 == beg[t] ? first[t] : ent[p]) : make_uint2(0u, 0u);
       const bool ok = p < end[t] && e.y == qc[t];
       uint32_t mask = (uint32_t)(__ballot(ok) >> gbase) & 0xffffu;
       while (mask) {
@@ -174,6 +204,9 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
     }
   }
   score(cand, nc);
+  // the winner's cosine, evaluated once
+  const double best = (best_s < 0 || nx2 == 0.0 || bnk2 == 0.0)
+                          ? 0.0 : bdot / (sqrt(nx2) * sqrt(bnk2));
   if (gl == 0) {
     const int64_t o = (int64_t)h * B + i;
     c.best_slot[o] = best_s;

@@ -324,17 +324,35 @@ __device__ __forceinline__ void store_mirror_vec(T* p, const float (&v)[E]) {
   }
 }
 
+constexpr int kApplyThreads = 512;
+constexpr int kApplyItems = kApplyThreads / kApplyGroup;  // 32: one MFMA tile of key rows
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// With bf16 storage the block then refreshes the codes of its merge groups'
+// slots: SimHash of the new key mirror rows (kept in LDS) against all L*b
+// hyperplanes, one 32-plane block per wave on the 32x32x16 MFMA with
+// hyperplanes as rows, the arithmetic of the hash kernel.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeArgs a) {
+__global__ __launch_bounds__(kApplyThreads) void apply_kernel(Dims dm, CacheDev c, MergeArgs a) {
 #pragma clang fp contract(off)
   constexpr int E = D / kApplyGroup;  // features per lane
+  constexpr bool kHash = sizeof(T) == 2;
+  // new key rows (bf16 bits, rows padded by 16 bytes against bank conflicts),
+  // the 32-bit words of sign bits per row and plane block, the rows' slots
+  __shared__ __attribute__((aligned(16))) uint16_t s_rows[kHash ? kApplyItems : 1][D + 8];
+  __shared__ uint32_t s_words[kApplyItems][9];
+  __shared__ int32_t s_slot[kApplyItems];
   const int h = blockIdx.y;
-  const int w = blockIdx.x * (256 / kApplyGroup) + (threadIdx.x / kApplyGroup);
+  const int item = threadIdx.x / kApplyGroup;
+  const int first = blockIdx.x * kApplyItems;
+  const int w = first + item;
   const int gl = threadIdx.x & (kApplyGroup - 1);
   const int B = dm.B, L = dm.L, Bp = dm.Bp;
   const int32_t* pl = c.plan + (int64_t)h * kPlanStride;
   const int ng = pl[kPlanGroups], nins = pl[kPlanInserts];
-  if (w >= ng + nins) return;
+  if (first >= ng + nins) return;  // the whole block is idle
   const int f = *c.frame;
   const T* kin = static_cast<const T*>(a.k) + (int64_t)h * a.sx_h;  // frame base, head h
   const T* vin = static_cast<const T*>(a.v) + (int64_t)h * a.sx_h;
@@ -342,7 +360,9 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
   T* vmir = static_cast<T*>(c.v_mirror);
   const int e0 = gl * E;
 
-  if (w < ng) {
+  if (w >= ng + nins) {
+    // idle item of a busy block: nothing to update
+  } else if (w < ng) {
     const int s = c.group_slot[(int64_t)h * B + w];
     const int k0 = c.group_start[(int64_t)h * (B + 1) + w];
     const int k1 = c.group_start[(int64_t)h * (B + 1) + w + 1];
@@ -388,6 +408,10 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
     const int64_t mrow = ((int64_t)h * Bp + s) * D + e0;
     store_mirror_vec<T, E>(kmir + mrow, km);
     store_mirror_vec<T, E>(vmir + mrow, vm);
+    if constexpr (kHash) {
+      store_mirror_vec<T, E>(reinterpret_cast<T*>(&s_rows[item][e0]), km);
+      if (gl == 0) s_slot[item] = s;
+    }
     if (gl == 0) {
       const int cnt = c0 + (k1 - k0);
       c.count[(int64_t)h * B + s] = cnt;
@@ -417,6 +441,45 @@ __global__ __launch_bounds__(256) void apply_kernel(Dims dm, CacheDev c, MergeAr
     if (gl < L)
       c.codes[((int64_t)h * L + gl) * B + s] =
           a.codes[((int64_t)h * L + gl) * a.codes_ld + a.codes_col0 + tok];
+  }
+
+  if constexpr (kHash) {
+    if (first < ng) {  // block-uniform: the block holds merge groups
+      __syncthreads();
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      const int m = lane & 31, hf = lane >> 5;
+      const int P = L * dm.b;
+      uint32_t word = 0u;
+      if (wave * 32 < P) {
+        // MFMA rows: hyperplane wave*32 + m (zero past L*b); columns: key row
+        // m; features hf*D/2 + ks*8 .. +7 in k-step ks for both
+        const int prow = wave * 32 + m;
+        const uint16_t* pp = static_cast<const uint16_t*>(c.planes) +
+                             (int64_t)(prow < P ? prow : 0) * D + hf * (D / 2);
+        f32x16_t acc = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(pp + ks * 8);
+          if (prow >= P) pa = bf16x8_t{};
+          const bf16x8_t xb = *reinterpret_cast<const bf16x8_t*>(&s_rows[m][hf * (D / 2) + ks * 8]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, xb, acc, 0, 0, 0);
+        }
+        // register j of lane l: plane 8*(j/4) + 4*(l/32) + j%4 of key row l%32
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bits |= (acc[j] > 0.0f ? 1u : 0u) << (8 * (j >> 2) + (j & 3));
+        bits <<= 4 * hf;
+        word = bits | __shfl_xor(bits, 32);
+      }
+      if (hf == 0) s_words[m][wave] = word;
+      if (threadIdx.x < kApplyItems) s_words[threadIdx.x][8] = 0u;
+      __syncthreads();
+      const int ngb = min(kApplyItems, ng - first);
+      for (int idx = threadIdx.x; idx < ngb * L; idx += kApplyThreads) {
+        const int r = idx / L, t = idx - r * L;
+        c.codes[((int64_t)h * L + t) * B + s_slot[r]] = extract_code(s_words[r], t * dm.b, dm.b);
+      }
+    }
   }
 }
 
@@ -456,15 +519,14 @@ hipError_t launch_plan(const Dims& dm, const CacheDev& c, const MergeArgs& a, hi
 
 hipError_t launch_apply(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  constexpr int kItems = 256 / kApplyGroup;
-  const dim3 grid((a.T + kItems - 1) / kItems, dm.H);
+  const dim3 grid((a.T + kApplyItems - 1) / kApplyItems, dm.H), block(kApplyThreads);
   if (dm.elem == 2) {
-    if (dm.d == 128) hipLaunchKernelGGL((apply_kernel<uint16_t, 128>), grid, dim3(256), 0, s, dm, c, a);
-    else hipLaunchKernelGGL((apply_kernel<uint16_t, 64>), grid, dim3(256), 0, s, dm, c, a);
-  } else {
-    if (dm.d == 128) hipLaunchKernelGGL((apply_kernel<float, 128>), grid, dim3(256), 0, s, dm, c, a);
-    else hipLaunchKernelGGL((apply_kernel<float, 64>), grid, dim3(256), 0, s, dm, c, a);
+    if (dm.d == 128) hipLaunchKernelGGL((apply_kernel<uint16_t, 128>), grid, block, 0, s, dm, c, a);
+    else hipLaunchKernelGGL((apply_kernel<uint16_t, 64>), grid, block, 0, s, dm, c, a);
+    return hipGetLastError();
   }
+  if (dm.d == 128) hipLaunchKernelGGL((apply_kernel<float, 128>), grid, block, 0, s, dm, c, a);
+  else hipLaunchKernelGGL((apply_kernel<float, 64>), grid, block, 0, s, dm, c, a);
   return hipGetLastError();
 }
 
