@@ -21,6 +21,12 @@ namespace fastar {
 namespace {
 
 constexpr int kGroup = 16;  // lanes per token
+#ifndef FASTAR_MATCH_BATCH
+#define FASTAR_MATCH_BATCH 4
+#endif
+#ifndef FASTAR_MATCH_OCC
+#define FASTAR_MATCH_OCC 4
+#endif
 
 template <typename T, int E>
 __device__ __forceinline__ void load_row(const T* p, float (&v)[E]) {
@@ -71,12 +77,12 @@ __device__ __forceinline__ double group_sum(double x) {
   return x;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchArgs a) {
+// LT: a bound on the number of tables (sizes the per-table registers)
+template <typename T, int D, int LT>
+__global__ __launch_bounds__(256, FASTAR_MATCH_OCC) void match_kernel(Dims dm, CacheDev c, MatchArgs a) {
   constexpr int E = D / kGroup;
-  constexpr int LT = FASTAR_MAX_TABLES_DEV;
   constexpr int kMaxCand = 16;  // candidates listed before scoring
-  constexpr int kBatch = 4;     // candidate rows in flight together
+  constexpr int kBatch = FASTAR_MATCH_BATCH;  // candidate rows in flight together
   const int h = blockIdx.y;
   const int i = blockIdx.x * (256 / kGroup) + (threadIdx.x / kGroup);
   const int gl = threadIdx.x & (kGroup - 1);
@@ -223,17 +229,23 @@ __global__ __launch_bounds__(256) void match_kernel(Dims dm, CacheDev c, MatchAr
 
 }  // namespace
 
-hipError_t launch_match(const Dims& dm, const CacheDev& c, const MatchArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
+template <int LT>
+hipError_t launch_match_lt(const Dims& dm, const CacheDev& c, const MatchArgs& a, hipStream_t s) {
   const dim3 grid((a.T + 15) / 16, dm.H);
   if (dm.elem == 2) {
-    if (dm.d == 128) hipLaunchKernelGGL((match_kernel<uint16_t, 128>), grid, dim3(256), 0, s, dm, c, a);
-    else hipLaunchKernelGGL((match_kernel<uint16_t, 64>), grid, dim3(256), 0, s, dm, c, a);
+    if (dm.d == 128) hipLaunchKernelGGL((match_kernel<uint16_t, 128, LT>), grid, dim3(256), 0, s, dm, c, a);
+    else hipLaunchKernelGGL((match_kernel<uint16_t, 64, LT>), grid, dim3(256), 0, s, dm, c, a);
   } else {
-    if (dm.d == 128) hipLaunchKernelGGL((match_kernel<float, 128>), grid, dim3(256), 0, s, dm, c, a);
-    else hipLaunchKernelGGL((match_kernel<float, 64>), grid, dim3(256), 0, s, dm, c, a);
+    if (dm.d == 128) hipLaunchKernelGGL((match_kernel<float, 128, LT>), grid, dim3(256), 0, s, dm, c, a);
+    else hipLaunchKernelGGL((match_kernel<float, 64, LT>), grid, dim3(256), 0, s, dm, c, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_match(const Dims& dm, const CacheDev& c, const MatchArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  static_assert(FASTAR_MAX_TABLES_DEV == 8, "table bounds below");
+  return dm.L <= 4 ? launch_match_lt<4>(dm, c, a, s) : launch_match_lt<8>(dm, c, a, s);
 }
 
 }  // namespace fastar

@@ -324,6 +324,12 @@ __device__ __forceinline__ void store_mirror_vec(T* p, const float (&v)[E]) {
   }
 }
 
+#ifndef FASTAR_APPLY_OCC
+#define FASTAR_APPLY_OCC 6
+#endif
+#ifndef FASTAR_APPLY_PREFETCH
+#define FASTAR_APPLY_PREFETCH 2
+#endif
 constexpr int kApplyThreads = 512;
 constexpr int kApplyItems = kApplyThreads / kApplyGroup;  // 32: one MFMA tile of key rows
 
@@ -335,7 +341,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 // hyperplanes, one 32-plane block per wave on the 32x32x16 MFMA with
 // hyperplanes as rows, the arithmetic of the hash kernel.
 template <typename T, int D>
-__global__ __launch_bounds__(kApplyThreads) void apply_kernel(Dims dm, CacheDev c, MergeArgs a) {
+__global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(Dims dm, CacheDev c, MergeArgs a) {
 #pragma clang fp contract(off)
   constexpr int E = D / kApplyGroup;  // features per lane
   constexpr bool kHash = sizeof(T) == 2;
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(Dims dm, CacheDev 
     // The updates run strictly in token order; only the loads run ahead: the
     // group's member ids are read kApplyGroup at a time (one per lane), and
     // the inputs of kPrefetch members are in flight together.
-    constexpr int kPrefetch = 4;
+    constexpr int kPrefetch = FASTAR_APPLY_PREFETCH;
     const int32_t* gt = c.group_tok + (int64_t)h * B;
     for (int b0 = k0; b0 < k1; b0 += kApplyGroup) {
       const int nb = min(kApplyGroup, k1 - b0);
