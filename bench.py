@@ -42,7 +42,8 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="dit1.3b", choices=["dit1.3b", "dit14b", "rollout"])
+    p.add_argument("--workload", default="dit1.3b",
+                   choices=["dit1.3b", "dit14b", "rollout", "annca"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads the CPU oracle times (0 = all for dit1.3b, 2 for dit14b)")
@@ -205,7 +206,8 @@ def measure_traffic(args):
         cmd = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", d, "-o", "pmc", "--",
                sys.executable, os.path.abspath(__file__), "--traffic-child", "--workload",
                args.workload]
-        cmds.append(" ".join(cmd[:6] + ["<dir>"] + cmd[7:]))
+        cmds.append(" ".join(cmd[:6] + ["<dir>", "-o", "pmc", "--", "python3", "<repo>/bench.py"]
+                             + cmd[12:]))
         subprocess.run(["timeout", "-s", "KILL", "300"] + cmd, check=True, cwd=d)
         rows = []
         for root, _, files in os.walk(d):
@@ -223,10 +225,26 @@ def measure_traffic(args):
         out[counter] = {"copy_kib": kib_copy, "attend_kib_mean": float(np.mean(att)),
                         "attend_dispatches": len(att),
                         "scale": (CALIB_BYTES / 1024.0) / kib_copy}
+        # every kernel of the step (merge path included), mean per dispatch
+        per = {}
+        for r in rows:
+            name = r["Kernel_Name"]
+            if "fastar::" not in name or r["Counter_Name"] != counter:
+                continue
+            short = (name.replace("(anonymous namespace)::", "").replace("void ", "")
+                     .split("(")[0].split("<")[0].split("::")[-1])
+            per.setdefault(short, []).append(float(r["Counter_Value"]))
+        out[counter]["kernels_kib_mean"] = {k: float(np.mean(v)) for k, v in per.items()}
+        out[counter]["kernels_dispatches"] = {k: len(v) for k, v in per.items()}
     fetch = out["FETCH_SIZE"]["attend_kib_mean"] * 1024 * out["FETCH_SIZE"]["scale"]
     write = out["WRITE_SIZE"]["attend_kib_mean"] * 1024 * out["WRITE_SIZE"]["scale"]
+    kernels = {}
+    for counter, key in (("FETCH_SIZE", "fetch_bytes"), ("WRITE_SIZE", "write_bytes")):
+        for k, kib in out[counter]["kernels_kib_mean"].items():
+            kernels.setdefault(k, {})[key] = kib * 1024 * out[counter]["scale"]
+            kernels[k]["dispatches"] = out[counter]["kernels_dispatches"][k]
     rec = {"workload": args.workload, "attend_fetch_bytes": fetch, "attend_write_bytes": write,
-           "attend_bytes": fetch + write, "counters": out,
+           "attend_bytes": fetch + write, "counters": out, "kernels": kernels,
            "attend_src_sha256_16": _attend_src_hash()}
     write_traffic(rec, cmds, _traffic_path(args.workload, args.out_dir))
     print(json.dumps(rec), flush=True)
@@ -247,6 +265,11 @@ def write_traffic(rec, cmds, path):
             f.write(f"# {k}: copy {v['copy_kib']:.0f} KiB, attend mean {v['attend_kib_mean']:.0f} KiB"
                     f" over {v['attend_dispatches']} dispatches, scale {v['scale']:.4f}\n")
         f.write(f"# attend HBM bytes per launch: fetch {fetch:.4g}, write {write:.4g}\n")
+        if rec.get("kernels"):
+            f.write("# every kernel, mean HBM bytes per dispatch (prefill chunks included):\n")
+            for k, v in sorted(rec["kernels"].items()):
+                f.write(f"#   {k:24s} fetch {v.get('fetch_bytes', 0):.4g}  write "
+                        f"{v.get('write_bytes', 0):.4g}  dispatches {v['dispatches']}\n")
         f.write("RESULT " + json.dumps(rec) + "\n")
 
 
@@ -275,6 +298,8 @@ def main():
         return traffic_child(args, fa, torch)
     if args.workload == "rollout":
         return rollout(args, fa, torch)
+    if args.workload == "annca":
+        return annca(args, fa, torch)
 
     w = WORKLOADS[args.workload]
     T, F = w.tokens_per_frame, w.frames_per_chunk
@@ -377,6 +402,77 @@ def main():
         heads = args.cpu_heads or (w.heads if w.heads <= 12 else 2)
         res["cpu_baseline"] = cpu_baseline(w, [(K, V, Q) for K, V, Q in frames], planes, heads)
     print(json.dumps(res), flush=True)
+
+
+def annca(args, fa, torch):
+    """AnnCA cross-attention step: hash queries, select prompt tokens per frame,
+    attend over the kept ones; timed against dense cross-attention (all prompt
+    tokens) through the same attention kernel."""
+    from synth import ClusterPrompt
+    cp = ClusterPrompt()
+    H, d, F = cp.heads, cp.head_dim, cp.frames
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()  # noqa: E731
+    q, kp, vp = dev(cp.Q), dev(cp.Kp), dev(cp.Vp)
+    planes = dev(cp.planes())
+    p_codes = fa.hash_codes(kp, planes, cp.tables, cp.bits)  # the fixed prompt, hashed once
+    q_codes = torch.empty((H, cp.tables, q.shape[1]), dtype=torch.int32, device="cuda")
+    sel_idx = torch.empty((H, F, kp.shape[1]), dtype=torch.int32, device="cuda")
+    sel_cnt = torch.empty((H, F), dtype=torch.int32, device="cuda")
+    o_sparse, o_dense = torch.empty_like(q), torch.empty_like(q)
+
+    def sparse():
+        fa.hash_codes(q, planes, cp.tables, cp.bits, out=q_codes)
+        fa.annca_select(q_codes, p_codes, F, sel_idx, sel_cnt)
+        fa.attend_subset(q, kp, vp, F, sel_idx, sel_cnt, out=o_sparse)
+
+    def dense():
+        fa.attend_subset(q, kp, vp, F, out=o_dense)
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("sparse", sparse), ("dense", dense)):
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        res[name] = {"ms_median": float(np.median(ms)), "ms_p95": float(np.percentile(ms, 95)),
+                     "query_tokens_per_s": q.shape[1] / (float(np.median(ms)) / 1e3)}
+    # accuracy of the sparse step against dense attention, and the dense
+    # probability mass of the dropped prompt tokens (float32 reference)
+    kept = sel_cnt.float().mean().item() / kp.shape[1]
+    err = (o_sparse.float() - o_dense.float()).abs().max().item()
+    qf = q.float().view(H, F, -1, d)
+    logits = torch.matmul(qf, kp.float().transpose(1, 2).contiguous().unsqueeze(1)) / d ** 0.5
+    prob = torch.softmax(logits, dim=-1)                      # [H][F][q][Np]
+    keep = torch.zeros((H, F, kp.shape[1]), device="cuda")
+    for hh in range(H):
+        for ff in range(F):
+            n = int(sel_cnt[hh, ff])
+            keep[hh, ff, sel_idx[hh, ff, :n].long()] = 1.0
+    dropped = (prob * (1.0 - keep.unsqueeze(2))).sum(-1)     # [H][F][q]
+    line = {
+        "metric": "query tokens/s per AnnCA cross-attention step",
+        "value": res["sparse"]["query_tokens_per_s"], "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["sparse"]["ms_median"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded clustered prompt; no dataset or trained weights)",
+        "config": {"workload": f"annca: {H} heads x d={d}, {F} frames x {cp.queries_per_frame} "
+                               f"queries, {kp.shape[1]}-token prompt ({cp.clusters} clusters), "
+                               f"{cp.tables} x {cp.bits}-bit codes"},
+        "detail": {"sparse": res["sparse"], "dense": res["dense"],
+                   "speedup_vs_dense": res["dense"]["ms_median"] / res["sparse"]["ms_median"],
+                   "kept_fraction": kept, "max_abs_sparse_vs_dense": err,
+                   "dropped_dense_mass_max": dropped.max().item(),
+                   "dropped_dense_mass_mean": dropped.mean().item()},
+    }
+    print(json.dumps(line), flush=True)
 
 
 def rollout(args, fa, torch):
