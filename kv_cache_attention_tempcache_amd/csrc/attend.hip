@@ -429,14 +429,14 @@ template <int D, int BN, int WAVES, int QB, int NBUF>
 __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kernel(
     Dims dm, CacheDev c, CacheAttendArgs a, int qtiles) {
   using C = CCfg<D, BN, WAVES, QB>;
-  static_assert(NBUF == 3 || NBUF == 4, "ring depth");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
   // A ring of NBUF distinct LDS objects: tile it is read from one while the
   // copies of tiles it+1 .. it+NBUF-1 are in flight into the others.  Distinct
   // objects let the compiler see that the reads never alias the copies in
   // flight.
   __shared__ __attribute__((aligned(16))) uint8_t buf0[C::kBuf];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kBuf];
-  __shared__ __attribute__((aligned(16))) uint8_t buf2[C::kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t buf2[NBUF >= 3 ? C::kBuf : 16];
   __shared__ __attribute__((aligned(16))) uint8_t buf3[NBUF == 4 ? C::kBuf : 16];
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lid / qtiles, qt = lid - h * qtiles;
@@ -654,7 +654,10 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     if (u < nt) issue(u * BN, u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : buf3);
   wait_barrier(min(nt, NBUF - 1) - 1);
   for (int it = 0; it < nt; it += NBUF) {
-    if (NBUF == 3) {
+    if (NBUF == 2) {
+      step(buf0, buf1, it, nt);
+      if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
+    } else if (NBUF == 3) {
       step(buf0, buf2, it, nt);
       if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
       if (it + 2 < nt) step(buf2, buf1, it + 2, nt);

@@ -21,11 +21,14 @@ namespace fastar {
 namespace {
 
 constexpr int kGroup = 16;  // lanes per token
+#ifndef FASTAR_MATCH_MAXCAND
+#define FASTAR_MATCH_MAXCAND 8
+#endif
 #ifndef FASTAR_MATCH_BATCH
-#define FASTAR_MATCH_BATCH 4
+#define FASTAR_MATCH_BATCH 2
 #endif
 #ifndef FASTAR_MATCH_OCC
-#define FASTAR_MATCH_OCC 4
+#define FASTAR_MATCH_OCC 5
 #endif
 
 template <typename T, int E>
@@ -81,7 +84,7 @@ __device__ __forceinline__ double group_sum(double x) {
 template <typename T, int D, int LT>
 __global__ __launch_bounds__(256, FASTAR_MATCH_OCC) void match_kernel(Dims dm, CacheDev c, MatchArgs a) {
   constexpr int E = D / kGroup;
-  constexpr int kMaxCand = 16;  // candidates listed before scoring
+  constexpr int kMaxCand = FASTAR_MATCH_MAXCAND;  // candidates listed before scoring
   constexpr int kBatch = FASTAR_MATCH_BATCH;  // candidate rows in flight together
   const int h = blockIdx.y;
   const int i = blockIdx.x * (256 / kGroup) + (threadIdx.x / kGroup);
