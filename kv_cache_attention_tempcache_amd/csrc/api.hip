@@ -88,7 +88,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 enum Region {
   kPlanes, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
   kNLive, kEvicted, kCounters, kOwner, kGsize, kFrame, kStateEnd = kFrame,
-  kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupStart, kGroupSlot, kInsTok, kInsSlot,
+  kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupSlot, kItems,
   kPlan, kNumRegions
 };
 
@@ -155,10 +155,8 @@ Layout make_layout(const Dims& dm) {
   sizes[kDec] = H * B * 4;
   sizes[kFrameCodes] = H * Lt * B * 4;
   sizes[kGroupTok] = H * B * 4;
-  sizes[kGroupStart] = H * (B + 1) * 4;
   sizes[kGroupSlot] = H * B * 4;
-  sizes[kInsTok] = H * B * 4;
-  sizes[kInsSlot] = H * B * 4;
+  sizes[kItems] = H * B * 16;
   sizes[kPlan] = H * kPlanStride * 4;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {
@@ -196,10 +194,8 @@ CacheDev carve(void* base, const Dims& dm) {
   c.dec = reinterpret_cast<int32_t*>(b + L.off[kDec]);
   c.frame_codes = reinterpret_cast<uint32_t*>(b + L.off[kFrameCodes]);
   c.group_tok = reinterpret_cast<int32_t*>(b + L.off[kGroupTok]);
-  c.group_start = reinterpret_cast<int32_t*>(b + L.off[kGroupStart]);
   c.group_slot = reinterpret_cast<int32_t*>(b + L.off[kGroupSlot]);
-  c.ins_tok = reinterpret_cast<int32_t*>(b + L.off[kInsTok]);
-  c.ins_slot = reinterpret_cast<int32_t*>(b + L.off[kInsSlot]);
+  c.items = reinterpret_cast<int4*>(b + L.off[kItems]);
   c.plan = reinterpret_cast<int32_t*>(b + L.off[kPlan]);
   return c;
 }

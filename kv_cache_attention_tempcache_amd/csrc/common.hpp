@@ -108,11 +108,11 @@ struct CacheDev {
   float* best_cos;     // [H][B]
   int32_t* dec;        // [H][B] merge target or -1 (insert)
   uint32_t* frame_codes;  // [H][L][B] codes of the frame when hashed here
-  int32_t* group_tok;  // [H][B] merging tokens sorted by (slot, token)
-  int32_t* group_start;   // [H][B+1]
-  int32_t* group_slot; // [H][B]
-  int32_t* ins_tok;    // [H][B]
-  int32_t* ins_slot;   // [H][B]
+  int32_t* group_tok;  // [H][B] merging tokens, group by group, ascending within a group
+  int32_t* group_slot; // [H][B] slot of each merge group
+  int4* items;         // [H][B] the frame's work items of the apply kernel: merge groups
+                       // {slot, first member in group_tok, members, leader token},
+                       // then inserts {slot, -1, 1, token}
   int32_t* plan;       // [H][kPlanStride]
 };
 

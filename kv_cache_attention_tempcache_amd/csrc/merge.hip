@@ -104,10 +104,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   const int M = (int)((tot >> kMemShift) & kField);
   const int m = (int)(tot & kField);
 
-  // 2. group lists (members ascending) and the insert list
+  // 2. merge groups (members ascending) and the insert list
   int32_t* g_tok = c.group_tok + (int64_t)h * B;
-  int32_t* g_start = c.group_start + (int64_t)h * (B + 1);
   int32_t* g_slot = c.group_slot + (int64_t)h * B;
+  int4* items = c.items + (int64_t)h * B;
   for (int i = t_lo; i < t_hi; ++i) {
     const int s = dec_s[i];
     if (s < 0) {
@@ -120,14 +120,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
     const int start = (int)((run >> kMemShift) & kField);
     const int size = gsize[s];
     g_slot[g] = s;
-    g_start[g] = start;
+    items[g] = make_int4(s, start, size, i);
     g_tok[start] = i;
     // the other members follow the leader in token order
     for (int j = i + 1, k = 1; k < size && j < T; ++j)
       if (dec_s[j] == s) g_tok[start + k++] = j;
     run += (1ull << kLeadShift) | ((uint64_t)size << kMemShift);
   }
-  if (tid == 0) g_start[n_groups] = M;
 
   // 3. eviction, only if the inserts do not fit: exactly `need` slots not
   //    merged into in this frame (owner unset), smallest (last, slot) first
@@ -221,14 +220,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   }
 
   // 5. slots for the inserts: evicted ids first, then never-used ids, ascending
-  int32_t* i_tok = c.ins_tok + (int64_t)h * B;
-  int32_t* i_slot = c.ins_slot + (int64_t)h * B;
   const bool want_out = a.slot_out != nullptr || a.merged_out != nullptr;
   for (int q = tid; q < m; q += kPlanThreads) {
     const int tok = ins_list[q];
     const int slot = q < need ? ev_list[q] : n_live + (q - need);
-    i_tok[q] = tok;
-    i_slot[q] = slot;
+    items[n_groups + q] = make_int4(slot, -1, 1, tok);
     if (want_out) {
       const int64_t o = (int64_t)h * a.out_ld + a.out_col0 + tok;
       if (a.slot_out) a.slot_out[o] = slot;
@@ -357,6 +353,9 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
   const int gl = threadIdx.x & (kApplyGroup - 1);
   const int B = dm.B, L = dm.L, Bp = dm.Bp;
   const int32_t* pl = c.plan + (int64_t)h * kPlanStride;
+  // the item record is read beside the plan summary (w < B keeps it in
+  // bounds; records past the frame's items are stale and left unused)
+  const int4 it = w < B ? c.items[(int64_t)h * B + w] : make_int4(0, 0, 0, 0);
   const int ng = pl[kPlanGroups], nins = pl[kPlanInserts];
   if (first >= ng + nins) return;  // the whole block is idle
   const int f = *c.frame;
@@ -369,20 +368,38 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
   if (w >= ng + nins) {
     // idle item of a busy block: nothing to update
   } else if (w < ng) {
-    const int s = c.group_slot[(int64_t)h * B + w];
-    const int k0 = c.group_start[(int64_t)h * (B + 1) + w];
-    const int k1 = c.group_start[(int64_t)h * (B + 1) + w + 1];
+    const int s = it.x, k0 = it.y, k1 = it.y + it.z, lead = it.w;
     const int64_t row = ((int64_t)h * B + s) * D + e0;
     const int c0 = c.count[(int64_t)h * B + s];
     float km[E], vm[E];
     load_f32vec<E>(c.k_master + row, km);
     load_f32vec<E>(c.v_master + row, vm);
     // The updates run strictly in token order; only the loads run ahead: the
-    // group's member ids are read kApplyGroup at a time (one per lane), and
-    // the inputs of kPrefetch members are in flight together.
+    // leader's inputs load beside the slot state, the other members' ids are
+    // read kApplyGroup at a time (one per lane), and the inputs of kPrefetch
+    // members are in flight together.
+    auto update = [&](const float (&xk)[E], const float (&xv)[E], int n_before) {
+#pragma clang fp contract(off)
+      const float div = (float)(c0 + n_before + 1);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float dk = xk[e] - km[e];
+        const float dv = xv[e] - vm[e];
+        const float qk = dk / div;
+        const float qv = dv / div;
+        km[e] = km[e] + qk;
+        vm[e] = vm[e] + qv;
+      }
+    };
+    {
+      float xk[E], xv[E];
+      load_vec<T, E>(kin + (int64_t)lead * a.sx_n + e0, xk);
+      load_vec<T, E>(vin + (int64_t)lead * a.sx_n + e0, xv);
+      update(xk, xv, 0);
+    }
     constexpr int kPrefetch = FASTAR_APPLY_PREFETCH;
     const int32_t* gt = c.group_tok + (int64_t)h * B;
-    for (int b0 = k0; b0 < k1; b0 += kApplyGroup) {
+    for (int b0 = k0 + 1; b0 < k1; b0 += kApplyGroup) {
       const int nb = min(kApplyGroup, k1 - b0);
       const int my_tok = gl < nb ? gt[b0 + gl] : 0;
       for (int j = 0; j < nb; j += kPrefetch) {
@@ -396,16 +413,7 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
 #pragma unroll
         for (int u = 0; u < kPrefetch; ++u) {
           if (j + u >= nb) break;
-          const float div = (float)(c0 + (b0 - k0) + j + u + 1);
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float dk = xk[u][e] - km[e];
-            const float dv = xv[u][e] - vm[e];
-            const float qk = dk / div;
-            const float qv = dv / div;
-            km[e] = km[e] + qk;
-            vm[e] = vm[e] + qv;
-          }
+          update(xk[u], xv[u], b0 - k0 + j + u);
         }
       }
     }
@@ -425,9 +433,7 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
       c.lb[(int64_t)h * Bp + s] = __log2f((float)cnt);
     }
   } else {
-    const int q = w - ng;
-    const int tok = c.ins_tok[(int64_t)h * B + q];
-    const int s = c.ins_slot[(int64_t)h * B + q];
+    const int s = it.x, tok = it.w;
     const int64_t row = ((int64_t)h * B + s) * D + e0;
     const int64_t mrow = ((int64_t)h * Bp + s) * D + e0;
     const T* kp = kin + (int64_t)tok * a.sx_n + e0;
