@@ -86,16 +86,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   for (int i = tid; i < T; i += kPlanThreads) dec_s[i] = c.dec[(int64_t)h * B + i];
   __syncthreads();
 
-  // 1. per token: leader of a merge group (its group size), or insert
+  // 1. per token: leader of a merge group (its group size), or insert.  A
+  //    thread's tokens are few (T <= FASTAR_MAX_TOKENS_PER_FRAME): their
+  //    leader flags and group sizes stay in registers for the passes below.
+  constexpr int kPerT = (FASTAR_MAX_TOKENS_PER_FRAME + kPlanThreads - 1) / kPlanThreads;
   const int per_t = (T + kPlanThreads - 1) / kPlanThreads;
   const int t_lo = min(T, tid * per_t), t_hi = min(T, t_lo + per_t);
+  int lead_size[kPerT];  // group size if token t_lo+k leads its group, else 0
   uint64_t mine = 0;
-  for (int i = t_lo; i < t_hi; ++i) {
+#pragma unroll
+  for (int k = 0; k < kPerT; ++k) {
+    const int i = t_lo + k;
+    lead_size[k] = 0;
+    if (i >= t_hi) continue;
     const int s = dec_s[i];
     if (s < 0) {
       mine += 1;
     } else if (owner[s] == i) {
-      mine += (1ull << kLeadShift) | ((uint64_t)gsize[s] << kMemShift);
+      lead_size[k] = gsize[s];
+      mine += (1ull << kLeadShift) | ((uint64_t)lead_size[k] << kMemShift);
     }
   }
   uint64_t tot = 0;
@@ -108,17 +117,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   int32_t* g_tok = c.group_tok + (int64_t)h * B;
   int32_t* g_slot = c.group_slot + (int64_t)h * B;
   int4* items = c.items + (int64_t)h * B;
-  for (int i = t_lo; i < t_hi; ++i) {
+#pragma unroll
+  for (int k = 0; k < kPerT; ++k) {
+    const int i = t_lo + k;
+    if (i >= t_hi) continue;
     const int s = dec_s[i];
     if (s < 0) {
       ins_list[(int)(run & kField)] = i;
       run += 1;
       continue;
     }
-    if (owner[s] != i) continue;
+    if (lead_size[k] == 0) continue;
     const int g = (int)(run >> kLeadShift);
     const int start = (int)((run >> kMemShift) & kField);
-    const int size = gsize[s];
+    const int size = lead_size[k];
     g_slot[g] = s;
     items[g] = make_int4(s, start, size, i);
     g_tok[start] = i;
@@ -211,12 +223,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   __syncthreads();
 
   // 4. reset the per-slot bookkeeping for the next frame (leaders own it)
-  for (int i = t_lo; i < t_hi; ++i) {
+#pragma unroll
+  for (int k = 0; k < kPerT; ++k) {
+    const int i = t_lo + k;
+    if (i >= t_hi || lead_size[k] == 0) continue;
     const int s = dec_s[i];
-    if (s >= 0 && owner[s] == i) {
-      owner[s] = kNoOwner;
-      gsize[s] = 0;
-    }
+    owner[s] = kNoOwner;
+    gsize[s] = 0;
   }
 
   // 5. slots for the inserts: evicted ids first, then never-used ids, ascending

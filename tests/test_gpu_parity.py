@@ -121,6 +121,12 @@ def _run_frames(w, frames, check_every=True, use_gpu_hash=False):
     ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048), 6),
     ("dit1.3b", dict(heads=3, tokens_per_frame=129, budget=180, seed=77), 8),   # eviction
     ("dit14b", dict(heads=2, tokens_per_frame=250, budget=300, head_dim=64, seed=78), 7),  # eviction
+    # 20-bit codes of 3 tables: table 1 straddles two 32-bit words of sign bits
+    ("dit1.3b", dict(heads=2, tokens_per_frame=200, budget=1024, tables=3, bits=20, seed=79), 5),
+    # 8 tables of 16 bits: the 8-table match path and longer candidate lists
+    ("dit1.3b", dict(heads=2, tokens_per_frame=150, budget=600, tables=8, bits=16, seed=80), 5),
+    # a frame as large as a budget that is not a multiple of 32 (eviction every frame)
+    ("dit1.3b", dict(heads=1, tokens_per_frame=100, budget=100, seed=81), 4),
 ])
 def test_match_merge_matches_oracle_given_codes(name, overrides, frames):
     w = WORKLOADS[name].with_(**overrides)
