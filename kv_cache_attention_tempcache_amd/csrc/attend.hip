@@ -3,7 +3,7 @@
 // are averaged and each logit is shifted by its group size), and the same
 // kernel over a per-frame subset of prompt keys for AnnCA (section 2B).
 //
-// bf16 path, per workgroup of 4 waves; each wave owns QB blocks of 32 queries:
+// bf16 path, per workgroup of 8 waves; each wave owns 32 queries:
 //   S^T = K Q^T on the 32x32x16 bf16 MFMA: A = a K tile row block from LDS,
 //     B = the wave's queries, held in registers for the whole key loop.  The
 //     accumulator gives each lane one query column and 16 key rows, so the
@@ -12,10 +12,10 @@
 //     max is refreshed lazily (only when a tile's max exceeds it by more than
 //     8), which keeps every weight <= 2^8 and skips most rescales of O.
 //   O^T += V^T P^T: B = the probabilities, converted to bf16 in registers in
-//     exactly the k-order the accumulator produced them; A = V^T, read from an
-//     LDS copy of the V tile that is transposed while it is written.
-//   K and V tiles (BN keys) are double-buffered in LDS: the next tile's global
-//     loads are in flight while the current one is multiplied.
+//     exactly the k-order the accumulator produced them; A = 8 keys of one
+//     feature, gathered from row-major V in LDS by transposing LDS reads.
+//   K, V (and log2-count) tiles of 64 keys move HBM -> LDS with direct-to-LDS
+//     loads into a ring of buffers, several tiles ahead of the one in use.
 //   Blocks are renumbered so each XCD (blocks are dealt round-robin over the 8
 //     XCDs) gets a contiguous range of (head, query tile) and shares its L2.
 // f32 path (small fp32 workloads): one thread per query, fp32 online softmax.
@@ -38,268 +38,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * q + min(x, r) + k;
 }
 
-template <int D, int QB, int BN>
-struct Cfg {
-  static constexpr int kWaves = 4;
-  static constexpr int kThreads = 256;
-  static constexpr int BM = kWaves * QB * 32;
-  static constexpr int KP = D * 2 + 16;   // bytes per K row in LDS
-  static constexpr int VP = BN * 2 + 8;   // bytes per V^T row in LDS
-  static constexpr int kKBytes = BN * KP;
-  static constexpr int kVBytes = D * VP;
-  static constexpr int kBufBytes = kKBytes + kVBytes + BN * 4;
-  static constexpr int kKPer = (BN * D / 8) / kThreads;         // 16-byte K chunks per thread
-  static constexpr int kVPer = ((BN / 2) * (D / 8)) / kThreads;  // (key pair, chunk) per thread
-  static_assert((BN * D / 8) % kThreads == 0, "K tile split");
-  static_assert(((BN / 2) * (D / 8)) % kThreads == 0, "V tile split");
-  static_assert(kBufBytes % 16 == 0, "buffer alignment");
-};
-
-template <int D, int QB, int BN, bool GATHER>
-__global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a, int qtiles) {
-  using C = Cfg<D, QB, BN>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int total = gridDim.x;
-  const int lb_id = xcd_remap(blockIdx.x, total);
-  const int per_head = a.F * qtiles;
-  const int h = lb_id / per_head;
-  const int g = (lb_id - h * per_head) / qtiles;
-  const int qt = lb_id - h * per_head - g * qtiles;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 31, hf = lane >> 5;
-  const int nkeys = a.n_keys ? a.n_keys[h * a.F + g] : a.n_keys_const;
-  const float cscale = a.scale * kLog2e;
-
-  const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.sq_h;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + (int64_t)h * a.sk_h;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + (int64_t)h * a.sk_h;
-  const int32_t* cnt = a.count ? a.count + (int64_t)h * a.count_ld : nullptr;
-  const int32_t* sel = GATHER ? a.sel + (int64_t)(h * a.F + g) * a.sel_ld : nullptr;
-  uint16_t* obase = static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h;
-
-  // queries of this wave: segment-local index qi = qt*BM + wave*QB*32 + qb*32 + m
-  bf16x8_t Qf[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qt * C::BM + wave * QB * 32 + qb * 32 + m;
-    const bool ok = qi < a.Nseg;
-    const uint16_t* qp = qbase + (int64_t)(g * a.Nseg + (ok ? qi : 0)) * a.sq_n + hf * (D / 2);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
-      if (!ok) v = bf16x8_t{};
-      Qf[qb][ks] = v;
-    }
-  }
-
-  f32x16_t O[D / 32][QB];
-  float mrun[QB], lrun[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    mrun[qb] = -__builtin_huge_valf();
-    lrun[qb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) O[db][qb] = f32x16_t{};
-  }
-
-  const int nt = (nkeys + BN - 1) / BN;
-  uint4 kreg[C::kKPer];
-  uint4 vreg[2 * C::kVPer];
-  float lbreg = 0.0f;
-
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < C::kKPer; ++i) {
-      const int chunk = tid + i * C::kThreads;
-      const int row = chunk / (D / 8), ch = chunk % (D / 8);
-      const int key = k0 + row;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (key < nkeys) {
-        const int src = GATHER ? sel[key] : key;
-        v = *reinterpret_cast<const uint4*>(kbase + (int64_t)src * a.sk_n + ch * 8);
-      }
-      kreg[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < C::kVPer; ++i) {
-      const int unit = tid + i * C::kThreads;
-      const int p = unit % (BN / 2), ch = unit / (BN / 2);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int key = k0 + 2 * p + u;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (key < nkeys) {
-          const int src = GATHER ? sel[key] : key;
-          v = *reinterpret_cast<const uint4*>(vbase + (int64_t)src * a.sk_n + ch * 8);
-        }
-        vreg[2 * i + u] = v;
-      }
-    }
-    if (tid < BN) {
-      const int key = k0 + tid;
-      float lbv = -__builtin_huge_valf();
-      if (key < nkeys) {
-        const int src = GATHER ? sel[key] : key;
-        lbv = cnt ? __log2f((float)cnt[src]) : 0.0f;
-      }
-      lbreg = lbv;
-    }
-  };
-
-  auto store_tile = [&](uint8_t* buf) {
-#pragma unroll
-    for (int i = 0; i < C::kKPer; ++i) {
-      const int chunk = tid + i * C::kThreads;
-      const int row = chunk / (D / 8), ch = chunk % (D / 8);
-      *reinterpret_cast<uint4*>(buf + row * C::KP + ch * 16) = kreg[i];
-    }
-    uint8_t* vt = buf + C::kKBytes;
-#pragma unroll
-    for (int i = 0; i < C::kVPer; ++i) {
-      const int unit = tid + i * C::kThreads;
-      const int p = unit % (BN / 2), ch = unit / (BN / 2);
-      const uint32_t a0[4] = {vreg[2 * i].x, vreg[2 * i].y, vreg[2 * i].z, vreg[2 * i].w};
-      const uint32_t a1[4] = {vreg[2 * i + 1].x, vreg[2 * i + 1].y, vreg[2 * i + 1].z,
-                              vreg[2 * i + 1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (e & 1) ? (a0[e >> 1] >> 16) : (a0[e >> 1] & 0xffffu);
-        const uint32_t hi = (e & 1) ? (a1[e >> 1] & 0xffff0000u) : (a1[e >> 1] << 16);
-        *reinterpret_cast<uint32_t*>(vt + (ch * 8 + e) * C::VP + p * 4) = lo | hi;
-      }
-    }
-    if (tid < BN) reinterpret_cast<float*>(buf + C::kKBytes + C::kVBytes)[tid] = lbreg;
-  };
-
-  if (nt > 0) {
-    load_tile(0);
-    store_tile(smem);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < nt; ++it) {
-    const bool has_next = it + 1 < nt;
-    if (has_next) load_tile((it + 1) * BN);
-    const uint8_t* buf = smem + (it & 1) * C::kBufBytes;
-    const uint8_t* ks_lds = buf;
-    const uint8_t* vt_lds = buf + C::kKBytes;
-    const float* lb_lds = reinterpret_cast<const float*>(buf + C::kKBytes + C::kVBytes);
-
-    // S^T = K Q^T
-    f32x16_t S[BN / 32][QB];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-            ks_lds + (kb * 32 + m) * C::KP + (hf * (D / 2) + ks * 8) * 2);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[qb][ks], S[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // logits, lazy running max, probabilities
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const float4 b4 = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
-        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            S[kb][qb][4 * jg + r] = __builtin_fmaf(S[kb][qb][4 * jg + r], cscale, bb[r]);
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -__builtin_huge_valf();
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, S[kb][qb][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool need = mx > mrun[qb] + 8.0f;
-      if (__ballot(need)) {
-        const float mnew = need ? mx : mrun[qb];
-        const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
-        lrun[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) O[db][qb][j] *= alpha;
-        mrun[qb] = mnew;
-      }
-      float ls = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float p = __builtin_amdgcn_exp2f(S[kb][qb][j] - mrun[qb]);
-          S[kb][qb][j] = p;
-          ls += p;
-        }
-      lrun[qb] += ls;
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t pf[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pf[qb][i] = (__bf16)S[kb][qb][8 * kk + i];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const uint8_t* vp = vt_lds + (db * 32 + m) * C::VP + (kb * 32 + kk * 16 + 4 * hf) * 2;
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vp);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vp + 16);
-          const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
-          const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&vv);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);
-        }
-      }
-    }
-
-    if (has_next) store_tile(smem + ((it + 1) & 1) * C::kBufBytes);
-    __syncthreads();
-  }
-
-  // normalise and store: lane holds O^T rows d = db*32 + 8*(j/4) + 4*hf + j%4
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qt * C::BM + wave * QB * 32 + qb * 32 + m;
-    const float lt = lrun[qb] + __shfl_xor(lrun[qb], 32);
-    if (qi >= a.Nseg) continue;
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    uint16_t* op = obase + (int64_t)(g * a.Nseg + qi) * a.so_n;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        uint32_t w0 = f32_to_bf16_bits(O[db][qb][4 * jg + 0] * inv) |
-                      (f32_to_bf16_bits(O[db][qb][4 * jg + 1] * inv) << 16);
-        uint32_t w1 = f32_to_bf16_bits(O[db][qb][4 * jg + 2] * inv) |
-                      (f32_to_bf16_bits(O[db][qb][4 * jg + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + db * 32 + 8 * jg + 4 * hf) = make_uint2(w0, w1);
-      }
-    if (a.lse && hf == 0)
-      a.lse[(int64_t)h * a.F * a.Nseg + (int64_t)g * a.Nseg + qi] =
-          lt > 0.0f ? (mrun[qb] + __log2f(lt)) * kLn2 : -__builtin_huge_valf();
-  }
-}
 
 template <int D, bool GATHER>
 __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles) {
@@ -425,11 +163,17 @@ struct CCfg {
 // QB blocks of 32 queries per wave: every K or V fragment read from LDS feeds
 // QB MFMAs, which is what keeps the kernel below the LDS bandwidth (one 1 KiB
 // operand per 32x32x16 MFMA would need all 128 B/clk of a CU's LDS).
-template <int D, int BN, int WAVES, int QB, int NBUF>
+// SUBSET = false: attention over the cache (mirror rows, log2-count bias, the
+// live count of each head).  SUBSET = true: every segment (frame) of sa.Nseg
+// queries attends over rows of arbitrary [H][N][d] key and value arrays with
+// no bias: all sa.n_keys_const rows, or the first n_keys[h][g] rows of the
+// segment's gather list sa.sel, staged in LDS at the start.
+template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET>
 __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kernel(
-    Dims dm, CacheDev c, CacheAttendArgs a, int qtiles) {
+    Dims dm, CacheDev c, CacheAttendArgs a, AttendArgs sa, int qtiles) {
   using C = CCfg<D, BN, WAVES, QB>;
   static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  extern __shared__ int32_t sel_lds[];  // SUBSET with a gather list
   // A ring of NBUF distinct LDS objects: tile it is read from one while the
   // copies of tiles it+1 .. it+NBUF-1 are in flight into the others.  Distinct
   // objects let the compiler see that the reads never alias the copies in
@@ -439,47 +183,91 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   __shared__ __attribute__((aligned(16))) uint8_t buf2[NBUF >= 3 ? C::kBuf : 16];
   __shared__ __attribute__((aligned(16))) uint8_t buf3[NBUF == 4 ? C::kBuf : 16];
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = lid / qtiles, qt = lid - h * qtiles;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform by construction: keeps the barrier paths below scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31, hf = lane >> 5;
-  const int Bp = dm.Bp;
-  const int nkeys = c.n_live[h];
-  const float cscale = a.scale * kLog2e;
-  const uint16_t* kg = static_cast<const uint16_t*>(c.k_mirror) + (int64_t)h * Bp * D;
-  const uint8_t* vg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(c.v_mirror) +
-                                                       (int64_t)h * Bp * D);
-  const float* lbg = c.lb + (int64_t)h * Bp;
+  int h, g, qt;
+  if constexpr (SUBSET) {
+    const int per_head = sa.F * qtiles;
+    h = lid / per_head;
+    g = (lid - h * per_head) / qtiles;
+    qt = lid - h * per_head - g * qtiles;
+  } else {
+    h = lid / qtiles;
+    g = 0;
+    qt = lid - h * qtiles;
+  }
+  // queries, outputs, key/value rows of this block
+  const int Np = SUBSET ? sa.n_keys_const : 0;  // rows of the subset arrays
+  const int nkeys = SUBSET ? (sa.n_keys ? min(max(sa.n_keys[h * sa.F + g], 0), Np) : Np)
+                           : c.n_live[h];
+  const float cscale = (SUBSET ? sa.scale : a.scale) * kLog2e;
+  const int nq = SUBSET ? sa.Nseg : a.Nq;
+  const int64_t sq_n = SUBSET ? sa.sq_n : a.sq_n, so_n = SUBSET ? sa.so_n : a.so_n;
+  const uint16_t* qbase =
+      SUBSET ? static_cast<const uint16_t*>(sa.q) + (int64_t)h * sa.sq_h + (int64_t)g * sa.Nseg * sa.sq_n
+             : static_cast<const uint16_t*>(a.q) + (int64_t)h * a.sq_h;
+  uint16_t* obase =
+      SUBSET ? static_cast<uint16_t*>(sa.o) + (int64_t)h * sa.so_h + (int64_t)g * sa.Nseg * sa.so_n
+             : static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h;
+  float* lse_row = SUBSET ? (sa.lse ? sa.lse + (int64_t)(h * sa.F + g) * sa.Nseg : nullptr)
+                          : (a.lse ? a.lse + (int64_t)h * a.Nq : nullptr);
+  const uint8_t* kg =
+      SUBSET ? static_cast<const uint8_t*>(sa.k) + (int64_t)h * sa.sk_h * 2
+             : reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(c.k_mirror) +
+                                                (int64_t)h * dm.Bp * D);
+  const uint8_t* vg =
+      SUBSET ? static_cast<const uint8_t*>(sa.v) + (int64_t)h * sa.sk_h * 2
+             : reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(c.v_mirror) +
+                                                (int64_t)h * dm.Bp * D);
+  const int64_t rs = SUBSET ? sa.sk_n * 2 : C::kRowBytes;  // bytes between key rows
+  const float* lbg = SUBSET ? nullptr : c.lb + (int64_t)h * dm.Bp;
+  const bool gather = SUBSET && sa.sel != nullptr;  // block-uniform
+  if (gather) {
+    const int32_t* sel = sa.sel + (int64_t)(h * sa.F + g) * sa.sel_ld;
+    for (int i = tid; i < nkeys; i += C::kThreads) sel_lds[i] = min(max(sel[i], 0), Np - 1);
+    __syncthreads();
+  }
 
   // Copy addresses: a wave-uniform tile base plus per-lane byte offsets that
   // do not change from tile to tile, so issuing a copy costs no vector math.
   // Wave w copies the 1 KiB chunks w, w + WAVES, ... of the K and V tiles; LDS
   // position (row, chunk) receives global chunk chunk ^ swz(row).
+  // In a subset, a lane's source row is looked up per tile instead (rows past
+  // the kept count read row 0 and are masked by their bias).
   constexpr int kPerWave = C::kKInstr / WAVES;
   uint32_t koff[kPerWave], voff[kPerWave];
+  int rrow[kPerWave];
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
     const int off = (wave + j * WAVES) * 1024 + lane * 16;
     const int row = off / C::kRowBytes;
     const int slot = (off - row * C::kRowBytes) >> 4;
-    koff[j] = (uint32_t)(row * C::kRowBytes + ((slot ^ C::kswz(row)) << 4));
-    voff[j] = (uint32_t)(row * C::kRowBytes + ((slot ^ C::vswz(row)) << 4));
+    rrow[j] = row;
+    const int rb = SUBSET ? 0 : row * C::kRowBytes;
+    koff[j] = (uint32_t)(rb + ((slot ^ C::kswz(row)) << 4));
+    voff[j] = (uint32_t)(rb + ((slot ^ C::vswz(row)) << 4));
   }
   auto issue = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
-    const uint8_t* kt = reinterpret_cast<const uint8_t*>(kg) + (int64_t)k0 * C::kRowBytes;
-    const uint8_t* vt = vg + (int64_t)k0 * C::kRowBytes;
+    const uint8_t* kt = kg + (SUBSET ? 0 : (int64_t)k0 * C::kRowBytes);
+    const uint8_t* vt = vg + (SUBSET ? 0 : (int64_t)k0 * C::kRowBytes);
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
       const int i = wave + j * WAVES;
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(kt + koff[j]), (lds_void_t*)(buf + i * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + voff[j]),
+      int64_t ro = 0;
+      if constexpr (SUBSET) {
+        const int key = k0 + rrow[j];
+        ro = (int64_t)(key < nkeys ? (gather ? sel_lds[key] : key) : 0) * rs;
+      }
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(kt + ro + koff[j]),
+                                       (lds_void_t*)(buf + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + ro + voff[j]),
                                        (lds_void_t*)(buf + C::kKBytes + i * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < (BN + 63) / 64; ++i) {
-      if (wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
+      if (!SUBSET && wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(lbg + k0 + i * 64 + (uint32_t)lane),
                                          (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256),
                                          4, 0, 0);
@@ -491,9 +279,8 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qt * C::BM + (wave * QB + qb) * 32 + m;
-    const bool qok = qi < a.Nq;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t)h * a.sq_h +
-                         (int64_t)(qok ? qi : 0) * a.sq_n + hf * (D / 2);
+    const bool qok = qi < nq;
+    const uint16_t* qp = qbase + (int64_t)(qok ? qi : 0) * sq_n + hf * (D / 2);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
@@ -529,7 +316,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   // Copies this wave issues per tile: K and V chunks, plus the bias row for
   // the last wave(s).
   constexpr int kCopies = 2 * C::kKInstr / WAVES;
-  const bool lb_wave = wave >= WAVES - (BN + 63) / 64;
+  const bool lb_wave = !SUBSET && wave >= WAVES - (BN + 63) / 64;
 
   // Wait until at most n tiles' copies issued by this wave are in flight
   // (every older tile has landed), finish this wave's LDS reads, then meet
@@ -576,8 +363,16 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg)
-        lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
+      for (int jg = 0; jg < 4; ++jg) {
+        if constexpr (SUBSET) {  // no bias; keys past the kept count are masked
+          const int k = it * BN + kb * 32 + 8 * jg + 4 * hf;
+          const float ninf = -__builtin_huge_valf();
+          lbr[kb][jg] = make_float4(k < nkeys ? 0.0f : ninf, k + 1 < nkeys ? 0.0f : ninf,
+                                    k + 2 < nkeys ? 0.0f : ninf, k + 3 < nkeys ? 0.0f : ninf);
+        } else {
+          lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
+        }
+      }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -__builtin_huge_valf();
@@ -673,9 +468,9 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qt * C::BM + (wave * QB + qb) * 32 + m;
     const float lt = lrun[qb] + __shfl_xor(lrun[qb], 32);
-    if (qi >= a.Nq) continue;
+    if (qi >= nq) continue;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h + (int64_t)qi * a.so_n;
+    uint16_t* op = obase + (int64_t)qi * so_n;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -686,9 +481,8 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
                             (f32_to_bf16_bits(O[db][qb][4 * jg + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(op + db * 32 + 8 * jg + 4 * hf) = make_uint2(w0, w1);
       }
-    if (a.lse && hf == 0)
-      a.lse[(int64_t)h * a.Nq + qi] =
-          lt > 0.0f ? (mrun[qb] + __log2f(lt)) * kLn2 : -__builtin_huge_valf();
+    if (lse_row && hf == 0)
+      lse_row[qi] = lt > 0.0f ? (mrun[qb] + __log2f(lt)) * kLn2 : -__builtin_huge_valf();
   }
 }
 
@@ -699,42 +493,35 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
   const int qtiles = (a.Nq + C::BM - 1) / C::BM;
   const int blocks = dm.H * qtiles;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF>), dim3(blocks), dim3(C::kThreads), 0,
-                     s, dm, c, a, qtiles);
+  hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false>), dim3(blocks),
+                     dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
   return hipGetLastError();
 }
 
-template <int D, int QB, int BN, bool GATHER>
-hipError_t launch_bf16_cfg(const AttendArgs& a, hipStream_t s) {
-  using C = Cfg<D, QB, BN>;
+// Subsets: 8 waves x 32 queries per workgroup per (head, segment); a gather
+// list is staged in LDS (up to 4 bytes per prompt row) beside a 2-deep ring.
+template <int D, int NBUF>
+hipError_t launch_subset_cfg(const AttendArgs& a, hipStream_t s) {
+  using C = CCfg<D, 64, 8, 1>;
   const int qtiles = (a.Nseg + C::BM - 1) / C::BM;
   const int blocks = a.H * a.F * qtiles;
   if (blocks == 0) return hipSuccess;
-  const size_t lds = 2 * (size_t)C::kBufBytes;
-  auto kern = attend_bf16_kernel<D, QB, BN, GATHER>;
+  const size_t lds = a.sel ? (size_t)a.n_keys_const * 4 : 0;
+  auto kern = attend_cache_kernel<D, 64, 8, 1, NBUF, true>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(C::kThreads), lds, s, a, qtiles);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(C::kThreads), lds, s, Dims{}, CacheDev{}, CacheAttendArgs{},
+                     a, qtiles);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Tile shape: 32-query blocks per wave and keys per LDS tile.
-#ifndef FASTAR_ATTN_QB128
-#define FASTAR_ATTN_QB128 1
-#endif
-#ifndef FASTAR_ATTN_BN
-#define FASTAR_ATTN_BN 64
-#endif
-
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
-  const bool gather = a.sel != nullptr;
-  constexpr int QB = FASTAR_ATTN_QB128, BN = FASTAR_ATTN_BN;
-  if (a.d == 128)
-    return gather ? launch_bf16_cfg<128, QB, BN, true>(a, s) : launch_bf16_cfg<128, QB, BN, false>(a, s);
-  return gather ? launch_bf16_cfg<64, 2, 64, true>(a, s) : launch_bf16_cfg<64, 2, 64, false>(a, s);
+  if (a.count != nullptr) return hipErrorInvalidValue;  // no count bias on subsets
+  if (a.d == 128) return a.sel ? launch_subset_cfg<128, 2>(a, s) : launch_subset_cfg<128, 4>(a, s);
+  return a.sel ? launch_subset_cfg<64, 2>(a, s) : launch_subset_cfg<64, 4>(a, s);
 }
 
 #ifndef FASTAR_CACHE_NBUF

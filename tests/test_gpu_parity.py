@@ -293,8 +293,9 @@ def test_lemma51_on_gpu_fp32():
 
 # ------------------------------------------------------------------ AnnCA
 
-def test_annca_select_and_sparse_attend_match_oracle():
-    cp = ClusterPrompt(heads=2, queries_per_frame=300, frames=3)
+@pytest.mark.parametrize("bits", [16, 20])  # 16: LDS bitmaps; 20: the hash-set path
+def test_annca_select_and_sparse_attend_match_oracle(bits):
+    cp = ClusterPrompt(heads=2, queries_per_frame=300, frames=3, bits=bits)
     H, F, Nf, Np = 2, 3, 300, cp.prompt_tokens
     planes = cp.planes()
     q_dev = to_device(cp.Q, "bf16")
