@@ -53,7 +53,77 @@ def _parse():
     p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"),
                    help="where --measure-traffic writes its summary")
     p.add_argument("--traffic-child", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--fenced-events", action="store_true",
+                   help="time with torch's default events (system-scope fence at every record)")
     return p.parse_args()
+
+
+class _HipEvents:
+    """Timing events recorded on a HIP stream without a system-scope fence.
+
+    torch's events are created with the default flags, under which every
+    record on ROCm also releases to system scope (an L2 write-back across all
+    XCDs) and so costs the stream a few microseconds between kernels.  The
+    timed step only needs device-side timestamps, so these events are created
+    with hipEventDisableSystemFence through the HIP runtime torch has loaded.
+    """
+
+    _FLAG_NO_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n, stream_handle):
+        import ctypes
+        self._ct = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._stream = ctypes.c_void_p(stream_handle)
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            self._check(self._hip.hipEventCreateWithFlags(ctypes.byref(e),
+                                                          ctypes.c_uint(self._FLAG_NO_SYSTEM_FENCE)),
+                        "hipEventCreateWithFlags")
+            self.ev.append(e)
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self, i):
+        self._check(self._hip.hipEventRecord(self.ev[i], self._stream), "hipEventRecord")
+
+    def elapsed_ms(self, i, j):
+        ms = self._ct.c_float()
+        self._check(self._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev[i], self.ev[j]),
+                    "hipEventElapsedTime")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.ev:
+            self._hip.hipEventDestroy(e)
+        self.ev = []
+
+
+class _TorchEvents:
+    """The same interface over torch.cuda.Event (default flags)."""
+
+    def __init__(self, n, stream):
+        import torch
+        self._stream = stream
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def record(self, i):
+        self.ev[i].record(self._stream)
+
+    def elapsed_ms(self, i, j):
+        return self.ev[i].elapsed_time(self.ev[j])
+
+    def close(self):
+        pass
+
+
+def _events(args, n, stream):
+    if args.fenced_events:
+        return _TorchEvents(n, stream)
+    return _HipEvents(n, stream.cuda_stream)
 
 
 def _workload_desc(w):
@@ -313,15 +383,14 @@ def main():
     # path of step i runs between the end of step i-1 and the start of its
     # attention, so no extra event sits between the steps
     stream = torch.cuda.current_stream()
-    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(nrep)]
-    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(nrep)]
+    ev = _events(args, 2 * nrep, stream)   # 2i: before attention of step i, 2i+1: after
 
     def step(i):
         c = caches[i]
         c.match_merge(ck, cv, T, F)
-        ev_a0[i].record(stream)
+        ev.record(2 * i)
         c.attend(cq, out=out)
-        ev_a1[i].record(stream)
+        ev.record(2 * i + 1)
 
     for i in range(args.warmup):
         step(i)
@@ -333,9 +402,10 @@ def main():
     elapsed = time.perf_counter() - t0
 
     timed = range(args.warmup, nrep)
-    attend_ms = [ev_a0[i].elapsed_time(ev_a1[i]) for i in timed]
+    attend_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in timed]
     # (from the second timed step: the first follows the host-side sync)
-    merge_ms = [ev_a1[i - 1].elapsed_time(ev_a0[i]) for i in range(args.warmup + 1, nrep)]
+    merge_ms = [ev.elapsed_ms(2 * i - 1, 2 * i) for i in range(args.warmup + 1, nrep)]
+    ev.close()
     post = caches[-1].stats()
     # every copy did identical work
     assert all(c.stats()["live_slots"] == post["live_slots"] for c in caches[:2])
@@ -391,6 +461,8 @@ def main():
             "evicted_slots_per_step": int(post["evicted_slots"] - pre["evicted_slots"]),
             "attend_gflop_per_step": attend_flops / 1e9,
             "workspace_mb_per_cache": caches[0].workspace.numel() / 2**20,
+            "timing_events": ("torch default (system fence)" if args.fenced_events
+                              else "hipEventDisableSystemFence"),
         },
         "context": "pages report end-to-end only: FAST-AR 5-10x vs dense FlashAttention-3 with "
                    "constant memory; LIPAR 1.45x (NVIDIA A6000); not comparable to this step",

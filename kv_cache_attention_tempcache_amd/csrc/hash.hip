@@ -3,12 +3,17 @@
 // [<r_tj, x> > 0], stored as 1u << j.
 //
 // bf16 path: the projection is a small GEMM (L*b x d) * (d x rows) on the
-// 32x32x16 bf16 MFMA.  A wave owns 32 rows and reads the hyperplane operands
-// straight from L2 (a few KiB shared by every wave), with no LDS staging and
-// no block barrier between the loads and the MFMAs.  With hyperplanes as the
-// MFMA rows, each lane's accumulators hold 16 of the 32 projections of one
-// key row, so it packs 16 sign bits locally and one lane exchange with the
-// other half-wave completes the 32-bit word, in LSB-first plane order.
+// 32x32x16 bf16 MFMA, hyperplanes as the MFMA rows and key rows as its
+// columns.  A workgroup copies the hyperplanes once into LDS, already in MFMA
+// operand order (one 1 KiB fragment per 32 planes and k-step, lane-major), so
+// the copy is a plain coalesced read and every later operand read is one
+// conflict-free 16-byte LDS load; its waves then take 32 key rows at a time.
+// The k-steps read features (2*ks + half)*8 .. +7, so the two half-waves load
+// adjacent 16 bytes of each row.  Each lane's accumulators hold 16 of the 32
+// projections of one key row; it packs 16 sign bits locally and one lane
+// exchange with the other half-wave completes the 32-bit word, in LSB-first
+// plane order.  Rows past the end and padding planes are read clamped to valid
+// memory and never stored.
 //
 // f32 path: one thread per (row, table), products and sums in float64.
 #include "common.hpp"
@@ -19,91 +24,119 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
-constexpr int kHashWaves = 4;
+constexpr int kHashWaves = 8;
+constexpr int kHashThreads = kHashWaves * kWave;
 
 template <int D>
-__global__ __launch_bounds__(256) void hash_bf16_kernel(HashArgs a, int tiles_per_head,
-                                                        int total_tiles) {
+__global__ __launch_bounds__(kHashThreads) void hash_bf16_kernel(HashArgs a, int tiles_per_head,
+                                                                 int total_tiles) {
+  constexpr int KS = D / 16;  // k-steps
+  extern __shared__ __attribute__((aligned(16))) bf16x8_t frag[];  // [Ppad/32][KS][64]
   const int P = a.L * a.b;
-  const int Ppad = (P + 31) & ~31;
+  const int npb = (P + 31) / 32;
   const uint16_t* planes = static_cast<const uint16_t*>(a.planes);
+  const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, hf = lane >> 5;
-  const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
 
-  for (int tile = blockIdx.x * kHashWaves + wave; tile < total_tiles;
-       tile += gridDim.x * kHashWaves) {
-    const int h = tile / tiles_per_head;
-    const int r0 = (tile - h * tiles_per_head) * 32;
-    const int nrows = a.rows ? a.n_rows[(int64_t)h * a.n_rows_stride] : a.N;
-    if (r0 >= nrows) continue;
-    const int r = r0 + m;
-    const bool valid = r < nrows;
-    int64_t xrow = r;
-    if (a.rows) xrow = valid ? a.rows[(int64_t)h * a.rows_ld + r] : 0;
-    else if (!valid) xrow = 0;
+  // tile -> head, row of this lane, and its source row (clamped into the
+  // tile when past the end); `live` is false for a tile wholly past the end
+  struct Tile {
+    int h, r;
+    int64_t xrow;
+    bool valid, live;
+  };
+  auto locate = [&](int tile) __attribute__((always_inline)) {
+    Tile t{0, 0, 0, false, false};
+    if (tile >= total_tiles) return t;
+    t.h = tile / tiles_per_head;
+    const int r0 = (tile - t.h * tiles_per_head) * 32;
+    const int nrows = a.rows ? a.n_rows[(int64_t)t.h * a.n_rows_stride] : a.N;
+    if (r0 >= nrows) return t;
+    t.live = true;
+    t.r = r0 + m;
+    t.valid = t.r < nrows;
+    t.xrow = t.valid ? t.r : r0;
+    if (a.rows) t.xrow = a.rows[(int64_t)t.h * a.rows_ld + t.xrow];
+    return t;
+  };
+  // k-step ks of this lane: features (2*ks + hf)*8 .. +7 of its row
+  auto load_x = [&](const Tile& t, bf16x8_t (&A)[KS]) __attribute__((always_inline)) {
+    const uint16_t* xp = xbase + (int64_t)t.h * a.sx_h + t.xrow * a.sx_n + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) A[ks] = *reinterpret_cast<const bf16x8_t*>(xp + ks * 16);
+  };
 
-    // A operand: row m, features hf*D/2 + ks*8 .. +7 for k-step ks (the same
-    // feature permutation is applied to the hyperplanes below).
-    bf16x8_t A[D / 16];
-    const uint16_t* xp = xbase + (int64_t)h * a.sx_h + xrow * a.sx_n + hf * (D / 2);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(xp + ks * 8);
-      if (!valid) v = bf16x8_t{};
-      A[ks] = v;
-    }
+  // the first tile's rows are requested before the hyperplane copy
+  int tile = blockIdx.x * kHashWaves + wave;
+  const int stride = gridDim.x * kHashWaves;
+  Tile cur = locate(tile);
+  bf16x8_t A[KS];
+  if (cur.live) load_x(cur, A);
 
-    uint32_t words[9];
+  // hyperplanes -> LDS fragments: chunk c (features 8c..8c+7) of plane p is
+  // k-step c/2, half c%2 of lane 32*(c%2) + p%32 in block p/32.  Four lanes
+  // read 64 contiguous bytes of a plane (their LDS stores then meet at most
+  // 4-way bank conflicts, once per workgroup).
+  // All of a thread's loads are issued before its first store.
+  constexpr int kFill = (FASTAR_MAX_TABLES * FASTAR_MAX_BITS * (D / 8) + kHashThreads - 1) /
+                        kHashThreads;
+  const int Ppad = npb * 32, n_chunks = Ppad * (D / 8);
+  bf16x8_t fv[kFill];
+  int fdst[kFill];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) words[k] = 0u;
-    // B operands straight from L2: hyperplane pb*32 + m (zero past L*b); the
-    // next block's operands are loaded while this block's MFMAs run
-    const int npb = Ppad / 32;
-    auto load_b = [&](int pb, bf16x8_t (&Bf)[D / 16]) __attribute__((always_inline)) {
-      const int prow = pb * 32 + m;
-      const uint16_t* pp = planes + (int64_t)(prow < P ? prow : 0) * D + hf * (D / 2);
+  for (int i = 0; i < kFill; ++i) {
+    const int idx = threadIdx.x + i * kHashThreads;
+    fdst[i] = -1;
+    if (idx >= n_chunks) continue;
+    const int rest = idx >> 2;
+    const int p = rest % Ppad, c = 4 * (rest / Ppad) + (idx & 3);
+    const int pc = p < P ? p : P - 1;
+    fv[i] = *reinterpret_cast<const bf16x8_t*>(planes + (int64_t)pc * D + c * 8);
+    fdst[i] = ((p >> 5) * KS + (c >> 1)) * 64 + (c & 1) * 32 + (p & 31);
+  }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) Bf[ks] = *reinterpret_cast<const bf16x8_t*>(pp + ks * 8);
-      if (pb * 32 + 32 > P) {  // only a last, partial block has padding planes
+  for (int i = 0; i < kFill; ++i)
+    if (fdst[i] >= 0) frag[fdst[i]] = fv[i];
+  __syncthreads();
+
+  for (; tile < total_tiles; tile += stride) {
+    // the next tile's rows load while this one is projected
+    const Tile nxt = locate(tile + stride);
+    bf16x8_t An[KS];
+    if (nxt.live) load_x(nxt, An);
+
+    if (cur.live) {
+      uint32_t words[9];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          if (prow >= P) Bf[ks] = bf16x8_t{};
+      for (int k = 0; k < 9; ++k) words[k] = 0u;
+      // register j of lane l: plane 32*pb + 8*(j/4) + 4*(l/32) + j%4 of key row l%32
+#pragma unroll
+      for (int pb = 0; pb < 8; ++pb) {
+        if (pb >= npb) break;
+        const bf16x8_t* fb = frag + pb * KS * 64 + lane;
+        f32x16_t acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks * 64], A[ks], acc, 0, 0, 0);
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          bits |= (acc[j] > 0.0f ? 1u : 0u) << (8 * (j >> 2) + (j & 3));
+        bits <<= 4 * hf;
+        words[pb] = bits | __shfl_xor(bits, 32);  // both halves: the word of row m
       }
-    };
-    // hyperplanes as MFMA rows, keys as columns: register j of lane l holds
-    // plane 8*(j/4) + 4*(l/32) + j%4 of key row l%32
-    auto block = [&](int pb, const bf16x8_t (&Bf)[D / 16]) __attribute__((always_inline)) {
-      f32x16_t acc = {};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bf[ks], A[ks], acc, 0, 0, 0);
-      uint32_t bits = 0u;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        bits |= (acc[j] > 0.0f ? 1u : 0u) << (8 * (j >> 2) + (j & 3));
-      bits <<= 4 * hf;
-      words[pb] = bits | __shfl_xor(bits, 32);  // both halves: the word of row m
-    };
-    bf16x8_t B0[D / 16], B1[D / 16];
-    load_b(0, B0);
-#pragma unroll
-    for (int pb = 0; pb < 8; pb += 2) {
-      if (pb >= npb) break;
-      if (pb + 1 < npb) load_b(pb + 1, B1);
-      block(pb, B0);
-      if (pb + 1 >= npb) break;
-      if (pb + 2 < npb) load_b(pb + 2, B0);
-      block(pb + 1, B1);
-    }
-
-    if (hf == 0 && valid) {
-      const int64_t col = a.rows ? xrow : (int64_t)r;
-      for (int t = 0; t < a.L; ++t) {
-        a.codes[((int64_t)h * a.L + t) * a.codes_ld + a.codes_col0 + col] =
-            extract_code(words, t * a.b, a.b);
+      if (hf == 0 && cur.valid) {
+        const int64_t col = a.rows ? cur.xrow : (int64_t)cur.r;
+        for (int t = 0; t < a.L; ++t) {
+          a.codes[((int64_t)cur.h * a.L + t) * a.codes_ld + a.codes_col0 + col] =
+              extract_code(words, t * a.b, a.b);
+        }
       }
     }
+    cur = nxt;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) A[ks] = An[ks];
   }
 }
 
@@ -137,15 +170,18 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(HashArgs a, int64_t total
 hipError_t launch_hash_bf16(const HashArgs& a, hipStream_t s) {
   const int tiles_per_head = (a.N + 31) / 32;
   const int total = a.H * tiles_per_head;
+  const int P = a.L * a.b;
   if (total == 0) return hipSuccess;
+  // one pass of 8-wave groups; a larger job loops, two workgroups per CU
   int blocks = (total + kHashWaves - 1) / kHashWaves;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 512) blocks = 512;
+  const size_t lds = (size_t)((P + 31) / 32) * 32 * a.d * sizeof(uint16_t);
   if (a.d == 128)
-    hipLaunchKernelGGL(hash_bf16_kernel<128>, dim3(blocks), dim3(256), 0, s, a, tiles_per_head,
-                       total);
+    hipLaunchKernelGGL(hash_bf16_kernel<128>, dim3(blocks), dim3(kHashThreads), lds, s, a,
+                       tiles_per_head, total);
   else
-    hipLaunchKernelGGL(hash_bf16_kernel<64>, dim3(blocks), dim3(256), 0, s, a, tiles_per_head,
-                       total);
+    hipLaunchKernelGGL(hash_bf16_kernel<64>, dim3(blocks), dim3(kHashThreads), lds, s, a,
+                       tiles_per_head, total);
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ def _planes_dev(planes, dtype):
     ("bf16", 2, 97, 64, 4, 16),
     ("bf16", 1, 33, 128, 3, 20),
     ("bf16", 2, 64, 128, 8, 32),
+    ("bf16", 8, 16999, 128, 4, 32),   # more 32-row tiles than one pass of the grid
     ("f32", 1, 64, 64, 1, 16),
     ("f32", 2, 50, 128, 4, 32),
 ])
@@ -211,6 +212,13 @@ def test_conservation_on_device():
     ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048), 6),
     ("dit1.3b", dict(heads=3, tokens_per_frame=131, budget=1024, head_dim=64, seed=3), 4),
     ("dit14b", dict(heads=2, tokens_per_frame=333, budget=4096, seed=4), 5),
+    # one frame into an empty cache: 1..5 key tiles of 64, so every position
+    # of the 4-buffer ring is the last tile once
+    ("dit1.3b", dict(heads=2, tokens_per_frame=40, budget=1024, seed=40), 1),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=100, budget=1024, seed=41), 1),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=150, budget=1024, seed=42), 1),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=250, budget=1024, seed=43), 1),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=1024, seed=44), 1),
 ])
 def test_attend_matches_oracle(name, overrides, frames):
     w = WORKLOADS[name].with_(**overrides)
