@@ -86,7 +86,7 @@ fastar_status make_dims(const fastar_config* cfg, Dims* dm) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 enum Region {
-  kPlanes, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
+  kPlanes, kPlanesFrag, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
   kNLive, kEvicted, kCounters, kOwner, kGsize, kFrame, kStateEnd = kFrame,
   kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupSlot, kItems,
   kPlan, kNumRegions
@@ -133,6 +133,7 @@ Layout make_layout(const Dims& dm) {
   const size_t H = dm.H, B = dm.B, d = dm.d, Lt = dm.L, e = dm.elem;
   size_t sizes[kNumRegions] = {};
   sizes[kPlanes] = (size_t)(dm.L * dm.b > 0 ? dm.L * dm.b : 1) * d * e;
+  sizes[kPlanesFrag] = e == 2 ? (size_t)dm.Ppad * d * 2 : 0;
   sizes[kKMaster] = H * B * d * 4;
   sizes[kVMaster] = H * B * d * 4;
   const size_t Bp = dm.Bp;
@@ -173,6 +174,7 @@ CacheDev carve(void* base, const Dims& dm) {
   uint8_t* b = static_cast<uint8_t*>(base);
   CacheDev c{};
   c.planes = b + L.off[kPlanes];
+  c.planes_frag = b + L.off[kPlanesFrag];
   c.k_master = reinterpret_cast<float*>(b + L.off[kKMaster]);
   c.v_master = reinterpret_cast<float*>(b + L.off[kVMaster]);
   c.k_mirror = b + L.off[kKMirror];
@@ -239,6 +241,26 @@ fastar_status fastar_cache_create(const fastar_config* cfg, const void* planes_h
   const size_t plane_bytes = (size_t)dm.L * dm.b * dm.d * dm.elem;
   if (plane_bytes) FASTAR_HIP(hipMemcpyAsync(dev.planes, planes_host, plane_bytes,
                                              hipMemcpyHostToDevice, s));
+  // bf16: the re-hash of merged keys reads the hyperplanes as MFMA A operands;
+  // fragment (block pb, k-step ks), lane l holds plane 32*pb + l%32, features
+  // (l/32)*d/2 + 8*ks .. +7, so each operand load is one contiguous 1 KiB read
+  std::vector<uint16_t> frag;
+  if (dm.elem == 2 && dm.Ppad > 0) {
+    const uint16_t* ph = static_cast<const uint16_t*>(planes_host);
+    const int KS = dm.d / 16, P = dm.L * dm.b;
+    frag.assign((size_t)dm.Ppad * dm.d, 0);
+    for (int pb = 0; pb < dm.Ppad / 32; ++pb)
+      for (int ks = 0; ks < KS; ++ks)
+        for (int l = 0; l < 64; ++l) {
+          const int p = pb * 32 + (l & 31);
+          if (p >= P) continue;
+          const int f0 = (l >> 5) * (dm.d / 2) + ks * 8;
+          for (int e = 0; e < 8; ++e)
+            frag[(((size_t)pb * KS + ks) * 64 + l) * 8 + e] = ph[(size_t)p * dm.d + f0 + e];
+        }
+    FASTAR_HIP(hipMemcpyAsync(dev.planes_frag, frag.data(), frag.size() * 2,
+                              hipMemcpyHostToDevice, s));
+  }
   FASTAR_HIP(launch_finalize_state(dm, dev, s));
   FASTAR_HIP(hipStreamSynchronize(s));
   fastar_cache_s* c = new fastar_cache_s;

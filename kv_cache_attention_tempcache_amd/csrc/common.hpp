@@ -84,6 +84,8 @@ struct Dims {
 // Device pointers into one cache's workspace.
 struct CacheDev {
   void* planes;        // [L*b][d] storage dtype
+  void* planes_frag;   // bf16 caches: the hyperplanes as 32x32x16 MFMA A fragments,
+                       // [Ppad/32][d/16][64 lanes] x 16 bytes, zero past L*b
   float* k_master;     // [H][B][d]
   float* v_master;     // [H][B][d]
   void* k_mirror;      // [H][Bp][d] storage dtype

@@ -476,16 +476,15 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
       const int P = L * dm.b;
       uint32_t word = 0u;
       if (wave * 32 < P) {
-        // MFMA rows: hyperplane wave*32 + m (zero past L*b); columns: key row
-        // m; features hf*D/2 + ks*8 .. +7 in k-step ks for both
-        const int prow = wave * 32 + m;
-        const uint16_t* pp = static_cast<const uint16_t*>(c.planes) +
-                             (int64_t)(prow < P ? prow : 0) * D + hf * (D / 2);
+        // MFMA rows: hyperplane wave*32 + m (zero past L*b), read from the
+        // cache's fragment-ordered copy; columns: key row m; features
+        // hf*D/2 + ks*8 .. +7 in k-step ks for both
+        const bf16x8_t* pf =
+            static_cast<const bf16x8_t*>(c.planes_frag) + wave * (D / 16) * 64 + lane;
         f32x16_t acc = {};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(pp + ks * 8);
-          if (prow >= P) pa = bf16x8_t{};
+          const bf16x8_t pa = pf[ks * 64];
           const bf16x8_t xb = *reinterpret_cast<const bf16x8_t*>(&s_rows[m][hf * (D / 2) + ks * 8]);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, xb, acc, 0, 0, 0);
         }
