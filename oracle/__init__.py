@@ -1,4 +1,4 @@
-"""CPU oracle for the TempCache attention step and AnnCA selection.
+"""CPU oracle for the TempCache attention step, AnnCA selection and AnnSA.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the HIP library and its Python
@@ -27,3 +27,4 @@ from .tempcache import (  # noqa: F401
     to_storage,
 )
 from . import annca  # noqa: F401
+from . import annsa  # noqa: F401

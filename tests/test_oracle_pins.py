@@ -387,3 +387,92 @@ def test_annca_sparse_is_masked_dense_and_bounded():
     vmax = np.abs(cp.Vp[0]).max()
     err = np.abs(r["o_sparse"] - r["o_dense"]).max(axis=1)
     assert (err <= 2 * r["delta"] * vmax + 1e-12).all()
+
+
+# ---------------------------------------------------------------- AnnSA
+
+from oracle import annsa as oannsa  # noqa: E402
+
+
+def _annsa_case(seed, n_q=60, S=90, d=64, L=3, alphabet=7):
+    """Random slot state and codes over a small alphabet (many shared buckets)."""
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((n_q, d))
+    k = rng.standard_normal((S, d))
+    v = rng.standard_normal((S, d))
+    count = rng.integers(1, 9, size=S)
+    cq = rng.integers(0, alphabet, size=(n_q, L)).astype(np.uint32)
+    ck = rng.integers(0, alphabet, size=(S, L)).astype(np.uint32)
+    return Q, k, v, count, cq, ck
+
+
+def test_annsa_mask_bruteforce_pairs():
+    _, _, _, _, cq, ck = _annsa_case(5)
+    mask = oannsa.shared_mask(cq, ck)
+    for i in range(cq.shape[0]):
+        for s in range(ck.shape[0]):
+            assert mask[i, s] == any(cq[i, t] == ck[s, t] for t in range(cq.shape[1]))
+
+
+def test_annsa_is_masked_sdpa_with_log_count_bias():
+    """Equals torch's attention with an additive mask: ln(count) where a bucket
+    is shared, -inf elsewhere (queries with no shared bucket give zeros)."""
+    Q, k, v, count, cq, ck = _annsa_case(6)
+    O, lse, n_shared = oannsa.annsa_attend(Q, k, v, count, cq, ck)
+    pairs = np.array([[any(cq[i, t] == ck[s, t] for t in range(cq.shape[1]))
+                       for s in range(ck.shape[0])] for i in range(cq.shape[0])])
+    assert (n_shared == pairs.sum(axis=1)).all() and 0 < pairs.mean() < 1
+    bias = np.where(pairs, np.log(count.astype(np.float64))[None, :], -np.inf)
+    rows = pairs.any(axis=1)
+    ref = _sdpa(Q[rows], k, v, scale=1 / math.sqrt(Q.shape[1]), mask=bias[rows])
+    np.testing.assert_allclose(O[rows], ref, atol=1e-12)
+    assert (O[~rows] == 0).all() and np.isneginf(lse[~rows]).all()
+
+
+def test_annsa_all_shared_is_cache_attention():
+    """One common bucket: AnnSA reduces to the dense step over the cache."""
+    w = WORKLOADS["tiny"]
+    orc, _, _, Q = _run_stream(w, 4)
+    hc = orc.heads[0]
+    S = hc.n_live
+    cq = np.zeros((Q.shape[1], 2), np.uint32)
+    ck = np.zeros((S, 2), np.uint32)
+    O, lse, _ = oannsa.annsa_attend(Q[0], hc.k_hat[:S], hc.v_hat[:S], hc.count[:S], cq, ck)
+    O_ref, lse_ref = hc.attend(Q[0])
+    np.testing.assert_allclose(O, O_ref, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-12)
+
+
+def test_annsa_union_of_tables_closed_form():
+    """Slots sharing a bucket in different tables are both attended; with equal
+    keys the output is their count-weighted value mean, the rest is ignored."""
+    d = 32
+    rng = np.random.default_rng(8)
+    key = rng.standard_normal(d)
+    k = np.stack([key, key, rng.standard_normal(d)])
+    v = np.stack([np.full(d, 1.0), np.full(d, 4.0), np.full(d, 1e6)])
+    count = np.array([3, 1, 5])
+    cq = np.array([[7, 9]], np.uint32)
+    ck = np.array([[7, 0], [1, 9], [2, 3]], np.uint32)   # table 0, table 1, none
+    O, _, n_shared = oannsa.annsa_attend(key[None], k, v, count, cq, ck)
+    assert n_shared[0] == 2
+    np.testing.assert_allclose(O[0], (3 * 1.0 + 1 * 4.0) / 4, rtol=0, atol=1e-12)
+
+
+def test_annsa_single_shared_slot_returns_its_value():
+    Q, k, v, count, _, _ = _annsa_case(9, n_q=5, S=20)
+    cq = np.arange(5, dtype=np.uint32)[:, None] + 100
+    ck = np.full((20, 1), 7, np.uint32)
+    ck[[3, 11, 4, 0, 19], 0] = cq[:, 0]          # query i shares only with one slot
+    O, lse, n_shared = oannsa.annsa_attend(Q, k, v, count, cq, ck)
+    assert (n_shared == 1).all()
+    np.testing.assert_array_equal(O, v[[3, 11, 4, 0, 19]])
+
+
+def test_annsa_slot_order_invariance():
+    Q, k, v, count, cq, ck = _annsa_case(10)
+    O, lse, _ = oannsa.annsa_attend(Q, k, v, count, cq, ck)
+    perm = np.random.default_rng(11).permutation(k.shape[0])
+    O2, lse2, _ = oannsa.annsa_attend(Q, k[perm], v[perm], count[perm], cq, ck[perm])
+    np.testing.assert_allclose(O2, O, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12)
