@@ -398,6 +398,72 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
   return ok();
 }
 
+fastar_status fastar_cache_hash_slots(fastar_cache_t c, const void* planes_dev, int32_t L,
+                                      int32_t b, uint32_t* codes_dev, int64_t codes_ld,
+                                      void* stream) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  const Dims& dm = c->dm;
+  FASTAR_REQUIRE(L >= 1 && L <= FASTAR_MAX_TABLES, "L out of range");
+  FASTAR_REQUIRE(b >= 0 && b <= FASTAR_MAX_BITS, "b out of range");
+  FASTAR_REQUIRE(planes_dev != nullptr || b == 0, "planes_dev is NULL");
+  FASTAR_REQUIRE(codes_dev != nullptr, "codes_dev is NULL");
+  FASTAR_REQUIRE(codes_ld >= dm.B, "codes_ld must be >= budget");
+  FASTAR_REQUIRE(aligned(planes_dev, 16) && aligned(codes_dev, 4), "misaligned pointer");
+  HashArgs a{};
+  a.x = c->dev.k_mirror;
+  a.sx_h = (int64_t)dm.Bp * dm.d;
+  a.sx_n = dm.d;
+  a.H = dm.H;
+  a.N = dm.B;
+  a.d = dm.d;
+  a.L = L;
+  a.b = b;
+  a.planes = planes_dev;
+  a.codes = codes_dev;
+  a.codes_ld = codes_ld;
+  a.codes_col0 = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FASTAR_HIP(dm.elem == 2 ? launch_hash_bf16(a, s) : launch_hash_f32(a, s));
+  return ok();
+}
+
+fastar_status fastar_annsa_attend(fastar_cache_t c, const void* q_dev, int64_t stride_h,
+                                  int64_t stride_n, int32_t Nq, const uint32_t* q_codes_dev,
+                                  const uint32_t* k_codes_dev, int64_t k_codes_ld, int32_t L,
+                                  float scale, void* o_dev, int64_t o_stride_h,
+                                  int64_t o_stride_n, float* lse_dev, void* stream) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  const Dims& dm = c->dm;
+  if (dm.elem != 2 || dm.d != 128)
+    return fail(FASTAR_ERR_UNSUPPORTED, "AnnSA needs a bf16 cache with head_dim 128");
+  FASTAR_REQUIRE(L >= 1 && L <= 4, "AnnSA takes 1 to 4 tables");
+  FASTAR_REQUIRE(Nq >= 0, "Nq must be >= 0");
+  if (Nq == 0) return ok();
+  FASTAR_REQUIRE(q_dev && o_dev && q_codes_dev && k_codes_dev, "NULL pointer");
+  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(o_dev, 16), "q and o must be 16-byte aligned");
+  FASTAR_REQUIRE(stride_h % 8 == 0 && stride_n % 8 == 0 && stride_n >= dm.d,
+                 "q strides must be multiples of 16 bytes");
+  FASTAR_REQUIRE(o_stride_h % 8 == 0 && o_stride_n % 8 == 0 && o_stride_n >= dm.d,
+                 "o strides must be multiples of 16 bytes");
+  FASTAR_REQUIRE(k_codes_ld >= dm.B && k_codes_ld % 4 == 0 && aligned(k_codes_dev, 16),
+                 "k_codes must be 16-byte aligned with ld >= budget, a multiple of 4");
+  FASTAR_REQUIRE(aligned(q_codes_dev, 4), "q_codes misaligned");
+  FASTAR_REQUIRE(lse_dev == nullptr || aligned(lse_dev, 4), "lse misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CacheAttendArgs ca{q_dev, stride_h, stride_n, o_dev, o_stride_h, o_stride_n, lse_dev, Nq,
+                     scale == 0.0f ? 1.0f / std::sqrt((float)dm.d) : scale};
+  ca.q_codes = q_codes_dev;
+  ca.k_codes = k_codes_dev;
+  ca.qc_ld = Nq;
+  ca.kc_ld = k_codes_ld;
+  ca.n_tables = L;
+  FASTAR_HIP(launch_annsa_bf16(dm, c->dev, ca, s));
+  return ok();
+}
+
 fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_h,
                             int64_t stride_n, int32_t Nq, float scale, void* o_dev,
                             int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream) {

@@ -187,9 +187,19 @@ struct CacheAttendArgs {
   float* lse;               // optional [H][Nq]
   int Nq;
   float scale;
+  // AnnSA only (n_tables > 0): query i attends to slot s iff their codes are
+  // equal in some table; q_codes[(h*n_tables + t)*qc_ld + i],
+  // k_codes[(h*n_tables + t)*kc_ld + s] (kc_ld a multiple of 4, base 16-byte
+  // aligned)
+  const uint32_t* q_codes;
+  const uint32_t* k_codes;
+  int64_t qc_ld, kc_ld;
+  int n_tables;
 };
 hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                                     hipStream_t s);
+hipError_t launch_annsa_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
+                             hipStream_t s);
 
 // Attention (TempCache over the live slots, or AnnCA over a per-frame subset).
 struct AttendArgs {

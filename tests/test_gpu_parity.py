@@ -340,3 +340,106 @@ def test_annca_select_and_sparse_attend_match_oracle(bits):
             assert np.abs(got[h, rows] - r["o_sparse"]).max() <= 2e-2
             assert np.abs(got_dense[h, rows] - r["o_dense"]).max() <= 2e-2
     print(f"AnnCA kept per frame: {cnt_h.tolist()} of {Np}")
+
+
+# ------------------------------------------------------------------ AnnSA
+
+from oracle import annsa as oannsa  # noqa: E402
+from synth import round_to_storage  # noqa: E402
+
+
+def _annsa_cache(overrides, frames):
+    w = WORKLOADS["dit1.3b"].with_(**overrides)
+    st = DriftStream(w)
+    planes = st.planes()
+    orc = TempCacheOracle.for_workload(w, planes)
+    Q = None
+    for _ in range(frames):
+        K, V, Q, _ = st.next_frame()
+        orc.process_frame(K, V)
+    cache = _cache_for(w, planes)
+    cache.import_state(oracle_state_for_import(orc, w.dtype))
+    return w, orc, cache, Q
+
+
+def _annsa_planes(L, b, d, seed):
+    rng = np.random.default_rng(seed)
+    return round_to_storage(rng.standard_normal((L, b, d)).astype(np.float32), "bf16")
+
+
+def _codes_dev(arr):
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint32).view(np.int32)).cuda()
+
+
+@pytest.mark.parametrize("L,b,seed", [(4, 6, 50), (4, 12, 51), (1, 4, 52), (3, 8, 53), (2, 16, 54)])
+def test_annsa_matches_oracle(L, b, seed):
+    """Same codes on both sides (the oracle's); outputs within the bf16 bound,
+    queries that share no bucket exactly zero with lse = -inf."""
+    w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=300, budget=2048, seed=seed), 5)
+    pl = _annsa_planes(L, b, w.head_dim, seed)
+    H, Nq = w.heads, Q.shape[1]
+    ld = cache.slot_codes_ld()
+    qc = np.zeros((H, L, Nq), np.uint32)
+    kc = np.full((H, L, ld), 0xFFFFFFFF, np.uint32)   # past n_live: never compared live
+    refs = []
+    for h in range(H):
+        hc = orc.heads[h]
+        S = hc.n_live
+        cq, ck = simhash(Q[h], pl)[0], simhash(hc.k_hat[:S], pl)[0]
+        qc[h], kc[h, :, :S] = cq.T, ck.T
+        refs.append(oannsa.annsa_attend(Q[h], hc.k_hat[:S], hc.v_hat[:S], hc.count[:S], cq, ck))
+    lse = torch.empty((H, Nq), dtype=torch.float32, device="cuda")
+    out = cache.annsa_attend(to_device(Q, w.dtype), _codes_dev(qc), _codes_dev(kc), lse=lse)
+    torch.cuda.synchronize()
+    got, glse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for h, (O, lse_ref, nsh) in enumerate(refs):
+        none = nsh == 0
+        err = np.abs(got[h] - O).max()
+        dens = nsh.mean() / orc.heads[h].n_live
+        print(f"annsa L={L} b={b} head {h}: S={orc.heads[h].n_live} shared/query={nsh.mean():.1f} "
+              f"({dens:.2%}) no-bucket queries={none.sum()} max-abs={err:.3e}")
+        assert err <= TOL["bf16"]
+        assert (got[h][none] == 0).all() and np.isneginf(glse[h][none]).all()
+        lerr = np.abs(glse[h][~none] - lse_ref[~none]).max() if (~none).any() else 0.0
+        assert lerr <= 1e-3 * max(1.0, np.abs(lse_ref[~none]).max() if (~none).any() else 1.0)
+
+
+def test_annsa_hash_slots_matches_oracle():
+    w, orc, cache, _ = _annsa_cache(dict(heads=2, tokens_per_frame=250, budget=1024, seed=55), 4)
+    pl = _annsa_planes(4, 16, w.head_dim, 55)
+    codes = cache.hash_slots(to_device(pl, "bf16").contiguous(), 4, 16)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy().view(np.uint32)
+    assert got.shape[2] == cache.slot_codes_ld()
+    amb = 0
+    for h in range(w.heads):
+        hc = orc.heads[h]
+        S = hc.n_live
+        nb, na = compare_codes(got[h][:, :S].T, simhash(hc.k_hat[:S], pl)[0],
+                               ambiguous_bit_mask(hc.k_hat[:S], pl))
+        assert nb == 0
+        amb += na
+    print(f"hash_slots: ambiguous differing bits={amb}")
+
+
+def test_annsa_all_shared_equals_attend():
+    """Every query shares one bucket with every slot: the dense cache attention."""
+    w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=300, budget=2048, seed=56), 4)
+    H, Nq, ld = w.heads, Q.shape[1], cache.slot_codes_ld()
+    q = to_device(Q, w.dtype)
+    dense = cache.attend(q)
+    sparse = cache.annsa_attend(q, _codes_dev(np.zeros((H, 2, Nq))), _codes_dev(np.zeros((H, 2, ld))))
+    torch.cuda.synchronize()
+    diff = (sparse.float() - dense.float()).abs().max().item()
+    print(f"annsa all-shared vs attend: max-abs {diff:.3e}")
+    assert torch.equal(sparse, dense)
+
+
+def test_annsa_nothing_shared_gives_zeros():
+    w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=100, budget=512, seed=57), 3)
+    H, Nq, ld = w.heads, Q.shape[1], cache.slot_codes_ld()
+    lse = torch.empty((H, Nq), dtype=torch.float32, device="cuda")
+    out = cache.annsa_attend(to_device(Q, w.dtype), _codes_dev(np.ones((H, 3, Nq))),
+                             _codes_dev(np.full((H, 3, ld), 2)), lse=lse)
+    torch.cuda.synchronize()
+    assert (out == 0).all() and torch.isneginf(lse).all()
