@@ -43,7 +43,8 @@ def _parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dit1.3b",
-                   choices=["dit1.3b", "dit14b", "rollout", "annca"])
+                   choices=["dit1.3b", "dit14b", "rollout", "annca", "annsa"])
+    p.add_argument("--annsa-bits", type=int, default=16, help="bits per table of the AnnSA buckets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads the CPU oracle times (0 = all for dit1.3b, 2 for dit14b)")
@@ -370,6 +371,8 @@ def main():
         return rollout(args, fa, torch)
     if args.workload == "annca":
         return annca(args, fa, torch)
+    if args.workload == "annsa":
+        return annsa(args, fa, torch)
 
     w = WORKLOADS[args.workload]
     T, F = w.tokens_per_frame, w.frames_per_chunk
@@ -543,6 +546,89 @@ def annca(args, fa, torch):
                    "kept_fraction": kept, "max_abs_sparse_vs_dense": err,
                    "dropped_dense_mass_max": dropped.max().item(),
                    "dropped_dense_mass_mean": dropped.mean().item()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def annsa(args, fa, torch):
+    """AnnSA at the 1.3B layer: after the timed chunk is merged, its 4680
+    queries attend only to the slots that share a bucket with them (4 tables
+    x --annsa-bits bits, hyperplanes of their own); the step is hashing the
+    queries, hashing and indexing the slot keys and the bucket-restricted
+    attention, timed against the dense step's attention over all live slots."""
+    from synth import WORKLOADS, make_planes
+    w = WORKLOADS["dit1.3b"]
+    base, _, (ck, cv, cq), _, _ = _build_step_caches(fa, torch, w, 0)
+    base.match_merge(ck, cv, w.tokens_per_frame, w.frames_per_chunk)
+    H, d, Nq = w.heads, w.head_dim, cq.shape[1]
+    L, b = 4, args.annsa_bits
+    pl = torch.from_numpy(make_planes(np.random.default_rng(2024), L, b, d, "bf16")).to(
+        torch.bfloat16).cuda().contiguous()
+    q_codes = torch.empty((H, L, Nq), dtype=torch.int32, device="cuda")
+    k_codes = torch.empty((H, L, w.budget), dtype=torch.int32, device="cuda")
+    o_sparse, o_dense = torch.empty_like(cq), torch.empty_like(cq)
+    fa.hash_codes(cq, pl, L, b, out=q_codes)
+    base.hash_slots(pl, L, b, out=k_codes)
+
+    def step():
+        fa.hash_codes(cq, pl, L, b, out=q_codes)
+        base.hash_slots(pl, L, b)
+        base.annsa_attend(cq, q_codes, out=o_sparse)
+
+    def kernel_only():
+        base.annsa_attend(cq, q_codes, out=o_sparse)
+
+    def dense():
+        base.attend(cq, out=o_dense)
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("step", step), ("annsa_attend", kernel_only), ("dense", dense)):
+        for _ in range(args.warmup):
+            fn()
+        ev = _events(args, 2 * args.steps, stream)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev.record(2 * i)
+            fn()
+            ev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        ms = np.array([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)])
+        ev.close()
+        res[name] = {"ms_median": float(np.median(ms)), "ms_p95": float(np.percentile(ms, 95))}
+    # how sparse the mask is: shared slots per query, queries with none, and
+    # the dense probability mass the shared slots carry (heads 0 and 1)
+    n_live = base.export_state()["n_live"]
+    shared_mean, none_frac, kept_mass = [], [], []
+    for h in range(H):
+        S = int(n_live[h])
+        qc, kc = q_codes[h], k_codes[h, :, :S]
+        m = (qc[:, :, None] == kc[:, None, :]).any(0)                  # [Nq][S]
+        shared_mean.append(m.sum(1).float().mean().item())
+        none_frac.append((m.sum(1) == 0).float().mean().item())
+        if h < 2:
+            st = base.export_state()
+            kf = torch.from_numpy((st["k_mirror"][h, :S].astype(np.uint32) << 16).view(np.float32)).cuda()
+            lc = torch.from_numpy(np.log(st["count"][h, :S].astype(np.float64))).float().cuda()
+            logits = cq[h].float() @ kf.T.contiguous() / d ** 0.5 + lc
+            kept_mass.append((torch.softmax(logits, -1) * m).sum(1).mean().item())
+    dense_flops = float(4 * Nq * n_live.astype(np.int64).sum() * d)
+    line = {
+        "metric": "query tokens/s per AnnSA attention step",
+        "value": Nq / (res["step"]["ms_median"] / 1e3), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["step"]["ms_median"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded drift-model frames; no dataset or trained weights)",
+        "config": {"workload": f"annsa: {H} heads x d={d}, {Nq} queries over the merged "
+                               f"1.3B-layer cache, {L} x {b}-bit buckets"},
+        "detail": {"step": res["step"], "annsa_attend": res["annsa_attend"], "dense_attend": res["dense"],
+                   "attend_speedup_vs_dense": res["dense"]["ms_median"] / res["annsa_attend"]["ms_median"],
+                   "step_speedup_vs_dense": res["dense"]["ms_median"] / res["step"]["ms_median"],
+                   "shared_slots_per_query": float(np.mean(shared_mean)),
+                   "shared_fraction": float(np.mean(shared_mean) / n_live.mean()),
+                   "queries_without_shared_slot": float(np.mean(none_frac)),
+                   "dense_mass_kept_mean_heads01": float(np.mean(kept_mass)),
+                   "dense_equivalent_tflops": dense_flops / (res["annsa_attend"]["ms_median"] / 1e3) / 1e12},
     }
     print(json.dumps(line), flush=True)
 

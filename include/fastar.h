@@ -177,12 +177,14 @@ fastar_status fastar_attend(fastar_cache_t cache, const void* q_dev, int64_t str
                             int64_t stride_n, int32_t Nq, float scale, void* o_dev,
                             int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream);
 
-/* SimHash codes of the cache's slot keys (the bf16 mirrors) under any
- * hyperplanes, for AnnSA (section 2C: the buckets of the cached keys).
- * planes_dev: [L][b][d] in the cfg dtype.  codes_dev: uint32, slot s of table
- * t of head h at codes_dev[(h*L + t)*codes_ld + s]; columns [0, budget) are
- * written, and only the first n_live columns of a head are meaningful.
- * codes_ld >= budget. */
+/* AnnSA set-up (section 2C: the buckets of the cached keys): SimHash codes of
+ * the cache's slot keys (its mirrors) under any hyperplanes, and a bucket
+ * index of them kept in the cache, which fastar_annsa_attend reads.  Call it
+ * after the last change of the cache (match_merge, import, reset) and before
+ * fastar_annsa_attend.  planes_dev: [L][b][d] in the cfg dtype, 1 <= L <= 4.
+ * codes_dev: optional copy of the codes, slot s of table t of head h at
+ * codes_dev[(h*L + t)*codes_ld + s] for s < budget (codes_ld >= budget); only
+ * the first n_live columns of a head are meaningful. */
 fastar_status fastar_cache_hash_slots(fastar_cache_t cache, const void* planes_dev, int32_t L,
                                       int32_t b, uint32_t* codes_dev, int64_t codes_ld,
                                       void* stream);
@@ -191,16 +193,16 @@ fastar_status fastar_cache_hash_slots(fastar_cache_t cache, const void* planes_d
  * share a bucket with the query (section 2C: each query attends only to the
  * keys of its own bucket(s); read as equal codes in at least one of L tables
  * of one LSH family).  Logits are shifted by the group size as in
- * fastar_attend.  q_codes_dev: uint32 [H][L][Nq] codes of the queries
- * (fastar_hash); k_codes_dev: the slots' codes under the same hyperplanes, as
- * written by fastar_cache_hash_slots with k_codes_ld, which must be a multiple
- * of 4 and >= budget, the base 16-byte aligned.  Requires a bf16 cache with
- * d = 128 and 1 <= L <= 4.  A query that shares no bucket gets a zero output
- * and lse = -inf.  Other arguments as fastar_attend. */
+ * fastar_attend.  q_codes_dev: uint32 [H][L][Nq] codes of the queries under
+ * the hyperplanes of the latest fastar_cache_hash_slots (fastar_hash), which
+ * must have been called with the same L after the last change of the cache
+ * (else FASTAR_ERR_INVALID_ARGUMENT).  The candidates come from the bucket
+ * index, so the work follows the number of shared (query, slot) pairs.  A
+ * query that shares no bucket gets a zero output and lse = -inf.  Other
+ * arguments as fastar_attend. */
 fastar_status fastar_annsa_attend(fastar_cache_t cache, const void* q_dev, int64_t stride_h,
                                   int64_t stride_n, int32_t Nq, const uint32_t* q_codes_dev,
-                                  const uint32_t* k_codes_dev, int64_t k_codes_ld, int32_t L,
-                                  float scale, void* o_dev, int64_t o_stride_h,
+                                  int32_t L, float scale, void* o_dev, int64_t o_stride_h,
                                   int64_t o_stride_n, float* lse_dev, void* stream);
 
 /* Totals over heads.  Synchronises `stream`. */

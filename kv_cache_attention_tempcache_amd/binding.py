@@ -78,8 +78,8 @@ _SIGS = {
                                           _VP]),
     "fastar_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _F, _VP, _I64, _I64, _VP, _VP]),
     "fastar_cache_hash_slots": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _I64, _VP]),
-    "fastar_annsa_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _VP, _VP, _I64, _I32, _F,
-                                           _VP, _I64, _I64, _VP, _VP]),
+    "fastar_annsa_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _VP, _I32, _F, _VP, _I64,
+                                           _I64, _VP, _VP]),
     "fastar_cache_stats": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(Stats)]),
     "fastar_cache_export": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(State)]),
     "fastar_cache_import": (ctypes.c_int, [_VP, ctypes.POINTER(State), _VP]),
@@ -274,41 +274,35 @@ class Cache:
                                        _ptr(lse), _stream(stream)))
         return out
 
-    def slot_codes_ld(self) -> int:
-        """Row length of the slot-code arrays of hash_slots / annsa_attend."""
-        return (self.cfg.budget + 3) // 4 * 4
-
     def hash_slots(self, planes: torch.Tensor, tables: int, bits: int,
-                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-        """Codes [H][L][slot_codes_ld()] of the slot keys under ``planes`` [L][b][d]."""
+                   out: torch.Tensor | None = None, stream=None):
+        """Hash the slot keys under ``planes`` [L][b][d] and index them for AnnSA;
+        the codes [H][L][budget] are also written to ``out`` if given."""
         _require(planes, "planes", self.torch_dtype)
         if not planes.is_contiguous() or planes.numel() != tables * bits * self.cfg.head_dim:
             raise ValueError("planes must be contiguous [L][b][d]")
-        ld = self.slot_codes_ld()
-        if out is None:
-            out = torch.empty((self.cfg.heads, tables, ld), dtype=torch.int32, device="cuda")
-        _require(out, "out", torch.int32)
-        if tuple(out.shape) != (self.cfg.heads, tables, ld) or not out.is_contiguous():
-            raise ValueError("out must be contiguous [H][L][slot_codes_ld()]")
+        ld = self.cfg.budget
+        if out is not None:
+            _require(out, "out", torch.int32)
+            if tuple(out.shape) != (self.cfg.heads, tables, ld) or not out.is_contiguous():
+                raise ValueError("out must be contiguous [H][L][budget]")
         _check(library().fastar_cache_hash_slots(self._h, _ptr(planes), tables, bits, _ptr(out),
                                                  ld, _stream(stream)))
         return out
 
-    def annsa_attend(self, q: torch.Tensor, q_codes: torch.Tensor, k_codes: torch.Tensor,
-                     scale: float = 0.0, out: torch.Tensor | None = None,
-                     lse: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-        """AnnSA: q [H][Nq][d] attends only to slots sharing a bucket (q_codes [H][L][Nq],
-        k_codes [H][L][slot_codes_ld()] from hash_slots with the same hyperplanes)."""
+    def annsa_attend(self, q: torch.Tensor, q_codes: torch.Tensor, scale: float = 0.0,
+                     out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+        """AnnSA: q [H][Nq][d] attends only to the slots that share a bucket with it;
+        q_codes [H][L][Nq] under the hyperplanes of the latest hash_slots."""
         _require(q, "q", self.torch_dtype)
         _require(q_codes, "q_codes", torch.int32)
-        _require(k_codes, "k_codes", torch.int32)
         H, Nq, d = q.shape
         if H != self.cfg.heads or d != self.cfg.head_dim:
             raise ValueError("q must be [heads][Nq][head_dim]")
         L = q_codes.shape[1]
-        if (tuple(q_codes.shape) != (H, L, Nq) or not q_codes.is_contiguous()
-                or tuple(k_codes.shape[:2]) != (H, L) or not k_codes.is_contiguous()):
-            raise ValueError("q_codes [H][L][Nq] and k_codes [H][L][ld] must be contiguous")
+        if tuple(q_codes.shape) != (H, L, Nq) or not q_codes.is_contiguous():
+            raise ValueError("q_codes must be contiguous [H][L][Nq]")
         if out is None:
             out = torch.empty((H, Nq, d), dtype=self.torch_dtype, device=q.device)
         _require(out, "out", self.torch_dtype)
@@ -317,9 +311,9 @@ class Cache:
             if tuple(lse.shape) != (H, Nq) or not lse.is_contiguous():
                 raise ValueError("lse must be contiguous [H][Nq]")
         _check(library().fastar_annsa_attend(self._h, _ptr(q), q.stride(0), q.stride(1), Nq,
-                                             _ptr(q_codes), _ptr(k_codes), k_codes.shape[2], L,
-                                             float(scale), _ptr(out), out.stride(0), out.stride(1),
-                                             _ptr(lse), _stream(stream)))
+                                             _ptr(q_codes), L, float(scale), _ptr(out),
+                                             out.stride(0), out.stride(1), _ptr(lse),
+                                             _stream(stream)))
         return out
 
     def stats(self, stream=None) -> dict:

@@ -24,6 +24,11 @@ struct fastar_cache_s {
   void* ws;
   size_t ws_bytes;
   int device;
+  // every change of the slot state bumps `version`; the AnnSA index is valid
+  // for the version it was built at, with annsa_L tables
+  uint64_t version = 0;
+  uint64_t annsa_version = ~0ull;
+  int annsa_L = 0;
 };
 
 namespace {
@@ -89,7 +94,7 @@ enum Region {
   kPlanes, kPlanesFrag, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
   kNLive, kEvicted, kCounters, kOwner, kGsize, kFrame, kStateEnd = kFrame,
   kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupSlot, kItems,
-  kPlan, kNumRegions
+  kPlan, kAnnsaCodes, kAnnsaOff, kAnnsaEnt, kNumRegions
 };
 
 fastar_status check_device_gfx950(int* device) {
@@ -159,6 +164,9 @@ Layout make_layout(const Dims& dm) {
   sizes[kGroupSlot] = H * B * 4;
   sizes[kItems] = H * B * 16;
   sizes[kPlan] = H * kPlanStride * 4;
+  sizes[kAnnsaCodes] = H * 4 * B * 4;
+  sizes[kAnnsaOff] = H * 4 * ((size_t)dm.NB + 1) * 4;
+  sizes[kAnnsaEnt] = H * 4 * B * 8;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {
     L.off[r] = off;
@@ -199,6 +207,9 @@ CacheDev carve(void* base, const Dims& dm) {
   c.group_slot = reinterpret_cast<int32_t*>(b + L.off[kGroupSlot]);
   c.items = reinterpret_cast<int4*>(b + L.off[kItems]);
   c.plan = reinterpret_cast<int32_t*>(b + L.off[kPlan]);
+  c.annsa_codes = reinterpret_cast<uint32_t*>(b + L.off[kAnnsaCodes]);
+  c.annsa_off = reinterpret_cast<int32_t*>(b + L.off[kAnnsaOff]);
+  c.annsa_ent = reinterpret_cast<uint2*>(b + L.off[kAnnsaEnt]);
   return c;
 }
 
@@ -283,6 +294,7 @@ fastar_status fastar_cache_destroy(fastar_cache_t cache) {
 fastar_status fastar_cache_reset(fastar_cache_t c, void* stream) {
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
+  ++c->version;
   uint8_t* b = static_cast<uint8_t*>(c->ws);
   const size_t lo = c->lay.off[kKMaster], hi = c->lay.off[kStateEnd + 1];
   FASTAR_HIP(zero_bytes(b + lo, hi - lo, static_cast<hipStream_t>(stream)));
@@ -338,6 +350,7 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
                                  int32_t* slot_out_dev, uint8_t* merged_out_dev, void* stream) {
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
+  ++c->version;
   const Dims& dm = c->dm;
   const int T = tokens_per_frame, F = num_frames;
   FASTAR_REQUIRE(T >= 1 && F >= 1, "tokens_per_frame and num_frames must be >= 1");
@@ -404,12 +417,13 @@ fastar_status fastar_cache_hash_slots(fastar_cache_t c, const void* planes_dev, 
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
   const Dims& dm = c->dm;
-  FASTAR_REQUIRE(L >= 1 && L <= FASTAR_MAX_TABLES, "L out of range");
+  FASTAR_REQUIRE(L >= 1 && L <= 4, "AnnSA takes 1 to 4 tables");
   FASTAR_REQUIRE(b >= 0 && b <= FASTAR_MAX_BITS, "b out of range");
   FASTAR_REQUIRE(planes_dev != nullptr || b == 0, "planes_dev is NULL");
-  FASTAR_REQUIRE(codes_dev != nullptr, "codes_dev is NULL");
-  FASTAR_REQUIRE(codes_ld >= dm.B, "codes_ld must be >= budget");
-  FASTAR_REQUIRE(aligned(planes_dev, 16) && aligned(codes_dev, 4), "misaligned pointer");
+  FASTAR_REQUIRE(aligned(planes_dev, 16), "planes must be 16-byte aligned");
+  FASTAR_REQUIRE(codes_dev == nullptr || (codes_ld >= dm.B && aligned(codes_dev, 4)),
+                 "codes_dev misaligned or codes_ld < budget");
+  hipStream_t s = static_cast<hipStream_t>(stream);
   HashArgs a{};
   a.x = c->dev.k_mirror;
   a.sx_h = (int64_t)dm.Bp * dm.d;
@@ -420,47 +434,60 @@ fastar_status fastar_cache_hash_slots(fastar_cache_t c, const void* planes_dev, 
   a.L = L;
   a.b = b;
   a.planes = planes_dev;
-  a.codes = codes_dev;
-  a.codes_ld = codes_ld;
+  a.codes = c->dev.annsa_codes;
+  a.codes_ld = dm.B;
   a.codes_col0 = 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   FASTAR_HIP(dm.elem == 2 ? launch_hash_bf16(a, s) : launch_hash_f32(a, s));
+  // the bucket index of those codes, by the cache's own index kernel
+  Dims da = dm;
+  da.L = L;
+  CacheDev ca = c->dev;
+  ca.codes = c->dev.annsa_codes;
+  ca.idx_off = c->dev.annsa_off;
+  ca.idx_ent = c->dev.annsa_ent;
+  FASTAR_HIP(launch_index(da, ca, false, s));
+  if (codes_dev)
+    FASTAR_HIP(hipMemcpy2DAsync(codes_dev, (size_t)codes_ld * 4, c->dev.annsa_codes,
+                                (size_t)dm.B * 4, (size_t)dm.B * 4, (size_t)dm.H * L,
+                                hipMemcpyDeviceToDevice, s));
+  c->annsa_version = c->version;
+  c->annsa_L = L;
   return ok();
 }
 
 fastar_status fastar_annsa_attend(fastar_cache_t c, const void* q_dev, int64_t stride_h,
                                   int64_t stride_n, int32_t Nq, const uint32_t* q_codes_dev,
-                                  const uint32_t* k_codes_dev, int64_t k_codes_ld, int32_t L,
-                                  float scale, void* o_dev, int64_t o_stride_h,
+                                  int32_t L, float scale, void* o_dev, int64_t o_stride_h,
                                   int64_t o_stride_n, float* lse_dev, void* stream) {
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
   const Dims& dm = c->dm;
-  if (dm.elem != 2 || dm.d != 128)
-    return fail(FASTAR_ERR_UNSUPPORTED, "AnnSA needs a bf16 cache with head_dim 128");
-  FASTAR_REQUIRE(L >= 1 && L <= 4, "AnnSA takes 1 to 4 tables");
+  FASTAR_REQUIRE(c->annsa_version == c->version && c->annsa_L == L,
+                 "call fastar_cache_hash_slots with these L tables after the last change of "
+                 "the cache");
   FASTAR_REQUIRE(Nq >= 0, "Nq must be >= 0");
   if (Nq == 0) return ok();
-  FASTAR_REQUIRE(q_dev && o_dev && q_codes_dev && k_codes_dev, "NULL pointer");
+  FASTAR_REQUIRE(q_dev && o_dev && q_codes_dev, "NULL pointer");
   FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  const int vec = dm.elem == 2 ? 8 : 4;
   FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(o_dev, 16), "q and o must be 16-byte aligned");
-  FASTAR_REQUIRE(stride_h % 8 == 0 && stride_n % 8 == 0 && stride_n >= dm.d,
+  FASTAR_REQUIRE(stride_h % vec == 0 && stride_n % vec == 0 && stride_n >= dm.d,
                  "q strides must be multiples of 16 bytes");
-  FASTAR_REQUIRE(o_stride_h % 8 == 0 && o_stride_n % 8 == 0 && o_stride_n >= dm.d,
+  FASTAR_REQUIRE(o_stride_h % vec == 0 && o_stride_n % vec == 0 && o_stride_n >= dm.d,
                  "o strides must be multiples of 16 bytes");
-  FASTAR_REQUIRE(k_codes_ld >= dm.B && k_codes_ld % 4 == 0 && aligned(k_codes_dev, 16),
-                 "k_codes must be 16-byte aligned with ld >= budget, a multiple of 4");
   FASTAR_REQUIRE(aligned(q_codes_dev, 4), "q_codes misaligned");
   FASTAR_REQUIRE(lse_dev == nullptr || aligned(lse_dev, 4), "lse misaligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  CacheAttendArgs ca{q_dev, stride_h, stride_n, o_dev, o_stride_h, o_stride_n, lse_dev, Nq,
-                     scale == 0.0f ? 1.0f / std::sqrt((float)dm.d) : scale};
-  ca.q_codes = q_codes_dev;
-  ca.k_codes = k_codes_dev;
-  ca.qc_ld = Nq;
-  ca.kc_ld = k_codes_ld;
-  ca.n_tables = L;
-  FASTAR_HIP(launch_annsa_bf16(dm, c->dev, ca, s));
+  AnnsaArgs a{q_dev, stride_h, stride_n, q_codes_dev, Nq,
+              scale == 0.0f ? 1.0f / std::sqrt((float)dm.d) : scale, o_dev, o_stride_h,
+              o_stride_n, lse_dev};
+  Dims da = dm;
+  da.L = L;
+  CacheDev ca = c->dev;
+  ca.codes = c->dev.annsa_codes;
+  ca.idx_off = c->dev.annsa_off;
+  ca.idx_ent = c->dev.annsa_ent;
+  FASTAR_HIP(launch_annsa(da, ca, a, s));
   return ok();
 }
 
@@ -581,6 +608,7 @@ fastar_status fastar_cache_export(fastar_cache_t c, void* stream, fastar_cache_s
 fastar_status fastar_cache_import(fastar_cache_t c, const fastar_cache_state* in, void* stream) {
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
+  ++c->version;
   FASTAR_REQUIRE(in != nullptr, "in is NULL");
   FASTAR_REQUIRE(in->frame >= 0 && in->frame < INT32_MAX, "frame out of range");
   const Dims& dm = c->dm;

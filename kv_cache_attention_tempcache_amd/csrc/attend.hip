@@ -168,31 +168,20 @@ struct CCfg {
 // queries attends over rows of arbitrary [H][N][d] key and value arrays with
 // no bias: all sa.n_keys_const rows, or the first n_keys[h][g] rows of the
 // segment's gather list sa.sel, staged in LDS at the start.
-// LT > 0 (AnnSA, cache path only): query i attends only to the slots that
-// share a bucket with it in one of a.n_tables <= LT tables.  Each tile then
-// also carries its slots' codes (one 256-byte row per table beside the
-// log2-count row); a wave builds its exact query x slot mask from them before
-// the tile's QK^T and skips the tile when none of its queries shares a bucket
-// with any of its slots.
-template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET, int LT = 0>
+template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET>
 __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kernel(
     Dims dm, CacheDev c, CacheAttendArgs a, AttendArgs sa, int qtiles) {
   using C = CCfg<D, BN, WAVES, QB>;
   static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
-  static_assert(LT == 0 || (!SUBSET && BN == 64 && QB == 1), "masked tiles: cache path, 64 keys");
-  // side rows per tile (log2 count, then one row of codes per table), copied
-  // four 256-byte rows per 1 KiB instruction
-  constexpr int kSideInstr = LT ? (1 + LT + 3) / 4 : 0;
-  constexpr int kBufBytes = LT ? C::kKBytes + C::kVBytes + kSideInstr * 1024 : C::kBuf;
   extern __shared__ int32_t sel_lds[];  // SUBSET with a gather list
   // A ring of NBUF distinct LDS objects: tile it is read from one while the
   // copies of tiles it+1 .. it+NBUF-1 are in flight into the others.  Distinct
   // objects let the compiler see that the reads never alias the copies in
   // flight.
-  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBufBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t buf1[kBufBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t buf2[NBUF >= 3 ? kBufBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t buf3[NBUF == 4 ? kBufBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[C::kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t buf2[NBUF >= 3 ? C::kBuf : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t buf3[NBUF == 4 ? C::kBuf : 16];
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform by construction: keeps the barrier paths below scalar branches
@@ -234,10 +223,6 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
                                                 (int64_t)h * dm.Bp * D);
   const int64_t rs = SUBSET ? sa.sk_n * 2 : C::kRowBytes;  // bytes between key rows
   const float* lbg = SUBSET ? nullptr : c.lb + (int64_t)h * dm.Bp;
-  // AnnSA: tables, side copies per tile, this head's slot codes
-  const int ntab = LT ? a.n_tables : 0;
-  const int n_side = LT ? (1 + ntab + 3) / 4 : 0;
-  const uint32_t* kcg = LT ? a.k_codes + (int64_t)h * ntab * a.kc_ld : nullptr;
   const bool gather = SUBSET && sa.sel != nullptr;  // block-uniform
   if (gather) {
     const int32_t* sel = sa.sel + (int64_t)(h * sa.F + g) * sa.sel_ld;
@@ -280,32 +265,12 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + ro + voff[j]),
                                        (lds_void_t*)(buf + C::kKBytes + i * 1024), 16, 0, 0);
     }
-    if constexpr (LT > 0) {
-      // side instruction j (issued by wave WAVES-1-j): lane l copies 16 bytes
-      // of row 4j + l/16, keys 4*(l%16) .. +3 of the tile; row 0 holds the
-      // log2 counts, row 1+t the codes of table t; rows past the last table,
-      // and columns past the codes' row length, repeat the counts (their
-      // codes are never compared against a live slot's)
 #pragma unroll
-      for (int j = 0; j < kSideInstr; ++j) {
-        if (j >= n_side || wave != WAVES - 1 - j) continue;
-        const int row = 4 * j + (lane >> 4);
-        const int col = k0 + 4 * (lane & 15);
-        const void* src = (row >= 1 && row <= ntab && col < a.kc_ld)
-                              ? (const void*)(kcg + (int64_t)(row - 1) * a.kc_ld + col)
-                              : (const void*)(lbg + col);
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)src,
-                                         (lds_void_t*)(buf + C::kKBytes + C::kVBytes + j * 1024),
-                                         16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < (BN + 63) / 64; ++i) {
-        if (!SUBSET && wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
-          __builtin_amdgcn_global_load_lds((gbl_void_t*)(lbg + k0 + i * 64 + (uint32_t)lane),
-                                           (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256),
-                                           4, 0, 0);
-      }
+    for (int i = 0; i < (BN + 63) / 64; ++i) {
+      if (!SUBSET && wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(lbg + k0 + i * 64 + (uint32_t)lane),
+                                         (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256),
+                                         4, 0, 0);
     }
   };
 
@@ -321,16 +286,6 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
       bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
       if (!qok) v = bf16x8_t{};
       Qf[qb][ks] = v;
-    }
-  }
-  // AnnSA: the codes of this lane's query in every table
-  uint32_t qcode[LT > 0 ? LT : 1];
-#pragma unroll
-  for (int t = 0; t < (LT > 0 ? LT : 1); ++t) {
-    qcode[t] = 0u;
-    if (LT > 0 && t < ntab) {
-      const int qi = qt * C::BM + wave * 32 * QB + m;
-      qcode[t] = a.q_codes[(int64_t)(h * ntab + t) * a.qc_ld + (qi < nq ? qi : 0)];
     }
   }
   // Transposing V reads: within each 16-lane group, source lane j reads 4
@@ -352,8 +307,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   float mrun[QB], lrun[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    // finite with masking, so that a fully masked tile gives weights of 0
-    mrun[qb] = LT ? -1e30f : -__builtin_huge_valf();
+    mrun[qb] = -__builtin_huge_valf();
     lrun[qb] = 0.0f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) O[db][qb] = f32x16_t{};
@@ -362,7 +316,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   // Copies this wave issues per tile: K and V chunks, plus the bias row for
   // the last wave(s).
   constexpr int kCopies = 2 * C::kKInstr / WAVES;
-  const bool lb_wave = LT ? wave >= WAVES - n_side : !SUBSET && wave >= WAVES - (BN + 63) / 64;
+  const bool lb_wave = !SUBSET && wave >= WAVES - (BN + 63) / 64;
 
   // Wait until at most n tiles' copies issued by this wave are in flight
   // (every older tile has landed), finish this wave's LDS reads, then meet
@@ -387,134 +341,100 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     const float* lb_lds = reinterpret_cast<const float*>(cur + C::kKBytes + C::kVBytes);
     if (it + NBUF - 1 < nt) issue((it + NBUF - 1) * BN, nxt);
 
-    // AnnSA: the bias of key kb*32 + 8*jg + 4*hf + r (accumulator register
-    // 4*jg + r) becomes -inf unless this lane's query shares a bucket with it;
-    // a wave whose queries share none with the tile skips it
-    float4 lbm[BN / 32][4];
-    bool active = true;
-    if constexpr (LT > 0) {
-      const uint32_t* code_lds = reinterpret_cast<const uint32_t*>(cur + C::kKBytes + C::kVBytes) + BN;
-      bool any = false;
+    f32x16_t S[BN / 32][QB];
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+    for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          bool o0 = false, o1 = false, o2 = false, o3 = false;
+      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16_t{};
 #pragma unroll
-          for (int t = 0; t < LT; ++t) {
-            if (t >= ntab) break;
-            const uint4 kc = *reinterpret_cast<const uint4*>(code_lds + t * BN + kb * 32 + 8 * jg + 4 * hf);
-            o0 |= kc.x == qcode[t];
-            o1 |= kc.y == qcode[t];
-            o2 |= kc.z == qcode[t];
-            o3 |= kc.w == qcode[t];
-          }
-          const float4 b = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
-          const float ninf = -__builtin_huge_valf();
-          lbm[kb][jg] = make_float4(o0 ? b.x : ninf, o1 ? b.y : ninf, o2 ? b.z : ninf, o3 ? b.w : ninf);
-          any |= o0 | o1 | o2 | o3;
-        }
-      active = __ballot(any) != 0;  // wave-uniform
-    }
-    if (active) {
-
-      f32x16_t S[BN / 32][QB];
-  #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-  #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16_t{};
-  #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-  #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-          const int row = kb * 32 + m;
-          const int chunk = hf * (D / 16) + ks;
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-              cur + row * C::kRowBytes + ((chunk ^ C::kswz(row)) << 4));
-  #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[qb][ks], S[kb][qb], 0, 0, 0);
-        }
-      }
-      float4 lbr[BN / 32][4];
-  #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-  #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          if constexpr (SUBSET) {  // no bias; keys past the kept count are masked
-            const int k = it * BN + kb * 32 + 8 * jg + 4 * hf;
-            const float ninf = -__builtin_huge_valf();
-            lbr[kb][jg] = make_float4(k < nkeys ? 0.0f : ninf, k + 1 < nkeys ? 0.0f : ninf,
-                                      k + 2 < nkeys ? 0.0f : ninf, k + 3 < nkeys ? 0.0f : ninf);
-          } else if constexpr (LT > 0) {
-            lbr[kb][jg] = lbm[kb][jg];
-          } else {
-            lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
-          }
-        }
-  #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -__builtin_huge_valf();
-  #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-  #pragma unroll
-          for (int jg = 0; jg < 4; ++jg) {
-            const float bb[4] = {lbr[kb][jg].x, lbr[kb][jg].y, lbr[kb][jg].z, lbr[kb][jg].w};
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float t = __builtin_fmaf(S[kb][qb][4 * jg + r], cscale, bb[r]);
-              S[kb][qb][4 * jg + r] = t;
-              mx = fmaxf(mx, t);
-            }
-          }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool need = mx > mrun[qb] + 8.0f;
-        if (__ballot(need)) {
-          const float mnew = need ? mx : mrun[qb];
-          const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
-          lrun[qb] *= alpha;
-  #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-  #pragma unroll
-            for (int j = 0; j < 16; ++j) O[db][qb][j] *= alpha;
-          mrun[qb] = mnew;
-        }
-      }
-  #pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
-  #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          bf16x8_t pf[QB];
-  #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-  #pragma unroll
-            for (int i = 0; i < 8; ++i)
-              pf[qb][i] = (__bf16)__builtin_amdgcn_exp2f(S[kb][qb][8 * kk + i] - mrun[qb]);
-            // row sum of the same bf16-rounded weights the MFMA multiplies
-            float ls = lrun[qb];
-  #pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-              const bf16x2_t pp = {pf[qb][i], pf[qb][i + 1]};
-              ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
-            }
-            lrun[qb] = ls;
+        const int row = kb * 32 + m;
+        const int chunk = hf * (D / 16) + ks;
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            cur + row * C::kRowBytes + ((chunk ^ C::kswz(row)) << 4));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[qb][ks], S[kb][qb], 0, 0, 0);
+      }
+    }
+    float4 lbr[BN / 32][4];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        if constexpr (SUBSET) {  // no bias; keys past the kept count are masked
+          const int k = it * BN + kb * 32 + 8 * jg + 4 * hf;
+          const float ninf = -__builtin_huge_valf();
+          lbr[kb][jg] = make_float4(k < nkeys ? 0.0f : ninf, k + 1 < nkeys ? 0.0f : ninf,
+                                    k + 2 < nkeys ? 0.0f : ninf, k + 3 < nkeys ? 0.0f : ninf);
+        } else {
+          lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
+        }
+      }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const float bb[4] = {lbr[kb][jg].x, lbr[kb][jg].y, lbr[kb][jg].z, lbr[kb][jg].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float t = __builtin_fmaf(S[kb][qb][4 * jg + r], cscale, bb[r]);
+            S[kb][qb][4 * jg + r] = t;
+            mx = fmaxf(mx, t);
           }
-          // A operand: feature db*32 + m, keys kb*32 + kk*16 + {4*hf..4*hf+3}
-          // then {8+4*hf..8+4*hf+3}, the key order of the P fragment
-          const uint8_t* vrow = vt_lds + (kb * 32 + kk * 16) * C::kRowBytes;
-  #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16_t*)(vrow + vtr[db]));
-            const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16_t*)(vrow + vtr[db] + 8 * C::kRowBytes));
-            const bf16x8_t vf = __builtin_bit_cast(
-                bf16x8_t, (v8i16_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-  #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > mrun[qb] + 8.0f;
+      if (__ballot(need)) {
+        const float mnew = need ? mx : mrun[qb];
+        const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
+        lrun[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) O[db][qb][j] *= alpha;
+        mrun[qb] = mnew;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t pf[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            pf[qb][i] = (__bf16)__builtin_amdgcn_exp2f(S[kb][qb][8 * kk + i] - mrun[qb]);
+          // row sum of the same bf16-rounded weights the MFMA multiplies
+          float ls = lrun[qb];
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            const bf16x2_t pp = {pf[qb][i], pf[qb][i + 1]};
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
           }
+          lrun[qb] = ls;
+        }
+        // A operand: feature db*32 + m, keys kb*32 + kk*16 + {4*hf..4*hf+3}
+        // then {8+4*hf..8+4*hf+3}, the key order of the P fragment
+        const uint8_t* vrow = vt_lds + (kb * 32 + kk * 16) * C::kRowBytes;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(vrow + vtr[db]));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(vrow + vtr[db] + 8 * C::kRowBytes));
+          const bf16x8_t vf = __builtin_bit_cast(
+              bf16x8_t, (v8i16_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);
         }
       }
     }
@@ -622,18 +542,6 @@ hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const Cac
   constexpr int BN = FASTAR_CACHE_BN, W = FASTAR_CACHE_WAVES, QB = FASTAR_CACHE_QB;
   if (dm.d == 128) return launch_cache_cfg<128, BN, W, QB, FASTAR_CACHE_NBUF>(dm, c, a, s);
   return launch_cache_cfg<64, 64, 4, 1, FASTAR_CACHE_NBUF>(dm, c, a, s);
-}
-
-hipError_t launch_annsa_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
-                             hipStream_t s) {
-  if (dm.d != 128 || a.n_tables < 1 || a.n_tables > 4) return hipErrorInvalidValue;
-  using C = CCfg<128, 64, 8, 1>;
-  const int qtiles = (a.Nq + C::BM - 1) / C::BM;
-  const int blocks = dm.H * qtiles;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attend_cache_kernel<128, 64, 8, 1, 4, false, 4>), dim3(blocks),
-                     dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
-  return hipGetLastError();
 }
 
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s) {

@@ -116,6 +116,10 @@ struct CacheDev {
                        // {slot, first member in group_tok, members, leader token},
                        // then inserts {slot, -1, 1, token}
   int32_t* plan;       // [H][kPlanStride]
+  // AnnSA: slot codes under the AnnSA hyperplanes and their bucket index
+  uint32_t* annsa_codes;  // [H][4][B]
+  int32_t* annsa_off;     // [H][4][NB+1]
+  uint2* annsa_ent;       // [H][4][B]
 };
 
 struct Layout {
@@ -198,6 +202,20 @@ struct CacheAttendArgs {
 };
 hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                                     hipStream_t s);
+
+// AnnSA over the cache: c.codes / c.idx_off / c.idx_ent and dm.L describe the
+// AnnSA slot codes and their bucket index (at most 4 tables).
+struct AnnsaArgs {
+  const void* q;            // query i of head h at q + h*sq_h + i*sq_n (cfg dtype)
+  int64_t sq_h, sq_n;
+  const uint32_t* q_codes;  // [H][L][Nq]
+  int Nq;
+  float scale;
+  void* o;
+  int64_t so_h, so_n;
+  float* lse;               // optional [H][Nq]
+};
+hipError_t launch_annsa(const Dims& dm, const CacheDev& c, const AnnsaArgs& a, hipStream_t s);
 hipError_t launch_annsa_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                              hipStream_t s);
 
