@@ -128,6 +128,45 @@ def test_dit13b_full_size_sampled_heads():
     print(f"dit1.3b full size: n_live={[h.n_live for h in s.orc.heads]} "
           f"attend max-abs={err:.3e} ambiguous bits={s.amb_bits} ({time.time() - t0:.1f} s)")
     assert err <= 2e-2
+    aerr = _annsa_check(s, qs, every=5)
+    print(f"dit1.3b full size AnnSA (4 x 16-bit buckets): max-abs={aerr:.3e}")
+    assert aerr <= 2e-2
+
+
+def _annsa_check(s: _Sampled, qs, every=1):
+    """AnnSA of all queries on the GPU with 4 x 16-bit buckets; the oracle on
+    every `every`-th query of the sampled heads, on the GPU's slot codes after
+    checking them against the oracle's SimHash (ambiguous bits excepted)."""
+    from oracle import annsa as oannsa
+    from synth import make_planes
+    w = s.w
+    L, b = 4, 16
+    pl = make_planes(np.random.default_rng(77), L, b, w.head_dim, w.dtype)
+    Q = np.concatenate(qs, axis=1)
+    slot_codes = torch.empty((w.heads, L, w.budget), dtype=torch.int32, device="cuda")
+    s.cache.hash_slots(to_device(pl, w.dtype).contiguous(), L, b, out=slot_codes)
+    qd = to_device(Q, w.dtype)
+    q_codes = fa.hash_codes(qd, to_device(pl, w.dtype).contiguous(), L, b)
+    out = s.cache.annsa_attend(qd, q_codes)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    kc_all = slot_codes.cpu().numpy().view(np.uint32)
+    qc_all = q_codes.cpu().numpy().view(np.uint32)
+    rows = np.arange(0, Q.shape[1], every)
+    err = 0.0
+    for j, h in enumerate(s.heads):
+        hc = s.orc.heads[j]
+        S = hc.n_live
+        ck = np.ascontiguousarray(kc_all[h][:, :S].T)
+        nb, _ = compare_codes(ck, simhash(hc.k_hat[:S], pl)[0], ambiguous_bit_mask(hc.k_hat[:S], pl))
+        assert nb == 0
+        cq = np.ascontiguousarray(qc_all[h][:, rows].T)
+        nb, _ = compare_codes(cq, simhash(Q[h][rows], pl)[0], ambiguous_bit_mask(Q[h][rows], pl))
+        assert nb == 0
+        O, _, nsh = oannsa.annsa_attend(Q[h][rows], hc.k_hat[:S], hc.v_hat[:S], hc.count[:S], cq, ck)
+        err = max(err, float(np.abs(got[h][rows] - O).max()))
+        print(f"  head {h}: shared slots per query {nsh.mean():.2f}, none for {int((nsh == 0).sum())}")
+    return err
 
 
 def test_dit14b_full_size_sampled_head():
