@@ -28,3 +28,4 @@ from .tempcache import (  # noqa: F401
 )
 from . import annca  # noqa: F401
 from . import annsa  # noqa: F401
+from . import pq  # noqa: F401

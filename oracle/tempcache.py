@@ -127,7 +127,7 @@ class FrameResult:
 class HeadCache:
     """The bounded, merged KV cache of one attention head."""
 
-    def __init__(self, head_dim, budget, tables, bits, threshold, dtype, planes):
+    def __init__(self, head_dim, budget, tables, bits, threshold, dtype, planes, subspaces=0):
         self.d = int(head_dim)
         self.B = int(budget)
         self.L = int(tables)
@@ -135,7 +135,14 @@ class HeadCache:
         self.dtype = dtype
         # The threshold as the library receives it: a binary32 number.
         self.tau = float(np.float32(threshold))
-        self.planes = np.asarray(planes, dtype=np.float64).reshape(self.L, self.b, self.d)
+        # subspaces = 0: SimHash hyperplanes [L][b][d]; M > 0: product
+        # quantization codebooks [L][M][2^(b/M)][d/M]
+        self.M = int(subspaces)
+        if self.M:
+            self.planes = np.asarray(planes, dtype=np.float64).reshape(
+                self.L, self.M, 1 << (self.b // self.M), self.d // self.M)
+        else:
+            self.planes = np.asarray(planes, dtype=np.float64).reshape(self.L, self.b, self.d)
         B, d = self.B, self.d
         self.K_m = np.zeros((B, d), dtype=np.float32)
         self.V_m = np.zeros((B, d), dtype=np.float32)
@@ -150,6 +157,13 @@ class HeadCache:
         self.frame = 0
         self.members = [[] for _ in range(B)]      # (frame, token) per slot
         self.buckets = [dict() for _ in range(self.L)]
+
+    def hash(self, x):
+        """Codes [n][L] of rows of ``x`` under this cache's LSH or quantizer."""
+        if self.M:
+            from .pq import pq_codes
+            return pq_codes(x, self.planes)[0]
+        return simhash(x, self.planes)[0]
 
     # -- index ---------------------------------------------------------------
     def _rebuild_buckets(self):
@@ -179,7 +193,10 @@ class HeadCache:
             raise CapacityError(f"{T} tokens in one frame exceed the budget {self.B}")
         proj = None
         if codes is None:
-            codes, proj = simhash(K, self.planes)
+            if self.M:
+                codes = self.hash(K)
+            else:
+                codes, proj = simhash(K, self.planes)
         codes = np.asarray(codes, dtype=np.uint32).reshape(T, self.L)
         f = self.frame
 
@@ -259,7 +276,7 @@ class HeadCache:
         # 5. re-hash merged slots from their new mirror key, rebuild buckets
         if groups:
             ms = np.array(sorted(groups), dtype=np.int64)
-            self.codes[ms] = simhash(self.k_hat[ms], self.planes)[0]
+            self.codes[ms] = self.hash(self.k_hat[ms])
         self._rebuild_buckets()
         self.tokens_seen += T
         self.frame += 1
@@ -297,14 +314,15 @@ class HeadCache:
 class TempCacheOracle:
     """Independent per-head caches for ``heads`` heads (heads never interact)."""
 
-    def __init__(self, heads, head_dim, budget, tables, bits, threshold, dtype, planes):
-        self.heads = [HeadCache(head_dim, budget, tables, bits, threshold, dtype, planes)
-                      for _ in range(heads)]
+    def __init__(self, heads, head_dim, budget, tables, bits, threshold, dtype, planes,
+                 subspaces=0):
+        self.heads = [HeadCache(head_dim, budget, tables, bits, threshold, dtype, planes,
+                                subspaces) for _ in range(heads)]
 
     @classmethod
     def for_workload(cls, w, planes, heads=None):
         return cls(w.heads if heads is None else heads, w.head_dim, w.budget, w.tables,
-                   w.bits, w.threshold, w.dtype, planes)
+                   w.bits, w.threshold, w.dtype, planes, getattr(w, "subspaces", 0))
 
     def process_frame(self, K, V, codes=None):
         """K, V: [H][T][d]; codes: optional [H][T][L].  Returns per-head results."""

@@ -13,4 +13,5 @@ from .drift import (  # noqa: F401
     ClusterPrompt,
     round_to_storage,
     make_planes,
+    make_codebooks,
 )

@@ -66,6 +66,16 @@ def make_planes(gen: np.random.Generator, tables: int, bits: int, dim: int,
     return round_to_storage(raw, dtype)
 
 
+def make_codebooks(gen: np.random.Generator, tables: int, subspaces: int, bits: int, dim: int,
+                   dtype: str) -> np.ndarray:
+    """Product-quantization codebooks [tables][subspaces][2^(bits/subspaces)]
+    [dim/subspaces], iid N(0, 1) (the distribution of the fresh keys),
+    storage-rounded."""
+    k = 1 << (bits // subspaces)
+    raw = gen.standard_normal((tables, subspaces, k, dim // subspaces), dtype=np.float32)
+    return round_to_storage(raw, dtype)
+
+
 @dataclass(frozen=True)
 class Workload:
     """Shape, drift mix and LSH settings of one synthetic TempCache workload."""
@@ -88,6 +98,7 @@ class Workload:
     sigma_pert: float = 0.05
     sigma_query: float = 0.1
     seed: int = 0
+    subspaces: int = 0       # 0: SimHash; M > 0: product quantization, M slices
 
     @property
     def chunk_tokens(self) -> int:
@@ -110,6 +121,13 @@ WORKLOADS = {
     # 240-frame streaming rollout at the 1.3B layer shape, 2% static->moving.
     "rollout": Workload("rollout", 12, 128, 1560, 3, "bf16", 0.60, 0.30, 4, 32,
                         0.95, 8192, 0, 240, moving_per_frame=31, seed=1002),
+    # The 1.3B layer with product-quantization codes: 4 tables, 4 slices of
+    # 32 features, 256 centroids each (32-bit codes); same keys as "dit1.3b".
+    "dit1.3b_pq": Workload("dit1.3b_pq", 12, 128, 1560, 3, "bf16", 0.60, 0.30, 4, 32,
+                           0.95, 8192, 21, 24, seed=1001, subspaces=4),
+    # "tiny" with product-quantization codes: 1 table, 2 slices x 16 centroids.
+    "tiny_pq": Workload("tiny_pq", 1, 64, 64, 1, "f32", 0.70, 0.20, 1, 8, 0.98,
+                        256, 4, 5, seed=1000, subspaces=2),
     # One attention layer shaped like a 14B video DiT (45x80 patches/frame).
     "dit14b": Workload("dit14b", 40, 128, 3600, 3, "bf16", 0.50, 0.35, 4, 32,
                        0.95, 16384, 21, 24, seed=1003),
@@ -137,8 +155,12 @@ class DriftStream:
         self.frame = 0
         self.prev = None
         self.moving = np.zeros(w.tokens_per_frame, dtype=bool)
-        self._planes = make_planes(self.gen["planes"], w.tables, w.bits,
-                                   w.head_dim, w.dtype)
+        if w.subspaces:
+            self._planes = make_codebooks(self.gen["planes"], w.tables, w.subspaces, w.bits,
+                                          w.head_dim, w.dtype)
+        else:
+            self._planes = make_planes(self.gen["planes"], w.tables, w.bits,
+                                       w.head_dim, w.dtype)
 
     def planes(self) -> np.ndarray:
         return self._planes.copy()

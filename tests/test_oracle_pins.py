@@ -476,3 +476,88 @@ def test_annsa_slot_order_invariance():
     O2, lse2, _ = oannsa.annsa_attend(Q, k[perm], v[perm], count[perm], cq, ck[perm])
     np.testing.assert_allclose(O2, O, atol=1e-12)
     np.testing.assert_allclose(lse2, lse, atol=1e-12)
+
+
+# ---------------------------------------------------------------- product quantization
+
+from oracle import pq as opq  # noqa: E402
+
+
+def test_pq_small_golden(golden_dir):
+    g = _load(golden_dir, "pq_small.json")
+    codes, _ = opq.pq_codes(np.array(g["inputs"]), np.array(g["codebooks"], dtype=np.float64))
+    assert codes.tolist() == g["expected_codes"]
+
+
+def test_pq_codes_match_scipy_vq():
+    """Each slice's index is scipy's nearest-centroid assignment."""
+    from scipy.cluster.vq import vq
+    rng = np.random.default_rng(21)
+    L, M, K, w = 3, 4, 16, 8
+    C = rng.standard_normal((L, M, K, w))
+    x = rng.standard_normal((200, M * w))
+    codes, _ = opq.pq_codes(x, C)
+    for t in range(L):
+        ref = np.zeros(200, dtype=np.uint64)
+        for m in range(M):
+            idx, _ = vq(x[:, m * w:(m + 1) * w], C[t, m])
+            ref |= idx.astype(np.uint64) << np.uint64(m * 4)
+        np.testing.assert_array_equal(codes[:, t], ref.astype(np.uint32))
+
+
+def test_pq_centroids_map_to_their_index_and_permute():
+    rng = np.random.default_rng(22)
+    L, M, K, w = 2, 2, 8, 4
+    C = rng.standard_normal((L, M, K, w))
+    # a row made of centroid (a, b) of table 0's slices codes as a + 8b there
+    rows = np.array([np.concatenate([C[0, 0, a], C[0, 1, b]]) for a in range(K) for b in range(K)])
+    codes, _ = opq.pq_codes(rows, C)
+    np.testing.assert_array_equal(codes[:, 0], [a + K * b for a in range(K) for b in range(K)])
+    perm = rng.permutation(K)
+    Cp = C.copy()
+    Cp[:, 0] = C[:, 0][:, perm]          # permute slice 0's centroids of every table
+    x = rng.standard_normal((100, M * w))
+    c1, _ = opq.pq_codes(x, C)
+    c2, _ = opq.pq_codes(x, Cp)
+    inv = np.argsort(perm)
+    np.testing.assert_array_equal(c2 & (K - 1), inv[c1 & (K - 1)])
+    np.testing.assert_array_equal(c2 >> 3, c1 >> 3)
+
+
+def test_pq_ties_go_to_the_lower_index():
+    C = np.zeros((1, 1, 4, 3))
+    C[0, 0, 1] = C[0, 0, 3] = [1.0, 2.0, 3.0]     # duplicate centroids
+    C[0, 0, 0] = C[0, 0, 2] = [9.0, 9.0, 9.0]
+    codes, gap = opq.pq_codes(np.array([[1.0, 2.0, 3.5]]), C)
+    assert codes[0, 0] == 1 and gap[0, 0, 0] == 0.0
+
+
+def test_lemma51_with_pq_codes():
+    """Exact copies share every PQ code, so they merge, and the merged step
+    equals dense attention over the raw tokens (Lemma 5.1) as with SimHash."""
+    w = WORKLOADS["tiny_lemma"].with_(subspaces=2, bits=8)
+    orc, Kr, Vr, Q = _run_stream(w, 5)
+    hc = orc.heads[0]
+    assert hc.M == 2 and hc.count[:hc.n_live].max() >= 4 and hc.n_live < Kr.shape[1]
+    O, _ = hc.attend(Q[0])
+    dense = _sdpa(Q[0], Kr[0], Vr[0], scale=1 / math.sqrt(w.head_dim))
+    assert np.abs(O - dense).max() < 1e-5
+
+
+def test_bucketed_match_with_pq_is_restricted_bruteforce():
+    w = WORKLOADS["tiny_pq"].with_(tables=2)
+    st = DriftStream(w)
+    hc = TempCacheOracle.for_workload(w, st.planes()).heads[0]
+    checked = 0
+    for _ in range(5):
+        K, V, _, _ = st.next_frame()
+        keys, codes = _snapshot(hc)
+        res = hc.process_frame(K[0], V[0])
+        np.testing.assert_array_equal(res.codes, opq.pq_codes(K[0], hc.planes)[0])
+        for i in range(K.shape[1]):
+            allowed = (codes == res.codes[i][None, :]).any(axis=1)
+            assert res.n_candidates[i] == allowed.sum()
+            b, _ = _bruteforce_best(K[0, i].astype(np.float64), keys, allowed)
+            assert res.best_slot[i] == b
+            checked += int(allowed.any())
+    assert checked > 50
