@@ -83,6 +83,9 @@ typedef struct {
   int32_t num_bits;      /* b: 0..FASTAR_MAX_BITS (0 = one bucket per table)    */
   float cos_threshold;   /* merge iff cosine >= this (any finite value)         */
   fastar_dtype dtype;    /* storage dtype of keys, values, queries, outputs    */
+  int32_t pq_subspaces;  /* 0: SimHash codes, planes [L][b][d]; M in {1, 2, 4,
+                          * 8 (d = 128 only)}: product-quantization codes,
+                          * codebooks [L][M][2^(b/M)][d/M], b = M x (1..8)    */
 } fastar_config;
 
 typedef struct fastar_cache_s* fastar_cache_t;
@@ -124,8 +127,9 @@ const char* fastar_last_error(void);
 fastar_status fastar_cache_workspace_bytes(const fastar_config* cfg, size_t* bytes);
 
 /* Create a cache in caller-provided device memory.
- * planes_host: the SimHash hyperplanes, [L][b][d] in cfg->dtype, copied into
- * the workspace.  workspace_dev: at least fastar_cache_workspace_bytes bytes,
+ * planes_host: the SimHash hyperplanes, [L][b][d] in cfg->dtype, or with
+ * pq_subspaces = M > 0 the product-quantization codebooks [L][M][2^(b/M)][d/M];
+ * copied into the workspace.  workspace_dev: at least fastar_cache_workspace_bytes bytes,
  * 256-byte aligned, kept alive by the caller until fastar_cache_destroy.
  * The cache starts empty (n_live = 0, frame = 0).  Returns
  * FASTAR_ERR_UNSUPPORTED if the current device is not gfx950.  On success
@@ -140,7 +144,8 @@ fastar_status fastar_cache_destroy(fastar_cache_t cache);
 /* Empty the cache (state zeroed, frame = 0) on `stream`. */
 fastar_status fastar_cache_reset(fastar_cache_t cache, void* stream);
 
-/* Device pointer of the cache's hyperplanes ([L][b][d], cfg dtype). */
+/* Device pointer of the cache's hyperplanes ([L][b][d], cfg dtype), or of its
+ * product-quantization codebooks ([L][M][2^(b/M)][d/M]) when pq_subspaces > 0. */
 fastar_status fastar_cache_planes(fastar_cache_t cache, const void** planes_dev);
 
 /* SimHash codes of H x N vectors (section 2A "Mecanismo": LSH as the ANN).
@@ -150,6 +155,19 @@ fastar_status fastar_cache_planes(fastar_cache_t cache, const void** planes_dev)
 fastar_status fastar_hash(const void* x_dev, fastar_dtype dtype, int32_t H, int32_t N, int32_t d,
                           int64_t stride_h, int64_t stride_n, const void* planes_dev, int32_t L,
                           int32_t b, uint32_t* codes_dev, void* stream);
+
+/* Product-quantization codes of H x N vectors (section 2: the nearest-
+ * neighbour search uses LSH or quantization; read as product quantization).
+ * Table t splits the d features into M equal slices; slice m takes the index
+ * of its nearest centroid (Euclidean, ties to the lowest index) among
+ * 2^(b/M) in codebooks_dev[t][m] ([L][M][2^(b/M)][d/M], same dtype as x),
+ * and the code holds slice m's index at bits [m*b/M, (m+1)*b/M).  x_dev,
+ * strides and codes_dev ([H][L][N]) as for fastar_hash.  M in {1, 2, 4, 8},
+ * d/M a multiple of 16, b = M x (1..8).  Stateless. */
+fastar_status fastar_pq_codes(const void* x_dev, fastar_dtype dtype, int32_t H, int32_t N,
+                              int32_t d, int64_t stride_h, int64_t stride_n,
+                              const void* codebooks_dev, int32_t L, int32_t M, int32_t b,
+                              uint32_t* codes_dev, void* stream);
 
 /* Match, merge, evict, insert and re-hash `num_frames` frames of new tokens
  * (section 2A: top-1 match against previous frames, merge above a threshold,

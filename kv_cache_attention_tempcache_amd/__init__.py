@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     annca_select,
     attend_subset,
     hash_codes,
+    pq_codes,
     library,
     planes_to_host,
     workspace_bytes,

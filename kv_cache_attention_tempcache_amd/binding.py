@@ -43,7 +43,7 @@ class Config(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("budget_slots", ctypes.c_int32), ("num_tables", ctypes.c_int32),
                 ("num_bits", ctypes.c_int32), ("cos_threshold", ctypes.c_float),
-                ("dtype", ctypes.c_int)]
+                ("dtype", ctypes.c_int), ("pq_subspaces", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -74,6 +74,8 @@ _SIGS = {
     "fastar_cache_planes": (ctypes.c_int, [_VP, ctypes.POINTER(_VP)]),
     "fastar_hash": (ctypes.c_int, [_VP, ctypes.c_int, _I32, _I32, _I32, _I64, _I64, _VP, _I32,
                                    _I32, _VP, _VP]),
+    "fastar_pq_codes": (ctypes.c_int, [_VP, ctypes.c_int, _I32, _I32, _I32, _I64, _I64, _VP, _I32,
+                                       _I32, _I32, _VP, _VP]),
     "fastar_match_merge": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _VP, _I32, _I32, _VP, _VP,
                                           _VP]),
     "fastar_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _F, _VP, _I64, _I64, _VP, _VP]),
@@ -167,6 +169,28 @@ def hash_codes(x: torch.Tensor, planes: torch.Tensor, tables: int, bits: int,
     return out
 
 
+def pq_codes(x: torch.Tensor, codebooks: torch.Tensor, tables: int, subspaces: int, bits: int,
+             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Product-quantization codes [H][L][N] (int32 bit patterns) of x [H][N][d]
+    under codebooks [L][M][2^(b/M)][d/M]."""
+    _require(x, "x")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _require(codebooks, "codebooks", x.dtype)
+    H, N, d = x.shape
+    if not codebooks.is_contiguous() or subspaces < 1 or bits % subspaces or \
+            codebooks.numel() != tables * (1 << (bits // subspaces)) * d:
+        raise ValueError("codebooks must be contiguous [L][M][2^(b/M)][d/M]")
+    if out is None:
+        out = torch.empty((H, tables, N), dtype=torch.int32, device=x.device)
+    _require(out, "out", torch.int32)
+    dt = BF16 if x.dtype == torch.bfloat16 else F32
+    _check(library().fastar_pq_codes(_ptr(x), dt, H, N, d, x.stride(0), x.stride(1),
+                                     _ptr(codebooks), tables, subspaces, bits, _ptr(out),
+                                     _stream(stream)))
+    return out
+
+
 @dataclass
 class CacheConfig:
     heads: int
@@ -176,10 +200,17 @@ class CacheConfig:
     bits: int
     threshold: float
     dtype: str = "bf16"
+    subspaces: int = 0   # 0: SimHash; M > 0: product quantization with M slices
 
     def c(self) -> Config:
         return Config(self.heads, self.head_dim, self.budget, self.tables, self.bits,
-                      float(self.threshold), _DTYPES[self.dtype][0])
+                      float(self.threshold), _DTYPES[self.dtype][0], self.subspaces)
+
+    def plane_elems(self) -> int:
+        """Elements of the hyperplanes [L][b][d] or PQ codebooks [L][M][2^(b/M)][d/M]."""
+        if self.subspaces:
+            return self.tables * (1 << (self.bits // self.subspaces)) * self.head_dim
+        return self.tables * self.bits * self.head_dim
 
 
 def workspace_bytes(cfg: CacheConfig) -> int:
@@ -198,8 +229,8 @@ class Cache:
         nbytes = workspace_bytes(cfg)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         host = planes_to_host(planes, cfg.dtype)
-        if host.size != cfg.tables * cfg.bits * cfg.head_dim:
-            raise ValueError("planes must have tables*bits*head_dim elements")
+        if host.size != cfg.plane_elems():
+            raise ValueError(f"planes must have {cfg.plane_elems()} elements")
         c = cfg.c()
         h = ctypes.c_void_p(0)
         _check(library().fastar_cache_create(ctypes.byref(c), host.ctypes.data,

@@ -73,22 +73,36 @@ fastar_status make_dims(const fastar_config* cfg, Dims* dm) {
   FASTAR_REQUIRE(cfg->num_bits >= 0 && cfg->num_bits <= FASTAR_MAX_BITS, "num_bits out of range");
   FASTAR_REQUIRE(std::isfinite(cfg->cos_threshold), "cos_threshold must be finite");
   FASTAR_REQUIRE(valid_dtype(cfg->dtype), "unknown dtype");
+  const int M = cfg->pq_subspaces;
+  FASTAR_REQUIRE(M == 0 || M == 1 || M == 2 || M == 4 || (M == 8 && cfg->head_dim == 128),
+                 "pq_subspaces must be 0 (SimHash) or 1, 2, 4 (8 with head_dim 128)");
+  FASTAR_REQUIRE(M == 0 || (cfg->num_bits % M == 0 && cfg->num_bits / M >= 1 &&
+                            cfg->num_bits / M <= 8),
+                 "product quantization needs num_bits = pq_subspaces x (1..8)");
   dm->H = cfg->num_heads;
   dm->d = cfg->head_dim;
   dm->B = cfg->budget_slots;
   dm->L = cfg->num_tables;
   dm->b = cfg->num_bits;
   dm->elem = elem_bytes(cfg->dtype);
+  dm->M = M;
   int nb = 6;  // at least 64 buckets
   while ((1 << nb) * kSlotsPerBucket < dm->B) ++nb;
   dm->nb_bits = nb;
   dm->NB = 1 << nb;
-  dm->Ppad = (dm->L * dm->b + 31) & ~31;
+  dm->Ppad = M ? 0 : (dm->L * dm->b + 31) & ~31;  // SimHash planes of the fused re-hash
   dm->Bp = (dm->B + kSlotPad - 1) / kSlotPad * kSlotPad;
   return FASTAR_OK;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Elements of the hyperplanes ([L][b][d]) or PQ codebooks ([L][M][2^(b/M)][d/M]).
+size_t plane_elems(const Dims& dm) {
+  if (dm.L * dm.b == 0) return (size_t)dm.d;
+  if (dm.M) return (size_t)dm.L * ((size_t)1 << (dm.b / dm.M)) * dm.d;
+  return (size_t)dm.L * dm.b * dm.d;
+}
 
 enum Region {
   kPlanes, kPlanesFrag, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
@@ -137,7 +151,7 @@ Layout make_layout(const Dims& dm) {
   Layout L{};
   const size_t H = dm.H, B = dm.B, d = dm.d, Lt = dm.L, e = dm.elem;
   size_t sizes[kNumRegions] = {};
-  sizes[kPlanes] = (size_t)(dm.L * dm.b > 0 ? dm.L * dm.b : 1) * d * e;
+  sizes[kPlanes] = plane_elems(dm) * e;
   sizes[kPlanesFrag] = e == 2 ? (size_t)dm.Ppad * d * 2 : 0;
   sizes[kKMaster] = H * B * d * 4;
   sizes[kVMaster] = H * B * d * 4;
@@ -249,7 +263,7 @@ fastar_status fastar_cache_create(const fastar_config* cfg, const void* planes_h
   hipStream_t s = static_cast<hipStream_t>(stream);
   CacheDev dev = carve(workspace_dev, dm);
   FASTAR_HIP(zero_bytes(workspace_dev, lay.off[kStateEnd + 1], s));
-  const size_t plane_bytes = (size_t)dm.L * dm.b * dm.d * dm.elem;
+  const size_t plane_bytes = dm.L * dm.b > 0 ? plane_elems(dm) * dm.elem : 0;
   if (plane_bytes) FASTAR_HIP(hipMemcpyAsync(dev.planes, planes_host, plane_bytes,
                                              hipMemcpyHostToDevice, s));
   // bf16: the re-hash of merged keys reads the hyperplanes as MFMA A operands;
@@ -344,6 +358,43 @@ fastar_status fastar_hash(const void* x_dev, fastar_dtype dtype, int32_t H, int3
   return ok();
 }
 
+fastar_status fastar_pq_codes(const void* x_dev, fastar_dtype dtype, int32_t H, int32_t N, int32_t d,
+                              int64_t stride_h, int64_t stride_n, const void* codebooks_dev,
+                              int32_t L, int32_t M, int32_t b, uint32_t* codes_dev, void* stream) {
+  FASTAR_REQUIRE(valid_dtype(dtype), "unknown dtype");
+  FASTAR_REQUIRE(H >= 0 && N >= 0, "H and N must be >= 0");
+  FASTAR_REQUIRE(d == 64 || d == 128, "d must be 64 or 128");
+  FASTAR_REQUIRE(L >= 1 && L <= FASTAR_MAX_TABLES, "L out of range");
+  FASTAR_REQUIRE(M == 1 || M == 2 || M == 4 || (M == 8 && d == 128),
+                 "M must be 1, 2, 4 (8 with d = 128)");
+  FASTAR_REQUIRE(b % M == 0 && b / M >= 1 && b / M <= 8, "b must be M x (1..8)");
+  if ((int64_t)H * N == 0) return ok();
+  FASTAR_REQUIRE(x_dev && codes_dev, "NULL pointer");
+  FASTAR_REQUIRE(codebooks_dev != nullptr, "codebooks_dev is NULL");
+  const int vec = dtype == FASTAR_BF16 ? 8 : 4;
+  FASTAR_REQUIRE(aligned(x_dev, 16) && aligned(codebooks_dev, 16) && aligned(codes_dev, 4),
+                 "x and codebooks must be 16-byte aligned");
+  FASTAR_REQUIRE(stride_h % vec == 0 && stride_n % vec == 0 && stride_n >= d,
+                 "strides must be multiples of 16 bytes and rows must not overlap");
+  HashArgs a{};
+  a.x = x_dev;
+  a.sx_h = stride_h;
+  a.sx_n = stride_n;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.L = L;
+  a.b = b;
+  a.planes = codebooks_dev;
+  a.M = M;
+  a.codes = codes_dev;
+  a.codes_ld = N;
+  a.codes_col0 = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FASTAR_HIP(dtype == FASTAR_BF16 ? launch_hash_bf16(a, s) : launch_hash_f32(a, s));
+  return ok();
+}
+
 fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void* v_dev,
                                  int64_t stride_h, int64_t stride_n, const uint32_t* codes_dev,
                                  int32_t tokens_per_frame, int32_t num_frames,
@@ -389,6 +440,7 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
         ha.L = dm.L;
         ha.b = dm.b;
         ha.planes = dev.planes;
+        ha.M = dm.M;
         ha.codes = dev.frame_codes;
         ha.codes_ld = dm.B;
         ha.codes_col0 = 0;
@@ -405,7 +457,7 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
     FASTAR_HIP(launch_plan(dm, dev, ga, s));
     FASTAR_HIP(launch_apply(dm, dev, ga, s));
     // bf16 storage: the apply kernel already refreshed the merged slots' codes
-    if (dm.elem != 2) FASTAR_HIP(launch_rehash(dm, dev, T, s));
+    if (dm.elem != 2 || dm.M > 0) FASTAR_HIP(launch_rehash(dm, dev, T, s));
     FASTAR_HIP(launch_index(dm, dev, true, s));
   }
   return ok();

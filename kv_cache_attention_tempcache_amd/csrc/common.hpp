@@ -74,6 +74,7 @@ constexpr int32_t kNoOwner = 0x7fffffff;
 
 struct Dims {
   int H, d, B, L, b;
+  int M;         // 0: SimHash codes; M > 0: product-quantization codes, M slices
   int Bp;        // B rounded up to a multiple of kSlotPad (mirror rows per head)
   int elem;      // storage bytes per element (2 or 4)
   int nb_bits;   // log2 of buckets per (head, table)
@@ -83,7 +84,7 @@ struct Dims {
 
 // Device pointers into one cache's workspace.
 struct CacheDev {
-  void* planes;        // [L*b][d] storage dtype
+  void* planes;        // SimHash: [L][b][d]; PQ: codebooks [L][M][2^(b/M)][d/M]; storage dtype
   void* planes_frag;   // bf16 caches: the hyperplanes as 32x32x16 MFMA A fragments,
                        // [Ppad/32][d/16][64 lanes] x 16 bytes, zero past L*b
   float* k_master;     // [H][B][d]
@@ -148,9 +149,12 @@ struct HashArgs {
   int64_t rows_ld;
   const int32_t* n_rows;    // per-head row count when gathering (device)
   int n_rows_stride;        // int32 stride between heads in n_rows
+  int M;                    // 0: SimHash with planes [L][b][d]; M > 0: product
+                            // quantization with codebooks [L][M][2^(b/M)][d/M]
 };
 hipError_t launch_hash_bf16(const HashArgs& a, hipStream_t s);
 hipError_t launch_hash_f32(const HashArgs& a, hipStream_t s);
+hipError_t launch_pq(const HashArgs& a, bool bf16, hipStream_t s);
 
 // One frame of matching.
 struct MatchArgs {

@@ -168,6 +168,7 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(HashArgs a, int64_t total
 }  // namespace
 
 hipError_t launch_hash_bf16(const HashArgs& a, hipStream_t s) {
+  if (a.M > 0) return launch_pq(a, true, s);
   const int tiles_per_head = (a.N + 31) / 32;
   const int total = a.H * tiles_per_head;
   const int P = a.L * a.b;
@@ -186,6 +187,7 @@ hipError_t launch_hash_bf16(const HashArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_hash_f32(const HashArgs& a, hipStream_t s) {
+  if (a.M > 0) return launch_pq(a, false, s);
   const int64_t total = (int64_t)a.H * a.N * a.L;
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;

@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
   }
 
   if constexpr (kHash) {
-    if (first < ng) {  // block-uniform: the block holds merge groups
+    if (first < ng && dm.M == 0) {  // block-uniform: SimHash codes of merge groups
       __syncthreads();
       const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
       const int m = lane & 31, hf = lane >> 5;
@@ -584,6 +584,7 @@ hipError_t launch_rehash(const Dims& dm, const CacheDev& c, int T, hipStream_t s
   h.rows_ld = dm.B;
   h.n_rows = c.plan + kPlanGroups;
   h.n_rows_stride = kPlanStride;
+  h.M = dm.M;
   return dm.elem == 2 ? launch_hash_bf16(h, s) : launch_hash_f32(h, s);
 }
 

@@ -39,16 +39,18 @@ def pq_codes(x, codebooks):
     assert 1 << bits == K and M * w == x64.shape[1]
     codes = np.zeros((n, L), dtype=np.uint64)
     gap = np.full((n, L, M), np.inf)
-    for t in range(L):
-        for m in range(M):
-            xs = x64[:, m * w:(m + 1) * w]
-            # squared Euclidean distance of every row to every centroid
-            dist = ((xs[:, None, :] - C[t, m][None, :, :]) ** 2).sum(axis=2)
-            idx = np.argmin(dist, axis=1)          # first minimum: lowest index
-            codes[:, t] |= idx.astype(np.uint64) << np.uint64(m * bits)
-            if K > 1:
-                part = np.partition(dist, 1, axis=1)
-                gap[:, t, m] = part[:, 1] - part[:, 0]
+    for r0 in range(0, n, 1024):              # rows are independent; bounded memory
+        r1 = min(n, r0 + 1024)
+        for t in range(L):
+            for m in range(M):
+                xs = x64[r0:r1, m * w:(m + 1) * w]
+                # squared Euclidean distance of every row to every centroid
+                dist = ((xs[:, None, :] - C[t, m][None, :, :]) ** 2).sum(axis=2)
+                idx = np.argmin(dist, axis=1)          # first minimum: lowest index
+                codes[r0:r1, t] |= idx.astype(np.uint64) << np.uint64(m * bits)
+                if K > 1:
+                    part = np.partition(dist, 1, axis=1)
+                    gap[r0:r1, t, m] = part[:, 1] - part[:, 0]
     return codes.astype(np.uint32), gap
 
 

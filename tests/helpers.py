@@ -55,6 +55,16 @@ def ambiguous_bit_mask(x: np.ndarray, planes: np.ndarray, tol: float = 1e-4) -> 
     return mask.astype(np.uint32)
 
 
+def code_ambiguity_mask(x: np.ndarray, planes: np.ndarray, subspaces: int) -> np.ndarray:
+    """[n][L] uint32 mask of code bits a lower precision may set differently:
+    SimHash bits with |proj| < 1e-4, or for product quantization every bit of
+    a code whose slice has two centroids at nearly the same distance."""
+    if subspaces:
+        from oracle.pq import ambiguous_codes
+        return np.where(ambiguous_codes(x, planes), np.uint32(0xFFFFFFFF), np.uint32(0))
+    return ambiguous_bit_mask(x, planes)
+
+
 def compare_codes(gpu: np.ndarray, ref: np.ndarray, amb: np.ndarray):
     """Return (#differing bits outside the ambiguity mask, #differing ambiguous bits)."""
     diff = (gpu.astype(np.uint32) ^ ref.astype(np.uint32))

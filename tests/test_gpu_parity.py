@@ -16,8 +16,9 @@ import kv_cache_attention_tempcache_amd as fa
 from oracle import TempCacheOracle, simhash
 from oracle import annca as oannca
 from synth import WORKLOADS, ClusterPrompt, DriftStream
-from tests.helpers import (ambiguous_bit_mask, compare_codes, compare_state, mirror_to_f32,
-                           oracle_codes_for_device, oracle_state_for_import, to_device)
+from tests.helpers import (ambiguous_bit_mask, code_ambiguity_mask, compare_codes, compare_state,
+                           mirror_to_f32, oracle_codes_for_device, oracle_state_for_import,
+                           to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +26,8 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
 def _cache_for(w, planes):
-    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype,
+                         w.subspaces)
     return fa.Cache(cfg, planes)
 
 
@@ -60,6 +62,35 @@ def test_hash_matches_oracle(dtype, H, N, d, L, b):
         bad += nb
         amb += na
     print(f"hash {dtype} H={H} N={N} d={d} L={L} b={b}: ambiguous differing bits={amb}")
+    assert bad == 0
+
+
+@pytest.mark.parametrize("dtype,H,N,d,L,M,b", [
+    ("bf16", 3, 200, 128, 4, 4, 32),
+    ("bf16", 2, 97, 64, 2, 2, 8),
+    ("bf16", 1, 33, 128, 1, 1, 8),
+    ("bf16", 2, 300, 128, 2, 8, 16),      # 4 centroids a slice: padded blocks
+    ("bf16", 1, 100, 128, 3, 1, 3),       # 8 centroids
+    ("bf16", 8, 4500, 128, 4, 4, 32),     # more 32-row tiles than one pass of the grid
+    ("f32", 1, 64, 64, 2, 2, 8),
+    ("f32", 2, 50, 128, 1, 4, 16),
+])
+def test_pq_codes_match_oracle(dtype, H, N, d, L, M, b):
+    from oracle.pq import pq_codes
+    from synth import make_codebooks, round_to_storage
+    rng = np.random.default_rng(300 + N)
+    x = round_to_storage(rng.standard_normal((H, N, d)).astype(np.float32), dtype)
+    cb = make_codebooks(rng, L, M, b, d, dtype)
+    codes = fa.pq_codes(to_device(x, dtype), to_device(cb, dtype).contiguous(), L, M, b)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy().view(np.uint32)
+    bad = amb = 0
+    for h in range(H):
+        ref, _ = pq_codes(x[h], cb)
+        nb, na = compare_codes(got[h].T, ref, code_ambiguity_mask(x[h], cb, M))
+        bad += nb
+        amb += na
+    print(f"pq {dtype} H={H} N={N} d={d} L={L} M={M} b={b}: ambiguous differing bits={amb}")
     assert bad == 0
 
 
@@ -105,7 +136,7 @@ def _run_frames(w, frames, check_every=True, use_gpu_hash=False):
             resync = False
             for h in range(H):
                 n = int(ost["n_live"][h])
-                mask = ambiguous_bit_mask(ost["k_hat"][h, :n], planes)
+                mask = code_ambiguity_mask(ost["k_hat"][h, :n], planes, w.subspaces)
                 nb, na = compare_codes(gst["codes"][h][:, :n].T, ost["codes"][h, :n], mask)
                 assert nb == 0, f"frame {f} head {h}: {nb} non-ambiguous code bits differ"
                 amb_total += na
@@ -128,6 +159,11 @@ def _run_frames(w, frames, check_every=True, use_gpu_hash=False):
     ("dit1.3b", dict(heads=2, tokens_per_frame=150, budget=600, tables=8, bits=16, seed=80), 5),
     # a frame as large as a budget that is not a multiple of 32 (eviction every frame)
     ("dit1.3b", dict(heads=1, tokens_per_frame=100, budget=100, seed=81), 4),
+    # product-quantization codes: fp32 (float64 distances) and bf16 (MFMA scores)
+    ("tiny_pq", {}, 5),
+    ("dit1.3b_pq", dict(heads=2, tokens_per_frame=300, budget=2048), 5),
+    ("dit1.3b_pq", dict(heads=2, tokens_per_frame=200, budget=260, subspaces=8, bits=16,
+                        seed=82), 5),                            # 4 centroids a slice, eviction
 ])
 def test_match_merge_matches_oracle_given_codes(name, overrides, frames):
     w = WORKLOADS[name].with_(**overrides)
@@ -144,9 +180,10 @@ def test_eviction_really_happens_in_the_small_budget_case():
     assert sum(h.evicted_tokens for h in orc.heads) > 0
 
 
-def test_gpu_hashing_end_to_end_matches_oracle():
+@pytest.mark.parametrize("name", ["dit1.3b", "dit1.3b_pq"])
+def test_gpu_hashing_end_to_end_matches_oracle(name):
     """Library hashes the keys itself (bf16 MFMA); decisions still match the oracle."""
-    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=256, budget=1024, seed=91)
+    w = WORKLOADS[name].with_(heads=2, tokens_per_frame=256, budget=1024, seed=91)
     _run_frames(w, 5, check_every=False, use_gpu_hash=True)
 
 
