@@ -43,11 +43,11 @@ def _parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dit1.3b",
-                   choices=["dit1.3b", "dit14b", "rollout", "annca", "annsa"])
+                   choices=["dit1.3b", "dit1.3b_pq", "dit14b", "rollout", "annca", "annsa"])
     p.add_argument("--annsa-bits", type=int, default=16, help="bits per table of the AnnSA buckets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=0,
-                   help="heads the CPU oracle times (0 = all for dit1.3b, 2 for dit14b)")
+                   help="heads the CPU oracle times (0 = all for dit1.3b, 2 for dit14b, 1 with PQ codes)")
     p.add_argument("--frames", type=int, default=240, help="rollout length")
     p.add_argument("--measure-traffic", action="store_true",
                    help="run rocprofv3 FETCH_SIZE / WRITE_SIZE passes and record them in profiles/")
@@ -136,6 +136,9 @@ def _workload_desc(w):
         "frames_per_chunk": w.frames_per_chunk, "queries_per_step": w.chunk_tokens,
         "prefill_frames": w.prefill_frames, "budget_slots": w.budget, "tables": w.tables,
         "bits": w.bits, "threshold": w.threshold, "dtype": w.dtype,
+        "codes": (f"product quantization: {w.tables} tables x {w.subspaces} slices x "
+                  f"{1 << (w.bits // w.subspaces)} centroids" if w.subspaces
+                  else f"SimHash: {w.tables} tables x {w.bits} bits"),
     }
 
 
@@ -165,6 +168,7 @@ def cpu_baseline(w, frames, planes, heads):
     for f in range(w.prefill_frames):
         K, V, _ = frames[f]
         orc.process_frame(K[hs], V[hs])
+        print(f"cpu baseline: prefill frame {f} done", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     Qs = []
     for f in range(w.prefill_frames, w.prefill_frames + w.frames_per_chunk):
@@ -229,7 +233,8 @@ def _build_step_caches(fa, torch, w, nrep):
         frames.append((K, V, Q))
     dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()  # noqa: E731
     T, F = w.tokens_per_frame, w.frames_per_chunk
-    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype,
+                         w.subspaces)
     base = fa.Cache(cfg, planes)
     for c0 in range(0, w.prefill_frames, F):
         n = min(F, w.prefill_frames - c0)
@@ -474,7 +479,7 @@ def main():
     if tr is not None:
         res["roofline"]["traffic"] = tr["attend_bytes"]
     if not args.no_cpu_baseline:
-        heads = args.cpu_heads or (w.heads if w.heads <= 12 else 2)
+        heads = args.cpu_heads or (1 if w.subspaces else w.heads if w.heads <= 12 else 2)
         res["cpu_baseline"] = cpu_baseline(w, [(K, V, Q) for K, V, Q in frames], planes, heads)
     print(json.dumps(res), flush=True)
 
@@ -641,7 +646,8 @@ def rollout(args, fa, torch):
     st = DriftStream(w)
     planes = st.planes()
     T, F = w.tokens_per_frame, w.frames_per_chunk
-    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype,
+                         w.subspaces)
     cache = fa.Cache(cfg, planes)
     dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()  # noqa: E731
     chunks = []

@@ -94,6 +94,37 @@ def test_pq_codes_match_oracle(dtype, H, N, d, L, M, b):
     assert bad == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pq_exact_ties_go_to_the_lowest_index(dtype):
+    """Rows equal to a centroid that has a duplicate: both score the same, and
+    the lower index must win (positive scores: the winner's score is |c|^2/2).
+    The pairs put the copy in the same register group, in the other half of
+    the wave, and in a later block of 32 centroids."""
+    from synth import make_codebooks
+    M, b, d = 4, 32, 128
+    w = d // M
+    rng = np.random.default_rng(77)
+    cb = make_codebooks(rng, 1, M, b, d, dtype)
+    pairs = [(1, 2), (4, 9), (6, 37), (8, 255), (12, 13), (33, 100), (40, 44), (0, 31)]
+    for a, c in pairs:
+        cb[0, :, c] = cb[0, :, a]
+    n = 3 * len(pairs)
+    x = np.zeros((1, n, d), dtype=np.float32)
+    want = np.zeros(n, dtype=np.uint64)
+    for i in range(n):
+        for m in range(M):
+            a = pairs[(i + m) % len(pairs)][0]
+            x[0, i, m * w:(m + 1) * w] = cb[0, m, a]
+            want[i] |= np.uint64(a) << np.uint64(m * (b // M))
+    codes = fa.pq_codes(to_device(x, dtype), to_device(cb, dtype).contiguous(), 1, M, b)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy().view(np.uint32)[0, 0]
+    from oracle.pq import pq_codes
+    ref, _ = pq_codes(x[0], cb)
+    assert np.array_equal(ref[:, 0], want.astype(np.uint32))
+    assert np.array_equal(got, want.astype(np.uint32))
+
+
 def test_hash_zero_bits_gives_zero_codes():
     x = torch.randn(2, 40, 128, device="cuda").to(torch.bfloat16)
     planes = torch.zeros(0, dtype=torch.bfloat16, device="cuda")
