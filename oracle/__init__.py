@@ -1,4 +1,5 @@
-"""CPU oracle for the TempCache attention step, AnnCA selection and AnnSA.
+"""CPU oracle for the TempCache attention step, AnnCA selection, AnnSA,
+product-quantization codes and the step inside a chunk's denoising loop.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the HIP library and its Python
@@ -29,3 +30,4 @@ from .tempcache import (  # noqa: F401
 from . import annca  # noqa: F401
 from . import annsa  # noqa: F401
 from . import pq  # noqa: F401
+from . import denoise  # noqa: F401

@@ -410,6 +410,51 @@ def test_annca_select_and_sparse_attend_match_oracle(bits):
     print(f"AnnCA kept per frame: {cnt_h.tolist()} of {Np}")
 
 
+def test_annca_with_pq_codes_matches_oracle():
+    """AnnCA with product-quantization buckets (4 tables x 4 slices x 16
+    centroids): GPU codes against the oracle's, then selection and sparse
+    attention given the oracle's codes."""
+    from oracle.pq import pq_codes
+    from synth import make_codebooks
+    cp = ClusterPrompt(heads=2, queries_per_frame=300, frames=3, bits=16)
+    H, F, Nf, L, M, b = 2, 3, 300, cp.tables, 4, 16
+    cb = make_codebooks(np.random.default_rng(1234), L, M, b, cp.head_dim, "bf16")
+    cb_dev = to_device(cb, "bf16").contiguous()
+    q_dev = to_device(cp.Q, "bf16")
+    kp_dev, vp_dev = to_device(cp.Kp, "bf16"), to_device(cp.Vp, "bf16")
+    qc = fa.pq_codes(q_dev, cb_dev, L, M, b)
+    pc = fa.pq_codes(kp_dev, cb_dev, L, M, b)
+    torch.cuda.synchronize()
+    oq = [pq_codes(cp.Q[h], cb)[0] for h in range(H)]
+    op = [pq_codes(cp.Kp[h], cb)[0] for h in range(H)]
+    for h in range(H):
+        for x, got, ref in ((cp.Q[h], qc[h], oq[h]), (cp.Kp[h], pc[h], op[h])):
+            nb, _ = compare_codes(got.cpu().numpy().view(np.uint32).T, ref,
+                                  code_ambiguity_mask(x, cb, M))
+            assert nb == 0
+    sel, cnt = fa.annca_select(oracle_codes_for_device(oq), oracle_codes_for_device(op), F)
+    out = fa.attend_subset(q_dev, kp_dev, vp_dev, F, sel, cnt)
+    torch.cuda.synchronize()
+    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    got = out.float().cpu().numpy()
+    kept = []
+    for h in range(H):
+        for g in range(F):
+            rows = slice(g * Nf, (g + 1) * Nf)
+            r = oannca.annca_frame(cp.Q[h, rows], cp.Kp[h], cp.Vp[h], None,
+                                   codes_q=oq[h][rows], codes_p=op[h])
+            n = int(cnt_h[h, g])
+            assert n == r["sel"].size
+            np.testing.assert_array_equal(sel_h[h, g, :n], r["sel"])
+            if n:
+                assert np.abs(got[h, rows] - r["o_sparse"]).max() <= 2e-2
+            else:
+                assert np.abs(got[h, rows]).max() == 0.0
+            kept.append(n)
+    print(f"AnnCA with PQ buckets kept per frame: {kept} of {cp.prompt_tokens}")
+    assert max(kept) > 0
+
+
 # ------------------------------------------------------------------ AnnSA
 
 from oracle import annsa as oannsa  # noqa: E402

@@ -561,3 +561,142 @@ def test_bucketed_match_with_pq_is_restricted_bruteforce():
             assert res.best_slot[i] == b
             checked += int(allowed.any())
     assert checked > 50
+
+
+# ---------------------------------------------------------------- denoising loop
+
+from oracle import denoise as odenoise  # noqa: E402
+
+
+def test_denoise_two_steps_golden(golden_dir):
+    g = _load(golden_dir, "denoise_two_steps.json")
+    orc = TempCacheOracle(1, g["head_dim"], g["budget"], g["tables"], g["bits"], g["threshold"],
+                          "f32", np.array(g["planes"], dtype=np.float64))
+    for fr in g["prefill"]:
+        orc.process_frame(np.array([fr["keys"]]), np.array([fr["values"]]))
+    steps = g["steps"]
+    Qs = [np.array([s["q"]]) for s in steps]
+    Ks = [np.array([s["k"]]) for s in steps]
+    Vs = [np.array([s["v"]]) for s in steps]
+    outs, lses, res = odenoise.denoise_chunk(orc, Qs, Ks, Vs, frames=1, scale=g["scale"])
+    for s in range(len(steps)):
+        np.testing.assert_allclose(outs[s][0], g["expected_output"][s], atol=1e-12)
+        np.testing.assert_allclose(lses[s][0], g["expected_lse"][s], atol=1e-12)
+    hc = orc.heads[0]
+    assert hc.n_live == len(g["expected_after_merge"]["count"])
+    np.testing.assert_array_equal(hc.count[:hc.n_live], g["expected_after_merge"]["count"])
+    np.testing.assert_allclose(hc.v_hat[:hc.n_live], g["expected_after_merge"]["value"], atol=1e-12)
+    assert bool(res[0][0].merged[0])
+
+
+def _history_with_duplicates(rng, d, n_distinct, T):
+    """Raw tokens whose keys repeat exactly (1 to 4 times each), the merged
+    slots Lemma 5.1 gives for them, and T fresh chunk tokens."""
+    keys = rng.standard_normal((n_distinct, d))
+    reps = rng.integers(1, 5, size=n_distinct)
+    raw_k = np.repeat(keys, reps, axis=0)
+    raw_v = rng.standard_normal((raw_k.shape[0], d))
+    owner = np.repeat(np.arange(n_distinct), reps)
+    v_hat = np.stack([raw_v[owner == i].mean(axis=0) for i in range(n_distinct)])
+    return raw_k, raw_v, keys, v_hat, reps, rng.standard_normal((T, d)), rng.standard_normal((T, d))
+
+
+def test_attend_with_chunk_lemma51_against_dense_raw_history():
+    """Merged slots plus raw chunk tokens equal torch's dense attention over the
+    uncompressed history followed by the chunk."""
+    rng = np.random.default_rng(21)
+    d = 32
+    raw_k, raw_v, k_hat, v_hat, count, Kn, Vn = _history_with_duplicates(rng, d, 40, 25)
+    Q = rng.standard_normal((17, d))
+    O, lse = odenoise.attend_with_chunk(Q, k_hat, v_hat, count, Kn, Vn)
+    ref = _sdpa(Q, np.concatenate([raw_k, Kn]), np.concatenate([raw_v, Vn]))
+    np.testing.assert_allclose(O, ref, atol=1e-12)
+    z = Q @ np.concatenate([raw_k, Kn]).T / math.sqrt(d)
+    np.testing.assert_allclose(lse, np.log(np.exp(z).sum(axis=1)), atol=1e-10)
+
+
+def test_attend_with_chunk_without_chunk_is_cache_attention():
+    w = WORKLOADS["tiny"]
+    orc, _, _, Q = _run_stream(w, 4)
+    hc = orc.heads[0]
+    S = hc.n_live
+    d = Q.shape[2]
+    O, lse = odenoise.attend_with_chunk(Q[0], hc.k_hat[:S], hc.v_hat[:S], hc.count[:S],
+                                        np.zeros((0, d)), np.zeros((0, d)))
+    O_ref, lse_ref = hc.attend(Q[0])
+    np.testing.assert_allclose(O, O_ref, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-12)
+
+
+def test_attend_with_chunk_on_empty_cache_is_sdpa():
+    rng = np.random.default_rng(22)
+    d = 16
+    Q, Kn, Vn = (rng.standard_normal((n, d)) for n in (9, 30, 30))
+    O, _ = odenoise.attend_with_chunk(Q, np.zeros((0, d)), np.zeros((0, d)), np.zeros(0), Kn, Vn)
+    np.testing.assert_allclose(O, _sdpa(Q, Kn, Vn), atol=1e-12)
+    O0, lse0 = odenoise.attend_with_chunk(Q, np.zeros((0, d)), np.zeros((0, d)), np.zeros(0),
+                                          np.zeros((0, d)), np.zeros((0, d)))
+    assert (O0 == 0).all() and np.isneginf(lse0).all()
+
+
+def test_chunk_token_equal_to_a_slot_counts_as_one_more_member():
+    """A chunk token with slot s's key and value weighs like count[s] + 1."""
+    rng = np.random.default_rng(23)
+    d, S = 24, 12
+    k = rng.standard_normal((S, d))
+    v = rng.standard_normal((S, d))
+    count = rng.integers(1, 6, size=S)
+    Q = rng.standard_normal((7, d))
+    s = 5
+    O, lse = odenoise.attend_with_chunk(Q, k, v, count, k[s:s + 1], v[s:s + 1])
+    c2 = count.copy()
+    c2[s] += 1
+    O_ref, lse_ref = odenoise.attend_with_chunk(Q, k, v, c2, np.zeros((0, d)), np.zeros((0, d)))
+    np.testing.assert_allclose(O, O_ref, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-12)
+
+
+def test_attend_with_chunk_is_order_invariant():
+    rng = np.random.default_rng(24)
+    d = 16
+    _, _, k_hat, v_hat, count, Kn, Vn = _history_with_duplicates(rng, d, 20, 33)
+    Q = rng.standard_normal((5, d))
+    O, _ = odenoise.attend_with_chunk(Q, k_hat, v_hat, count, Kn, Vn)
+    ps, pc = rng.permutation(len(count)), rng.permutation(Kn.shape[0])
+    O2, _ = odenoise.attend_with_chunk(Q, k_hat[ps], v_hat[ps], count[ps], Kn[pc], Vn[pc])
+    np.testing.assert_allclose(O, O2, atol=1e-12)
+
+
+def test_denoise_chunk_merges_only_the_final_step():
+    """The cache after the loop equals a cache that saw only the final step's
+    frames; every step attends with the cache as it was before the chunk."""
+    w = WORKLOADS["tiny"]
+    st = DriftStream(w)
+    planes = st.planes()
+    a = TempCacheOracle.for_workload(w, planes)
+    b = TempCacheOracle.for_workload(w, planes)
+    for _ in range(3):
+        K, V, _, _ = st.next_frame()
+        a.process_frame(K, V)
+        b.process_frame(K, V)
+    frames = [st.next_frame() for _ in range(2)]
+    Kc = np.concatenate([f[0] for f in frames], axis=1)
+    Vc = np.concatenate([f[1] for f in frames], axis=1)
+    Qc = np.concatenate([f[2] for f in frames], axis=1)
+    rng = np.random.default_rng(25)
+    noisy = [Kc + s * rng.standard_normal(Kc.shape) for s in (0.5, 0.25)]
+    Ks, Vs, Qs = noisy + [Kc], [Vc + 0.3, Vc - 0.1, Vc], [Qc, Qc, Qc]
+    before = [(hc.k_hat[:hc.n_live].copy(), hc.v_hat[:hc.n_live].copy(),
+               hc.count[:hc.n_live].copy()) for hc in a.heads]
+    outs, _, _ = odenoise.denoise_chunk(a, Qs, Ks, Vs, frames=2)
+    for f in range(2):
+        T = w.tokens_per_frame
+        b.process_frame(Kc[:, f * T:(f + 1) * T], Vc[:, f * T:(f + 1) * T])
+    for ha, hb in zip(a.heads, b.heads):
+        assert ha.n_live == hb.n_live
+        np.testing.assert_array_equal(ha.count[:ha.n_live], hb.count[:hb.n_live])
+        np.testing.assert_array_equal(ha.k_hat[:ha.n_live], hb.k_hat[:hb.n_live])
+    for s in range(3):
+        for h, (k, v, c) in enumerate(before):
+            O, _ = odenoise.attend_with_chunk(Qs[s][h], k, v, c, Ks[s][h], Vs[s][h])
+            np.testing.assert_array_equal(outs[s][h], O)
