@@ -195,6 +195,24 @@ fastar_status fastar_attend(fastar_cache_t cache, const void* q_dev, int64_t str
                             int64_t stride_n, int32_t Nq, float scale, void* o_dev,
                             int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream);
 
+/* Attention of one denoising step of a chunk (the problem statement: frames
+ * are streamed by an autoregressive diffusion model over a KV cache of the
+ * frames already generated; section 2A, Lemma 5.1): each of Nq queries per
+ * head attends, in one softmax, over the live slots (logit + ln count) and
+ * n_new raw tokens of the chunk being denoised (count 1, no shift).  The
+ * cache is read only; merging the chunk's final tokens is a separate
+ * fastar_match_merge.  k_new_dev, v_new_dev: (h, j, k) at
+ * k_new_dev[h*kv_stride_h + j*kv_stride_n + k] for j < n_new, cfg dtype,
+ * 16-byte aligned, strides multiples of 16 bytes; the buffers stay the
+ * caller's.  n_new = 0 is fastar_attend.  Other arguments and outputs as
+ * fastar_attend; no slots and n_new = 0 give zero outputs and lse = -inf. */
+fastar_status fastar_attend_with_chunk(fastar_cache_t cache, const void* q_dev, int64_t stride_h,
+                                       int64_t stride_n, int32_t Nq, const void* k_new_dev,
+                                       const void* v_new_dev, int64_t kv_stride_h,
+                                       int64_t kv_stride_n, int32_t n_new, float scale, void* o_dev,
+                                       int64_t o_stride_h, int64_t o_stride_n, float* lse_dev,
+                                       void* stream);
+
 /* AnnSA set-up (section 2C: the buckets of the cached keys): SimHash codes of
  * the cache's slot keys (its mirrors) under any hyperplanes, and a bucket
  * index of them kept in the cache, which fastar_annsa_attend reads.  Call it

@@ -79,6 +79,8 @@ _SIGS = {
     "fastar_match_merge": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _VP, _I32, _I32, _VP, _VP,
                                           _VP]),
     "fastar_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _F, _VP, _I64, _I64, _VP, _VP]),
+    "fastar_attend_with_chunk": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _VP, _VP, _I64, _I64,
+                                                _I32, _F, _VP, _I64, _I64, _VP, _VP]),
     "fastar_cache_hash_slots": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _I64, _VP]),
     "fastar_annsa_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _VP, _I32, _F, _VP, _I64,
                                            _I64, _VP, _VP]),
@@ -303,6 +305,33 @@ class Cache:
         _check(library().fastar_attend(self._h, _ptr(q), q.stride(0), q.stride(1), Nq,
                                        float(scale), _ptr(out), out.stride(0), out.stride(1),
                                        _ptr(lse), _stream(stream)))
+        return out
+
+    def attend_with_chunk(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                          scale: float = 0.0, out: torch.Tensor | None = None,
+                          lse: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """One denoising step: q [H][Nq][d] attends over the live slots (ln(count)
+        bias) and the chunk's raw tokens k_new, v_new [H][n_new][d] (count 1)."""
+        _require(q, "q", self.torch_dtype)
+        _require(k_new, "k_new", self.torch_dtype)
+        _require(v_new, "v_new", self.torch_dtype)
+        H, Nq, d = q.shape
+        if H != self.cfg.heads or d != self.cfg.head_dim:
+            raise ValueError("q must be [heads][Nq][head_dim]")
+        if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or \
+                k_new.dim() != 3 or k_new.shape[0] != H or k_new.shape[2] != d:
+            raise ValueError("k_new and v_new must be [heads][n_new][head_dim] with equal strides")
+        if out is None:
+            out = torch.empty((H, Nq, d), dtype=self.torch_dtype, device=q.device)
+        _require(out, "out", self.torch_dtype)
+        if lse is not None:
+            _require(lse, "lse", torch.float32)
+            if tuple(lse.shape) != (H, Nq) or not lse.is_contiguous():
+                raise ValueError("lse must be contiguous [H][Nq]")
+        _check(library().fastar_attend_with_chunk(
+            self._h, _ptr(q), q.stride(0), q.stride(1), Nq, _ptr(k_new), _ptr(v_new),
+            k_new.stride(0), k_new.stride(1), k_new.shape[1], float(scale), _ptr(out),
+            out.stride(0), out.stride(1), _ptr(lse), _stream(stream)))
         return out
 
     def hash_slots(self, planes: torch.Tensor, tables: int, bits: int,

@@ -543,13 +543,17 @@ fastar_status fastar_annsa_attend(fastar_cache_t c, const void* q_dev, int64_t s
   return ok();
 }
 
-fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_h,
-                            int64_t stride_n, int32_t Nq, float scale, void* o_dev,
-                            int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream) {
+// Attention over the live slots, optionally followed by n_new raw tokens
+// (count 1) in the same softmax.
+static fastar_status attend_impl(fastar_cache_t c, const void* q_dev, int64_t stride_h, int64_t stride_n,
+                          int32_t Nq, const void* k_new, const void* v_new, int64_t kv_stride_h,
+                          int64_t kv_stride_n, int32_t n_new, float scale, void* o_dev,
+                          int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream) {
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
   const Dims& dm = c->dm;
   FASTAR_REQUIRE(Nq >= 0, "Nq must be >= 0");
+  FASTAR_REQUIRE(n_new >= 0, "n_new must be >= 0");
   if (Nq == 0) return ok();
   FASTAR_REQUIRE(q_dev && o_dev, "q or o is NULL");
   FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
@@ -560,10 +564,24 @@ fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_
   FASTAR_REQUIRE(o_stride_h % vec == 0 && o_stride_n % vec == 0 && o_stride_n >= dm.d,
                  "o strides must be multiples of 16 bytes");
   FASTAR_REQUIRE(lse_dev == nullptr || aligned(lse_dev, 4), "lse misaligned");
+  if (n_new > 0) {
+    FASTAR_REQUIRE(k_new && v_new, "k_new or v_new is NULL");
+    FASTAR_REQUIRE(aligned(k_new, 16) && aligned(v_new, 16), "k_new and v_new must be 16-byte aligned");
+    FASTAR_REQUIRE(kv_stride_h % vec == 0 && kv_stride_n % vec == 0 && kv_stride_n >= dm.d &&
+                       kv_stride_h >= 0,
+                   "k_new / v_new strides must be multiples of 16 bytes");
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float sc = scale == 0.0f ? 1.0f / std::sqrt((float)dm.d) : scale;
   if (dm.elem == 2) {
     CacheAttendArgs ca{q_dev, stride_h, stride_n, o_dev, o_stride_h, o_stride_n, lse_dev, Nq, sc};
+    if (n_new > 0) {
+      ca.xk = k_new;
+      ca.xv = v_new;
+      ca.sx_h = kv_stride_h;
+      ca.sx_n = kv_stride_n;
+      ca.n_x = n_new;
+    }
     FASTAR_HIP(launch_attend_cache_bf16(dm, c->dev, ca, s));
     return ok();
   }
@@ -590,8 +608,32 @@ fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_
   a.Nseg = Nq;
   a.F = 1;
   a.scale = sc;
+  if (n_new > 0) {
+    a.xk = k_new;
+    a.xv = v_new;
+    a.sx_h = kv_stride_h;
+    a.sx_n = kv_stride_n;
+    a.n_x = n_new;
+  }
   FASTAR_HIP(launch_attend_f32(a, s));
   return ok();
+}
+
+fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_h,
+                            int64_t stride_n, int32_t Nq, float scale, void* o_dev,
+                            int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream) {
+  return attend_impl(c, q_dev, stride_h, stride_n, Nq, nullptr, nullptr, 0, 0, 0, scale, o_dev,
+                     o_stride_h, o_stride_n, lse_dev, stream);
+}
+
+fastar_status fastar_attend_with_chunk(fastar_cache_t c, const void* q_dev, int64_t stride_h,
+                                       int64_t stride_n, int32_t Nq, const void* k_new_dev,
+                                       const void* v_new_dev, int64_t kv_stride_h,
+                                       int64_t kv_stride_n, int32_t n_new, float scale, void* o_dev,
+                                       int64_t o_stride_h, int64_t o_stride_n, float* lse_dev,
+                                       void* stream) {
+  return attend_impl(c, q_dev, stride_h, stride_n, Nq, k_new_dev, v_new_dev, kv_stride_h,
+                     kv_stride_n, n_new, scale, o_dev, o_stride_h, o_stride_n, lse_dev, stream);
 }
 
 fastar_status fastar_cache_stats(fastar_cache_t c, void* stream, fastar_stats* out) {

@@ -60,6 +60,10 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles
   const float* vbase = static_cast<const float*>(a.v) + (int64_t)h * a.sk_h;
   const int32_t* cnt = a.count ? a.count + (int64_t)h * a.count_ld : nullptr;
   const int32_t* sel = GATHER ? a.sel + (int64_t)(h * a.F + g) * a.sel_ld : nullptr;
+  // raw tokens after the keys (count 1): key nkeys + j is row j of xk / xv
+  const int ntot = nkeys + a.n_x;
+  const float* xkb = a.n_x ? static_cast<const float*>(a.xk) + (int64_t)h * a.sx_h : nullptr;
+  const float* xvb = a.n_x ? static_cast<const float*>(a.xv) + (int64_t)h * a.sx_h : nullptr;
 
   float qv[D], o[D];
 #pragma unroll
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles
     o[e] = 0.0f;
   }
   float mrun = -__builtin_huge_valf(), l = 0.0f;
-  for (int k0 = 0; k0 < nkeys; k0 += KT) {
+  for (int k0 = 0; k0 < ntot; k0 += KT) {
     for (int idx = tid; idx < KT * D; idx += 64) {
       const int r = idx / D, e = idx % D;
       const int key = k0 + r;
@@ -77,6 +81,9 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles
         const int src = GATHER ? sel[key] : key;
         kx = kbase[(int64_t)src * a.sk_n + e];
         vx = vbase[(int64_t)src * a.sk_n + e];
+      } else if (key < ntot) {
+        kx = xkb[(int64_t)(key - nkeys) * a.sx_n + e];
+        vx = xvb[(int64_t)(key - nkeys) * a.sx_n + e];
       }
       Ks[r][e] = kx;
       Vs[r][e] = vx;
@@ -87,11 +94,13 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles
       if (key < nkeys) {
         const int src = GATHER ? sel[key] : key;
         lbv = cnt ? log2f((float)cnt[src]) : 0.0f;
+      } else if (key < ntot) {
+        lbv = 0.0f;
       }
       lbs[tid] = lbv;
     }
     __syncthreads();
-    const int nr = min(KT, nkeys - k0);
+    const int nr = min(KT, ntot - k0);
     for (int r = 0; r < nr; ++r) {
       float dot = 0.0f;
 #pragma unroll
@@ -223,6 +232,14 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
                                                 (int64_t)h * dm.Bp * D);
   const int64_t rs = SUBSET ? sa.sk_n * 2 : C::kRowBytes;  // bytes between key rows
   const float* lbg = SUBSET ? nullptr : c.lb + (int64_t)h * dm.Bp;
+  // Raw tokens (count 1, no logit shift) follow the slots: key tiles ntc ..
+  // of the loop read rows of a.xk / a.xv, rows past a.n_x read row 0 and are
+  // masked by their bias.
+  const int ntc = (nkeys + BN - 1) / BN;
+  const int nx = SUBSET ? 0 : a.n_x;
+  const uint8_t* xkg = nx ? static_cast<const uint8_t*>(a.xk) + (int64_t)h * a.sx_h * 2 : nullptr;
+  const uint8_t* xvg = nx ? static_cast<const uint8_t*>(a.xv) + (int64_t)h * a.sx_h * 2 : nullptr;
+  const int64_t xrs = SUBSET ? 0 : a.sx_n * 2;  // bytes between raw rows
   const bool gather = SUBSET && sa.sel != nullptr;  // block-uniform
   if (gather) {
     const int32_t* sel = sa.sel + (int64_t)(h * sa.F + g) * sa.sel_ld;
@@ -250,27 +267,40 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     voff[j] = (uint32_t)(rb + ((slot ^ C::vswz(row)) << 4));
   }
   auto issue = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
-    const uint8_t* kt = kg + (SUBSET ? 0 : (int64_t)k0 * C::kRowBytes);
-    const uint8_t* vt = vg + (SUBSET ? 0 : (int64_t)k0 * C::kRowBytes);
+    const bool raw = !SUBSET && k0 >= ntc * BN;  // block-uniform
+    const uint8_t* kt = kg + (SUBSET || raw ? 0 : (int64_t)k0 * C::kRowBytes);
+    const uint8_t* vt = vg + (SUBSET || raw ? 0 : (int64_t)k0 * C::kRowBytes);
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
       const int i = wave + j * WAVES;
-      int64_t ro = 0;
+      const uint8_t* ks;
+      const uint8_t* vs;
       if constexpr (SUBSET) {
         const int key = k0 + rrow[j];
-        ro = (int64_t)(key < nkeys ? (gather ? sel_lds[key] : key) : 0) * rs;
+        const int64_t ro = (int64_t)(key < nkeys ? (gather ? sel_lds[key] : key) : 0) * rs;
+        ks = kt + ro + koff[j];
+        vs = vt + ro + voff[j];
+      } else if (raw) {  // koff / voff hold the mirror row offset; swap it for the raw row's
+        const int key = k0 - ntc * BN + rrow[j];
+        const int64_t ro = (int64_t)(key < nx ? key : 0) * xrs - rrow[j] * C::kRowBytes;
+        ks = xkg + ro + koff[j];
+        vs = xvg + ro + voff[j];
+      } else {
+        ks = kt + koff[j];
+        vs = vt + voff[j];
       }
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(kt + ro + koff[j]),
-                                       (lds_void_t*)(buf + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(vt + ro + voff[j]),
-                                       (lds_void_t*)(buf + C::kKBytes + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)ks, (lds_void_t*)(buf + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)vs, (lds_void_t*)(buf + C::kKBytes + i * 1024),
+                                       16, 0, 0);
     }
+    // the bias row (also for raw tiles, whose bias is computed, so that every
+    // tile issues the same copies: any in-bounds row serves)
 #pragma unroll
     for (int i = 0; i < (BN + 63) / 64; ++i) {
       if (!SUBSET && wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(lbg + k0 + i * 64 + (uint32_t)lane),
-                                         (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256),
-                                         4, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (gbl_void_t*)(lbg + (raw ? 0 : k0) + i * 64 + (uint32_t)lane),
+            (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256), 4, 0, 0);
     }
   };
 
@@ -364,11 +394,12 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        if constexpr (SUBSET) {  // no bias; keys past the kept count are masked
-          const int k = it * BN + kb * 32 + 8 * jg + 4 * hf;
+        if (SUBSET || it >= ntc) {  // no bias; keys past the kept or raw count are masked
+          const int k = (SUBSET ? it : it - ntc) * BN + kb * 32 + 8 * jg + 4 * hf;
+          const int n = SUBSET ? nkeys : nx;
           const float ninf = -__builtin_huge_valf();
-          lbr[kb][jg] = make_float4(k < nkeys ? 0.0f : ninf, k + 1 < nkeys ? 0.0f : ninf,
-                                    k + 2 < nkeys ? 0.0f : ninf, k + 3 < nkeys ? 0.0f : ninf);
+          lbr[kb][jg] = make_float4(k < n ? 0.0f : ninf, k + 1 < n ? 0.0f : ninf,
+                                    k + 2 < n ? 0.0f : ninf, k + 3 < n ? 0.0f : ninf);
         } else {
           lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
         }
@@ -443,7 +474,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     wait_barrier(min(nt - 1, it + NBUF - 1) - (it + 1));
   };
 
-  const int nt = (nkeys + BN - 1) / BN;
+  const int nt = ntc + (nx + BN - 1) / BN;
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u)
     if (u < nt) issue(u * BN, u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : buf3);

@@ -195,14 +195,12 @@ struct CacheAttendArgs {
   float* lse;               // optional [H][Nq]
   int Nq;
   float scale;
-  // AnnSA only (n_tables > 0): query i attends to slot s iff their codes are
-  // equal in some table; q_codes[(h*n_tables + t)*qc_ld + i],
-  // k_codes[(h*n_tables + t)*kc_ld + s] (kc_ld a multiple of 4, base 16-byte
-  // aligned)
-  const uint32_t* q_codes;
-  const uint32_t* k_codes;
-  int64_t qc_ld, kc_ld;
-  int n_tables;
+  // optional raw tokens attended after the slots with count 1 (no logit
+  // shift): key j of head h at xk + h*sx_h + j*sx_n (same for xv), j < n_x
+  const void* xk;
+  const void* xv;
+  int64_t sx_h, sx_n;
+  int n_x;
 };
 hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                                     hipStream_t s);
@@ -220,8 +218,6 @@ struct AnnsaArgs {
   float* lse;               // optional [H][Nq]
 };
 hipError_t launch_annsa(const Dims& dm, const CacheDev& c, const AnnsaArgs& a, hipStream_t s);
-hipError_t launch_annsa_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
-                             hipStream_t s);
 
 // Attention (TempCache over the live slots, or AnnCA over a per-frame subset).
 struct AttendArgs {
@@ -241,6 +237,12 @@ struct AttendArgs {
   float* lse;               // optional [H][F*Nseg]
   int H, d, Nseg, F;        // F segments (frames) of Nseg queries each
   float scale;              // logit scale
+  // f32 only, with F = 1: raw tokens attended after the keys with no logit
+  // shift (count 1), as in CacheAttendArgs
+  const void* xk;
+  const void* xv;
+  int64_t sx_h, sx_n;
+  int n_x;
 };
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s);

@@ -14,4 +14,5 @@ from .drift import (  # noqa: F401
     round_to_storage,
     make_planes,
     make_codebooks,
+    denoising_steps,
 )

@@ -76,6 +76,23 @@ def make_codebooks(gen: np.random.Generator, tables: int, subspaces: int, bits: 
     return round_to_storage(raw, dtype)
 
 
+def denoising_steps(gen: np.random.Generator, x: np.ndarray, steps: int, sigma0: float,
+                    dtype: str) -> list:
+    """The tokens of a chunk at each of ``steps`` denoising steps: ``x`` plus
+    sigma_s * N(0, 1) with sigma_s falling linearly from ``sigma0`` at the
+    first step to 0 at the last, which returns ``x`` itself (the clean tokens
+    that are merged), each storage-rounded."""
+    out = []
+    for s in range(steps):
+        sig = sigma0 * (steps - 1 - s) / (steps - 1) if steps > 1 else 0.0
+        if sig == 0.0:
+            out.append(np.array(x, dtype=np.float32))
+        else:
+            out.append(round_to_storage(
+                x + np.float32(sig) * gen.standard_normal(x.shape, dtype=np.float32), dtype))
+    return out
+
+
 @dataclass(frozen=True)
 class Workload:
     """Shape, drift mix and LSH settings of one synthetic TempCache workload."""

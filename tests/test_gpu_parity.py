@@ -15,7 +15,7 @@ import torch
 import kv_cache_attention_tempcache_amd as fa
 from oracle import TempCacheOracle, simhash
 from oracle import annca as oannca
-from synth import WORKLOADS, ClusterPrompt, DriftStream
+from synth import WORKLOADS, ClusterPrompt, DriftStream, denoising_steps, round_to_storage
 from tests.helpers import (ambiguous_bit_mask, code_ambiguity_mask, compare_codes, compare_state,
                            mirror_to_f32, oracle_codes_for_device, oracle_state_for_import,
                            to_device)
@@ -337,6 +337,121 @@ def test_attend_empty_cache_gives_zeros():
     out = cache.attend(q, lse=lse)
     torch.cuda.synchronize()
     assert (out.float() == 0).all() and torch.isinf(lse).all()
+
+
+# ------------------------------------------------------------------ denoising loop
+
+from oracle import denoise as odenoise  # noqa: E402
+
+
+@pytest.mark.parametrize("name,overrides,frames,n_new", [
+    ("tiny", {}, 4, 0),
+    ("tiny", {}, 4, 1),
+    ("tiny", {}, 4, 65),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048), 5, 1),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048), 5, 64),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048), 5, 333),
+    ("dit1.3b", dict(heads=3, tokens_per_frame=131, budget=1024, head_dim=64, seed=3), 3, 200),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=250, budget=1024, seed=43), 1, 0),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=1024, seed=44), 0, 700),  # no slots
+])
+def test_attend_with_chunk_matches_oracle(name, overrides, frames, n_new):
+    w = WORKLOADS[name].with_(**overrides)
+    print(f"attend_with_chunk: {w.name} {overrides} frames={frames} n_new={n_new}", flush=True)
+    st = DriftStream(w)
+    planes = st.planes()
+    orc = TempCacheOracle.for_workload(w, planes)
+    for _ in range(frames):
+        K, V, _, _ = st.next_frame()
+        orc.process_frame(K, V)
+    H, d = w.heads, w.head_dim
+    rng = np.random.default_rng(500 + n_new)
+    Q = round_to_storage(rng.standard_normal((H, 257, d), dtype=np.float32), w.dtype)
+    # the chunk as a strided view: rows 3 .. 3+n_new of a longer buffer
+    buf_k = round_to_storage(rng.standard_normal((H, n_new + 5, d), dtype=np.float32), w.dtype)
+    buf_v = round_to_storage(rng.standard_normal((H, n_new + 5, d), dtype=np.float32), w.dtype)
+    cache = _cache_for(w, planes)
+    if frames:
+        cache.import_state(oracle_state_for_import(orc, w.dtype))
+    kd, vd = to_device(buf_k, w.dtype), to_device(buf_v, w.dtype)
+    lse = torch.empty((H, Q.shape[1]), dtype=torch.float32, device="cuda")
+    out = cache.attend_with_chunk(to_device(Q, w.dtype), kd[:, 3:3 + n_new], vd[:, 3:3 + n_new],
+                                  lse=lse)
+    torch.cuda.synchronize()
+    got, gl = out.float().cpu().numpy(), lse.cpu().numpy()
+    for h, hc in enumerate(orc.heads):
+        n = hc.n_live
+        O_ref, lse_ref = odenoise.attend_with_chunk(Q[h], hc.k_hat[:n], hc.v_hat[:n], hc.count[:n],
+                                                    buf_k[h, 3:3 + n_new], buf_v[h, 3:3 + n_new])
+        err = np.abs(got[h] - O_ref).max()
+        lerr = np.abs(gl[h] - lse_ref).max()
+        print(f"  head {h}: slots={n} max-abs={err:.3e} lse={lerr:.3e}")
+        assert err <= TOL[w.dtype]
+        assert lerr <= (1e-3 if w.dtype == "bf16" else 1e-5) * max(1.0, np.abs(lse_ref).max())
+
+
+def test_attend_with_chunk_without_tokens_is_attend():
+    """n_new = 0 runs the plain step: bit-identical outputs."""
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=300, budget=2048, seed=45)
+    st = DriftStream(w)
+    planes = st.planes()
+    cache = _cache_for(w, planes)
+    K, V, Q = st.frames(3)
+    cache.match_merge(to_device(K, w.dtype), to_device(V, w.dtype), w.tokens_per_frame, 3)
+    q = to_device(Q, w.dtype)
+    empty = torch.empty((2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    a = cache.attend(q)
+    b = cache.attend_with_chunk(q, empty, empty)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("tiny", {}),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048, seed=46)),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=200, budget=450, seed=47)),  # eviction at the merge
+])
+def test_denoising_loop_matches_oracle(name, overrides):
+    """Three denoising steps over the cache plus the noisy chunk, then the
+    clean chunk merged frame by frame: every step's output, the merge
+    decisions and the cache state against the oracle."""
+    w = WORKLOADS[name].with_(**overrides)
+    print(f"denoising loop: {w.name} {overrides}", flush=True)
+    prefill, F, S = 3, 2, 3
+    orc, cache, _, _ = _run_frames(w, prefill, check_every=False)
+    st = DriftStream(w)
+    planes = st.planes()
+    for _ in range(prefill):
+        st.next_frame()
+    Kc, Vc, Qc = st.frames(F)
+    rng = np.random.default_rng(900)
+    Ks = denoising_steps(rng, Kc, S, 0.5, w.dtype)
+    Vs = denoising_steps(rng, Vc, S, 0.5, w.dtype)
+    Qs = denoising_steps(rng, Qc, S, 0.5, w.dtype)
+    outs = [cache.attend_with_chunk(to_device(Qs[s], w.dtype), to_device(Ks[s], w.dtype),
+                                    to_device(Vs[s], w.dtype)) for s in range(S)]
+    ref_outs, _, res = odenoise.denoise_chunk(orc, Qs, Ks, Vs, frames=F)
+    torch.cuda.synchronize()
+    for s in range(S):
+        err = np.abs(outs[s].float().cpu().numpy() - ref_outs[s]).max()
+        print(f"  step {s}: max-abs={err:.3e}")
+        assert err <= TOL[w.dtype]
+    T, H = w.tokens_per_frame, w.heads
+    for f in range(F):
+        for r in res[f]:
+            assert int(r.near_tie.sum()) == 0
+        codes = oracle_codes_for_device([r.codes for r in res[f]])
+        slot_out = torch.full((H, T), -7, dtype=torch.int32, device="cuda")
+        merged_out = torch.full((H, T), 7, dtype=torch.uint8, device="cuda")
+        cache.match_merge(to_device(Kc[:, f * T:(f + 1) * T], w.dtype),
+                          to_device(Vc[:, f * T:(f + 1) * T], w.dtype), T, 1, codes=codes,
+                          slot_out=slot_out, merged_out=merged_out)
+        torch.cuda.synchronize()
+        so, mo = slot_out.cpu().numpy(), merged_out.cpu().numpy()
+        for h in range(H):
+            np.testing.assert_array_equal(mo[h].astype(bool), res[f][h].merged)
+            np.testing.assert_array_equal(so[h], res[f][h].slot)
+    compare_state(cache.export_state(), orc, w.dtype)
 
 
 def test_lemma51_on_gpu_fp32():
