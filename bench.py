@@ -43,8 +43,10 @@ def _parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dit1.3b",
-                   choices=["dit1.3b", "dit1.3b_pq", "dit14b", "rollout", "annca", "annsa"])
+                   choices=["dit1.3b", "dit1.3b_pq", "dit14b", "rollout", "annca", "annsa",
+                            "denoise"])
     p.add_argument("--annsa-bits", type=int, default=16, help="bits per table of the AnnSA buckets")
+    p.add_argument("--denoise-steps", type=int, default=4, help="denoising steps per chunk")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads the CPU oracle times (0 = all for dit1.3b, 2 for dit14b, 1 with PQ codes)")
@@ -378,6 +380,8 @@ def main():
         return annca(args, fa, torch)
     if args.workload == "annsa":
         return annsa(args, fa, torch)
+    if args.workload == "denoise":
+        return denoise(args, fa, torch)
 
     w = WORKLOADS[args.workload]
     T, F = w.tokens_per_frame, w.frames_per_chunk
@@ -634,6 +638,80 @@ def annsa(args, fa, torch):
                    "queries_without_shared_slot": float(np.mean(none_frac)),
                    "dense_mass_kept_mean_heads01": float(np.mean(kept_mass)),
                    "dense_equivalent_tflops": dense_flops / (res["annsa_attend"]["ms_median"] / 1e3) / 1e12},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def denoise(args, fa, torch):
+    """A chunk through its denoising loop at the 1.3B layer: each of
+    --denoise-steps steps attends the chunk's 4680 queries over the compressed
+    past (the cache before the chunk) plus the chunk's 4680 current tokens
+    (count 1), whose noise falls linearly to zero at the last step; then the
+    clean chunk is hashed and merged.  One step of this workload is the whole
+    chunk: S attention launches and one merge path."""
+    from synth import WORKLOADS, denoising_steps
+    w = WORKLOADS["dit1.3b"]
+    S = args.denoise_steps
+    T, F = w.tokens_per_frame, w.frames_per_chunk
+    nrep = args.warmup + args.steps
+    base, caches, (ck, cv, cq), frames, _ = _build_step_caches(fa, torch, w, nrep)
+    chunk = [np.concatenate([frames[f][i] for f in range(w.prefill_frames, len(frames))], axis=1)
+             for i in range(3)]
+    rng = np.random.default_rng(2025)
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()  # noqa: E731
+    Ks, Vs, Qs = ([dev(x) for x in denoising_steps(rng, chunk[i], S, 0.5, "bf16")] for i in range(3))
+    out = torch.empty_like(cq)
+    n_live = base.export_state()["n_live"].astype(np.int64)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    per = S + 2   # before attention 0, after each attention, after the merge
+    ev = _events(args, per * nrep, stream)
+
+    def step(i):
+        c = caches[i]
+        ev.record(per * i)
+        for s in range(S):
+            c.attend_with_chunk(Qs[s], Ks[s], Vs[s], out=out)
+            ev.record(per * i + s + 1)
+        c.match_merge(ck, cv, T, F)
+        ev.record(per * i + S + 1)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nrep):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timed = range(args.warmup, nrep)
+    att = np.array([[ev.elapsed_ms(per * i + s, per * i + s + 1) for s in range(S)] for i in timed])
+    merge = np.array([ev.elapsed_ms(per * i + S, per * i + S + 1) for i in timed])
+    ev.close()
+    Nq = cq.shape[1]
+    flops = float(4 * Nq * (n_live.sum() + w.heads * Nq) * w.head_dim)   # QK^T and PV
+    att_s = float(np.mean(att)) / 1e3
+    tflops = flops / att_s / 1e12
+    ms_chunk = elapsed * 1e3 / args.steps
+    line = {
+        "metric": "query tokens/s per denoising-step attention (compressed past + chunk)",
+        "value": S * Nq * args.steps / elapsed, "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_chunk,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded drift-model frames, Gaussian noise on the chunk's tokens; "
+                "no dataset or trained weights)",
+        "config": {"workload": f"denoise: {w.heads} heads x d={w.head_dim}, {S} denoising steps "
+                               f"of {Nq} queries over ~{int(n_live.mean())} slots per head plus "
+                               f"{Nq} chunk tokens, then the merge of the clean chunk "
+                               f"({F} frames x {T} tokens)"},
+        "roofline": {"bound": "mfma", "kernel": "attend_cache_kernel (slots + chunk tiles)",
+                     "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "detail": {"attend_ms_mean": float(np.mean(att)), "attend_ms_p95": float(np.percentile(att, 95)),
+                   "merge_path_ms_mean": float(np.mean(merge)),
+                   "chunk_ms": ms_chunk, "generated_tokens_per_s": Nq * args.steps / elapsed,
+                   "slots_per_head_mean": float(n_live.mean()), "chunk_tokens": Nq,
+                   "attend_gflop_per_step": flops / 1e9},
     }
     print(json.dumps(line), flush=True)
 

@@ -177,7 +177,7 @@ struct CCfg {
 // queries attends over rows of arbitrary [H][N][d] key and value arrays with
 // no bias: all sa.n_keys_const rows, or the first n_keys[h][g] rows of the
 // segment's gather list sa.sel, staged in LDS at the start.
-template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET>
+template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET, bool RAW>
 __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kernel(
     Dims dm, CacheDev c, CacheAttendArgs a, AttendArgs sa, int qtiles) {
   using C = CCfg<D, BN, WAVES, QB>;
@@ -232,11 +232,12 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
                                                 (int64_t)h * dm.Bp * D);
   const int64_t rs = SUBSET ? sa.sk_n * 2 : C::kRowBytes;  // bytes between key rows
   const float* lbg = SUBSET ? nullptr : c.lb + (int64_t)h * dm.Bp;
-  // Raw tokens (count 1, no logit shift) follow the slots: key tiles ntc ..
-  // of the loop read rows of a.xk / a.xv, rows past a.n_x read row 0 and are
-  // masked by their bias.
+  // RAW: raw tokens (count 1, no logit shift) follow the slots: key tiles
+  // ntc .. of the loop read rows of a.xk / a.xv, rows past a.n_x read row 0
+  // and are masked by their bias.
+  static_assert(!(RAW && SUBSET), "raw tokens follow cache slots only");
   const int ntc = (nkeys + BN - 1) / BN;
-  const int nx = SUBSET ? 0 : a.n_x;
+  const int nx = RAW ? a.n_x : 0;
   const uint8_t* xkg = nx ? static_cast<const uint8_t*>(a.xk) + (int64_t)h * a.sx_h * 2 : nullptr;
   const uint8_t* xvg = nx ? static_cast<const uint8_t*>(a.xv) + (int64_t)h * a.sx_h * 2 : nullptr;
   const int64_t xrs = SUBSET ? 0 : a.sx_n * 2;  // bytes between raw rows
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     voff[j] = (uint32_t)(rb + ((slot ^ C::vswz(row)) << 4));
   }
   auto issue = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
-    const bool raw = !SUBSET && k0 >= ntc * BN;  // block-uniform
+    const bool raw = RAW && k0 >= ntc * BN;  // block-uniform
     const uint8_t* kt = kg + (SUBSET || raw ? 0 : (int64_t)k0 * C::kRowBytes);
     const uint8_t* vt = vg + (SUBSET || raw ? 0 : (int64_t)k0 * C::kRowBytes);
 #pragma unroll
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        if (SUBSET || it >= ntc) {  // no bias; keys past the kept or raw count are masked
+        if (SUBSET || (RAW && it >= ntc)) {  // no bias; keys past the kept or raw count are masked
           const int k = (SUBSET ? it : it - ntc) * BN + kb * 32 + 8 * jg + 4 * hf;
           const int n = SUBSET ? nkeys : nx;
           const float ninf = -__builtin_huge_valf();
@@ -524,8 +525,12 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
   const int qtiles = (a.Nq + C::BM - 1) / C::BM;
   const int blocks = dm.H * qtiles;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false>), dim3(blocks),
-                     dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
+  if (a.n_x > 0)
+    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, true>), dim3(blocks),
+                       dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
+  else
+    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false>), dim3(blocks),
+                       dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
   return hipGetLastError();
 }
 
@@ -538,7 +543,7 @@ hipError_t launch_subset_cfg(const AttendArgs& a, hipStream_t s) {
   const int blocks = a.H * a.F * qtiles;
   if (blocks == 0) return hipSuccess;
   const size_t lds = a.sel ? (size_t)a.n_keys_const * 4 : 0;
-  auto kern = attend_cache_kernel<D, 64, 8, 1, NBUF, true>;
+  auto kern = attend_cache_kernel<D, 64, 8, 1, NBUF, true, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
