@@ -700,3 +700,62 @@ def test_denoise_chunk_merges_only_the_final_step():
         for h, (k, v, c) in enumerate(before):
             O, _ = odenoise.attend_with_chunk(Qs[s][h], k, v, c, Ks[s][h], Vs[s][h])
             np.testing.assert_array_equal(outs[s][h], O)
+
+
+# ---------------------------------------------------------------- K projection + hash
+
+from oracle import project as oproject  # noqa: E402
+
+
+def test_round_bf16_exact_hand_values():
+    e = 2.0 ** -8
+    cases = {
+        1.0 + e: 1.0,                       # halfway between 1 and 1 + 2^-7: to even
+        1.0 + 3 * e: 1.0 + 4 * e,           # halfway between 1 + 2^-7 and 1 + 2^-6: to even
+        1.0 + e + 2.0 ** -30: 1.0 + 2 * e,  # just above halfway
+        -(1.0 + e): -1.0,
+        3.0: 3.0, 0.0: 0.0,
+        255.5: 256.0,                       # 8 significant bits: 255 | 256, halfway to even
+        2.0 ** -100 * (1 + 2 * e): 2.0 ** -100 * (1 + 2 * e),
+    }
+    for v, want in cases.items():
+        assert oproject.round_bf16_exact(v) == want, v
+
+
+def test_round_bf16_exact_matches_torch_on_binary32_values():
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oproject.round_bf16_exact(x.astype(np.float64)), ref)
+
+
+def test_project_keys_identity_weight_is_the_input():
+    rng = np.random.default_rng(32)
+    H, d, N = 3, 16, 40
+    X = bf16_round(rng.standard_normal((N, H * d)).astype(np.float32))
+    planes = bf16_round(rng.standard_normal((2, 8, d)).astype(np.float32)).reshape(2, 8, d)
+    K, codes, _ = oproject.project_keys(X, np.eye(H * d), H, planes)
+    for h in range(H):
+        np.testing.assert_array_equal(K[h], X[:, h * d:(h + 1) * d])
+        np.testing.assert_array_equal(codes[h], simhash(X[:, h * d:(h + 1) * d], planes)[0])
+
+
+def test_project_keys_small_integers_by_loops():
+    """Integer inputs small enough for every product and sum to be exact in
+    bfloat16: keys and sign bits by plain Python loops."""
+    rng = np.random.default_rng(33)
+    H, d, Din, N, L, b = 2, 4, 6, 5, 2, 3
+    X = rng.integers(-3, 4, size=(N, Din)).astype(np.float64)
+    W = rng.integers(-2, 3, size=(H * d, Din)).astype(np.float64)
+    P = rng.integers(-2, 3, size=(L, b, d)).astype(np.float64)
+    K, codes, _ = oproject.project_keys(X, W, H, P)
+    for h in range(H):
+        for n in range(N):
+            k = [sum(X[n][i] * W[h * d + f][i] for i in range(Din)) for f in range(d)]
+            assert list(K[h, n]) == k
+            for t in range(L):
+                code = 0
+                for j in range(b):
+                    if sum(P[t][j][f] * k[f] for f in range(d)) > 0:
+                        code |= 1 << j
+                assert codes[h, n, t] == code
