@@ -44,7 +44,7 @@ def _parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dit1.3b",
                    choices=["dit1.3b", "dit1.3b_pq", "dit14b", "rollout", "annca", "annsa",
-                            "denoise"])
+                            "denoise", "project"])
     p.add_argument("--annsa-bits", type=int, default=16, help="bits per table of the AnnSA buckets")
     p.add_argument("--denoise-steps", type=int, default=4, help="denoising steps per chunk")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -382,6 +382,8 @@ def main():
         return annsa(args, fa, torch)
     if args.workload == "denoise":
         return denoise(args, fa, torch)
+    if args.workload == "project":
+        return project(args, fa, torch)
 
     w = WORKLOADS[args.workload]
     T, F = w.tokens_per_frame, w.frames_per_chunk
@@ -712,6 +714,78 @@ def denoise(args, fa, torch):
                    "chunk_ms": ms_chunk, "generated_tokens_per_s": Nq * args.steps / elapsed,
                    "slots_per_head_mean": float(n_live.mean()), "chunk_tokens": Nq,
                    "attend_gflop_per_step": flops / 1e9},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def project(args, fa, torch):
+    """The chunk's key projection with the SimHash codes in its epilogue, at
+    the 1.3B layer: 4680 tokens of width 1536 through a 1536 x 1536 key weight
+    (12 heads x 128), codes of 4 tables x 32 bits; against torch's bf16
+    matmul followed by the library's hash kernel on its output."""
+    from synth import WORKLOADS, DriftStream
+    w = WORKLOADS["dit1.3b"]
+    H, d, N, Din = w.heads, w.head_dim, w.chunk_tokens, 1536
+    st = DriftStream(w)
+    planes = st.planes()
+    cfg = fa.CacheConfig(H, d, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+    cache = fa.Cache(cfg, planes)
+    g = torch.Generator(device="cuda").manual_seed(2026)
+    x = torch.randn((N, Din), generator=g, device="cuda").to(torch.bfloat16)
+    wt = (torch.randn((H * d, Din), generator=g, device="cuda") / Din ** 0.5).to(torch.bfloat16)
+    pl = torch.from_numpy(planes).to(torch.bfloat16).cuda().contiguous()
+    k = torch.empty((H, N, d), dtype=torch.bfloat16, device="cuda")
+    codes = torch.empty((H, w.tables, N), dtype=torch.int32, device="cuda")
+    kk = torch.empty((N, H * d), dtype=torch.bfloat16, device="cuda")
+    codes2 = torch.empty_like(codes)
+
+    def fused():
+        cache.project_keys(x, wt, k_out=k, codes_out=codes)
+
+    def matmul():
+        torch.matmul(x, wt.t(), out=kk)
+
+    def hash_only():
+        fa.hash_codes(kk.view(N, H, d).transpose(0, 1), pl, w.tables, w.bits, out=codes2)
+
+    def unfused():
+        matmul()
+        hash_only()
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("fused", fused), ("unfused", unfused), ("matmul", matmul), ("hash", hash_only)):
+        for _ in range(args.warmup):
+            fn()
+        ev = _events(args, 2 * args.steps, stream)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev.record(2 * i)
+            fn()
+            ev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        ms = np.array([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)])
+        ev.close()
+        res[name] = {"ms_median": float(np.median(ms)), "ms_p95": float(np.percentile(ms, 95))}
+    same_k = bool(torch.equal(k, kk.view(N, H, d).transpose(0, 1)))
+    flops = 2.0 * N * Din * H * d
+    tf = flops / (res["fused"]["ms_median"] / 1e3) / 1e12
+    line = {
+        "metric": "tokens/s through the key projection with SimHash codes",
+        "value": N / (res["fused"]["ms_median"] / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["fused"]["ms_median"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (Gaussian tokens and weights; no trained weights)",
+        "config": {"workload": f"project: {N} tokens x {Din} -> {H} heads x {d}, "
+                               f"{w.tables} x {w.bits}-bit SimHash codes"},
+        "roofline": {"bound": "mfma", "kernel": "project_hash_kernel", "achieved": tf,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+        "detail": {"fused": res["fused"], "unfused_matmul_then_hash": res["unfused"],
+                   "torch_matmul": res["matmul"], "hash_kernel": res["hash"],
+                   "speedup_vs_unfused": res["unfused"]["ms_median"] / res["fused"]["ms_median"],
+                   "keys_bit_identical_to_torch_matmul": same_k,
+                   "gemm_gflop": flops / 1e9},
     }
     print(json.dumps(line), flush=True)
 

@@ -185,6 +185,24 @@ fastar_status fastar_match_merge(fastar_cache_t cache, const void* k_dev, const 
                                  int32_t tokens_per_frame, int32_t num_frames,
                                  int32_t* slot_out_dev, uint8_t* merged_out_dev, void* stream);
 
+/* Key projection with the SimHash codes taken in its epilogue (section 2A,
+ * "Mecanismo": the keys TempCache hashes are the attention layer's keys).
+ * For n_tok tokens x (row n at x_dev + n*x_stride, d_in bf16) and the layer's
+ * key weight w (nn.Linear layout: out feature r at w_dev + r*w_stride, d_in
+ * bf16; head h owns rows [h*d, (h+1)*d)), writes the bf16 keys k = x w^T,
+ * rounded to nearest even once from fp32 accumulation, to (h, n, k) at
+ * k_out_dev[h*k_stride_h + n*k_stride_n + k], and their codes under the
+ * cache's hyperplanes to codes_dev[(h*L + t)*codes_ld + n] (uint32, the layout
+ * fastar_match_merge takes).  No bias, normalisation or rotation.  Requires a
+ * bf16 cache with SimHash codes (else FASTAR_ERR_UNSUPPORTED), d_in a
+ * positive multiple of 32, 16-byte aligned x, w, k_out and row strides that
+ * are multiples of 16 bytes, codes_ld >= n_tok.  Reads the cache's
+ * hyperplanes only; all buffers stay the caller's. */
+fastar_status fastar_project_keys(fastar_cache_t cache, const void* x_dev, int64_t x_stride,
+                                  int32_t n_tok, int32_t d_in, const void* w_dev, int64_t w_stride,
+                                  void* k_out_dev, int64_t k_stride_h, int64_t k_stride_n,
+                                  uint32_t* codes_dev, int64_t codes_ld, void* stream);
+
 /* Attention of Nq queries per head over the live slots (section 2A, Lemma 5.1:
  * logits shifted by the group size).  q_dev: (h, n, k) at q_dev[h*stride_h +
  * n*stride_n + k]; o_dev likewise with o_stride_h, o_stride_n (cfg dtype);

@@ -79,6 +79,8 @@ _SIGS = {
     "fastar_match_merge": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _VP, _I32, _I32, _VP, _VP,
                                           _VP]),
     "fastar_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _F, _VP, _I64, _I64, _VP, _VP]),
+    "fastar_project_keys": (ctypes.c_int, [_VP, _VP, _I64, _I32, _I32, _VP, _I64, _VP, _I64, _I64,
+                                           _VP, _I64, _VP]),
     "fastar_attend_with_chunk": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _VP, _VP, _I64, _I64,
                                                 _I32, _F, _VP, _I64, _I64, _VP, _VP]),
     "fastar_cache_hash_slots": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _I64, _VP]),
@@ -306,6 +308,34 @@ class Cache:
                                        float(scale), _ptr(out), out.stride(0), out.stride(1),
                                        _ptr(lse), _stream(stream)))
         return out
+
+    def project_keys(self, x: torch.Tensor, w: torch.Tensor, k_out: torch.Tensor | None = None,
+                     codes_out: torch.Tensor | None = None, stream=None):
+        """Keys k = x w^T of tokens x [N][D_in] under the key weight w [H*d][D_in]
+        (bf16) and their codes under the cache's hyperplanes, in one kernel.
+        Returns (k [H][N][d], codes [H][L][N] int32 bit patterns)."""
+        _require(x, "x", torch.bfloat16)
+        _require(w, "w", torch.bfloat16)
+        H, d, L = self.cfg.heads, self.cfg.head_dim, self.cfg.tables
+        if x.dim() != 2 or x.stride(1) != 1 or w.dim() != 2 or w.stride(1) != 1:
+            raise ValueError("x and w must be 2-D with contiguous rows")
+        N, din = x.shape
+        if tuple(w.shape) != (H * d, din):
+            raise ValueError("w must be [heads*head_dim][D_in]")
+        if k_out is None:
+            k_out = torch.empty((H, N, d), dtype=torch.bfloat16, device=x.device)
+        _require(k_out, "k_out", torch.bfloat16)
+        if tuple(k_out.shape) != (H, N, d):
+            raise ValueError("k_out must be [heads][N][head_dim]")
+        if codes_out is None:
+            codes_out = torch.empty((H, L, N), dtype=torch.int32, device=x.device)
+        _require(codes_out, "codes_out", torch.int32)
+        if tuple(codes_out.shape) != (H, L, N) or not codes_out.is_contiguous():
+            raise ValueError("codes_out must be contiguous [heads][tables][N]")
+        _check(library().fastar_project_keys(
+            self._h, _ptr(x), x.stride(0), N, din, _ptr(w), w.stride(0), _ptr(k_out),
+            k_out.stride(0), k_out.stride(1), _ptr(codes_out), N, _stream(stream)))
+        return k_out, codes_out
 
     def attend_with_chunk(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                           scale: float = 0.0, out: torch.Tensor | None = None,

@@ -619,6 +619,48 @@ static fastar_status attend_impl(fastar_cache_t c, const void* q_dev, int64_t st
   return ok();
 }
 
+fastar_status fastar_project_keys(fastar_cache_t c, const void* x_dev, int64_t x_stride,
+                                  int32_t n_tok, int32_t d_in, const void* w_dev, int64_t w_stride,
+                                  void* k_out_dev, int64_t k_stride_h, int64_t k_stride_n,
+                                  uint32_t* codes_dev, int64_t codes_ld, void* stream) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  const Dims& dm = c->dm;
+  if (dm.elem != 2 || dm.M != 0)
+    return fail(FASTAR_ERR_UNSUPPORTED, "fastar_project_keys needs a bf16 cache with SimHash codes");
+  FASTAR_REQUIRE(n_tok >= 0, "n_tok must be >= 0");
+  FASTAR_REQUIRE(d_in > 0 && d_in % 32 == 0, "d_in must be a positive multiple of 32");
+  if (n_tok == 0) return ok();
+  FASTAR_REQUIRE(x_dev && w_dev && k_out_dev && codes_dev, "NULL pointer");
+  FASTAR_REQUIRE(aligned(x_dev, 16) && aligned(w_dev, 16) && aligned(k_out_dev, 16) &&
+                     aligned(codes_dev, 4),
+                 "x, w and k_out must be 16-byte aligned, codes 4-byte aligned");
+  FASTAR_REQUIRE(x_stride % 8 == 0 && x_stride >= d_in && w_stride % 8 == 0 && w_stride >= d_in,
+                 "x and w row strides must be multiples of 16 bytes and >= d_in");
+  FASTAR_REQUIRE(k_stride_h % 8 == 0 && k_stride_n % 8 == 0 && k_stride_n >= dm.d,
+                 "k_out strides must be multiples of 16 bytes");
+  FASTAR_REQUIRE(codes_ld >= n_tok, "codes_ld must be >= n_tok");
+  ProjArgs a{};
+  a.x = static_cast<const uint16_t*>(x_dev);
+  a.sx = x_stride;
+  a.w = static_cast<const uint16_t*>(w_dev);
+  a.sw = w_stride;
+  a.N = n_tok;
+  a.Din = d_in;
+  a.H = dm.H;
+  a.L = dm.L;
+  a.b = dm.b;
+  a.Ppad = dm.Ppad;
+  a.k = static_cast<uint16_t*>(k_out_dev);
+  a.sk_h = k_stride_h;
+  a.sk_n = k_stride_n;
+  a.codes = codes_dev;
+  a.codes_ld = codes_ld;
+  a.planes_frag = c->dev.planes_frag;
+  FASTAR_HIP(launch_project_hash(a, dm.d, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
 fastar_status fastar_attend(fastar_cache_t c, const void* q_dev, int64_t stride_h,
                             int64_t stride_n, int32_t Nq, float scale, void* o_dev,
                             int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream) {

@@ -32,12 +32,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  const int q = total >> 3, r = total & 7;
-  const int x = bid & 7, k = bid >> 3;
-  return x * q + min(x, r) + k;
-}
-
 
 template <int D, bool GATHER>
 __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles) {

@@ -22,6 +22,16 @@ constexpr int kSlotPad = 128;  // mirror rows per head are padded to a multiple 
 // slots per bucket cost it nothing while shrinking the index rebuild.
 constexpr int kSlotsPerBucket = FASTAR_SLOTS_PER_BUCKET;
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i to XCD
+// i % 8).  Renumbering them so that XCD x runs the contiguous range
+// [x*q + min(x, r), ...) of logical ids keeps neighbouring tiles, which share
+// operands, on one XCD and its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = bid & 7, k = bid >> 3;
+  return x * q + min(x, r) + k;
+}
+
 // ---------------------------------------------------------------- bfloat16
 // bfloat16 values travel as raw 16-bit patterns.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -246,6 +256,23 @@ struct AttendArgs {
 };
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s);
+
+// Key projection with SimHash codes in its epilogue: k = x W^T for N tokens,
+// head h owning rows [h*d, (h+1)*d) of W, rounded to bf16 and stored, then
+// hashed under the cache's fragment-ordered hyperplanes.
+struct ProjArgs {
+  const uint16_t* x;        // token n at x + n*sx (Din bf16)
+  int64_t sx;
+  const uint16_t* w;        // row r (out feature) at w + r*sw (Din bf16)
+  int64_t sw;
+  int N, Din, H, L, b, Ppad;
+  uint16_t* k;              // (h, n, :) at k + h*sk_h + n*sk_n
+  int64_t sk_h, sk_n;
+  uint32_t* codes;          // [H][L][codes_ld]
+  int64_t codes_ld;
+  const void* planes_frag;  // [Ppad/32][d/16][64] x 16 B
+};
+hipError_t launch_project_hash(const ProjArgs& a, int d, hipStream_t s);
 
 // AnnCA per-frame selection.
 struct SelectArgs {

@@ -339,6 +339,90 @@ def test_attend_empty_cache_gives_zeros():
     assert (out.float() == 0).all() and torch.isinf(lse).all()
 
 
+# ------------------------------------------------------------------ K projection + hash
+
+from oracle import project as oproject  # noqa: E402
+
+
+@pytest.mark.parametrize("H,d,N,Din,L,b", [
+    (2, 128, 300, 256, 4, 32),
+    (3, 128, 129, 1536, 4, 32),      # a ragged tile of one token
+    (2, 64, 200, 512, 2, 20),        # d = 64, 20-bit codes straddling words
+    (12, 128, 1000, 1536, 4, 32),    # the 1.3B layer's head count and width
+    (1, 128, 1, 64, 8, 32),          # one token, 8 tables (all 256 planes)
+    (2, 128, 700, 96, 3, 16),        # 3 stages: one pass of the copy ring
+    (2, 128, 64, 160, 1, 7),         # 5 stages, 7-bit codes
+])
+def test_project_keys_matches_oracle(H, d, N, Din, L, b):
+    print(f"project_keys: H={H} d={d} N={N} Din={Din} L={L} b={b}", flush=True)
+    rng = np.random.default_rng(700 + N)
+    X = round_to_storage(rng.standard_normal((N, Din), dtype=np.float32), "bf16")
+    W = round_to_storage((rng.standard_normal((H * d, Din)) / math.sqrt(Din)).astype(np.float32),
+                         "bf16")
+    planes = round_to_storage(rng.standard_normal((L, b, d), dtype=np.float32), "bf16")
+    cfg = fa.CacheConfig(H, d, 2 * N + 64, L, b, 0.95, "bf16")
+    cache = fa.Cache(cfg, planes)
+    k, codes = cache.project_keys(to_device(X, "bf16"), to_device(W, "bf16"))
+    torch.cuda.synchronize()
+    K_ref, c_ref, proj = oproject.project_keys(X, W, H, planes)
+    got = k.float().cpu().numpy().astype(np.float64)
+    # The stored keys: the bf16 rounding of the product.  fp32 accumulation of
+    # Din products errs by at most Din * 2^-24 * sum |x_i w_i| (recursive
+    # summation bound), and rounding either sum to bf16 adds at most one unit
+    # in the last place; keys near zero are where the first term dominates.
+    ulp = np.ldexp(1.0, np.frexp(np.abs(K_ref))[1] - 8)
+    acc_err = Din * 2.0 ** -24 * (np.abs(X.astype(np.float64)) @ np.abs(W.astype(np.float64)).T)
+    tol = ulp + acc_err.reshape(N, H, d).transpose(1, 0, 2)
+    diff = np.abs(got - K_ref)
+    assert (diff <= tol).all()
+    exact = float((diff == 0).mean())
+    assert exact > 0.99
+    # codes: a bit may differ only where that change of every key element
+    # could move its projection across zero (or |projection| < 1e-4)
+    P = planes.astype(np.float64).reshape(L * b, d)
+    bound = (tol @ np.abs(P).T).reshape(H, N, L, b) + 1e-4
+    amb = np.abs(proj) < bound
+    gc = codes.cpu().numpy().view(np.uint32)           # [H][L][N]
+    bad = differ = 0
+    for j in range(b):
+        gbit = (gc.transpose(0, 2, 1) >> j) & 1         # [H][N][L]
+        rbit = (c_ref >> j) & 1
+        bad += int(((gbit != rbit) & ~amb[..., j]).sum())
+        differ += int((gbit != rbit).sum())
+    print(f"  exact keys {exact:.5f}, ambiguous bits {int(amb.sum())}, differing bits {differ}")
+    assert bad == 0
+    # the bound is a worst case; in fact almost every bit agrees
+    assert differ <= 1e-3 * amb.size
+
+
+def test_project_keys_feeds_match_merge():
+    """Codes from the fused projection drive the merge like the library's own
+    hashing of the same keys, up to ambiguous bits: identical decisions."""
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=256, budget=1024, seed=92)
+    st = DriftStream(w)
+    planes = st.planes()
+    rng = np.random.default_rng(93)
+    Din = 256
+    W = round_to_storage((rng.standard_normal((w.heads * w.head_dim, Din)) / 16).astype(np.float32),
+                         "bf16")
+    wd = to_device(W, "bf16")
+    a, b_ = _cache_for(w, planes), _cache_for(w, planes)
+    for f in range(4):
+        X = round_to_storage(rng.standard_normal((w.tokens_per_frame, Din), dtype=np.float32), "bf16")
+        if f:
+            X[:150] = Xprev[:150]                        # repeated tokens: identical keys, merges
+        Xprev = X
+        k, codes = a.project_keys(to_device(X, "bf16"), wd)
+        v = torch.randn_like(k)
+        a.match_merge(k, v, w.tokens_per_frame, 1, codes=codes)
+        b_.match_merge(k, v, w.tokens_per_frame, 1)
+        torch.cuda.synchronize()
+    sa, sb = a.export_state(), b_.export_state()
+    for key in ("count", "n_live", "k_master", "v_master"):
+        np.testing.assert_array_equal(sa[key], sb[key], err_msg=key)
+    assert int(sa["count"].max()) >= 4
+
+
 # ------------------------------------------------------------------ denoising loop
 
 from oracle import denoise as odenoise  # noqa: E402
