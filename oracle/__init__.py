@@ -1,6 +1,6 @@
 """CPU oracle for the TempCache attention step, AnnCA selection, AnnSA,
-product-quantization codes, the step inside a chunk's denoising loop and
-the key projection with its SimHash codes.
+product-quantization codes, the step inside a chunk's denoising loop, the key projection with its
+SimHash codes, and the rotation-corrected M-degree approximation.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the HIP library and its Python
@@ -33,3 +33,4 @@ from . import annsa  # noqa: F401
 from . import pq  # noqa: F401
 from . import denoise  # noqa: F401
 from . import project  # noqa: F401
+from . import rope  # noqa: F401

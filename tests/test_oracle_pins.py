@@ -759,3 +759,111 @@ def test_project_keys_small_integers_by_loops():
                     if sum(P[t][j][f] * k[f] for f in range(d)) > 0:
                         code |= 1 << j
                 assert codes[h, n, t] == code
+
+
+# ---------------------------------------------------------------- rotation-corrected M-degree
+
+from oracle import rope as orope  # noqa: E402
+
+
+def test_rope_t_closed_forms():
+    # one pair, frequency 1: (1, 0) turned by `frame` radians
+    for t in (0.0, 0.5, 2.0, -1.25):
+        np.testing.assert_allclose(orope.rope_t([1.0, 0.0], t, 2), [math.cos(t), math.sin(t)],
+                                   atol=1e-15)
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((6, 16))
+    y = orope.rope_t(x, 7, 10)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    np.testing.assert_array_equal(y[:, 10:], x[:, 10:])            # untouched features
+    np.testing.assert_allclose(orope.rope_t(orope.rope_t(x, 3, 10), 4, 10), y, atol=1e-12)
+    # only the frame difference matters: <R(a) q, R(b) k> = <q, R(b - a) k>
+    q, k = rng.standard_normal(16), rng.standard_normal(16)
+    lhs = orope.rope_t(q, 5, 10) @ orope.rope_t(k, 11, 10)
+    np.testing.assert_allclose(lhs, q @ orope.rope_t(k, 6, 10), atol=1e-12)
+
+
+def _static_cache(rng, d, d_t, frames=4, static=6, fresh=5):
+    """Frames whose first `static` tokens repeat exactly (key and value), plus
+    fresh tokens; returns the oracle cache and the raw (rotated) history."""
+    hc = HeadCache(d, 64, 1, 4, 0.98, "f32", rng.standard_normal((1, 4, d)))
+    sk = rng.standard_normal((static, d)).astype(np.float32)
+    sv = rng.standard_normal((static, d)).astype(np.float32)
+    raw_k, raw_v = [], []
+    for f in range(frames):
+        K = np.concatenate([sk, rng.standard_normal((fresh, d)).astype(np.float32)])
+        V = np.concatenate([sv, rng.standard_normal((fresh, d)).astype(np.float32)])
+        hc.process_frame(K, V)
+        raw_k.append(orope.rope_t(K, f, d_t))
+        raw_v.append(V)
+    return hc, np.concatenate(raw_k), np.concatenate(raw_v)
+
+
+def test_mdegree_with_every_member_is_dense_attention_over_rotated_tokens():
+    """Static tokens (identical key and value in every frame) merge; with m at
+    least their count the approximation is exact: dense attention (torch) over
+    the raw tokens, each rotated to its own frame."""
+    rng = np.random.default_rng(42)
+    d, d_t = 32, 16
+    hc, rk, rv = _static_cache(rng, d, d_t)
+    n = hc.n_live
+    assert hc.count[:n].max() == 4 and n < rk.shape[0]
+    Q = orope.rope_t(rng.standard_normal((9, d)), 4, d_t)
+    fr = orope.recent_frames(hc, 4)
+    O, lse = orope.mdegree_attend(Q, hc.k_hat[:n], hc.v_hat[:n], hc.count[:n], fr, 4, d_t)
+    np.testing.assert_allclose(O, _sdpa(Q, rk, rv), atol=1e-12)
+    z = Q @ rk.T / math.sqrt(d)
+    np.testing.assert_allclose(lse, np.log(np.exp(z).sum(axis=1)), atol=1e-12)
+    # with m = 1 it is not exact (the static slots' rotations differ by frame)
+    O1, _ = orope.mdegree_attend(Q, hc.k_hat[:n], hc.v_hat[:n], hc.count[:n], fr, 1, d_t)
+    assert np.abs(O1 - O).max() > 1e-3
+
+
+def test_mdegree_without_rotation_is_the_cache_step():
+    rng = np.random.default_rng(43)
+    hc, _, _ = _static_cache(rng, 32, 16)
+    n = hc.n_live
+    Q = rng.standard_normal((7, 32))
+    O_ref, lse_ref = hc.attend(Q)
+    for m in (1, 2, 3, 4):
+        O, lse = orope.mdegree_attend(Q, hc.k_hat[:n], hc.v_hat[:n], hc.count[:n],
+                                      orope.recent_frames(hc, m), m, 0)
+        np.testing.assert_allclose(O, O_ref, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_ref, atol=1e-12)
+
+
+def test_mdegree_one_is_log_count_attention_at_the_last_rotation():
+    rng = np.random.default_rng(44)
+    d, d_t = 32, 16
+    hc, _, _ = _static_cache(rng, d, d_t)
+    n = hc.n_live
+    Q = rng.standard_normal((7, d))
+    last = np.array([hc.members[s][-1][0] for s in range(n)])
+    rk = np.stack([orope.rope_t(hc.k_hat[s], last[s], d_t) for s in range(n)])
+    bias = np.broadcast_to(np.log(hc.count[:n].astype(np.float64)), (7, n)).copy()
+    O, _ = orope.mdegree_attend(Q, hc.k_hat[:n], hc.v_hat[:n], hc.count[:n],
+                                orope.recent_frames(hc, 1), 1, d_t)
+    np.testing.assert_allclose(O, _sdpa(Q, rk, hc.v_hat[:n], mask=bias), atol=1e-12)
+
+
+def test_mdegree_depends_on_frame_differences_only():
+    rng = np.random.default_rng(45)
+    d, d_t = 32, 16
+    hc, _, _ = _static_cache(rng, d, d_t)
+    n = hc.n_live
+    Qh = rng.standard_normal((5, d))
+    fr = orope.recent_frames(hc, 3)
+    O, _ = orope.mdegree_attend(orope.rope_t(Qh, 4, d_t), hc.k_hat[:n], hc.v_hat[:n],
+                                hc.count[:n], fr, 3, d_t)
+    shifted = [[f + 9 for f in fs] for fs in fr]
+    O2, _ = orope.mdegree_attend(orope.rope_t(Qh, 13, d_t), hc.k_hat[:n], hc.v_hat[:n],
+                                 hc.count[:n], shifted, 3, d_t)
+    np.testing.assert_allclose(O, O2, atol=1e-12)
+
+
+def test_recent_frames_most_recent_first():
+    rng = np.random.default_rng(46)
+    hc, _, _ = _static_cache(rng, 16, 8, frames=5, static=2, fresh=1)
+    fr = orope.recent_frames(hc, 3)
+    assert fr[0] == [4, 3, 2] and fr[1] == [4, 3, 2]       # static slots: a member per frame
+    assert hc.count[0] == 5
