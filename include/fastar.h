@@ -86,6 +86,8 @@ typedef struct {
   int32_t pq_subspaces;  /* 0: SimHash codes, planes [L][b][d]; M in {1, 2, 4,
                           * 8 (d = 128 only)}: product-quantization codes,
                           * codebooks [L][M][2^(b/M)][d/M], b = M x (1..8)    */
+  int32_t rope_members;  /* 0..4: frames of each slot's most recent members kept
+                          * for fastar_attend_rope (its largest m)           */
 } fastar_config;
 
 typedef struct fastar_cache_s* fastar_cache_t;
@@ -106,7 +108,9 @@ typedef struct {
 /* Host-side image of a cache's state; any pointer may be NULL to skip it.
  * Shapes: k/v_master float [H][B][d]; k/v_mirror dtype [H][B][d];
  * count, last int32 [H][B]; codes uint32 [H][L][B]; n_live int32 [H];
- * evicted_tokens int64 [H]. */
+ * evicted_tokens int64 [H]; member_frames int32 [H][B][rope_members]: the
+ * frames of each slot's most recent members, most recent first (entries past
+ * the slot's count unspecified). */
 typedef struct {
   float* k_master;
   float* v_master;
@@ -118,6 +122,7 @@ typedef struct {
   int32_t* n_live;
   int64_t* evicted_tokens;
   int64_t frame;
+  int32_t* member_frames;
 } fastar_cache_state;
 
 /* Thread-local text of the last error (empty string if none). */
@@ -230,6 +235,25 @@ fastar_status fastar_attend_with_chunk(fastar_cache_t cache, const void* q_dev, 
                                        int64_t kv_stride_n, int32_t n_new, float scale, void* o_dev,
                                        int64_t o_stride_h, int64_t o_stride_n, float* lse_dev,
                                        void* stream);
+
+/* Attention with the rotation-corrected M-degree approximation (LIPAR summary,
+ * section 2B "Recuperação de Atenção", 1. "Aproximação de Grau-M": a group's
+ * exponential sum from its m most recent tokens, corrected for the rotary
+ * embedding; applied to the TempCache groups of section 2A).  The cache holds
+ * keys without their temporal rotation; each live slot of count c contributes
+ * the keys R(t_i) k_hat of its m' = min(m, c) most recent members' frames
+ * t_i, each with logit shift ln(c / m'), and its value v_hat; queries arrive
+ * rotated at their own frame.  R(t) turns features (2p, 2p+1),
+ * p < rope_dims / 2, by t * rope_base^(-2p / rope_dims); frames are the
+ * cache's frame counter at each member's merge.  Requires a bf16 cache made
+ * with rope_members >= m >= 1 (else FASTAR_ERR_UNSUPPORTED / invalid
+ * argument), rope_dims even in [0, d], rope_base > 0.  Other arguments and
+ * outputs as fastar_attend.  The rotated keys are built in the cache's
+ * workspace, so calls on one cache must not overlap. */
+fastar_status fastar_attend_rope(fastar_cache_t cache, const void* q_dev, int64_t stride_h,
+                                 int64_t stride_n, int32_t Nq, int32_t m, int32_t rope_dims,
+                                 float rope_base, float scale, void* o_dev, int64_t o_stride_h,
+                                 int64_t o_stride_n, float* lse_dev, void* stream);
 
 /* AnnSA set-up (section 2C: the buckets of the cached keys): SimHash codes of
  * the cache's slot keys (its mirrors) under any hyperplanes, and a bucket

@@ -43,7 +43,8 @@ class Config(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("budget_slots", ctypes.c_int32), ("num_tables", ctypes.c_int32),
                 ("num_bits", ctypes.c_int32), ("cos_threshold", ctypes.c_float),
-                ("dtype", ctypes.c_int), ("pq_subspaces", ctypes.c_int32)]
+                ("dtype", ctypes.c_int), ("pq_subspaces", ctypes.c_int32),
+                ("rope_members", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -59,7 +60,11 @@ class State(ctypes.Structure):
                 ("k_mirror", ctypes.c_void_p), ("v_mirror", ctypes.c_void_p),
                 ("count", ctypes.c_void_p), ("last", ctypes.c_void_p),
                 ("codes", ctypes.c_void_p), ("n_live", ctypes.c_void_p),
-                ("evicted_tokens", ctypes.c_void_p), ("frame", ctypes.c_int64)]
+                ("evicted_tokens", ctypes.c_void_p), ("frame", ctypes.c_int64),
+                ("member_frames", ctypes.c_void_p)]
+
+# the array members of State, in order (all but `frame`)
+_STATE_ARRAYS = [n for n, _ in State._fields_ if n != "frame"]
 
 
 # name -> (restype, argtypes); the C ABI of include/fastar.h
@@ -81,6 +86,8 @@ _SIGS = {
     "fastar_attend": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _F, _VP, _I64, _I64, _VP, _VP]),
     "fastar_project_keys": (ctypes.c_int, [_VP, _VP, _I64, _I32, _I32, _VP, _I64, _VP, _I64, _I64,
                                            _VP, _I64, _VP]),
+    "fastar_attend_rope": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _I32, _I32, _F, _F, _VP,
+                                          _I64, _I64, _VP, _VP]),
     "fastar_attend_with_chunk": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I32, _VP, _VP, _I64, _I64,
                                                 _I32, _F, _VP, _I64, _I64, _VP, _VP]),
     "fastar_cache_hash_slots": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _I64, _VP]),
@@ -205,10 +212,12 @@ class CacheConfig:
     threshold: float
     dtype: str = "bf16"
     subspaces: int = 0   # 0: SimHash; M > 0: product quantization with M slices
+    rope_members: int = 0  # frames of each slot's most recent members kept (0..4)
 
     def c(self) -> Config:
         return Config(self.heads, self.head_dim, self.budget, self.tables, self.bits,
-                      float(self.threshold), _DTYPES[self.dtype][0], self.subspaces)
+                      float(self.threshold), _DTYPES[self.dtype][0], self.subspaces,
+                      self.rope_members)
 
     def plane_elems(self) -> int:
         """Elements of the hyperplanes [L][b][d] or PQ codebooks [L][M][2^(b/M)][d/M]."""
@@ -337,6 +346,29 @@ class Cache:
             k_out.stride(0), k_out.stride(1), _ptr(codes_out), N, _stream(stream)))
         return k_out, codes_out
 
+    def attend_rope(self, q: torch.Tensor, m: int, rope_dims: int, rope_base: float = 10000.0,
+                    scale: float = 0.0, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Attention of rotated queries q [H][Nq][d] with the M-degree
+        approximation: each slot's m most recent members' rotations, each
+        with logit shift ln(count / min(m, count))."""
+        _require(q, "q", self.torch_dtype)
+        H, Nq, d = q.shape
+        if H != self.cfg.heads or d != self.cfg.head_dim:
+            raise ValueError("q must be [heads][Nq][head_dim]")
+        if out is None:
+            out = torch.empty((H, Nq, d), dtype=self.torch_dtype, device=q.device)
+        _require(out, "out", self.torch_dtype)
+        if lse is not None:
+            _require(lse, "lse", torch.float32)
+            if tuple(lse.shape) != (H, Nq) or not lse.is_contiguous():
+                raise ValueError("lse must be contiguous [H][Nq]")
+        _check(library().fastar_attend_rope(self._h, _ptr(q), q.stride(0), q.stride(1), Nq, m,
+                                            rope_dims, float(rope_base), float(scale), _ptr(out),
+                                            out.stride(0), out.stride(1), _ptr(lse),
+                                            _stream(stream)))
+        return out
+
     def attend_with_chunk(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                           scale: float = 0.0, out: torch.Tensor | None = None,
                           lse: torch.Tensor | None = None, stream=None) -> torch.Tensor:
@@ -421,10 +453,13 @@ class Cache:
             "count": np.empty((H, B), np.int32), "last": np.empty((H, B), np.int32),
             "codes": np.empty((H, L, B), np.uint32), "n_live": np.empty(H, np.int32),
             "evicted_tokens": np.empty(H, np.int64),
+            "member_frames": np.empty((H, B, max(c.rope_members, 1)), np.int32),
         }
-        st = State(*[out[name].ctypes.data for name, _ in State._fields_[:-1]], 0)
+        st = State(**{name: out[name].ctypes.data for name in _STATE_ARRAYS}, frame=0)
         _check(library().fastar_cache_export(self._h, _stream(stream), ctypes.byref(st)))
         out["frame"] = int(st.frame)
+        if not c.rope_members:
+            del out["member_frames"]
         return out
 
     def import_state(self, state: dict, stream=None):
@@ -435,21 +470,22 @@ class Cache:
                 "k_mirror": ((H, B, d), mir), "v_mirror": ((H, B, d), mir),
                 "count": ((H, B), np.int32), "last": ((H, B), np.int32),
                 "codes": ((H, L, B), np.uint32), "n_live": ((H,), np.int32),
-                "evicted_tokens": ((H,), np.int64)}
+                "evicted_tokens": ((H,), np.int64),
+                "member_frames": ((H, B, c.rope_members), np.int32)}
         keep = {}
-        ptrs = []
-        for name, _ in State._fields_[:-1]:
+        ptrs = {}
+        for name in _STATE_ARRAYS:
             arr = state.get(name)
             if arr is None:
-                ptrs.append(None)
+                ptrs[name] = None
                 continue
             shape, dt = spec[name]
             a = np.ascontiguousarray(arr, dtype=dt)
             if a.shape != shape:
                 raise ValueError(f"{name} must have shape {shape}, got {a.shape}")
             keep[name] = a
-            ptrs.append(a.ctypes.data)
-        st = State(*ptrs, int(state.get("frame", 0)))
+            ptrs[name] = a.ctypes.data
+        st = State(**ptrs, frame=int(state.get("frame", 0)))
         _check(library().fastar_cache_import(self._h, ctypes.byref(st), _stream(stream)))
 
 

@@ -22,7 +22,7 @@ LIB_NAME = "libfastar.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["api.hip", "hash.hip", "match.hip", "merge.hip", "index.hip", "attend.hip",
-           "annca.hip", "annsa.hip", "pq.hip", "project.hip"]
+           "annca.hip", "annsa.hip", "pq.hip", "project.hip", "rope.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

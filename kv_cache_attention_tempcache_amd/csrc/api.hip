@@ -79,6 +79,7 @@ fastar_status make_dims(const fastar_config* cfg, Dims* dm) {
   FASTAR_REQUIRE(M == 0 || (cfg->num_bits % M == 0 && cfg->num_bits / M >= 1 &&
                             cfg->num_bits / M <= 8),
                  "product quantization needs num_bits = pq_subspaces x (1..8)");
+  FASTAR_REQUIRE(cfg->rope_members >= 0 && cfg->rope_members <= 4, "rope_members must be 0..4");
   dm->H = cfg->num_heads;
   dm->d = cfg->head_dim;
   dm->B = cfg->budget_slots;
@@ -92,6 +93,7 @@ fastar_status make_dims(const fastar_config* cfg, Dims* dm) {
   dm->NB = 1 << nb;
   dm->Ppad = M ? 0 : (dm->L * dm->b + 31) & ~31;  // SimHash planes of the fused re-hash
   dm->Bp = (dm->B + kSlotPad - 1) / kSlotPad * kSlotPad;
+  dm->R = cfg->rope_members;
   return FASTAR_OK;
 }
 
@@ -105,10 +107,10 @@ size_t plane_elems(const Dims& dm) {
 }
 
 enum Region {
-  kPlanes, kPlanesFrag, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kCodes, kIdxOff, kIdxSlot,
-  kNLive, kEvicted, kCounters, kOwner, kGsize, kFrame, kStateEnd = kFrame,
+  kPlanes, kPlanesFrag, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kHist, kCodes,
+  kIdxOff, kIdxSlot, kNLive, kEvicted, kCounters, kOwner, kGsize, kFrame, kStateEnd = kFrame,
   kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupSlot, kItems,
-  kPlan, kAnnsaCodes, kAnnsaOff, kAnnsaEnt, kNumRegions
+  kPlan, kAnnsaCodes, kAnnsaOff, kAnnsaEnt, kRopeK, kRopeLb, kNumRegions
 };
 
 fastar_status check_device_gfx950(int* device) {
@@ -161,6 +163,7 @@ Layout make_layout(const Dims& dm) {
   sizes[kLb] = H * Bp * 4;
   sizes[kCount] = H * B * 4;
   sizes[kLast] = H * B * 4;
+  sizes[kHist] = H * B * (size_t)dm.R * 4;
   sizes[kCodes] = H * Lt * B * 4;
   sizes[kIdxOff] = H * Lt * ((size_t)dm.NB + 1) * 4;
   sizes[kIdxSlot] = H * Lt * B * 8;
@@ -181,6 +184,8 @@ Layout make_layout(const Dims& dm) {
   sizes[kAnnsaCodes] = H * 4 * B * 4;
   sizes[kAnnsaOff] = H * 4 * ((size_t)dm.NB + 1) * 4;
   sizes[kAnnsaEnt] = H * 4 * B * 8;
+  sizes[kRopeK] = e == 2 ? H * (size_t)dm.R * Bp * d * 2 : 0;
+  sizes[kRopeLb] = e == 2 ? H * (size_t)dm.R * Bp * 4 : 0;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {
     L.off[r] = off;
@@ -204,6 +209,7 @@ CacheDev carve(void* base, const Dims& dm) {
   c.lb = reinterpret_cast<float*>(b + L.off[kLb]);
   c.count = reinterpret_cast<int32_t*>(b + L.off[kCount]);
   c.last = reinterpret_cast<int32_t*>(b + L.off[kLast]);
+  c.hist = reinterpret_cast<int32_t*>(b + L.off[kHist]);
   c.codes = reinterpret_cast<uint32_t*>(b + L.off[kCodes]);
   c.idx_off = reinterpret_cast<int32_t*>(b + L.off[kIdxOff]);
   c.idx_ent = reinterpret_cast<uint2*>(b + L.off[kIdxSlot]);
@@ -224,6 +230,8 @@ CacheDev carve(void* base, const Dims& dm) {
   c.annsa_codes = reinterpret_cast<uint32_t*>(b + L.off[kAnnsaCodes]);
   c.annsa_off = reinterpret_cast<int32_t*>(b + L.off[kAnnsaOff]);
   c.annsa_ent = reinterpret_cast<uint2*>(b + L.off[kAnnsaEnt]);
+  c.rope_k = b + L.off[kRopeK];
+  c.rope_lb = reinterpret_cast<float*>(b + L.off[kRopeLb]);
   return c;
 }
 
@@ -678,6 +686,38 @@ fastar_status fastar_attend_with_chunk(fastar_cache_t c, const void* q_dev, int6
                      kv_stride_n, n_new, scale, o_dev, o_stride_h, o_stride_n, lse_dev, stream);
 }
 
+fastar_status fastar_attend_rope(fastar_cache_t c, const void* q_dev, int64_t stride_h,
+                                 int64_t stride_n, int32_t Nq, int32_t m, int32_t rope_dims,
+                                 float rope_base, float scale, void* o_dev, int64_t o_stride_h,
+                                 int64_t o_stride_n, float* lse_dev, void* stream) {
+  fastar_status st = check_handle(c);
+  if (st != FASTAR_OK) return st;
+  const Dims& dm = c->dm;
+  if (dm.elem != 2 || dm.R == 0)
+    return fail(FASTAR_ERR_UNSUPPORTED, "fastar_attend_rope needs a bf16 cache with rope_members > 0");
+  FASTAR_REQUIRE(m >= 1 && m <= dm.R, "m must be in 1..rope_members");
+  FASTAR_REQUIRE(rope_dims >= 0 && rope_dims <= dm.d && rope_dims % 2 == 0,
+                 "rope_dims must be even and in [0, d]");
+  FASTAR_REQUIRE(std::isfinite(rope_base) && rope_base > 0.0f, "rope_base must be > 0");
+  FASTAR_REQUIRE(Nq >= 0, "Nq must be >= 0");
+  if (Nq == 0) return ok();
+  FASTAR_REQUIRE(q_dev && o_dev, "q or o is NULL");
+  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(o_dev, 16), "q and o must be 16-byte aligned");
+  FASTAR_REQUIRE(stride_h % 8 == 0 && stride_n % 8 == 0 && stride_n >= dm.d,
+                 "q strides must be multiples of 16 bytes");
+  FASTAR_REQUIRE(o_stride_h % 8 == 0 && o_stride_n % 8 == 0 && o_stride_n >= dm.d,
+                 "o strides must be multiples of 16 bytes");
+  FASTAR_REQUIRE(lse_dev == nullptr || aligned(lse_dev, 4), "lse misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float sc = scale == 0.0f ? 1.0f / std::sqrt((float)dm.d) : scale;
+  FASTAR_HIP(launch_rope_expand(dm, c->dev, m, rope_dims, rope_base, s));
+  CacheAttendArgs ca{q_dev, stride_h, stride_n, o_dev, o_stride_h, o_stride_n, lse_dev, Nq, sc};
+  ca.n_reg = m;
+  FASTAR_HIP(launch_attend_cache_bf16(dm, c->dev, ca, s));
+  return ok();
+}
+
 fastar_status fastar_cache_stats(fastar_cache_t c, void* stream, fastar_stats* out) {
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
@@ -734,6 +774,7 @@ fastar_status fastar_cache_export(fastar_cache_t c, void* stream, fastar_cache_s
   FASTAR_HIP(cp(out->codes, d.codes, HB * dm.L * 4));
   FASTAR_HIP(cp(out->n_live, d.n_live, (size_t)dm.H * 4));
   FASTAR_HIP(cp(out->evicted_tokens, d.evicted_tokens, (size_t)dm.H * 8));
+  if (dm.R > 0) FASTAR_HIP(cp(out->member_frames, d.hist, HB * dm.R * 4));
   int32_t frame = 0;
   FASTAR_HIP(hipMemcpyAsync(&frame, d.frame, 4, hipMemcpyDeviceToHost, s));
   FASTAR_HIP(hipStreamSynchronize(s));
@@ -772,6 +813,7 @@ fastar_status fastar_cache_import(fastar_cache_t c, const fastar_cache_state* in
   FASTAR_HIP(cp(d.codes, in->codes, HB * dm.L * 4));
   FASTAR_HIP(cp(d.n_live, in->n_live, (size_t)dm.H * 4));
   FASTAR_HIP(cp(d.evicted_tokens, in->evicted_tokens, (size_t)dm.H * 8));
+  if (dm.R > 0) FASTAR_HIP(cp(d.hist, in->member_frames, HB * dm.R * 4));
   const int32_t frame = (int32_t)in->frame;
   FASTAR_HIP(hipMemcpyAsync(d.frame, &frame, 4, hipMemcpyHostToDevice, s));
   FASTAR_HIP(launch_finalize_state(dm, d, s));

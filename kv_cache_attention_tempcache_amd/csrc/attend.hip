@@ -171,7 +171,7 @@ struct CCfg {
 // queries attends over rows of arbitrary [H][N][d] key and value arrays with
 // no bias: all sa.n_keys_const rows, or the first n_keys[h][g] rows of the
 // segment's gather list sa.sel, staged in LDS at the start.
-template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET, bool RAW>
+template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET, bool RAW, bool REG>
 __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kernel(
     Dims dm, CacheDev c, CacheAttendArgs a, AttendArgs sa, int qtiles) {
   using C = CCfg<D, BN, WAVES, QB>;
@@ -216,8 +216,11 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
              : static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h;
   float* lse_row = SUBSET ? (sa.lse ? sa.lse + (int64_t)(h * sa.F + g) * sa.Nseg : nullptr)
                           : (a.lse ? a.lse + (int64_t)h * a.Nq : nullptr);
+  // REG: keys (and shifts) from the M-degree regions, r * Bp rows apart
   const uint8_t* kg =
       SUBSET ? static_cast<const uint8_t*>(sa.k) + (int64_t)h * sa.sk_h * 2
+      : REG  ? reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(c.rope_k) +
+                                                (int64_t)h * dm.R * dm.Bp * D)
              : reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(c.k_mirror) +
                                                 (int64_t)h * dm.Bp * D);
   const uint8_t* vg =
@@ -225,11 +228,14 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
              : reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(c.v_mirror) +
                                                 (int64_t)h * dm.Bp * D);
   const int64_t rs = SUBSET ? sa.sk_n * 2 : C::kRowBytes;  // bytes between key rows
-  const float* lbg = SUBSET ? nullptr : c.lb + (int64_t)h * dm.Bp;
+  const float* lbg = SUBSET ? nullptr
+                     : REG  ? c.rope_lb + (int64_t)h * dm.R * dm.Bp
+                            : c.lb + (int64_t)h * dm.Bp;
   // RAW: raw tokens (count 1, no logit shift) follow the slots: key tiles
   // ntc .. of the loop read rows of a.xk / a.xv, rows past a.n_x read row 0
   // and are masked by their bias.
   static_assert(!(RAW && SUBSET), "raw tokens follow cache slots only");
+  static_assert(!(REG && (RAW || SUBSET)), "regions replace the slots' keys only");
   const int ntc = (nkeys + BN - 1) / BN;
   const int nx = RAW ? a.n_x : 0;
   const uint8_t* xkg = nx ? static_cast<const uint8_t*>(a.xk) + (int64_t)h * a.sx_h * 2 : nullptr;
@@ -263,8 +269,15 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   }
   auto issue = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
     const bool raw = RAW && k0 >= ntc * BN;  // block-uniform
-    const uint8_t* kt = kg + (SUBSET || raw ? 0 : (int64_t)k0 * C::kRowBytes);
-    const uint8_t* vt = vg + (SUBSET || raw ? 0 : (int64_t)k0 * C::kRowBytes);
+    // REG: tile k0/BN is tile u of region r; K and shift rows r*Bp + u*BN, V rows u*BN
+    int kr = k0, vr = k0;
+    if constexpr (REG) {
+      const int tr = k0 / BN, r = tr / ntc, u = tr - r * ntc;
+      kr = r * dm.Bp + u * BN;
+      vr = u * BN;
+    }
+    const uint8_t* kt = kg + (SUBSET || raw ? 0 : (int64_t)kr * C::kRowBytes);
+    const uint8_t* vt = vg + (SUBSET || raw ? 0 : (int64_t)vr * C::kRowBytes);
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
       const int i = wave + j * WAVES;
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     for (int i = 0; i < (BN + 63) / 64; ++i) {
       if (!SUBSET && wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
         __builtin_amdgcn_global_load_lds(
-            (gbl_void_t*)(lbg + (raw ? 0 : k0) + i * 64 + (uint32_t)lane),
+            (gbl_void_t*)(lbg + (raw ? 0 : kr) + i * 64 + (uint32_t)lane),
             (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256), 4, 0, 0);
     }
   };
@@ -469,7 +482,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     wait_barrier(min(nt - 1, it + NBUF - 1) - (it + 1));
   };
 
-  const int nt = ntc + (nx + BN - 1) / BN;
+  const int nt = REG ? a.n_reg * ntc : ntc + (nx + BN - 1) / BN;
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u)
     if (u < nt) issue(u * BN, u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : buf3);
@@ -519,12 +532,15 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
   const int qtiles = (a.Nq + C::BM - 1) / C::BM;
   const int blocks = dm.H * qtiles;
   if (blocks == 0) return hipSuccess;
-  if (a.n_x > 0)
-    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, true>), dim3(blocks),
-                       dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
+  if (a.n_reg > 0)
+    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, true>),
+                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
+  else if (a.n_x > 0)
+    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, true, false>),
+                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
   else
-    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false>), dim3(blocks),
-                       dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
+    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, false>),
+                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
   return hipGetLastError();
 }
 
@@ -537,7 +553,7 @@ hipError_t launch_subset_cfg(const AttendArgs& a, hipStream_t s) {
   const int blocks = a.H * a.F * qtiles;
   if (blocks == 0) return hipSuccess;
   const size_t lds = a.sel ? (size_t)a.n_keys_const * 4 : 0;
-  auto kern = attend_cache_kernel<D, 64, 8, 1, NBUF, true, false>;
+  auto kern = attend_cache_kernel<D, 64, 8, 1, NBUF, true, false, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -90,6 +90,7 @@ struct Dims {
   int nb_bits;   // log2 of buckets per (head, table)
   int NB;        // buckets per (head, table)
   int Ppad;      // L*b rounded up to a multiple of 32
+  int R;         // frames of each slot's most recent members kept (0: none)
 };
 
 // Device pointers into one cache's workspace.
@@ -131,6 +132,12 @@ struct CacheDev {
   uint32_t* annsa_codes;  // [H][4][B]
   int32_t* annsa_off;     // [H][4][NB+1]
   uint2* annsa_ent;       // [H][4][B]
+  // R > 0: frames of each slot's R most recent members, most recent first
+  // (entries past the slot's count are unspecified), and the rotated keys and
+  // log-count shifts of the M-degree attention, region r = member r
+  int32_t* hist;          // [H][B][R]
+  void* rope_k;           // bf16 [H][R*Bp][d]
+  float* rope_lb;         // [H][R*Bp]
 };
 
 struct Layout {
@@ -211,7 +218,14 @@ struct CacheAttendArgs {
   const void* xv;
   int64_t sx_h, sx_n;
   int n_x;
+  // n_reg > 0: keys and log2 shifts from c.rope_k / c.rope_lb, n_reg regions
+  // of Bp rows per head; region r's row s pairs with the V mirror row s
+  int n_reg;
 };
+// The M-degree regions: rotated keys of each live slot's m most recent
+// members' frames and their log2(count/m') shifts (-inf past m' or n_live).
+hipError_t launch_rope_expand(const Dims& dm, const CacheDev& c, int m, int rope_dims,
+                              float rope_base, hipStream_t s);
 hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                                     hipStream_t s);
 

@@ -444,6 +444,22 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
       c.count[(int64_t)h * B + s] = cnt;
       c.last[(int64_t)h * B + s] = f;
       c.lb[(int64_t)h * Bp + s] = __log2f((float)cnt);
+      if (dm.R > 0) {  // this frame's k1 - k0 members become the most recent
+        int32_t* hr = c.hist + ((int64_t)h * B + s) * dm.R;
+        int32_t old[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) old[i] = i < dm.R ? hr[i] : 0;
+        const int g = k1 - k0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i >= dm.R) break;
+          int32_t v = f;  // entry i after the shift: old entry i - g, if any
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j == i - g) v = old[j];
+          hr[i] = v;
+        }
+      }
     }
   } else {
     const int s = it.x, tok = it.w;
@@ -463,6 +479,7 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
       c.last[(int64_t)h * B + s] = f;
       c.lb[(int64_t)h * Bp + s] = 0.0f;
     }
+    if (gl < dm.R) c.hist[((int64_t)h * B + s) * dm.R + gl] = f;
     if (gl < L)
       c.codes[((int64_t)h * L + gl) * B + s] =
           a.codes[((int64_t)h * L + gl) * a.codes_ld + a.codes_col0 + tok];

@@ -25,9 +25,9 @@ pytestmark = pytest.mark.gpu
 TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
-def _cache_for(w, planes):
+def _cache_for(w, planes, rope_members=0):
     cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype,
-                         w.subspaces)
+                         w.subspaces, rope_members)
     return fa.Cache(cfg, planes)
 
 
@@ -135,11 +135,11 @@ def test_hash_zero_bits_gives_zero_codes():
 
 # ------------------------------------------------------------------ match / merge
 
-def _run_frames(w, frames, check_every=True, use_gpu_hash=False):
+def _run_frames(w, frames, check_every=True, use_gpu_hash=False, rope_members=0):
     st = DriftStream(w)
     planes = st.planes()
     orc = TempCacheOracle.for_workload(w, planes)
-    cache = _cache_for(w, planes)
+    cache = _cache_for(w, planes, rope_members)
     H, T = w.heads, w.tokens_per_frame
     amb_total = 0
     last_q = None
@@ -536,6 +536,99 @@ def test_denoising_loop_matches_oracle(name, overrides):
             np.testing.assert_array_equal(mo[h].astype(bool), res[f][h].merged)
             np.testing.assert_array_equal(so[h], res[f][h].slot)
     compare_state(cache.export_state(), orc, w.dtype)
+
+
+# ------------------------------------------------------------------ rotation-corrected M-degree
+
+from oracle import rope as orope  # noqa: E402
+
+
+@pytest.mark.parametrize("name,overrides,frames,R", [
+    ("tiny", {}, 6, 2),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048, seed=94), 6, 4),
+    ("dit1.3b", dict(heads=3, tokens_per_frame=129, budget=180, seed=77), 8, 3),   # eviction
+])
+def test_member_frames_match_oracle(name, overrides, frames, R):
+    w = WORKLOADS[name].with_(**overrides)
+    print(f"member frames: {w.name} {overrides} R={R}", flush=True)
+    orc, cache, _, _ = _run_frames(w, frames, check_every=False, rope_members=R)
+    g = cache.export_state()
+    for h, hc in enumerate(orc.heads):
+        fr = orope.recent_frames(hc, R)
+        for s in range(hc.n_live):
+            k = min(R, int(hc.count[s]))
+            assert list(g["member_frames"][h, s, :k]) == fr[s][:k], (h, s)
+
+
+def _rope_state(orc, w, R):
+    st = oracle_state_for_import(orc, w.dtype)
+    mf = np.zeros((w.heads, w.budget, R), np.int32)
+    for h, hc in enumerate(orc.heads):
+        for s, fs in enumerate(orope.recent_frames(hc, R)):
+            mf[h, s, :len(fs)] = fs
+    st["member_frames"] = mf
+    return st
+
+
+@pytest.mark.parametrize("name,overrides,frames,m,d_t", [
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048, seed=95), 6, 1, 32),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048, seed=95), 6, 2, 32),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048, seed=95), 6, 4, 32),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=2048, seed=95), 6, 3, 128),
+    ("dit1.3b", dict(heads=3, tokens_per_frame=131, budget=1024, head_dim=64, seed=3), 5, 4, 16),
+    ("dit1.3b", dict(heads=3, tokens_per_frame=129, budget=180, seed=77), 8, 2, 32),  # eviction
+    ("dit1.3b", dict(heads=2, tokens_per_frame=40, budget=1024, seed=40), 1, 4, 32),  # one tile
+])
+def test_attend_rope_matches_oracle(name, overrides, frames, m, d_t):
+    w = WORKLOADS[name].with_(**overrides)
+    print(f"attend_rope: {w.name} {overrides} frames={frames} m={m} d_t={d_t}", flush=True)
+    st = DriftStream(w)
+    planes = st.planes()
+    orc = TempCacheOracle.for_workload(w, planes)
+    for _ in range(frames):
+        K, V, _, _ = st.next_frame()
+        orc.process_frame(K, V)
+    R = 4
+    cache = _cache_for(w, planes, R)
+    cache.import_state(_rope_state(orc, w, R))
+    rng = np.random.default_rng(600 + m)
+    Qh = rng.standard_normal((w.heads, 200, w.head_dim))
+    Q = round_to_storage(np.stack([orope.rope_t(Qh[h], frames, d_t) for h in range(w.heads)])
+                         .astype(np.float32), w.dtype)
+    lse = torch.empty((w.heads, Q.shape[1]), dtype=torch.float32, device="cuda")
+    out = cache.attend_rope(to_device(Q, w.dtype), m, d_t, lse=lse)
+    torch.cuda.synchronize()
+    got, gl = out.float().cpu().numpy(), lse.cpu().numpy()
+    for h, hc in enumerate(orc.heads):
+        n = hc.n_live
+        O_ref, lse_ref = orope.mdegree_attend(Q[h], hc.k_hat[:n], hc.v_hat[:n], hc.count[:n],
+                                              orope.recent_frames(hc, m), m, d_t)
+        err = np.abs(got[h] - O_ref).max()
+        lerr = np.abs(gl[h] - lse_ref).max()
+        print(f"  head {h}: slots={n} max-abs={err:.3e} lse={lerr:.3e}")
+        assert err <= TOL[w.dtype]
+        assert lerr <= 1e-3 * max(1.0, np.abs(lse_ref).max())
+
+
+def test_attend_rope_without_rotation_is_the_cache_step():
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=300, budget=2048, seed=96)
+    orc, cache, _, Q = _run_frames(w, 5, check_every=False, rope_members=4)
+    q = to_device(Q, w.dtype)
+    a = cache.attend(q)
+    for m in (1, 4):
+        b = cache.attend_rope(q, m, 0)
+        torch.cuda.synchronize()
+        assert (a.float() - b.float()).abs().max().item() <= 1e-2
+
+
+def test_attend_rope_empty_cache_gives_zeros():
+    w = WORKLOADS["dit1.3b"].with_(heads=2, budget=256)
+    cache = _cache_for(w, DriftStream(w).planes(), 2)
+    q = torch.randn(2, 70, 128, device="cuda").to(torch.bfloat16)
+    lse = torch.zeros(2, 70, device="cuda")
+    out = cache.attend_rope(q, 2, 32, lse=lse)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isinf(lse).all()
 
 
 def test_lemma51_on_gpu_fp32():
