@@ -16,8 +16,8 @@ import torch
 import kv_cache_attention_tempcache_amd as fa
 from oracle import TempCacheOracle, simhash
 from synth import WORKLOADS, DriftStream
-from tests.helpers import (ambiguous_bit_mask, compare_codes, compare_state, mirror_to_f32,
-                           to_device)
+from tests.helpers import (ambiguous_bit_mask, code_ambiguity_mask, compare_codes, compare_state,
+                           mirror_to_f32, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,16 +25,28 @@ pytestmark = pytest.mark.gpu
 class _Sampled:
     """A GPU cache over all heads plus an oracle over sampled heads."""
 
-    def __init__(self, w, heads):
+    def __init__(self, w, heads, rope_members=0):
         self.w = w
         self.heads = heads
         self.st = DriftStream(w)
         self.planes = self.st.planes()
         self.orc = TempCacheOracle.for_workload(w, self.planes, heads=len(heads))
-        cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+        cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype,
+                             w.subspaces, rope_members)
         self.cache = fa.Cache(cfg, self.planes)
         self.pl_dev = to_device(self.planes, w.dtype).contiguous()
         self.amb_bits = 0
+
+    def codes_of(self, kd):
+        w = self.w
+        if w.subspaces:
+            return fa.pq_codes(kd, self.pl_dev, w.tables, w.subspaces, w.bits)
+        return fa.hash_codes(kd, self.pl_dev, w.tables, w.bits)
+
+    def amb_mask(self, x):
+        if self.w.subspaces:
+            return code_ambiguity_mask(x, self.planes, self.w.subspaces)
+        return ambiguous_bit_mask(x, self.planes)
 
     def frames(self, n):
         ks, vs, qs = [], [], []
@@ -51,7 +63,7 @@ class _Sampled:
         K = np.concatenate(ks, axis=1)
         V = np.concatenate(vs, axis=1)
         kd, vd = to_device(K, w.dtype), to_device(V, w.dtype)
-        codes = fa.hash_codes(kd, self.pl_dev, w.tables, w.bits)  # [H][L][F*T]
+        codes = self.codes_of(kd)  # [H][L][F*T]
         torch.cuda.synchronize()
         gcodes = codes.cpu().numpy().view(np.uint32)
         results = []
@@ -60,8 +72,7 @@ class _Sampled:
             results.append(res)
             for j, h in enumerate(self.heads):
                 got = gcodes[h][:, f * T:(f + 1) * T].T
-                nb, na = compare_codes(got, res[j].codes,
-                                       ambiguous_bit_mask(ks[f][h], self.planes))
+                nb, na = compare_codes(got, res[j].codes, self.amb_mask(ks[f][h]))
                 assert nb == 0
                 self.amb_bits += na
                 assert int(res[j].near_tie.sum()) == 0
@@ -87,7 +98,7 @@ class _Sampled:
         resync = False
         for j, h in enumerate(self.heads):
             n = int(ost["n_live"][j])
-            mask = ambiguous_bit_mask(ost["k_hat"][j, :n], self.planes)
+            mask = self.amb_mask(ost["k_hat"][j, :n])
             nb, na = compare_codes(gst["codes"][h][:, :n].T, ost["codes"][j, :n], mask)
             assert nb == 0
             self.amb_bits += na
@@ -204,4 +215,75 @@ def test_rollout_240_frames_sampled_head():
           f"device evicted slots={stats['evicted_slots']} attend max-abs={err:.3e} "
           f"ambiguous bits={s.amb_bits} ({time.time() - t0:.1f} s)")
     assert hc.n_live == w.budget and hc.evicted_tokens > 0
+    assert err <= 2e-2
+
+
+def test_dit13b_full_size_denoising_steps_then_mdegree():
+    """The 1.3B layer at full size on a sampled head: after the 21-frame
+    prefill, two denoising steps of the chunk's 4680 queries over the cache
+    plus the chunk's 4680 noisy tokens (every 5th query checked), then the
+    clean chunk merged, then the M-degree attention (m = 2) of its queries."""
+    from oracle import denoise as odenoise
+    from oracle import rope as orope
+    from synth import denoising_steps, round_to_storage
+    w = WORKLOADS["dit1.3b"]
+    s = _Sampled(w, heads=[5], rope_members=4)
+    for _ in range(w.prefill_frames):
+        ks, vs, _ = s.frames(1)
+        s.step(ks, vs, check=False)
+    s.check_state()
+    ks, vs, qs = s.frames(3)
+    K, V, Q = (np.concatenate(x, axis=1) for x in (ks, vs, qs))
+    rng = np.random.default_rng(910)
+    Ks, Vs, Qs = (denoising_steps(rng, x, 2, 0.5, w.dtype) for x in (K, V, Q))
+    hc = s.orc.heads[0]
+    n = hc.n_live
+    rows = np.arange(0, Q.shape[1], 5)
+    err = 0.0
+    for step in range(2):
+        out = s.cache.attend_with_chunk(to_device(Qs[step], w.dtype), to_device(Ks[step], w.dtype),
+                                        to_device(Vs[step], w.dtype))
+        torch.cuda.synchronize()
+        ref, _ = odenoise.attend_with_chunk(Qs[step][5][rows], hc.k_hat[:n], hc.v_hat[:n],
+                                            hc.count[:n], Ks[step][5], Vs[step][5])
+        err = max(err, float(np.abs(out[5].float().cpu().numpy()[rows] - ref).max()))
+    print(f"denoising steps at full size: slots={n} + {K.shape[1]} chunk tokens, max-abs={err:.3e}")
+    assert err <= 2e-2
+    s.step(ks, vs)
+    s.check_state()
+    hc = s.orc.heads[0]
+    n = hc.n_live
+    d_t = 32
+    Qr = round_to_storage(np.stack([orope.rope_t(Q[h], w.prefill_frames + 3, d_t)
+                                    for h in range(w.heads)]).astype(np.float32), w.dtype)
+    mf = s.cache.export_state()["member_frames"]
+    fr = orope.recent_frames(hc, 2)
+    for sl in range(n):
+        k = min(2, int(hc.count[sl]))
+        assert list(mf[5, sl, :k]) == fr[sl][:k]
+    out = s.cache.attend_rope(to_device(Qr, w.dtype), 2, d_t)
+    torch.cuda.synchronize()
+    ref, _ = orope.mdegree_attend(Qr[5][rows], hc.k_hat[:n], hc.v_hat[:n], hc.count[:n], fr, 2, d_t)
+    merr = float(np.abs(out[5].float().cpu().numpy()[rows] - ref).max())
+    print(f"M-degree (m = 2) at full size: slots={n}, max-abs={merr:.3e}")
+    assert merr <= 2e-2
+
+
+def test_dit13b_pq_full_size_sampled_head():
+    """Product-quantization codes at the 1.3B layer's full size: the GPU hashes
+    every head itself; a sampled head's codes, decisions and state against the
+    oracle after the prefill and the timed chunk, then attention."""
+    w = WORKLOADS["dit1.3b_pq"]
+    s = _Sampled(w, heads=[3])
+    t0 = time.time()
+    for _ in range(w.prefill_frames):
+        ks, vs, _ = s.frames(1)
+        s.step(ks, vs)
+    s.check_state()
+    ks, vs, qs = s.frames(3)
+    s.step(ks, vs)
+    s.check_state()
+    err = _attend_check(s, qs, every=5)
+    print(f"dit1.3b_pq full size: n_live={[h.n_live for h in s.orc.heads]} attend max-abs={err:.3e} "
+          f"ambiguous codes={s.amb_bits} ({time.time() - t0:.1f} s)")
     assert err <= 2e-2

@@ -349,6 +349,7 @@ from oracle import project as oproject  # noqa: E402
     (3, 128, 129, 1536, 4, 32),      # a ragged tile of one token
     (2, 64, 200, 512, 2, 20),        # d = 64, 20-bit codes straddling words
     (12, 128, 1000, 1536, 4, 32),    # the 1.3B layer's head count and width
+    (12, 128, 4680, 1536, 4, 32),    # the 1.3B layer's whole chunk (bench.py --workload project)
     (1, 128, 1, 64, 8, 32),          # one token, 8 tables (all 256 planes)
     (2, 128, 700, 96, 3, 16),        # 3 stages: one pass of the copy ring
     (2, 128, 64, 160, 1, 7),         # 5 stages, 7-bit codes
