@@ -3,14 +3,14 @@
 // layer's keys, so they can be hashed where the projection produces them,
 // instead of being written out and read back by a separate hash pass).
 //
-// A workgroup computes the d x 128 tile K^T = W_h X^T of one head and 128
-// tokens on the 32x32x16 bf16 MFMA (out features as MFMA rows, tokens as
+// A workgroup computes the d x 256 (d = 64: d x 128) tile K^T = W_h X^T of
+// one head on the 32x32x16 bf16 MFMA (out features as MFMA rows, tokens as
 // columns; both operands have D_in contiguous).  Chunks of 32 D_in columns
 // move HBM -> LDS with direct-to-LDS loads in MFMA operand order (a lane
 // fetches the 16 bytes it will later read as an operand, so every operand
-// read is one conflict-free 16-byte LDS load) through a ring of three
-// distinct LDS buffers.  The epilogue rounds the tile to bf16 into two of
-// those buffers (token rows, 16-byte chunks permuted by row), stores the keys
+// read is one conflict-free 16-byte LDS load) through a ring of four
+// distinct LDS buffers.  The epilogue rounds the tile to bf16 into those
+// buffers (64 token rows each, 16-byte chunks permuted by row), stores the keys
 // and hashes them against the cache's fragment-ordered hyperplanes, one
 // 32-token block per wave, the arithmetic of the hash kernel.
 #include "common.hpp"
@@ -23,36 +23,44 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
-constexpr int kPjWaves = 4;
-constexpr int kPjThreads = kPjWaves * kWave;
-constexpr int kPjTok = 128;  // tokens per workgroup
-
+// d = 128: 8 waves on a 256-token tile (each wave 64 features x 64 tokens),
+// which brings 24 KiB of operands per 2 MFLOP, within what a CU's load path
+// delivers at full MFMA rate; d = 64: 4 waves on 128 tokens.
 template <int D>
 struct PjCfg {
+  static constexpr int kWaves = D == 128 ? 8 : 4;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kTok = D == 128 ? 256 : 128;    // tokens per workgroup
   static constexpr int kFB = D / 32;                    // feature blocks of a head
-  static constexpr int kTB = kPjTok / 32;               // token blocks
-  static constexpr int kWF = D == 128 ? 2 : 1;          // waves along features
-  static constexpr int kWT = kPjWaves / kWF;            // waves along tokens
+  static constexpr int kTB = kTok / 32;                 // token blocks
+  static constexpr int kWF = 2;                         // waves along features
+  static constexpr int kWT = kWaves / kWF;              // waves along tokens
   static constexpr int kFBw = kFB / kWF, kTBw = kTB / kWT;  // blocks per wave
   static constexpr int kFrags = 2 * (kFB + kTB);        // 1 KiB fragments per stage
   static constexpr int kStage = kFrags * 1024;
-  static constexpr int kPerWave = kFrags / kPjWaves;    // copies per wave and stage
+  static constexpr int kPerWave = kFrags / kWaves;      // copies per wave and stage
   static constexpr int kChunks = D / 8;                 // 16-byte chunks of a key row
-  static_assert(kFrags % kPjWaves == 0, "every wave issues the same copies");
+  static_assert(kFrags % kWaves == 0, "every wave issues the same copies");
+  static_assert(kFBw >= 1 && kTBw >= 1, "whole blocks per wave");
   static_assert(64 * D * 2 <= kStage, "64 epilogue key rows fit one ring buffer");
+  static_assert(kTok / 64 <= 4, "the epilogue rows fit the four ring buffers");
   // epilogue key rows: chunk c of token row t sits at chunk c ^ (t % kChunks)
   static __device__ __forceinline__ int swz(int t) { return t & (kChunks - 1); }
 };
 
 template <int D>
-__global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a, int tiles) {
+__global__ __launch_bounds__(PjCfg<D>::kThreads, 2) void project_hash_kernel(ProjArgs a) {
   using C = PjCfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t buf0[C::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t buf2[C::kStage];
-  __shared__ uint32_t s_words[kPjTok][9];
+  __shared__ __attribute__((aligned(16))) uint8_t buf3[C::kStage];
+  __shared__ uint32_t s_words[C::kTok][9];
+  // logical ids run over heads first: an XCD's contiguous range covers all
+  // heads of a few token tiles, so each token tile's rows are fetched into one
+  // L2 and only the (smaller) key weight is read by every XCD
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = lid / tiles, n0 = (lid - h * tiles) * kPjTok;
+  const int tt = lid / a.H, h = lid - tt * a.H, n0 = tt * C::kTok;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31, hf = lane >> 5;
@@ -66,7 +74,7 @@ __global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a,
   const uint8_t* src[C::kPerWave];
 #pragma unroll
   for (int j = 0; j < C::kPerWave; ++j) {
-    const int i = wave + j * kPjWaves;
+    const int i = wave + j * C::kWaves;
     const int ks = i & 1;
     if (i < 2 * C::kFB) {
       const int64_t row = (int64_t)h * D + (i >> 1) * 32 + m;
@@ -80,14 +88,16 @@ __global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a,
 #pragma unroll
     for (int j = 0; j < C::kPerWave; ++j)
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[j] + (int64_t)stage * 64),
-                                       (lds_void_t*)(dst + (wave + j * kPjWaves) * 1024), 16, 0, 0);
+                                       (lds_void_t*)(dst + (wave + j * C::kWaves) * 1024), 16, 0, 0);
   };
-  // Every copy of the stage about to be read has landed (this wave's: at most
-  // n copies, the next stage's, are still in flight), this wave's LDS reads
-  // are done, then all waves meet.  A plain barrier: __syncthreads() would
-  // also wait for the next stage's copies.
-  auto wait_barrier = [&](bool next_in_flight) __attribute__((always_inline)) {
-    if (next_in_flight)
+  // Wait until at most n stages' copies issued by this wave are in flight
+  // (every older stage has landed), finish this wave's LDS reads, then meet
+  // the other waves.  A plain barrier: __syncthreads() would also wait for
+  // the copies that are meant to stay in flight.
+  auto wait_barrier = [&](int n) __attribute__((always_inline)) {
+    if (n >= 2)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * C::kPerWave) : "memory");
+    else if (n == 1)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(C::kPerWave) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -100,10 +110,12 @@ __global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a,
     for (int tb = 0; tb < C::kTBw; ++tb) acc[fb][tb] = f32x16_t{};
 
   const int nk = a.Din / 32;
-  // read stage s from cur, then refill nxt (read at stage s-1) with stage
-  // s+2 (issued after this stage's operand reads, so that no read waits for it)
+  // A ring of four stage buffers: step s reads stage s from cur after issuing
+  // the copy of stage s+3 into nxt (the buffer read at step s-1), then waits
+  // until stage s+1 has landed, the copies of stages s+2, s+3 staying in
+  // flight.
   auto step = [&](const uint8_t* cur, uint8_t* nxt, int s) __attribute__((always_inline)) {
-    wait_barrier(s + 1 < nk);
+    if (s + 3 < nk) issue(s + 3, nxt);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t A[C::kFBw], B[C::kTBw];
@@ -120,14 +132,17 @@ __global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a,
         for (int tb = 0; tb < C::kTBw; ++tb)
           acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[fb], B[tb], acc[fb][tb], 0, 0, 0);
     }
-    if (s + 2 < nk) issue(s + 2, nxt);
+    wait_barrier(min(nk - 1, s + 3) - (s + 1));
   };
-  issue(0, buf0);
-  if (nk > 1) issue(1, buf1);
-  for (int s = 0; s < nk; s += 3) {
-    step(buf0, buf2, s);
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+    if (u < nk) issue(u, u == 0 ? buf0 : u == 1 ? buf1 : buf2);
+  wait_barrier(min(nk, 3) - 1);
+  for (int s = 0; s < nk; s += 4) {
+    step(buf0, buf3, s);
     if (s + 1 < nk) step(buf1, buf0, s + 1);
     if (s + 2 < nk) step(buf2, buf1, s + 2);
+    if (s + 3 < nk) step(buf3, buf2, s + 3);
   }
   __syncthreads();  // the ring is read; buf0 / buf1 now take the key rows
 
@@ -152,15 +167,20 @@ __global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a,
   for (int fb = 0; fb < C::kFBw; ++fb)
 #pragma unroll
     for (int tb = 0; tb < C::kTBw; ++tb) {
-      const int blk = wt * C::kTBw + tb;  // wave-uniform
-      if (blk < 2) put_rows(buf0, fb, tb, blk * 32 + m);
-      else put_rows(buf1, fb, tb, (blk - 2) * 32 + m);
+      const int blk = wt * C::kTBw + tb;  // wave-uniform; 64 token rows per buffer
+      const int t = (blk & 1) * 32 + m;
+      switch (blk >> 1) {
+        case 0: put_rows(buf0, fb, tb, t); break;
+        case 1: put_rows(buf1, fb, tb, t); break;
+        case 2: put_rows(buf2, fb, tb, t); break;
+        default: put_rows(buf3, fb, tb, t); break;
+      }
     }
   __syncthreads();
 
   // the keys, 16 bytes per store
   auto store_rows = [&](const uint8_t* rows, int t0) __attribute__((always_inline)) {
-    for (int idx = tid; idx < 64 * C::kChunks; idx += kPjThreads) {
+    for (int idx = tid; idx < 64 * C::kChunks; idx += C::kThreads) {
       const int t = idx / C::kChunks, c = idx - t * C::kChunks;
       if (n0 + t0 + t >= a.N) continue;
       const uint4 v = *reinterpret_cast<const uint4*>(rows + t * D * 2 + ((c ^ C::swz(t)) << 4));
@@ -169,6 +189,10 @@ __global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a,
   };
   store_rows(buf0, 0);
   store_rows(buf1, 64);
+  if (C::kTok > 128) {
+    store_rows(buf2, 128);
+    store_rows(buf3, 192);
+  }
 
   // SimHash of the stored keys: wave w takes tokens 32w .. 32w+31 against
   // every block of 32 hyperplanes (MFMA rows, from the fragment-ordered
@@ -199,10 +223,17 @@ __global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a,
     if (hf == 0)
       for (int pb = a.Ppad / 32; pb < 9; ++pb) s_words[tw][pb] = 0u;
   };
-  if (wave < 2) hash_rows(buf0, wave * 32 + m);
-  else hash_rows(buf1, (wave - 2) * 32 + m);
+  {
+    const int t = (wave & 1) * 32 + m;
+    switch (wave >> 1) {  // wave-uniform
+      case 0: hash_rows(buf0, t); break;
+      case 1: hash_rows(buf1, t); break;
+      case 2: hash_rows(buf2, t); break;
+      default: hash_rows(buf3, t); break;
+    }
+  }
   __syncthreads();
-  for (int idx = tid; idx < kPjTok * a.L; idx += kPjThreads) {
+  for (int idx = tid; idx < C::kTok * a.L; idx += C::kThreads) {
     const int t = idx / a.L, tb = idx - t * a.L;
     if (n0 + t >= a.N) continue;
     a.codes[((int64_t)h * a.L + tb) * a.codes_ld + n0 + t] = extract_code(s_words[t], tb * a.b, a.b);
@@ -211,10 +242,11 @@ __global__ __launch_bounds__(kPjThreads, 2) void project_hash_kernel(ProjArgs a,
 
 template <int D>
 hipError_t launch_d(const ProjArgs& a, hipStream_t s) {
-  const int tiles = (a.N + kPjTok - 1) / kPjTok;
+  using C = PjCfg<D>;
+  const int tiles = (a.N + C::kTok - 1) / C::kTok;
   const int blocks = a.H * tiles;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((project_hash_kernel<D>), dim3(blocks), dim3(kPjThreads), 0, s, a, tiles);
+  hipLaunchKernelGGL((project_hash_kernel<D>), dim3(blocks), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
