@@ -36,25 +36,32 @@ struct PjCfg {
   static constexpr int kWF = 2;                         // waves along features
   static constexpr int kWT = kWaves / kWF;              // waves along tokens
   static constexpr int kFBw = kFB / kWF, kTBw = kTB / kWT;  // blocks per wave
-  static constexpr int kFrags = 2 * (kFB + kTB);        // 1 KiB fragments per stage
-  static constexpr int kStage = kFrags * 1024;
-  static constexpr int kPerWave = kFrags / kWaves;      // copies per wave and stage
+  // A stage is 64 D_in columns (128 bytes) of the head's D weight rows, then
+  // of the tile's kTok token rows, row after row in LDS.
+  static constexpr int kRows = D + kTok;
+  static constexpr int kStage = kRows * 128;
+  static constexpr int kInstr = kRows / 8;              // 1 KiB copies per stage
+  static constexpr int kPerWave = kInstr / kWaves;      // copies per wave and stage
   static constexpr int kChunks = D / 8;                 // 16-byte chunks of a key row
-  static_assert(kFrags % kWaves == 0, "every wave issues the same copies");
+  static_assert(kInstr % kWaves == 0, "every wave issues the same copies");
   static_assert(kFBw >= 1 && kTBw >= 1, "whole blocks per wave");
-  static_assert(64 * D * 2 <= kStage, "64 epilogue key rows fit one ring buffer");
-  static_assert(kTok / 64 <= 4, "the epilogue rows fit the four ring buffers");
+  static_assert(2 * 64 * D * 2 <= kStage, "two blocks of 64 epilogue key rows fit a ring buffer");
+  static_assert(kTok / 64 <= 4, "the epilogue rows fit the ring buffers");
+  // stage rows: 16-byte chunk q of row r sits at chunk q ^ ((r / 2) % 8), so
+  // the 16 lanes an LDS read serves at once (16 rows, one chunk) hit
+  // distinct banks: row parity picks a 128-byte half of the 256 banks' span,
+  // the permutation spreads the 8 rows of each parity over its 8 chunks
+  static __device__ __forceinline__ int sw(int r) { return (r >> 1) & 7; }
   // epilogue key rows: chunk c of token row t sits at chunk c ^ (t % kChunks)
   static __device__ __forceinline__ int swz(int t) { return t & (kChunks - 1); }
 };
 
 template <int D>
-__global__ __launch_bounds__(PjCfg<D>::kThreads, 2) void project_hash_kernel(ProjArgs a) {
+__global__ __launch_bounds__(PjCfg<D>::kThreads, 1) void project_hash_kernel(ProjArgs a) {
   using C = PjCfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t buf0[C::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t buf2[C::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t buf3[C::kStage];
   __shared__ uint32_t s_words[C::kTok][9];
   // logical ids run over heads first: an XCD's contiguous range covers all
   // heads of a few token tiles, so each token tile's rows are fetched into one
@@ -66,38 +73,43 @@ __global__ __launch_bounds__(PjCfg<D>::kThreads, 2) void project_hash_kernel(Pro
   const int m = lane & 31, hf = lane >> 5;
   const int wf = wave % C::kWF, wt = wave / C::kWF;
 
-  // Copy sources.  Stage fragment i < 2*kFB: W rows of feature block i/2,
-  // k-step i%2; the others: X rows of token block (i - 2*kFB)/2.  Lane l
-  // fetches row 32*block + l%32, columns 16*(i%2) + 8*(l/32) .. +7 of the
-  // stage's 32; tokens past N fetch the last token (their keys are never
-  // stored).
+  // Copy sources.  Copy i of a stage fills stage rows 8i .. 8i+7: lane l
+  // fetches 16-byte chunk (l%8) ^ sw(row) of row 8i + l/8 (whole 128-byte
+  // lines, 8 per copy) and the copy lands it at chunk l%8.  Rows < D are the
+  // head's weight rows, the others tokens (past N: the last token, never
+  // stored).  In a last stage of 32 columns (D_in % 64 == 32) chunks 4..7 of
+  // a row are refetched from chunks 0..3 instead (read, never used).
   const uint8_t* src[C::kPerWave];
+  uint32_t hi_chunk = 0u;  // bit j: copy j fetches a chunk >= 4
 #pragma unroll
   for (int j = 0; j < C::kPerWave; ++j) {
-    const int i = wave + j * C::kWaves;
-    const int ks = i & 1;
-    if (i < 2 * C::kFB) {
-      const int64_t row = (int64_t)h * D + (i >> 1) * 32 + m;
-      src[j] = reinterpret_cast<const uint8_t*>(a.w + row * a.sw + ks * 16 + hf * 8);
+    const int r = (wave + j * C::kWaves) * 8 + (lane >> 3);
+    const int q = (lane & 7) ^ C::sw(r);
+    hi_chunk |= (uint32_t)(q >> 2) << j;
+    if (r < D) {
+      src[j] = reinterpret_cast<const uint8_t*>(a.w + ((int64_t)h * D + r) * a.sw + q * 8);
     } else {
-      const int64_t tok = min(n0 + ((i - 2 * C::kFB) >> 1) * 32 + m, a.N - 1);
-      src[j] = reinterpret_cast<const uint8_t*>(a.x + tok * a.sx + ks * 16 + hf * 8);
+      const int64_t tok = min(n0 + r - D, a.N - 1);
+      src[j] = reinterpret_cast<const uint8_t*>(a.x + tok * a.sx + q * 8);
     }
   }
+  const int nk = (a.Din + 63) / 64;
+  const bool half_tail = (a.Din & 63) != 0;  // the last stage has 32 columns
   auto issue = [&](int stage, uint8_t* dst) __attribute__((always_inline)) {
+    const bool tail = half_tail && stage == nk - 1;
 #pragma unroll
-    for (int j = 0; j < C::kPerWave; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[j] + (int64_t)stage * 64),
+    for (int j = 0; j < C::kPerWave; ++j) {
+      const int64_t back = tail && ((hi_chunk >> j) & 1u) ? 64 : 0;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[j] + (int64_t)stage * 128 - back),
                                        (lds_void_t*)(dst + (wave + j * C::kWaves) * 1024), 16, 0, 0);
+    }
   };
   // Wait until at most n stages' copies issued by this wave are in flight
   // (every older stage has landed), finish this wave's LDS reads, then meet
   // the other waves.  A plain barrier: __syncthreads() would also wait for
   // the copies that are meant to stay in flight.
   auto wait_barrier = [&](int n) __attribute__((always_inline)) {
-    if (n >= 2)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * C::kPerWave) : "memory");
-    else if (n == 1)
+    if (n >= 1)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(C::kPerWave) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -109,42 +121,44 @@ __global__ __launch_bounds__(PjCfg<D>::kThreads, 2) void project_hash_kernel(Pro
 #pragma unroll
     for (int tb = 0; tb < C::kTBw; ++tb) acc[fb][tb] = f32x16_t{};
 
-  const int nk = a.Din / 32;
-  // A ring of four stage buffers: step s reads stage s from cur after issuing
-  // the copy of stage s+3 into nxt (the buffer read at step s-1), then waits
-  // until stage s+1 has landed, the copies of stages s+2, s+3 staying in
-  // flight.
+  // A ring of three stage buffers: step s issues the copy of stage s+2 into
+  // nxt (the buffer read at step s-1), reads stage s from cur, then waits
+  // until stage s+1 has landed, the copy of stage s+2 staying in flight.
   auto step = [&](const uint8_t* cur, uint8_t* nxt, int s) __attribute__((always_inline)) {
-    if (s + 3 < nk) issue(s + 3, nxt);
+    if (s + 2 < nk) issue(s + 2, nxt);
+    const int nks = half_tail && s == nk - 1 ? 2 : 4;  // k-steps of 16 columns
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks >= nks) break;
+      const int q = 2 * ks + hf;  // this lane's 8 columns of the k-step
       bf16x8_t A[C::kFBw], B[C::kTBw];
 #pragma unroll
-      for (int fb = 0; fb < C::kFBw; ++fb)
-        A[fb] = *reinterpret_cast<const bf16x8_t*>(cur + (((wf * C::kFBw + fb) * 2 + ks) * 64 + lane) * 16);
+      for (int fb = 0; fb < C::kFBw; ++fb) {
+        const int r = (wf * C::kFBw + fb) * 32 + m;
+        A[fb] = *reinterpret_cast<const bf16x8_t*>(cur + r * 128 + ((q ^ C::sw(r)) << 4));
+      }
 #pragma unroll
-      for (int tb = 0; tb < C::kTBw; ++tb)
-        B[tb] = *reinterpret_cast<const bf16x8_t*>(
-            cur + ((2 * C::kFB + (wt * C::kTBw + tb) * 2 + ks) * 64 + lane) * 16);
+      for (int tb = 0; tb < C::kTBw; ++tb) {
+        const int r = D + (wt * C::kTBw + tb) * 32 + m;
+        B[tb] = *reinterpret_cast<const bf16x8_t*>(cur + r * 128 + ((q ^ C::sw(r)) << 4));
+      }
 #pragma unroll
       for (int fb = 0; fb < C::kFBw; ++fb)
 #pragma unroll
         for (int tb = 0; tb < C::kTBw; ++tb)
           acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[fb], B[tb], acc[fb][tb], 0, 0, 0);
     }
-    wait_barrier(min(nk - 1, s + 3) - (s + 1));
+    wait_barrier(min(nk - 1, s + 2) - (s + 1));
   };
-#pragma unroll
-  for (int u = 0; u < 3; ++u)
-    if (u < nk) issue(u, u == 0 ? buf0 : u == 1 ? buf1 : buf2);
-  wait_barrier(min(nk, 3) - 1);
-  for (int s = 0; s < nk; s += 4) {
-    step(buf0, buf3, s);
+  issue(0, buf0);
+  if (nk > 1) issue(1, buf1);
+  wait_barrier(min(nk, 2) - 1);
+  for (int s = 0; s < nk; s += 3) {
+    step(buf0, buf2, s);
     if (s + 1 < nk) step(buf1, buf0, s + 1);
     if (s + 2 < nk) step(buf2, buf1, s + 2);
-    if (s + 3 < nk) step(buf3, buf2, s + 3);
   }
-  __syncthreads();  // the ring is read; buf0 / buf1 now take the key rows
+  __syncthreads();  // the ring is read; it now takes the key rows
 
   // bf16 keys into token rows: tokens 0..63 in buf0, 64..127 in buf1 (every
   // access below names one of the two buffers, never a choice between them,
@@ -167,13 +181,13 @@ __global__ __launch_bounds__(PjCfg<D>::kThreads, 2) void project_hash_kernel(Pro
   for (int fb = 0; fb < C::kFBw; ++fb)
 #pragma unroll
     for (int tb = 0; tb < C::kTBw; ++tb) {
-      const int blk = wt * C::kTBw + tb;  // wave-uniform; 64 token rows per buffer
+      const int blk = wt * C::kTBw + tb;  // wave-uniform; 64 token rows per region
       const int t = (blk & 1) * 32 + m;
       switch (blk >> 1) {
         case 0: put_rows(buf0, fb, tb, t); break;
         case 1: put_rows(buf1, fb, tb, t); break;
         case 2: put_rows(buf2, fb, tb, t); break;
-        default: put_rows(buf3, fb, tb, t); break;
+        default: put_rows(buf0 + 64 * D * 2, fb, tb, t); break;
       }
     }
   __syncthreads();
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(PjCfg<D>::kThreads, 2) void project_hash_kernel(Pro
   store_rows(buf1, 64);
   if (C::kTok > 128) {
     store_rows(buf2, 128);
-    store_rows(buf3, 192);
+    store_rows(buf0 + 64 * D * 2, 192);
   }
 
   // SimHash of the stored keys: wave w takes tokens 32w .. 32w+31 against
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(PjCfg<D>::kThreads, 2) void project_hash_kernel(Pro
       case 0: hash_rows(buf0, t); break;
       case 1: hash_rows(buf1, t); break;
       case 2: hash_rows(buf2, t); break;
-      default: hash_rows(buf3, t); break;
+      default: hash_rows(buf0 + 64 * D * 2, t); break;
     }
   }
   __syncthreads();
