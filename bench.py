@@ -157,6 +157,29 @@ def _cpu_info():
     return name
 
 
+def _oracle_leg(fn, units, unit, what, scale=1.0):
+    """Time one call of an oracle function on the host: `units` of the bench
+    line's metric per second (a one-head sample counts as 1/H of a query
+    token's work, noted through `scale`), for a bench line's cpu_baseline."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report what numpy would use
+        blas_threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    return {"value": units / dt, "unit": unit, "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{what}; {dt:.2f} s measured{'' if scale == 1.0 else f', counted as {scale:.4g} of the work per query token (one of all heads)'}; "
+                      f"float64 numpy on {blas_threads} BLAS threads; host '{_cpu_info()}'"}
+
+
+def _random_slots(rng, S, d):
+    """Slot state of the GPU workload's shape (timing does not depend on values)."""
+    return (rng.standard_normal((S, d)), rng.standard_normal((S, d)),
+            rng.integers(1, 12, size=S))
+
+
 def cpu_baseline(w, frames, planes, heads):
     """Time the CPU oracle (as it stands) on one chunk step of `heads` heads."""
     from oracle import TempCacheOracle
@@ -643,6 +666,17 @@ def annsa(args, fa, torch):
                    "dense_mass_kept_mean_heads01": float(np.mean(kept_mass)),
                    "dense_equivalent_tflops": dense_flops / (res["annsa_attend"]["ms_median"] / 1e3) / 1e12},
     }
+    if not args.no_cpu_baseline:
+        from oracle import annsa as oannsa
+        rng = np.random.default_rng(10)
+        S = int(n_live.mean())
+        kh, vh, cnt = _random_slots(rng, S, d)
+        cqs = rng.integers(0, 1 << b, size=(Nq, L)).astype(np.uint32)
+        cks = rng.integers(0, 1 << b, size=(S, L)).astype(np.uint32)
+        q = rng.standard_normal((Nq, d))
+        line["cpu_baseline"] = _oracle_leg(
+            lambda: oannsa.annsa_attend(q, kh, vh, cnt, cqs, cks), Nq / H, "query tokens/s",
+            f"AnnSA of the {Nq} queries of one head over {S} slots, {L} x {b}-bit codes", scale=1.0 / H)
     print(json.dumps(line), flush=True)
 
 
@@ -717,6 +751,17 @@ def denoise(args, fa, torch):
                    "slots_per_head_mean": float(n_live.mean()), "chunk_tokens": Nq,
                    "attend_gflop_per_step": flops / 1e9},
     }
+    if not args.no_cpu_baseline:
+        from oracle import denoise as odenoise
+        rng = np.random.default_rng(7)
+        H, d, n_slots = w.heads, w.head_dim, int(n_live.mean())
+        kh, vh, cnt = _random_slots(rng, n_slots, d)
+        q = rng.standard_normal((Nq, d))
+        kn, vn = rng.standard_normal((Nq, d)), rng.standard_normal((Nq, d))
+        line["cpu_baseline"] = _oracle_leg(
+            lambda: odenoise.attend_with_chunk(q, kh, vh, cnt, kn, vn), Nq / H,
+            "query tokens/s", f"one denoising step of the {Nq} queries of one head over {n_slots} "
+            f"slots plus {Nq} chunk tokens, shapes of the GPU workload", scale=1.0 / H)
     print(json.dumps(line), flush=True)
 
 
@@ -789,6 +834,14 @@ def project(args, fa, torch):
                    "keys_bit_identical_to_torch_matmul": same_k,
                    "gemm_gflop": flops / 1e9},
     }
+    if not args.no_cpu_baseline:
+        from oracle import project as oproject
+        rng = np.random.default_rng(9)
+        xs = rng.standard_normal((N, Din))
+        ws = rng.standard_normal((H * d, Din)) / Din ** 0.5
+        line["cpu_baseline"] = _oracle_leg(
+            lambda: oproject.project_keys(xs, ws, H, planes), N, "tokens/s",
+            f"projection and codes of the chunk's {N} tokens for all {H} heads")
     print(json.dumps(line), flush=True)
 
 
@@ -880,6 +933,17 @@ def rope(args, fa, torch):
                                                              for k, v in acc.items()},
                    "slots_per_head_mean": float(n_live.mean())},
     }
+    if not args.no_cpu_baseline:
+        from oracle import rope as orope
+        rng = np.random.default_rng(8)
+        S = int(n_live.mean())
+        kh, vh, cnt = _random_slots(rng, S, d)
+        fr = [list(range(24, 24 - 4, -1))] * S
+        q = rng.standard_normal((cq.shape[1] // 10, d))
+        line["cpu_baseline"] = _oracle_leg(
+            lambda: orope.mdegree_attend(q, kh, vh, cnt, fr, 4, d_t), (cq.shape[1] // 10) / H,
+            "query tokens/s", f"M-degree attention (m = 4) of {cq.shape[1] // 10} queries (every "
+            f"10th) of one head over {S} slots, shapes of the GPU workload", scale=1.0 / H)
     print(json.dumps(line), flush=True)
 
 
