@@ -95,24 +95,27 @@ __global__ __launch_bounds__(PjCfg<D>::kThreads, 1) void project_hash_kernel(Pro
   }
   const int nk = (a.Din + 63) / 64;
   const bool half_tail = (a.Din & 63) != 0;  // the last stage has 32 columns
-  auto issue = [&](int stage, uint8_t* dst) __attribute__((always_inline)) {
-    const bool tail = half_tail && stage == nk - 1;
+  // Copies go through registers: the compiler counts those loads exactly, so
+  // a stage's loads can be issued two compute phases before they are written
+  // to LDS with no conservative waits in between.
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  struct Regs {
+    u32x4_t v[C::kPerWave];
+  };
+  auto load = [&](int stage) __attribute__((always_inline)) {
+    const uint32_t tail = (uint32_t)(half_tail && stage == nk - 1);
+    Regs R;
 #pragma unroll
     for (int j = 0; j < C::kPerWave; ++j) {
-      const int64_t back = tail && ((hi_chunk >> j) & 1u) ? 64 : 0;
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[j] + (int64_t)stage * 128 - back),
-                                       (lds_void_t*)(dst + (wave + j * C::kWaves) * 1024), 16, 0, 0);
+      const int back = (int)(((hi_chunk >> j) & tail) << 6);  // branch free
+      R.v[j] = *reinterpret_cast<const u32x4_t*>(src[j] + (stage * 128 - back));
     }
+    return R;
   };
-  // Wait until at most n stages' copies issued by this wave are in flight
-  // (every older stage has landed), finish this wave's LDS reads, then meet
-  // the other waves.  A plain barrier: __syncthreads() would also wait for
-  // the copies that are meant to stay in flight.
-  auto wait_barrier = [&](int n) __attribute__((always_inline)) {
-    if (n >= 1)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(C::kPerWave) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  auto store = [&](const Regs& R, uint8_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < C::kPerWave; ++j)
+      *reinterpret_cast<u32x4_t*>(dst + (wave + j * C::kWaves) * 1024 + lane * 16) = R.v[j];
   };
 
   f32x16_t acc[C::kFBw][C::kTBw];
@@ -121,11 +124,16 @@ __global__ __launch_bounds__(PjCfg<D>::kThreads, 1) void project_hash_kernel(Pro
 #pragma unroll
     for (int tb = 0; tb < C::kTBw; ++tb) acc[fb][tb] = f32x16_t{};
 
-  // A ring of three stage buffers: step s issues the copy of stage s+2 into
-  // nxt (the buffer read at step s-1), reads stage s from cur, then waits
-  // until stage s+1 has landed, the copy of stage s+2 staying in flight.
-  auto step = [&](const uint8_t* cur, uint8_t* nxt, int s) __attribute__((always_inline)) {
-    if (s + 2 < nk) issue(s + 2, nxt);
+  // Step s: issue the loads of stage s+2 (returned), multiply stage s from
+  // cur, write stage s+1 (loaded at step s-1) from Rp into nxt (read at step
+  // s-1), then meet the other waves.  The registers travel as values so that
+  // they stay in registers; the main loop loads unconditionally so that the
+  // count of loads in flight, and so each wait, is exact.
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, const Regs& Rp, int s, bool may_load,
+                  bool may_store)
+      __attribute__((always_inline)) {
+    Regs Rn{};
+    if (may_load) Rn = load(s + 2);
     const int nks = half_tail && s == nk - 1 ? 2 : 4;  // k-steps of 16 columns
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -148,16 +156,23 @@ __global__ __launch_bounds__(PjCfg<D>::kThreads, 1) void project_hash_kernel(Pro
         for (int tb = 0; tb < C::kTBw; ++tb)
           acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[fb], B[tb], acc[fb][tb], 0, 0, 0);
     }
-    wait_barrier(min(nk - 1, s + 2) - (s + 1));
+    if (may_store) store(Rp, nxt);
+    __syncthreads();
+    return Rn;
   };
-  issue(0, buf0);
-  if (nk > 1) issue(1, buf1);
-  wait_barrier(min(nk, 2) - 1);
-  for (int s = 0; s < nk; s += 3) {
-    step(buf0, buf2, s);
-    if (s + 1 < nk) step(buf1, buf0, s + 1);
-    if (s + 2 < nk) step(buf2, buf1, s + 2);
+  Regs Ra = load(0), Rb{};
+  if (nk > 1) Rb = load(1);
+  store(Ra, buf0);
+  __syncthreads();
+  int s = 0;
+  for (; s + 3 < nk; s += 2) {  // stages s+2 and s+3 exist
+    Ra = step(buf0, buf1, Rb, s, true, true);
+    Rb = step(buf1, buf0, Ra, s + 1, true, true);
   }
+  // 1 to 3 steps remain
+  Ra = step(buf0, buf1, Rb, s, s + 2 < nk, s + 1 < nk);
+  if (s + 1 < nk) step(buf1, buf0, Ra, s + 1, false, s + 2 < nk);
+  if (s + 2 < nk) step(buf0, buf1, Regs{}, s + 2, false, false);
   __syncthreads();  // the ring is read; it now takes the key rows
 
   // bf16 keys into token rows: tokens 0..63 in buf0, 64..127 in buf1 (every
