@@ -380,8 +380,8 @@ def main():
         return measure_traffic(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the TempCache step "
-              "shards by head with no exchange inside the step, and multi-GPU runs are not "
-              "part of this build.", file=sys.stderr)
+              "shards by head with no exchange inside the step, and this library runs it on "
+              "a single GPU.", file=sys.stderr)
         sys.exit(2)
 
     import torch
