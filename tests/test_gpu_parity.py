@@ -211,6 +211,29 @@ def test_eviction_really_happens_in_the_small_budget_case():
     assert sum(h.evicted_tokens for h in orc.heads) > 0
 
 
+def test_maximum_budget_and_frame_size_with_eviction():
+    """The declared maxima: 8192 tokens per frame into 32768 slots per head.
+    Half of each frame is fresh, so the budget fills at frame 6 and frames
+    6-8 evict; the state after frame 8 is bit-exact and the attention of all
+    8192 queries over the 32768 slots matches on 512 sampled queries."""
+    w = WORKLOADS["dit1.3b"].with_(heads=2, tokens_per_frame=8192, budget=32768, p_exact=0.3,
+                                   p_pert=0.2, seed=2024)
+    print(f"maximum sizes: T={w.tokens_per_frame} B={w.budget} H={w.heads}", flush=True)
+    orc, cache, _, Q = _run_frames(w, 9, check_every=False)
+    stats = cache.stats()
+    assert stats["evicted_slots"] > 0
+    for h in range(w.heads):
+        assert orc.heads[h].n_live == w.budget
+        assert orc.heads[h].evicted_tokens > 0
+    out = cache.attend(to_device(Q, w.dtype))
+    torch.cuda.synchronize()
+    rows = np.arange(0, w.tokens_per_frame, 16)
+    O_ref, _ = orc.attend(Q[:, rows])
+    err = np.abs(out.float().cpu().numpy()[:, rows] - O_ref).max()
+    print(f"  evicted slots {stats['evicted_slots']}; attend max-abs on {len(rows)} queries {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("name", ["dit1.3b", "dit1.3b_pq"])
 def test_gpu_hashing_end_to_end_matches_oracle(name):
     """Library hashes the keys itself (bf16 MFMA); decisions still match the oracle."""
