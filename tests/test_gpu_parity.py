@@ -195,6 +195,13 @@ def _run_frames(w, frames, check_every=True, use_gpu_hash=False, rope_members=0)
     ("dit1.3b_pq", dict(heads=2, tokens_per_frame=300, budget=2048), 5),
     ("dit1.3b_pq", dict(heads=2, tokens_per_frame=200, budget=260, subspaces=8, bits=16,
                         seed=82), 5),                            # 4 centroids a slice, eviction
+    # one token per frame into one slot: it merges every frame, or (no
+    # repeated keys) evicts the slot every frame
+    ("dit1.3b", dict(heads=2, tokens_per_frame=1, budget=1, seed=83), 6),
+    ("dit1.3b", dict(heads=2, tokens_per_frame=1, budget=1, p_exact=0.4, p_pert=0.0, seed=83), 10),
+    # zero-bit codes: every live slot is in the one bucket, merges and evictions
+    ("dit1.3b", dict(heads=2, tokens_per_frame=64, budget=200, bits=0, tables=1, p_exact=0.3,
+                     p_pert=0.2, seed=85), 8),
 ])
 def test_match_merge_matches_oracle_given_codes(name, overrides, frames):
     w = WORKLOADS[name].with_(**overrides)
@@ -310,6 +317,8 @@ def test_conservation_on_device():
     ("dit1.3b", dict(heads=2, tokens_per_frame=150, budget=1024, seed=42), 1),
     ("dit1.3b", dict(heads=2, tokens_per_frame=250, budget=1024, seed=43), 1),
     ("dit1.3b", dict(heads=2, tokens_per_frame=300, budget=1024, seed=44), 1),
+    # one query over one live slot (one token per frame, always merged)
+    ("dit1.3b", dict(heads=2, tokens_per_frame=1, budget=5, seed=84), 12),
 ])
 def test_attend_matches_oracle(name, overrides, frames):
     w = WORKLOADS[name].with_(**overrides)
