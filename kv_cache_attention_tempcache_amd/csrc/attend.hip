@@ -32,6 +32,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
+// Logit shifts of a raw-token key tile of 64 rows: 64 zeros, then 64 -inf.
+// A tile with r rows left reads its 64 shifts from entry 64 - r on, so rows
+// past the chunk get -inf by the same LDS copy that brings slot tiles their
+// log2-counts, with no masking in registers.
+constexpr int kRawTile = 64;
+struct RawShifts {
+  float v[2 * kRawTile];
+};
+constexpr RawShifts make_raw_shifts() {
+  RawShifts t{};
+  for (int i = 0; i < 2 * kRawTile; ++i) t.v[i] = i < kRawTile ? 0.0f : -__builtin_huge_valf();
+  return t;
+}
+__device__ const RawShifts raw_shifts = make_raw_shifts();
+
 
 template <int D, bool GATHER>
 __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles) {
@@ -301,14 +316,19 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
       __builtin_amdgcn_global_load_lds((gbl_void_t*)vs, (lds_void_t*)(buf + C::kKBytes + i * 1024),
                                        16, 0, 0);
     }
-    // the bias row (also for raw tiles, whose bias is computed, so that every
-    // tile issues the same copies: any in-bounds row serves)
+    // the bias row: slots' log2-counts, or for a raw tile zeros up to the
+    // chunk's last row and -inf past it
+    static_assert(!RAW || BN == kRawTile, "raw shifts cover one 64-row tile");
+    const float* lsrc = lbg + kr;
+    if (RAW && raw) {
+      const int left = min(max(nx - (k0 - ntc * BN), 0), BN);  // rows of the chunk in the tile
+      lsrc = raw_shifts.v + (BN - left);
+    }
 #pragma unroll
     for (int i = 0; i < (BN + 63) / 64; ++i) {
       if (!SUBSET && wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
-        __builtin_amdgcn_global_load_lds(
-            (gbl_void_t*)(lbg + (raw ? 0 : kr) + i * 64 + (uint32_t)lane),
-            (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(lsrc + i * 64 + (uint32_t)lane),
+                                         (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256), 4, 0, 0);
     }
   };
 
@@ -402,9 +422,9 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        if (SUBSET || (RAW && it >= ntc)) {  // no bias; keys past the kept or raw count are masked
-          const int k = (SUBSET ? it : it - ntc) * BN + kb * 32 + 8 * jg + 4 * hf;
-          const int n = SUBSET ? nkeys : nx;
+        if (SUBSET) {  // no bias; keys past the kept count are masked
+          const int k = it * BN + kb * 32 + 8 * jg + 4 * hf;
+          const int n = nkeys;
           const float ninf = -__builtin_huge_valf();
           lbr[kb][jg] = make_float4(k < n ? 0.0f : ninf, k + 1 < n ? 0.0f : ninf,
                                     k + 2 < n ? 0.0f : ninf, k + 3 < n ? 0.0f : ninf);
