@@ -316,17 +316,18 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
       __builtin_amdgcn_global_load_lds((gbl_void_t*)vs, (lds_void_t*)(buf + C::kKBytes + i * 1024),
                                        16, 0, 0);
     }
-    // the bias row: slots' log2-counts, or for a raw tile zeros up to the
-    // chunk's last row and -inf past it
-    static_assert(!RAW || BN == kRawTile, "raw shifts cover one 64-row tile");
-    const float* lsrc = lbg + kr;
-    if (RAW && raw) {
-      const int left = min(max(nx - (k0 - ntc * BN), 0), BN);  // rows of the chunk in the tile
+    // the bias row: slots' log2-counts, or for a raw or subset tile zeros up
+    // to the last kept row and -inf past it
+    static_assert((!RAW && !SUBSET) || BN == kRawTile, "constant shifts cover one 64-row tile");
+    const float* lsrc = SUBSET ? nullptr : lbg + kr;
+    if (SUBSET || (RAW && raw)) {
+      // rows of the chunk, or of the kept subset, in the tile
+      const int left = min(max(SUBSET ? nkeys - k0 : nx - (k0 - ntc * BN), 0), BN);
       lsrc = raw_shifts.v + (BN - left);
     }
 #pragma unroll
     for (int i = 0; i < (BN + 63) / 64; ++i) {
-      if (!SUBSET && wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
+      if (wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(lsrc + i * 64 + (uint32_t)lane),
                                          (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256), 4, 0, 0);
     }
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   // Copies this wave issues per tile: K and V chunks, plus the bias row for
   // the last wave(s).
   constexpr int kCopies = 2 * C::kKInstr / WAVES;
-  const bool lb_wave = !SUBSET && wave >= WAVES - (BN + 63) / 64;
+  const bool lb_wave = wave >= WAVES - (BN + 63) / 64;
 
   // Wait until at most n tiles' copies issued by this wave are in flight
   // (every older tile has landed), finish this wave's LDS reads, then meet
@@ -422,15 +423,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        if (SUBSET) {  // no bias; keys past the kept count are masked
-          const int k = it * BN + kb * 32 + 8 * jg + 4 * hf;
-          const int n = nkeys;
-          const float ninf = -__builtin_huge_valf();
-          lbr[kb][jg] = make_float4(k < n ? 0.0f : ninf, k + 1 < n ? 0.0f : ninf,
-                                    k + 2 < n ? 0.0f : ninf, k + 3 < n ? 0.0f : ninf);
-        } else {
-          lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
-        }
+        lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
       }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
