@@ -499,6 +499,9 @@ def main():
             "inserted_tokens_per_step": int(post["inserted_tokens"] - pre["inserted_tokens"]),
             "evicted_slots_per_step": int(post["evicted_slots"] - pre["evicted_slots"]),
             "attend_gflop_per_step": attend_flops / 1e9,
+            "step_roofline": _step_roofline(w, int(post["merged_tokens"] - pre["merged_tokens"]),
+                                            int(post["inserted_tokens"] - pre["inserted_tokens"]),
+                                            int(n_live.sum()), ms_per_step),
             "workspace_mb_per_cache": caches[0].workspace.numel() / 2**20,
             "timing_events": ("torch default (system fence)" if args.fenced_events
                               else "hipEventDisableSystemFence"),
@@ -513,6 +516,40 @@ def main():
         heads = args.cpu_heads or (1 if w.subspaces else w.heads if w.heads <= 12 else 2)
         res["cpu_baseline"] = cpu_baseline(w, [(K, V, Q) for K, V, Q in frames], planes, heads)
     print(json.dumps(res), flush=True)
+
+
+def _step_roofline(w, merged, inserted, live_slots, step_ms):
+    """Time one step needs at the roofline: for every kernel the larger of its
+    algorithmic flops over the bf16 MFMA peak and its algorithmic bytes over
+    the HBM peak, summed over the step's launches; and that over the measured
+    step time.  Bytes per unit (storage bf16, fp32 masters): hash 2d + 4L per
+    new key; match 4d + 4L + 8 per token (its key, codes, one candidate row,
+    the decision); plan 16 per token; apply 24d + 16 + 4L per merged token
+    and 16d + 16 + 4L per inserted one (inputs, masters read and written,
+    mirrors, counters, codes); index 12 per live slot and table plus the
+    bucket offsets; attend Q and O once, every live slot's K, V and shift once.
+    The index and attend terms use the live count at attend time (an upper
+    bound for the earlier frames)."""
+    d, L, H, F, T = w.head_dim, w.tables, w.heads, w.frames_per_chunk, w.tokens_per_frame
+    nb = 6
+    while (1 << nb) * 4 < w.budget:
+        nb += 1
+    hbm = PEAK_HBM_GBS * 1e9
+    mfma = PEAK_BF16_TFLOPS * 1e12
+    nbytes = {
+        "hash": H * F * T * (2 * d + 4 * L),
+        "match": H * F * T * (4 * d + 4 * L + 8),
+        "plan": H * F * T * 16,
+        "apply": merged * (24 * d + 16 + 4 * L) + inserted * (16 * d + 16 + 4 * L),
+        "index": F * (live_slots * L * 12 + H * L * ((1 << nb) + 1) * 4),
+        "attend": H * F * T * d * 2 * 2 + live_slots * (d * 2 * 2 + 4),
+    }
+    flops = {"hash": 2 * d * L * w.bits * H * F * T, "attend": 4 * F * T * live_slots * d}
+    us = {k: max(b / hbm, flops.get(k, 0) / mfma) * 1e6 for k, b in nbytes.items()}
+    total = sum(us.values())
+    return {"bound_us": {k: round(v, 2) for k, v in us.items()}, "bound_us_total": total,
+            "measured_us": step_ms * 1e3, "frac": total / (step_ms * 1e3),
+            "algorithmic_bytes": nbytes}
 
 
 def annca(args, fa, torch):
