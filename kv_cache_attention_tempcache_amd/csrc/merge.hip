@@ -554,9 +554,11 @@ __global__ __launch_bounds__(256) void finalize_kernel(Dims dm, CacheDev c) {
 
 hipError_t launch_plan(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.T * 3 * 4;  // 96 KiB at FASTAR_MAX_TOKENS_PER_FRAME
-  hipError_t e = hipFuncSetAttribute((const void*)plan_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
+  if (lds > 64 * 1024) {  // beyond the default dynamic LDS limit of a launch
+    hipError_t e = hipFuncSetAttribute((const void*)plan_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(plan_kernel, dim3(dm.H), dim3(kPlanThreads), lds, s, dm, c, a);
   return hipGetLastError();
 }
