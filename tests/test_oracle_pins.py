@@ -25,9 +25,10 @@ def _load(golden_dir, name):
         return json.load(f)
 
 
-def _cache_from(g):
-    return HeadCache(g["head_dim"], g["budget"], g["tables"], g["bits"], g["threshold"],
-                     "f32", np.array(g["planes"], dtype=np.float64))
+def _cache_from(g, threshold=None):
+    return HeadCache(g["head_dim"], g["budget"], g["tables"], g["bits"],
+                     g["threshold"] if threshold is None else threshold,
+                     g.get("dtype", "f32"), np.array(g["planes"], dtype=np.float64))
 
 
 def _sdpa(q, k, v, scale=None, mask=None):
@@ -140,6 +141,95 @@ def test_lru_eviction_golden(golden_dir):
     assert res[2].evicted == e["evicted_frame2"]
     assert hc.count[:3].tolist() == e["count"] and hc.last[:3].tolist() == e["last"]
     assert hc.evicted_tokens == e["evicted_tokens"] and hc.n_live == e["n_live"]
+
+
+def test_rehash_from_mirror_golden(golden_dir):
+    """A merge moves the bf16 mirror across a hyperplane: the slot's codes and the
+    next frame's candidates follow the mirror, not the master or the old codes."""
+    g = _load(golden_dir, "rehash_mirror.json")
+    hc = _cache_from(g)
+    e = g["expected"]
+    res = []
+    for f, fr in enumerate(g["frames"]):
+        res.append(hc.process_frame(np.array(fr["keys"]), np.array(fr["values"])))
+        assert hc.codes[:hc.n_live].tolist() == e["codes_after_frame"][f], f
+    assert res[1].merged.tolist() == e["merged_frame1"]
+    assert hc.K_m[0].tolist() == e["K_m_slot0"]
+    assert hc.k_hat[0].tolist() == e["k_hat_slot0"]
+    assert hc.V_m[0].tolist() == e["V_m_slot0"]
+    assert res[2].best_slot.tolist() == e["best_slot_frame2"]
+    assert res[2].n_candidates.tolist() == e["n_candidates_frame2"]
+    assert res[2].merged.tolist() == e["merged_frame2"]
+    np.testing.assert_allclose(res[2].best_cos, e["best_cos_frame2"], rtol=0, atol=1e-15)
+    assert res[2].slot.tolist() == e["slot_frame2"]
+    assert hc.count[:hc.n_live].tolist() == e["count"] and hc.n_live == e["n_live"]
+
+
+def test_zero_key_golden(golden_dir):
+    """A zero-norm key has cosine 0: inserted at threshold 0.95, merged at 0."""
+    g = _load(golden_dir, "zero_key.json")
+    for case in g["cases"]:
+        hc = _cache_from(g, threshold=case["threshold"])
+        for f, fr in enumerate(g["frames"][:case["frames"]]):
+            r = hc.process_frame(np.array(fr["keys"]), np.array(fr["values"]))
+            assert r.best_slot.tolist() == case["best_slot"][f]
+            want = [np.nan if c is None else c for c in case["best_cos"][f]]
+            np.testing.assert_array_equal(r.best_cos, np.array(want))
+            assert r.n_candidates.tolist() == case["n_candidates"][f]
+            assert r.merged.tolist() == case["merged"][f]
+            assert r.slot.tolist() == case["slot"][f]
+        assert hc.count[:hc.n_live].tolist() == case["count"] and hc.n_live == case["n_live"]
+        if "K_m_slot0" in case:
+            assert hc.K_m[0].tolist() == case["K_m_slot0"]
+            assert hc.V_m[0].tolist() == case["V_m_slot0"]
+            assert hc.codes[0].tolist() == case["codes_slot0"]
+
+
+def _codes_by_loops(key, planes):
+    """SimHash code of one key with explicit loops over tables, bits and features."""
+    L, b, d = planes.shape
+    code, margin = [], math.inf
+    for t in range(L):
+        word = 0
+        for j in range(b):
+            acc = 0.0
+            for k in range(d):
+                acc += float(planes[t, j, k]) * float(key[k])
+            margin = min(margin, abs(acc))
+            if acc > 0.0:
+                word |= 1 << j
+        code.append(word)
+    return code, margin
+
+
+def test_slot_codes_are_the_mirror_keys_codes_every_frame():
+    """After every frame, each live slot's stored codes equal SimHash of its bf16
+    mirror key, recomputed here by plain loops (merged slots were re-hashed, the
+    inserted ones carry their token's codes, which is the same thing since a new
+    slot's mirror is the token's key)."""
+    w = WORKLOADS["dit1.3b"].with_(heads=1, tokens_per_frame=96, budget=400, head_dim=64,
+                                  tables=2, bits=16)
+    st = DriftStream(w)
+    planes = np.asarray(st.planes(), dtype=np.float64).reshape(w.tables, w.bits, w.head_dim)
+    hc = TempCacheOracle.for_workload(w, st.planes()).heads[0]
+    checked_merged = 0
+    for f in range(6):
+        K, V, _, _ = st.next_frame()
+        res = hc.process_frame(K[0], V[0])
+        merged_slots = set(res.best_slot[res.merged].tolist())
+        for s in range(hc.n_live):
+            code, margin = _codes_by_loops(hc.k_hat[s], planes)
+            if margin < 1e-9:            # loop and matmul round differently at ~0
+                continue
+            assert hc.codes[s].tolist() == code, (f, s)
+            checked_merged += s in merged_slots
+    # the master and the mirror of merged slots differ; the check above must
+    # have seen many merged slots, and the masters must hash differently often
+    # enough that a re-hash from the master would be caught
+    assert checked_merged > 200
+    S = hc.n_live
+    differs = (simhash(hc.K_m[:S], planes)[0] != simhash(hc.k_hat[:S], planes)[0]).any(axis=1)
+    assert differs.sum() >= 1
 
 
 # ---------------------------------------------------------------- Lemma 5.1
@@ -487,6 +577,15 @@ def test_pq_small_golden(golden_dir):
     g = _load(golden_dir, "pq_small.json")
     codes, _ = opq.pq_codes(np.array(g["inputs"]), np.array(g["codebooks"], dtype=np.float64))
     assert codes.tolist() == g["expected_codes"]
+
+
+def test_pq_ambiguous_golden(golden_dir):
+    g = _load(golden_dir, "pq_ambiguous.json")
+    C = np.array(g["codebooks"], dtype=np.float64)
+    rows = np.array(g["rows"], dtype=np.float64)
+    codes, _ = opq.pq_codes(rows, C)
+    assert codes.tolist() == g["expected_codes"]
+    assert opq.ambiguous_codes(rows, C).tolist() == g["expected_ambiguous"]
 
 
 def test_pq_codes_match_scipy_vq():
