@@ -102,10 +102,15 @@ typedef struct {
   int64_t evicted_slots;   /* slots evicted to make room                      */
   int64_t evicted_tokens;  /* tokens those slots held (sum of their counts)   */
   int32_t max_live;        /* largest n_live over heads                       */
-  int32_t reserved;
+  int32_t refused_frames;  /* (head, frame) pairs the merge refused because
+                            * fewer slots were evictable than its inserts
+                            * needed; such a frame changes nothing.  Stays 0
+                            * for states built by the library or accepted by
+                            * fastar_cache_import.                           */
 } fastar_stats;
 
-/* Host-side image of a cache's state; any pointer may be NULL to skip it.
+/* Host-side image of a cache's state; any pointer may be NULL to skip it, and
+ * frame = -1 skips the frame counter (next frame to merge).
  * Shapes: k/v_master float [H][B][d]; k/v_mirror dtype [H][B][d];
  * count, last int32 [H][B]; codes uint32 [H][L][B]; n_live int32 [H];
  * evicted_tokens int64 [H]; member_frames int32 [H][B][rope_members]: the
@@ -128,10 +133,16 @@ typedef struct {
 /* Thread-local text of the last error (empty string if none). */
 const char* fastar_last_error(void);
 
-/* Bytes of device workspace a cache with this configuration needs (host only). */
+/* Bytes of device workspace a cache with this configuration needs (host only).
+ * The size depends only on the configuration, never on how many frames are
+ * merged: the cache is bounded so memory stays constant over a rollout
+ * (section 2A "Benefício"). */
 fastar_status fastar_cache_workspace_bytes(const fastar_config* cfg, size_t* bytes);
 
-/* Create a cache in caller-provided device memory.
+/* Create a cache in caller-provided device memory (section 2A "Benefício": a
+ * fixed budget of slots per head holds the merged groups, so this one
+ * workspace serves a rollout of any length; "Mecanismo": the LSH hyperplanes
+ * the cache hashes with are fixed at creation).
  * planes_host: the SimHash hyperplanes, [L][b][d] in cfg->dtype, or with
  * pq_subspaces = M > 0 the product-quantization codebooks [L][M][2^(b/M)][d/M];
  * copied into the workspace.  workspace_dev: at least fastar_cache_workspace_bytes bytes,
@@ -143,14 +154,21 @@ fastar_status fastar_cache_create(const fastar_config* cfg, const void* planes_h
                                   void* workspace_dev, size_t workspace_bytes, void* stream,
                                   fastar_cache_t* out);
 
-/* Free the host handle (the workspace stays the caller's). */
+/* Free the host handle (the workspace stays the caller's).  Library plumbing:
+ * the pages describe no API. */
 fastar_status fastar_cache_destroy(fastar_cache_t cache);
 
-/* Empty the cache (state zeroed, frame = 0) on `stream`. */
+/* Empty the cache (state zeroed, frame = 0) on `stream`: the start of a new
+ * rollout, whose first frame has no earlier frames to match (section 2A
+ * "Mecanismo").  Changes the cache, so an AnnSA index built before it is
+ * refused afterwards. */
 fastar_status fastar_cache_reset(fastar_cache_t cache, void* stream);
 
 /* Device pointer of the cache's hyperplanes ([L][b][d], cfg dtype), or of its
- * product-quantization codebooks ([L][M][2^(b/M)][d/M]) when pq_subspaces > 0. */
+ * product-quantization codebooks ([L][M][2^(b/M)][d/M]) when pq_subspaces > 0
+ * (section 2A "Mecanismo": the same LSH family hashes the new keys, e.g. with
+ * fastar_hash, and the cached ones).  The pointer stays owned by the cache and
+ * valid until its workspace is freed. */
 fastar_status fastar_cache_planes(fastar_cache_t cache, const void** planes_dev);
 
 /* SimHash codes of H x N vectors (section 2A "Mecanismo": LSH as the ANN).
@@ -283,14 +301,23 @@ fastar_status fastar_annsa_attend(fastar_cache_t cache, const void* q_dev, int64
                                   int32_t L, float scale, void* o_dev, int64_t o_stride_h,
                                   int64_t o_stride_n, float* lse_dev, void* stream);
 
-/* Totals over heads.  Synchronises `stream`. */
+/* Totals over heads (section 2A "Benefício": the live-slot and eviction counts
+ * show the cache staying within its budget).  Library plumbing for tests and
+ * monitoring; synchronises `stream`. */
 fastar_status fastar_cache_stats(fastar_cache_t cache, void* stream, fastar_stats* out);
 
-/* Copy the state to host buffers.  Synchronises `stream`. */
+/* Copy the state to host buffers (library plumbing for checkpoints and tests;
+ * the pages describe no API).  Buffers are the caller's, shaped as in
+ * fastar_cache_state; NULL members are skipped.  Synchronises `stream`. */
 fastar_status fastar_cache_export(fastar_cache_t cache, void* stream, fastar_cache_state* out);
 
-/* Overwrite the state from host buffers (NULL members keep the current
- * contents), then rebuild the bucket index.  Synchronises `stream`. */
+/* Overwrite the state from host buffers, for resume and tests (library
+ * plumbing; the pages describe no API).  NULL members and frame = -1 keep the
+ * current contents; then the bucket index is rebuilt.  The state it would leave
+ * is checked first (members not given are read back from the device): n_live
+ * in [0, budget], and every live slot s < n_live with count >= 1 and last in
+ * [0, frame).  A state that fails returns FASTAR_ERR_INVALID_ARGUMENT and
+ * leaves the cache unchanged.  Synchronises `stream`. */
 fastar_status fastar_cache_import(fastar_cache_t cache, const fastar_cache_state* in, void* stream);
 
 /* AnnCA selection (section 2B: keep the prompt tokens that share a bucket with

@@ -52,7 +52,7 @@ class Stats(ctypes.Structure):
                 ("live_slots", ctypes.c_int64), ("merged_tokens", ctypes.c_int64),
                 ("inserted_tokens", ctypes.c_int64), ("evicted_slots", ctypes.c_int64),
                 ("evicted_tokens", ctypes.c_int64), ("max_live", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("refused_frames", ctypes.c_int32)]
 
 
 class State(ctypes.Structure):
@@ -441,7 +441,7 @@ class Cache:
     def stats(self, stream=None) -> dict:
         st = Stats()
         _check(library().fastar_cache_stats(self._h, _stream(stream), ctypes.byref(st)))
-        return {name: getattr(st, name) for name, _ in Stats._fields_ if name != "reserved"}
+        return {name: getattr(st, name) for name, _ in Stats._fields_}
 
     def export_state(self, stream=None) -> dict:
         c = self.cfg
@@ -485,7 +485,8 @@ class Cache:
                 raise ValueError(f"{name} must have shape {shape}, got {a.shape}")
             keep[name] = a
             ptrs[name] = a.ctypes.data
-        st = State(**ptrs, frame=int(state.get("frame", 0)))
+        # no "frame" key keeps the device's frame counter (-1)
+        st = State(**ptrs, frame=int(state.get("frame", -1)))
         _check(library().fastar_cache_import(self._h, ctypes.byref(st), _stream(stream)))
 
 

@@ -409,7 +409,6 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
                                  int32_t* slot_out_dev, uint8_t* merged_out_dev, void* stream) {
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
-  ++c->version;
   const Dims& dm = c->dm;
   const int T = tokens_per_frame, F = num_frames;
   FASTAR_REQUIRE(T >= 1 && F >= 1, "tokens_per_frame and num_frames must be >= 1");
@@ -422,6 +421,8 @@ fastar_status fastar_match_merge(fastar_cache_t c, const void* k_dev, const void
   FASTAR_REQUIRE(stride_h % vec == 0 && stride_n % vec == 0 && stride_n >= dm.d,
                  "strides must be multiples of 16 bytes and rows must not overlap");
   FASTAR_REQUIRE(codes_dev == nullptr || aligned(codes_dev, 4), "codes misaligned");
+  // every check passed: from here on the slot state changes
+  ++c->version;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const CacheDev& dev = c->dev;
   const int64_t N = (int64_t)T * F;
@@ -744,6 +745,7 @@ fastar_status fastar_cache_stats(fastar_cache_t c, void* stream, fastar_stats* o
     r.merged_tokens += cn[h * kNumCounters + kCntMerged];
     r.inserted_tokens += cn[h * kNumCounters + kCntInserted];
     r.evicted_slots += cn[h * kNumCounters + kCntEvictedSlots];
+    r.refused_frames += (int32_t)cn[h * kNumCounters + kCntRefused];
   }
   *out = r;
   return ok();
@@ -785,17 +787,42 @@ fastar_status fastar_cache_export(fastar_cache_t c, void* stream, fastar_cache_s
 fastar_status fastar_cache_import(fastar_cache_t c, const fastar_cache_state* in, void* stream) {
   fastar_status st = check_handle(c);
   if (st != FASTAR_OK) return st;
-  ++c->version;
   FASTAR_REQUIRE(in != nullptr, "in is NULL");
-  FASTAR_REQUIRE(in->frame >= 0 && in->frame < INT32_MAX, "frame out of range");
+  FASTAR_REQUIRE(in->frame >= -1 && in->frame < INT32_MAX,
+                 "frame out of range (-1 keeps the current frame counter)");
   const Dims& dm = c->dm;
-  if (in->n_live) {
-    for (int h = 0; h < dm.H; ++h)
-      FASTAR_REQUIRE(in->n_live[h] >= 0 && in->n_live[h] <= dm.B, "n_live out of range");
-  }
   const CacheDev& d = c->dev;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t HBd = (size_t)dm.H * dm.B * dm.d, HB = (size_t)dm.H * dm.B;
+  // The merge step relies on every live slot holding at least one token and
+  // having been updated before the current frame (so eviction always finds
+  // room).  Check that on the state as it will be after the import: members
+  // not given are read back from the device first.
+  std::vector<int32_t> n_live(dm.H), count(HB), last(HB);
+  int32_t frame = (int32_t)in->frame;
+  if (!in->n_live) FASTAR_HIP(hipMemcpyAsync(n_live.data(), d.n_live, (size_t)dm.H * 4,
+                                             hipMemcpyDeviceToHost, s));
+  if (!in->count) FASTAR_HIP(hipMemcpyAsync(count.data(), d.count, HB * 4, hipMemcpyDeviceToHost, s));
+  if (!in->last) FASTAR_HIP(hipMemcpyAsync(last.data(), d.last, HB * 4, hipMemcpyDeviceToHost, s));
+  if (in->frame < 0) FASTAR_HIP(hipMemcpyAsync(&frame, d.frame, 4, hipMemcpyDeviceToHost, s));
+  FASTAR_HIP(hipStreamSynchronize(s));
+  if (in->n_live) std::memcpy(n_live.data(), in->n_live, (size_t)dm.H * 4);
+  if (in->count) std::memcpy(count.data(), in->count, HB * 4);
+  if (in->last) std::memcpy(last.data(), in->last, HB * 4);
+  for (int h = 0; h < dm.H; ++h) {
+    FASTAR_REQUIRE(n_live[h] >= 0 && n_live[h] <= dm.B,
+                   "n_live[" + std::to_string(h) + "] out of range");
+    for (int sl = 0; sl < n_live[h]; ++sl) {
+      const size_t i = (size_t)h * dm.B + sl;
+      FASTAR_REQUIRE(count[i] >= 1, "live slot " + std::to_string(sl) + " of head " +
+                                        std::to_string(h) + " has count < 1");
+      FASTAR_REQUIRE(last[i] >= 0 && last[i] < frame,
+                     "live slot " + std::to_string(sl) + " of head " + std::to_string(h) +
+                         " has a last-update frame outside [0, frame)");
+    }
+  }
+  // every check passed: from here on the slot state changes
+  ++c->version;
   auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
     return src ? hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s) : hipSuccess;
   };
@@ -814,8 +841,7 @@ fastar_status fastar_cache_import(fastar_cache_t c, const fastar_cache_state* in
   FASTAR_HIP(cp(d.n_live, in->n_live, (size_t)dm.H * 4));
   FASTAR_HIP(cp(d.evicted_tokens, in->evicted_tokens, (size_t)dm.H * 8));
   if (dm.R > 0) FASTAR_HIP(cp(d.hist, in->member_frames, HB * dm.R * 4));
-  const int32_t frame = (int32_t)in->frame;
-  FASTAR_HIP(hipMemcpyAsync(d.frame, &frame, 4, hipMemcpyHostToDevice, s));
+  if (in->frame >= 0) FASTAR_HIP(hipMemcpyAsync(d.frame, &frame, 4, hipMemcpyHostToDevice, s));
   FASTAR_HIP(launch_finalize_state(dm, d, s));
   FASTAR_HIP(launch_index(dm, d, false, s));
   FASTAR_HIP(hipStreamSynchronize(s));

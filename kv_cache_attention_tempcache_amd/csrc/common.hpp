@@ -76,8 +76,13 @@ __device__ __forceinline__ uint32_t extract_code(const uint32_t (&w)[9], int off
 
 // ---------------------------------------------------------------- cache layout
 // Per-head counters (int64): tokens seen, merged tokens, inserted tokens,
-// evicted slots.
-enum { kCntTokens = 0, kCntMerged = 1, kCntInserted = 2, kCntEvictedSlots = 3, kNumCounters = 4 };
+// evicted slots, and frames the planning step refused because fewer slots
+// were evictable than the inserts needed (only an inconsistent state can do
+// that; the refused frame changes nothing).
+enum {
+  kCntTokens = 0, kCntMerged = 1, kCntInserted = 2, kCntEvictedSlots = 3, kCntRefused = 4,
+  kNumCounters = 5
+};
 // Per-head plan summary written by the planning kernel of each frame (int32).
 enum { kPlanGroups = 0, kPlanInserts = 1, kPlanMergeTokens = 2, kPlanEvict = 3, kPlanStride = 8 };
 constexpr int32_t kNoOwner = 0x7fffffff;

@@ -59,6 +59,7 @@ __device__ V block_excl_scan(V v, V* s_scan, V& total) {
 
 struct PlanShared {
   int digit, krem;
+  int refused;  // fewer evictable slots than needed: the frame changes nothing
   unsigned long long evicted_count;
 };
 
@@ -143,6 +144,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   // 3. eviction, only if the inserts do not fit: exactly `need` slots not
   //    merged into in this frame (owner unset), smallest (last, slot) first
   const int need = max(0, m - (B - n_live));
+  if (tid == 0) ps.refused = 0;
   if (need > 0) {
     if (tid == 0) {
       ps.krem = need;
@@ -202,7 +204,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
     }
     int ev_total = 0;
     int ep = block_excl_scan<int>(evc, s_scan, ev_total);
-    {
+    // With tokens_per_frame <= budget and every live slot's last update
+    // before this frame (both checked on the host), the eligible slots always
+    // cover `need`.  Otherwise ev_list would be short: refuse the frame.
+    if (ev_total < need) {
+      if (tid == 0) ps.refused = 1;
+    } else {
       int er = eq_base;
       unsigned long long tok = 0ull;
       const int32_t* count = c.count + (int64_t)h * B;
@@ -230,6 +237,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
     const int s = dec_s[i];
     owner[s] = kNoOwner;
     gsize[s] = 0;
+  }
+
+  if (ps.refused) {
+    if (tid == 0) {
+      c.counters[(int64_t)h * kNumCounters + kCntRefused] += 1;
+      int32_t* pl = c.plan + (int64_t)h * kPlanStride;
+      pl[kPlanGroups] = 0;
+      pl[kPlanInserts] = 0;
+      pl[kPlanMergeTokens] = 0;
+      pl[kPlanEvict] = 0;
+    }
+    if (a.slot_out != nullptr || a.merged_out != nullptr) {
+      for (int i = tid; i < T; i += kPlanThreads) {
+        const int64_t o = (int64_t)h * a.out_ld + a.out_col0 + i;
+        if (a.slot_out) a.slot_out[o] = -1;
+        if (a.merged_out) a.merged_out[o] = 0;
+      }
+    }
+    return;
   }
 
   // 5. slots for the inserts: evicted ids first, then never-used ids, ascending

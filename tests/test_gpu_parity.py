@@ -934,3 +934,45 @@ def test_annsa_refuses_a_stale_index():
     with pytest.raises(fa.FastarError):
         cache.annsa_attend(q, qc)                      # the cache changed since
     torch.cuda.synchronize()
+
+
+def test_rejected_calls_leave_the_state_and_the_annsa_index_intact():
+    """Argument errors are found before anything changes: a refused
+    match_merge or import leaves the slot state as it was, and an AnnSA index
+    built before it stays usable."""
+    w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=100, budget=512, seed=60), 3)
+    H, Nq = w.heads, Q.shape[1]
+    q, qc = to_device(Q, w.dtype), _codes_dev(np.zeros((H, 2, Nq)))
+    cache.hash_slots(to_device(_annsa_planes(2, 8, w.head_dim, 60), "bf16").contiguous(), 2, 8)
+    ref = cache.annsa_attend(q, qc).float().cpu()
+    before = cache.export_state()
+    # more tokens in a frame than the budget: refused on the host
+    K = to_device(np.zeros((H, 600, w.head_dim), np.float32), w.dtype)
+    with pytest.raises(fa.FastarError):
+        cache.match_merge(K, K, 600, 1)
+    good = oracle_state_for_import(orc, w.dtype)
+    bad_count = {k: v.copy() if isinstance(v, np.ndarray) else v for k, v in good.items()}
+    bad_count["count"][1, 5] = 0                       # a live slot with no token
+    bad_last = {k: v.copy() if isinstance(v, np.ndarray) else v for k, v in good.items()}
+    bad_last["last"][0, 7] = good["frame"]             # updated "at" the next frame
+    bad_nlive = {"n_live": np.array([513, 3], np.int32)}
+    stale_frame = {"frame": 0}                         # live slots updated at frames 0..2
+    for bad in (bad_count, bad_last, bad_nlive, stale_frame):
+        with pytest.raises(fa.FastarError):
+            cache.import_state(bad)
+    after = cache.export_state()
+    for k in before:
+        np.testing.assert_array_equal(np.asarray(after[k]), np.asarray(before[k]), err_msg=k)
+    again = cache.annsa_attend(q, qc).float().cpu()     # the index is still current
+    torch.cuda.synchronize()
+    assert torch.equal(again, ref)
+    assert cache.stats()["refused_frames"] == 0
+
+
+def test_import_without_frame_keeps_the_frame_counter():
+    w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=100, budget=512, seed=61), 3)
+    frame = cache.stats()["frame"]
+    assert frame == 3
+    st = cache.export_state()
+    cache.import_state({"codes": st["codes"]})
+    assert cache.stats()["frame"] == frame
