@@ -5,16 +5,18 @@ SimHash of the chunk's keys, then per frame match -> merge/evict/insert ->
 re-hash -> bucket-index rebuild, then attention of the chunk's queries over the
 merged cache with the ln(count) bias.
 
-Default workload: one attention layer shaped like a 1.3B video DiT (12 heads,
-d=128, 1560 tokens/frame, chunks of 3 frames = 4680 queries, bf16, SimHash
-4 tables x 32 bits, threshold 0.95, 8192 slots/head), cache pre-filled with 21
-frames of the drift model (60% exact, 30% perturbed, 10% fresh).  Every timed
+Default workload: one attention layer shaped like a 14B video DiT (40 heads,
+d=128, 3600 tokens/frame, chunks of 3 frames = 10800 queries, bf16, SimHash
+4 tables x 32 bits, threshold 0.95, 16384 slots/head), cache pre-filled with 21
+frames of the drift model (50% exact, 35% perturbed, 15% fresh).  Every timed
 step processes the chunk of frames 21-23 on its own copy of the pre-filled
 cache, so all steps do identical work; the copies are made before the timed
-region and every input is resident in HBM.
+region and every input is resident in HBM.  The line's `detail` also carries
+the 1.3B-layer step, the tiny fp32 step, the 240-frame rollout's per-chunk
+latency and memory, and the chunk's hash bits against the CPU oracle.
 
-Prints one JSON line (rank 0).  `--workload rollout` instead streams 240
-frames through one cache and prints per-chunk latency and memory.
+Prints one JSON line (rank 0).  Other workloads (`--workload`): dit1.3b,
+dit1.3b_pq, rollout, annca, annsa, denoise, project, rope.
 """
 
 from __future__ import annotations
@@ -42,12 +44,14 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="dit1.3b",
+    p.add_argument("--workload", default="dit14b",
                    choices=["dit1.3b", "dit1.3b_pq", "dit14b", "rollout", "annca", "annsa",
                             "denoise", "project", "rope"])
     p.add_argument("--annsa-bits", type=int, default=16, help="bits per table of the AnnSA buckets")
     p.add_argument("--denoise-steps", type=int, default=4, help="denoising steps per chunk")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--headline-only", action="store_true",
+                   help="dit14b: skip the 1.3B-layer step, tiny step and rollout in the detail")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads the CPU oracle times (0 = all for dit1.3b, 2 for dit14b, 1 with PQ codes)")
     p.add_argument("--frames", type=int, default=240, help="rollout length")
@@ -180,8 +184,14 @@ def _random_slots(rng, S, d):
             rng.integers(1, 12, size=S))
 
 
-def cpu_baseline(w, frames, planes, heads):
-    """Time the CPU oracle (as it stands) on one chunk step of `heads` heads."""
+def cpu_baseline(w, frames, planes, heads, gpu_codes=None):
+    """Time the CPU oracle (as it stands) on one chunk step of `heads` heads.
+
+    With `gpu_codes` ([heads][L][chunk tokens], the library's SimHash codes of
+    the chunk's keys), also count the hash bits where they differ from the
+    oracle's, split by whether the oracle's float64 projection is below 1e-4
+    in magnitude (ambiguous) or not.  Returns (baseline, bit counts or None).
+    """
     from oracle import TempCacheOracle
     try:
         from threadpoolctl import threadpool_info
@@ -195,15 +205,15 @@ def cpu_baseline(w, frames, planes, heads):
         orc.process_frame(K[hs], V[hs])
         print(f"cpu baseline: prefill frame {f} done", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    Qs = []
+    Qs, results = [], []
     for f in range(w.prefill_frames, w.prefill_frames + w.frames_per_chunk):
         K, V, Q = frames[f]
-        orc.process_frame(K[hs], V[hs])
+        results.append(orc.process_frame(K[hs], V[hs]))
         Qs.append(Q[hs])
     orc.attend(np.concatenate(Qs, axis=1))
     dt = time.perf_counter() - t0
     full = dt * w.heads / len(hs)
-    return {
+    base = {
         "value": w.chunk_tokens / full,
         "unit": "query tokens/s",
         "cores": int(blas_threads),
@@ -215,6 +225,29 @@ def cpu_baseline(w, frames, planes, heads):
                    f"{blas_threads} BLAS threads; host '{_cpu_info()}', "
                    f"{len(os.sched_getaffinity(0))} cores visible"),
     }
+    if gpu_codes is None:
+        return base, None
+    T = w.tokens_per_frame
+    total = differ = differ_amb = amb = 0
+    for fi, res in enumerate(results):
+        for h in hs:
+            fr = res[h]
+            got = gpu_codes[h][:, fi * T:(fi + 1) * T].T.astype(np.uint64)   # [T][L]
+            want = fr.codes.astype(np.uint64)
+            ambig = np.abs(fr.proj) < 1e-4                                   # [T][L][b]
+            for j in range(w.bits):
+                bit = np.uint64(1) << np.uint64(j)
+                dif = ((got & bit) != (want & bit))
+                a = ambig[:, :, j]
+                total += dif.size
+                differ += int(dif.sum())
+                differ_amb += int((dif & a).sum())
+                amb += int(a.sum())
+    return base, {"heads_checked": len(hs), "tokens_per_head": w.chunk_tokens,
+                  "bits_compared": total, "ambiguous_bits": amb,
+                  "differing_bits": differ, "differing_ambiguous": differ_amb,
+                  "differing_not_ambiguous": differ - differ_amb,
+                  "rule": "bits may differ only where the oracle's float64 |projection| < 1e-4"}
 
 
 ATTEND_SRC = os.path.join(ROOT, "kv_cache_attention_tempcache_amd", "csrc", "attend.hip")
@@ -410,9 +443,14 @@ def main():
     if args.workload == "rope":
         return rope(args, fa, torch)
 
-    w = WORKLOADS[args.workload]
+    return step_line(args, fa, torch, WORKLOADS[args.workload])
+
+
+def _measure_step(args, fa, torch, w, steps, warmup):
+    """Time `steps` chunk steps of workload `w` (each on its own copy of the
+    prefilled cache) after `warmup` untimed ones; returns the measurements."""
     T, F = w.tokens_per_frame, w.frames_per_chunk
-    nrep = args.warmup + args.steps
+    nrep = warmup + steps
     base, caches, (ck, cv, cq), frames, planes = _build_step_caches(fa, torch, w, nrep)
     pre = base.stats()
     out = torch.empty_like(cq)
@@ -431,45 +469,181 @@ def main():
         c.attend(cq, out=out)
         ev.record(2 * i + 1)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, nrep):
+    for i in range(warmup, nrep):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    timed = range(args.warmup, nrep)
+    timed = range(warmup, nrep)
     attend_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in timed]
     # (from the second timed step: the first follows the host-side sync)
-    merge_ms = [ev.elapsed_ms(2 * i - 1, 2 * i) for i in range(args.warmup + 1, nrep)]
+    merge_ms = [ev.elapsed_ms(2 * i - 1, 2 * i) for i in range(warmup + 1, nrep)]
     ev.close()
     post = caches[-1].stats()
     # every copy did identical work
     assert all(c.stats()["live_slots"] == post["live_slots"] for c in caches[:2])
     ex = caches[-1].export_state()
     n_live = ex["n_live"].astype(np.int64)
-    ms_per_step = elapsed * 1e3 / args.steps
-    qps = w.chunk_tokens * args.steps / elapsed
-
+    ms_per_step = elapsed * 1e3 / steps
     # attention: algorithmic flops = 4 * Nq * S_h * d summed over heads (QK^T and PV)
     attend_flops = float(4 * w.chunk_tokens * n_live.sum() * w.head_dim)
     attend_avg_s = float(np.mean(attend_ms)) / 1e3
-    attend_tflops = attend_flops / attend_avg_s / 1e12
-    # algorithmic HBM bytes of one attend launch: Q and O once, every live
-    # slot's K and V rows and its log2-count once per head
-    attend_bytes = float(w.heads * w.chunk_tokens * w.head_dim * 2 * 2 +
-                         n_live.sum() * (w.head_dim * 2 * 2 + 4))
+    merged = int(post["merged_tokens"] - pre["merged_tokens"])
+    inserted = int(post["inserted_tokens"] - pre["inserted_tokens"])
+    r = {
+        "qps": w.chunk_tokens * steps / elapsed,
+        "ms_per_step": ms_per_step,
+        "attend_ms": attend_ms,
+        "merge_ms": merge_ms,
+        "attend_flops": attend_flops,
+        "attend_tflops": attend_flops / attend_avg_s / 1e12,
+        # algorithmic HBM bytes of one attend launch: Q and O once, every live
+        # slot's K and V rows and its log2-count once per head
+        "attend_bytes": float(w.heads * w.chunk_tokens * w.head_dim * 2 * 2 +
+                              n_live.sum() * (w.head_dim * 2 * 2 + 4)),
+        "n_live": n_live,
+        "pre": pre,
+        "post": post,
+        "merged": merged,
+        "inserted": inserted,
+        "workspace_mb": caches[0].workspace.numel() / 2**20,
+        "frames": frames,
+        "planes": planes,
+        "chunk_keys": ck,
+    }
+    del base, caches, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return r
 
+
+def _step_summary(w, r):
+    """The figures of one measured step workload, for the bench line's detail."""
+    return {
+        "workload": _workload_desc(w)["workload"],
+        "query_tokens_per_s": r["qps"],
+        "ms_per_step": r["ms_per_step"],
+        "attend_ms_mean": float(np.mean(r["attend_ms"])),
+        "attend_frac_of_bf16_peak": r["attend_tflops"] / PEAK_BF16_TFLOPS,
+        "merge_path_ms_mean": float(np.mean(r["merge_ms"])) if r["merge_ms"] else None,
+        "n_live_at_attend": int(r["n_live"].sum()),
+        "merged_tokens_per_step": r["merged"],
+        "inserted_tokens_per_step": r["inserted"],
+        "evicted_slots_per_step": int(r["post"]["evicted_slots"] - r["pre"]["evicted_slots"]),
+        "step_roofline_frac": _step_roofline(w, r["merged"], r["inserted"], int(r["n_live"].sum()),
+                                             r["ms_per_step"])["frac"],
+        "workspace_mb_per_cache": r["workspace_mb"],
+    }
+
+
+def _tiny_step(args, fa, torch, reps=50):
+    """Latency of the tiny fp32 step: 4 frames merged one at a time, then the
+    fifth frame merged and its 64 queries attending (median over reps, each on
+    a copy of the cache after the first four frames)."""
+    from synth import WORKLOADS, DriftStream
+    w = WORKLOADS["tiny"]
+    st = DriftStream(w)
+    planes = st.planes()
+    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+    base = fa.Cache(cfg, planes)
+    dev = lambda x: torch.from_numpy(x).cuda()  # noqa: E731
+    for _ in range(4):
+        K, V, _, _ = st.next_frame()
+        base.match_merge(dev(K), dev(V), w.tokens_per_frame, 1)
+    K, V, Q, _ = st.next_frame()
+    k, v, q = dev(K), dev(V), dev(Q)
+    caches = []
+    for _ in range(reps):
+        c = fa.Cache(cfg, planes)
+        c.workspace.copy_(base.workspace)
+        caches.append(c)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    ev = _events(args, 2 * reps, stream)
+    torch.cuda.synchronize()
+    for i, c in enumerate(caches):
+        ev.record(2 * i)
+        c.match_merge(k, v, w.tokens_per_frame, 1)
+        c.attend(q, out=out)
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    us = [1e3 * ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]
+    ev.close()
+    return {"workload": "tiny: 1 head x d=64, 64 tokens/frame, fp32, SimHash 1 x 16 bits, "
+                        "threshold 0.98, 256 slots; frame 4 merged, then its 64 queries attend",
+            "us_median": float(np.median(us)), "us_p95": float(np.percentile(us, 95)),
+            "live_slots": int(caches[0].stats()["live_slots"]), "reps": reps}
+
+
+def _rollout_series(fa, torch, frames_total=240):
+    """The 240-frame rollout (1.3B layer shape, 2 %/frame of positions turning
+    from static to moving, 8192 slots/head, from an empty cache): per-chunk
+    latency of merge + attention against frame index, and memory."""
+    from synth import WORKLOADS, DriftStream
+    w = WORKLOADS["rollout"].with_(total_frames=frames_total)
+    st = DriftStream(w)
+    planes = st.planes()
+    T, F = w.tokens_per_frame, w.frames_per_chunk
+    cfg = fa.CacheConfig(w.heads, w.head_dim, w.budget, w.tables, w.bits, w.threshold, w.dtype)
+    cache = fa.Cache(cfg, planes)
+    stream = torch.cuda.current_stream()
+    n_chunks = w.total_frames // F
+    ms, live, evicted = [], [], []
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    out = None
+    for i in range(n_chunks):
+        ks, vs, qs = [], [], []
+        for _ in range(F):
+            K, V, Q, _ = st.next_frame()
+            ks.append(K)
+            vs.append(V)
+            qs.append(Q)
+        k, v, q = (torch.from_numpy(np.concatenate(x, 1)).to(torch.bfloat16).cuda()
+                   for x in (ks, vs, qs))
+        if out is None:
+            out = torch.empty_like(q)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.match_merge(k, v, T, F)
+        cache.attend(q, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        s = cache.stats()
+        live.append(int(s["live_slots"]))
+        evicted.append(int(s["evicted_slots"]))
+    ms = np.array(ms)
+    half = len(ms) // 2
+    slope = float(np.polyfit(np.arange(half, len(ms)) * F, ms[half:], 1)[0])
+    return {"workload": f"rollout: {w.total_frames} frames of the 1.3B layer shape, chunks of {F}, "
+                        f"2 %/frame static->moving, {w.budget} slots/head, from empty",
+            "chunk_ms": [round(float(x), 4) for x in ms],
+            "live_slots": live, "evicted_slots_cumulative": evicted,
+            "ms_mean_first_half": float(ms[:half].mean()),
+            "ms_mean_second_half": float(ms[half:].mean()),
+            "ms_slope_per_frame_second_half": slope,
+            "workspace_mb": cache.workspace.numel() / 2**20,
+            "max_memory_allocated_mb": torch.cuda.max_memory_allocated() / 2**20}
+
+
+def step_line(args, fa, torch, w):
+    """The bench line of a step workload (the 14B layer by default)."""
+    r = _measure_step(args, fa, torch, w, args.steps, args.warmup)
+    n_live = r["n_live"]
     res = {
         "metric": "query tokens/s per compressed-KV attention step",
-        "value": qps,
+        "value": r["qps"],
         "unit": "query tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -479,30 +653,30 @@ def main():
         "roofline": {
             "bound": "mfma",
             "kernel": "attend_cache_kernel",
-            "achieved": attend_tflops,
+            "achieved": r["attend_tflops"],
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": attend_tflops / PEAK_BF16_TFLOPS,
+            "frac": r["attend_tflops"] / PEAK_BF16_TFLOPS,
             "traffic": None,
-            "algorithmic_bytes": attend_bytes,
+            "algorithmic_bytes": r["attend_bytes"],
         },
         "detail": {
-            "attend_ms_mean": float(np.mean(attend_ms)),
-            "attend_ms_p95": float(np.percentile(attend_ms, 95)),
-            "merge_path_ms_mean": float(np.mean(merge_ms)) if merge_ms else None,
-            "step_ms_median_events": (float(np.median(np.array(attend_ms[1:]) + np.array(merge_ms)))
-                                      if merge_ms else None),
-            "n_live_after_prefill": int(pre["live_slots"]),
+            "attend_ms_mean": float(np.mean(r["attend_ms"])),
+            "attend_ms_p95": float(np.percentile(r["attend_ms"], 95)),
+            "merge_path_ms_mean": float(np.mean(r["merge_ms"])) if r["merge_ms"] else None,
+            "step_ms_median_events": (float(np.median(np.array(r["attend_ms"][1:]) +
+                                                      np.array(r["merge_ms"])))
+                                      if r["merge_ms"] else None),
+            "n_live_after_prefill": int(r["pre"]["live_slots"]),
             "n_live_at_attend": int(n_live.sum()),
             "n_live_per_head_mean": float(n_live.mean()),
-            "merged_tokens_per_step": int(post["merged_tokens"] - pre["merged_tokens"]),
-            "inserted_tokens_per_step": int(post["inserted_tokens"] - pre["inserted_tokens"]),
-            "evicted_slots_per_step": int(post["evicted_slots"] - pre["evicted_slots"]),
-            "attend_gflop_per_step": attend_flops / 1e9,
-            "step_roofline": _step_roofline(w, int(post["merged_tokens"] - pre["merged_tokens"]),
-                                            int(post["inserted_tokens"] - pre["inserted_tokens"]),
-                                            int(n_live.sum()), ms_per_step),
-            "workspace_mb_per_cache": caches[0].workspace.numel() / 2**20,
+            "merged_tokens_per_step": r["merged"],
+            "inserted_tokens_per_step": r["inserted"],
+            "evicted_slots_per_step": int(r["post"]["evicted_slots"] - r["pre"]["evicted_slots"]),
+            "attend_gflop_per_step": r["attend_flops"] / 1e9,
+            "step_roofline": _step_roofline(w, r["merged"], r["inserted"], int(n_live.sum()),
+                                            r["ms_per_step"]),
+            "workspace_mb_per_cache": r["workspace_mb"],
             "timing_events": ("torch default (system fence)" if args.fenced_events
                               else "hipEventDisableSystemFence"),
         },
@@ -512,9 +686,30 @@ def main():
     tr = _load_traffic(args.workload)
     if tr is not None:
         res["roofline"]["traffic"] = tr["attend_bytes"]
+    if args.workload == "dit14b" and not args.headline_only:
+        from synth import WORKLOADS
+        w13 = WORKLOADS["dit1.3b"]
+        r13 = _measure_step(args, fa, torch, w13, args.steps, args.warmup)
+        res["detail"]["dit1.3b_step"] = _step_summary(w13, r13)
+        del r13
+        print("bench: 1.3B-layer step done", file=sys.stderr, flush=True)
+        res["detail"]["tiny_f32_step"] = _tiny_step(args, fa, torch)
+        res["detail"]["rollout_240"] = _rollout_series(fa, torch)
+        print("bench: rollout done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         heads = args.cpu_heads or (1 if w.subspaces else w.heads if w.heads <= 12 else 2)
-        res["cpu_baseline"] = cpu_baseline(w, [(K, V, Q) for K, V, Q in frames], planes, heads)
+        gpu_codes = None
+        if not w.subspaces:
+            # the codes the library's hash kernel gives the chunk's keys, for
+            # the heads the oracle runs (the same kernel hashes inside
+            # match_merge when no codes are passed)
+            ck = r["chunk_keys"][:heads].contiguous()
+            pl = torch.from_numpy(np.asarray(r["planes"])).to(torch.bfloat16).cuda().contiguous()
+            gpu_codes = fa.hash_codes(ck, pl, w.tables, w.bits).cpu().numpy().view(np.uint32)
+        base, bits = cpu_baseline(w, r["frames"], r["planes"], heads, gpu_codes)
+        res["cpu_baseline"] = base
+        if bits is not None:
+            res["detail"]["hash_bits_vs_oracle"] = bits
     print(json.dumps(res), flush=True)
 
 
