@@ -346,6 +346,31 @@ fastar_status fastar_attend_subset(const void* q_dev, int64_t q_stride_h, int64_
                                    void* o_dev, int64_t o_stride_h, int64_t o_stride_n,
                                    void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the AnnCA
+ * step of fastar_annca_select followed by fastar_attend_subset, with the
+ * per-frame selection (the kept prompt ids and their counts) held in a device
+ * array inside the library instead of caller buffers.  It allocates nothing:
+ * the array is a static device object of
+ * (FASTAR_ANNCA_STATIC_MAX_SELECTED + FASTAR_ANNCA_STATIC_MAX_SEGMENTS) int32
+ * (4 MiB + 16 KiB) that each GPU the library runs on holds until the process
+ * ends.  Requires H*F <= FASTAR_ANNCA_STATIC_MAX_SEGMENTS and
+ * H*F*Np <= FASTAR_ANNCA_STATIC_MAX_SELECTED (else FASTAR_ERR_CAPACITY).
+ * Every call on one GPU shares that GPU's array and leaves its selection
+ * there; calls that overlap on one GPU (other streams, other threads) race and
+ * must be ordered by the caller.  Arguments as fastar_annca_select (q_codes_dev
+ * [H][L][F*Nf], p_codes_dev [H][L][Np]) and fastar_attend_subset (q, k, v, o and
+ * their strides, d, dtype, scale); the output equals that pair's. */
+#define FASTAR_ANNCA_STATIC_MAX_SELECTED (1 << 20)
+#define FASTAR_ANNCA_STATIC_MAX_SEGMENTS 4096
+fastar_status fastar_annca_attend_static(const void* q_dev, int64_t q_stride_h, int64_t q_stride_n,
+                                         const uint32_t* q_codes_dev, const void* k_dev,
+                                         const void* v_dev, int64_t kv_stride_h,
+                                         int64_t kv_stride_n, const uint32_t* p_codes_dev,
+                                         int32_t Nf, int32_t F, int32_t Np, int32_t H, int32_t d,
+                                         int32_t L, fastar_dtype dtype, float scale, void* o_dev,
+                                         int64_t o_stride_h, int64_t o_stride_n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -101,6 +101,9 @@ _SIGS = {
     "fastar_attend_subset": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _I64, _I64, _VP, _VP,
                                             _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _F, _VP,
                                             _I64, _I64, _VP]),
+    "fastar_annca_attend_static": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _I64, _I64,
+                                                  _VP, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                  ctypes.c_int, _F, _VP, _I64, _I64, _VP]),
 }
 
 _lib = None
@@ -535,5 +538,35 @@ def attend_subset(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, frames: int
     _check(library().fastar_attend_subset(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
         _ptr(sel_idx), _ptr(sel_count), NQ // frames, frames, Np, H, d, dt, float(scale),
+        _ptr(out), out.stride(0), out.stride(1), _stream(stream)))
+    return out
+
+
+def annca_attend_static(q: torch.Tensor, q_codes: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        p_codes: torch.Tensor, frames: int, scale: float = 0.0,
+                        out: torch.Tensor | None = None, stream=None):
+    """AnnCA select + sparse attention with the selection in the library's
+    static device array (no device allocation inside the call; `out` is
+    allocated here only when not given)."""
+    _require(q, "q")
+    _require(k, "k", q.dtype)
+    _require(v, "v", q.dtype)
+    _require(q_codes, "q_codes", torch.int32)
+    _require(p_codes, "p_codes", torch.int32)
+    H, NQ, d = q.shape
+    Np = k.shape[1]
+    L = q_codes.shape[1]
+    if k.shape != v.shape or k.stride() != v.stride() or NQ % frames:
+        raise ValueError("bad shapes")
+    if tuple(q_codes.shape) != (H, L, NQ) or tuple(p_codes.shape) != (H, L, Np):
+        raise ValueError("q_codes [H][L][F*Nf] and p_codes [H][L][Np] disagree")
+    if not (q_codes.is_contiguous() and p_codes.is_contiguous()):
+        raise ValueError("codes must be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    dt = BF16 if q.dtype == torch.bfloat16 else F32
+    _check(library().fastar_annca_attend_static(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(q_codes), _ptr(k), _ptr(v), k.stride(0),
+        k.stride(1), _ptr(p_codes), NQ // frames, frames, Np, H, d, L, dt, float(scale),
         _ptr(out), out.stride(0), out.stride(1), _stream(stream)))
     return out

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -906,6 +907,110 @@ fastar_status fastar_attend_subset(const void* q_dev, int64_t q_stride_h, int64_
   a.F = F;
   a.scale = scale == 0.0f ? 1.0f / std::sqrt((float)d) : scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  FASTAR_HIP(dtype == FASTAR_BF16 ? launch_attend_bf16(a, s) : launch_attend_f32(a, s));
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// AnnCA without allocation.  The per-frame selection (kept prompt ids and
+// their count per head and frame) lives in this file-scope device array
+// instead of caller buffers.  Each GPU holds its own copy until the process
+// ends; host code uses only the address hipGetSymbolAddress gives for the
+// current device, never the array's name.
+static __device__ __align__(256) int32_t scratch[FASTAR_ANNCA_STATIC_MAX_SELECTED +
+                                                  FASTAR_ANNCA_STATIC_MAX_SEGMENTS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device.
+fastar_status scratch_for_current_device(int32_t** out) {
+  int dev = 0;
+  FASTAR_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FASTAR_ERR_UNSUPPORTED, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    FASTAR_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return fail(FASTAR_ERR_HIP, "hipGetSymbolAddress gave a NULL address");
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FASTAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fastar_status fastar_annca_attend_static(const void* q_dev, int64_t q_stride_h, int64_t q_stride_n,
+                                         const uint32_t* q_codes_dev, const void* k_dev,
+                                         const void* v_dev, int64_t kv_stride_h,
+                                         int64_t kv_stride_n, const uint32_t* p_codes_dev,
+                                         int32_t Nf, int32_t F, int32_t Np, int32_t H, int32_t d,
+                                         int32_t L, fastar_dtype dtype, float scale, void* o_dev,
+                                         int64_t o_stride_h, int64_t o_stride_n, void* stream) {
+  FASTAR_REQUIRE(valid_dtype(dtype), "unknown dtype");
+  FASTAR_REQUIRE(d == 64 || d == 128, "d must be 64 or 128");
+  FASTAR_REQUIRE(H >= 1 && F >= 1 && L >= 1 && L <= FASTAR_MAX_TABLES, "H, F, L out of range");
+  FASTAR_REQUIRE(Nf >= 1 && Nf <= FASTAR_MAX_ANNCA_QUERIES_PER_FRAME, "Nf out of range");
+  FASTAR_REQUIRE(Np >= 1 && Np <= FASTAR_MAX_ANNCA_PROMPT, "Np out of range");
+  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  if ((int64_t)H * F > FASTAR_ANNCA_STATIC_MAX_SEGMENTS ||
+      (int64_t)H * F * Np > FASTAR_ANNCA_STATIC_MAX_SELECTED)
+    return fail(FASTAR_ERR_CAPACITY,
+                "H*F = " + std::to_string((int64_t)H * F) + " and H*F*Np = " +
+                    std::to_string((int64_t)H * F * Np) + " must stay within " +
+                    std::to_string(FASTAR_ANNCA_STATIC_MAX_SEGMENTS) + " and " +
+                    std::to_string(FASTAR_ANNCA_STATIC_MAX_SELECTED));
+  FASTAR_REQUIRE(q_dev && q_codes_dev && k_dev && v_dev && p_codes_dev && o_dev, "NULL pointer");
+  const int vec = dtype == FASTAR_BF16 ? 8 : 4;
+  FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(k_dev, 16) && aligned(v_dev, 16) &&
+                     aligned(o_dev, 16) && aligned(q_codes_dev, 4) && aligned(p_codes_dev, 4),
+                 "q, k, v, o must be 16-byte aligned, codes 4-byte aligned");
+  FASTAR_REQUIRE(q_stride_h % vec == 0 && q_stride_n % vec == 0 && kv_stride_h % vec == 0 &&
+                     kv_stride_n % vec == 0 && o_stride_h % vec == 0 && o_stride_n % vec == 0,
+                 "strides must be multiples of 16 bytes");
+  int32_t* sp = nullptr;
+  fastar_status st = scratch_for_current_device(&sp);
+  if (st != FASTAR_OK) return st;
+  int32_t* sel_idx = sp;                                    // [H][F][Np]
+  int32_t* sel_count = sp + FASTAR_ANNCA_STATIC_MAX_SELECTED;  // [H][F]
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the select kernel writes every (head, frame) count and the first `count`
+  // ids of each list, which is all the attention reads: nothing needs clearing
+  SelectArgs sa{q_codes_dev, p_codes_dev, Nf, F, Np, H, L, sel_idx, sel_count};
+  FASTAR_HIP(launch_annca_select(sa, s));
+  AttendArgs a{};
+  a.q = q_dev;
+  a.sq_h = q_stride_h;
+  a.sq_n = q_stride_n;
+  a.k = k_dev;
+  a.v = v_dev;
+  a.sk_h = kv_stride_h;
+  a.sk_n = kv_stride_n;
+  a.count = nullptr;
+  a.count_ld = 0;
+  a.n_keys = sel_count;
+  a.n_keys_const = Np;
+  a.sel = sel_idx;
+  a.sel_ld = Np;
+  a.o = o_dev;
+  a.so_h = o_stride_h;
+  a.so_n = o_stride_n;
+  a.lse = nullptr;
+  a.H = H;
+  a.d = d;
+  a.Nseg = Nf;
+  a.F = F;
+  a.scale = scale == 0.0f ? 1.0f / std::sqrt((float)d) : scale;
   FASTAR_HIP(dtype == FASTAR_BF16 ? launch_attend_bf16(a, s) : launch_attend_f32(a, s));
   return ok();
 }

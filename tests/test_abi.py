@@ -85,3 +85,16 @@ def test_host_validation_before_any_launch():
                                     1, 0.0, None, 0, 0, None) == 1
     # zero-sized hash is a no-op that succeeds without touching the device
     assert lib.fastar_hash(None, 1, 0, 5, 128, 128, 128, None, 4, 32, None, None) == 0
+
+
+def test_static_annca_refuses_sizes_beyond_its_array_on_host():
+    lib = fa.library()
+    # H * F = 4097 segments: beyond the static array, refused before any HIP call
+    st = lib.fastar_annca_attend_static(None, 0, 0, None, None, None, 0, 0, None, 1, 4097, 8, 1,
+                                        128, 4, 1, 0.0, None, 0, 0, None)
+    assert st == 3  # FASTAR_ERR_CAPACITY
+    assert "4096" in lib.fastar_last_error().decode()
+    # H * F * Np beyond 2^20 selected ids
+    st = lib.fastar_annca_attend_static(None, 0, 0, None, None, None, 0, 0, None, 1, 64, 16384, 2,
+                                        128, 4, 1, 0.0, None, 0, 0, None)
+    assert st == 3
