@@ -229,9 +229,12 @@ fastar_status fastar_project_keys(fastar_cache_t cache, const void* x_dev, int64
 /* Attention of Nq queries per head over the live slots (section 2A, Lemma 5.1:
  * logits shifted by the group size).  q_dev: (h, n, k) at q_dev[h*stride_h +
  * n*stride_n + k]; o_dev likewise with o_stride_h, o_stride_n (cfg dtype);
- * scale: logit scale, 0 means 1/sqrt(d); lse_dev: optional float [H][Nq],
+ * scale: logit scale, > 0, or 0 for 1/sqrt(d) (negative values are refused);
+ * lse_dev: optional float [H][Nq],
  * natural-log partition function.  An empty cache gives zero outputs and
- * lse = -inf. */
+ * lse = -inf.  The call writes the slots' log-count shifts divided by the
+ * scale into the cache's workspace before attending (a few bytes per slot), so
+ * attention calls on one cache must not overlap. */
 fastar_status fastar_attend(fastar_cache_t cache, const void* q_dev, int64_t stride_h,
                             int64_t stride_n, int32_t Nq, float scale, void* o_dev,
                             int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream);
@@ -337,7 +340,7 @@ fastar_status fastar_annca_select(const uint32_t* q_codes_dev, int32_t Nf, int32
  * kv_stride_h, kv_stride_n; sel_idx_dev / sel_count_dev as produced by
  * fastar_annca_select, or both NULL to attend over all Np keys (dense);
  * o_dev like q_dev with o strides.  A frame with an empty subset gets zero
- * outputs.  scale 0 means 1/sqrt(d). */
+ * outputs.  scale > 0, or 0 for 1/sqrt(d). */
 fastar_status fastar_attend_subset(const void* q_dev, int64_t q_stride_h, int64_t q_stride_n,
                                    const void* k_dev, const void* v_dev, int64_t kv_stride_h,
                                    int64_t kv_stride_n, const int32_t* sel_idx_dev,

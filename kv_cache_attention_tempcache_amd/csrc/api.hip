@@ -111,8 +111,10 @@ enum Region {
   kPlanes, kPlanesFrag, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kHist, kCodes,
   kIdxOff, kIdxSlot, kNLive, kEvicted, kCounters, kOwner, kGsize, kFrame, kStateEnd = kFrame,
   kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupSlot, kItems,
-  kPlan, kAnnsaCodes, kAnnsaOff, kAnnsaEnt, kRopeK, kRopeLb, kNumRegions
+  kPlan, kAnnsaCodes, kAnnsaOff, kAnnsaEnt, kRopeK, kRopeLb, kLbc, kNumRegions
 };
+static_assert(kNumRegions + 1 <= (int)(sizeof(Layout::off) / sizeof(size_t)),
+              "Layout::off holds every region's offset and the total");
 
 fastar_status check_device_gfx950(int* device) {
   FASTAR_HIP(hipGetDevice(device));
@@ -187,6 +189,7 @@ Layout make_layout(const Dims& dm) {
   sizes[kAnnsaEnt] = H * 4 * B * 8;
   sizes[kRopeK] = e == 2 ? H * (size_t)dm.R * Bp * d * 2 : 0;
   sizes[kRopeLb] = e == 2 ? H * (size_t)dm.R * Bp * 4 : 0;
+  sizes[kLbc] = e == 2 ? H * (size_t)std::max(dm.R, 1) * Bp * 4 : 0;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {
     L.off[r] = off;
@@ -233,6 +236,7 @@ CacheDev carve(void* base, const Dims& dm) {
   c.annsa_ent = reinterpret_cast<uint2*>(b + L.off[kAnnsaEnt]);
   c.rope_k = b + L.off[kRopeK];
   c.rope_lb = reinterpret_cast<float*>(b + L.off[kRopeLb]);
+  c.lbc = reinterpret_cast<float*>(b + L.off[kLbc]);
   return c;
 }
 
@@ -530,7 +534,8 @@ fastar_status fastar_annsa_attend(fastar_cache_t c, const void* q_dev, int64_t s
   FASTAR_REQUIRE(Nq >= 0, "Nq must be >= 0");
   if (Nq == 0) return ok();
   FASTAR_REQUIRE(q_dev && o_dev && q_codes_dev, "NULL pointer");
-  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  FASTAR_REQUIRE(std::isfinite(scale) && scale >= 0.0f,
+                 "scale must be finite and >= 0 (0 selects 1/sqrt(d))");
   const int vec = dm.elem == 2 ? 8 : 4;
   FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(o_dev, 16), "q and o must be 16-byte aligned");
   FASTAR_REQUIRE(stride_h % vec == 0 && stride_n % vec == 0 && stride_n >= dm.d,
@@ -566,7 +571,8 @@ static fastar_status attend_impl(fastar_cache_t c, const void* q_dev, int64_t st
   FASTAR_REQUIRE(n_new >= 0, "n_new must be >= 0");
   if (Nq == 0) return ok();
   FASTAR_REQUIRE(q_dev && o_dev, "q or o is NULL");
-  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  FASTAR_REQUIRE(std::isfinite(scale) && scale >= 0.0f,
+                 "scale must be finite and >= 0 (0 selects 1/sqrt(d))");
   const int vec = dm.elem == 2 ? 8 : 4;
   FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(o_dev, 16), "q and o must be 16-byte aligned");
   FASTAR_REQUIRE(stride_h % vec == 0 && stride_n % vec == 0 && stride_n >= dm.d,
@@ -704,7 +710,8 @@ fastar_status fastar_attend_rope(fastar_cache_t c, const void* q_dev, int64_t st
   FASTAR_REQUIRE(Nq >= 0, "Nq must be >= 0");
   if (Nq == 0) return ok();
   FASTAR_REQUIRE(q_dev && o_dev, "q or o is NULL");
-  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  FASTAR_REQUIRE(std::isfinite(scale) && scale >= 0.0f,
+                 "scale must be finite and >= 0 (0 selects 1/sqrt(d))");
   FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(o_dev, 16), "q and o must be 16-byte aligned");
   FASTAR_REQUIRE(stride_h % 8 == 0 && stride_n % 8 == 0 && stride_n >= dm.d,
                  "q strides must be multiples of 16 bytes");
@@ -873,7 +880,8 @@ fastar_status fastar_attend_subset(const void* q_dev, int64_t q_stride_h, int64_
   FASTAR_REQUIRE(H >= 1 && F >= 1 && Nf >= 0 && Np >= 0, "sizes out of range");
   FASTAR_REQUIRE((sel_idx_dev == nullptr) == (sel_count_dev == nullptr),
                  "sel_idx and sel_count must both be given or both be NULL");
-  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  FASTAR_REQUIRE(std::isfinite(scale) && scale >= 0.0f,
+                 "scale must be finite and >= 0 (0 selects 1/sqrt(d))");
   if (Nf == 0) return ok();
   FASTAR_REQUIRE(q_dev && k_dev && v_dev && o_dev, "NULL pointer");
   const int vec = dtype == FASTAR_BF16 ? 8 : 4;
@@ -962,7 +970,8 @@ fastar_status fastar_annca_attend_static(const void* q_dev, int64_t q_stride_h, 
   FASTAR_REQUIRE(H >= 1 && F >= 1 && L >= 1 && L <= FASTAR_MAX_TABLES, "H, F, L out of range");
   FASTAR_REQUIRE(Nf >= 1 && Nf <= FASTAR_MAX_ANNCA_QUERIES_PER_FRAME, "Nf out of range");
   FASTAR_REQUIRE(Np >= 1 && Np <= FASTAR_MAX_ANNCA_PROMPT, "Np out of range");
-  FASTAR_REQUIRE(std::isfinite(scale), "scale must be finite");
+  FASTAR_REQUIRE(std::isfinite(scale) && scale >= 0.0f,
+                 "scale must be finite and >= 0 (0 selects 1/sqrt(d))");
   if ((int64_t)H * F > FASTAR_ANNCA_STATIC_MAX_SEGMENTS ||
       (int64_t)H * F * Np > FASTAR_ANNCA_STATIC_MAX_SELECTED)
     return fail(FASTAR_ERR_CAPACITY,

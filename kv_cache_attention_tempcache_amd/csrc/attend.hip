@@ -8,7 +8,10 @@
 //     B = the wave's queries, held in registers for the whole key loop.  The
 //     accumulator gives each lane one query column and 16 key rows, so the
 //     running max and sum stay in the lane (plus one exchange with lane^32).
-//   logits in log2 units: t = s * scale * log2(e) + log2(count).  The running
+//   logits in log2 units: t = s * scale * log2(e) + log2(count), computed as
+//     (s + log2(count) / (scale * log2(e))) * scale * log2(e): the accumulators
+//     start at the divided shift, and each weight is one FMA and one exp2
+//     (the shifts are divided once per call by a small kernel).  The running
 //     max is refreshed lazily (only when a tile's max exceeds it by more than
 //     8), which keeps every weight <= 2^8 and skips most rescales of O.
 //   O^T += V^T P^T: B = the probabilities, converted to bf16 in registers in
@@ -19,6 +22,8 @@
 //   Blocks are renumbered so each XCD (blocks are dealt round-robin over the 8
 //     XCDs) gets a contiguous range of (head, query tile) and shares its L2.
 // f32 path (small fp32 workloads): one thread per query, fp32 online softmax.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace fastar {
@@ -243,9 +248,11 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
              : reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(c.v_mirror) +
                                                 (int64_t)h * dm.Bp * D);
   const int64_t rs = SUBSET ? sa.sk_n * 2 : C::kRowBytes;  // bytes between key rows
+  // slot shifts divided by the logit scale (written by scale_shift_kernel
+  // just before this launch), so they can start the QK^T accumulators
   const float* lbg = SUBSET ? nullptr
-                     : REG  ? c.rope_lb + (int64_t)h * dm.R * dm.Bp
-                            : c.lb + (int64_t)h * dm.Bp;
+                     : REG  ? c.lbc + (int64_t)h * dm.R * dm.Bp
+                            : c.lbc + (int64_t)h * dm.Bp;
   // RAW: raw tokens (count 1, no logit shift) follow the slots: key tiles
   // ntc .. of the loop read rows of a.xk / a.xv, rows past a.n_x read row 0
   // and are masked by their bias.
@@ -400,11 +407,24 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     const float* lb_lds = reinterpret_cast<const float*>(cur + C::kKBytes + C::kVBytes);
     if (it + NBUF - 1 < nt) issue((it + NBUF - 1) * BN, nxt);
 
+    // The accumulators start at the tile's shifts (already divided by the
+    // logit scale): the rows of lane (m, hf) are 8*jg + 4*hf + 0..3 of each
+    // 32-key block, so S = K Q^T + shift / scale directly.
     f32x16_t S[BN / 32][QB];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      f32x16_t init;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16_t{};
+      for (int jg = 0; jg < 4; ++jg) {
+        const float4 b4 = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
+        init[4 * jg + 0] = b4.x;
+        init[4 * jg + 1] = b4.y;
+        init[4 * jg + 2] = b4.z;
+        init[4 * jg + 3] = b4.w;
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = init;
+    }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
@@ -418,29 +438,16 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
           S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[qb][ks], S[kb][qb], 0, 0, 0);
       }
     }
-    float4 lbr[BN / 32][4];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        lbr[kb][jg] = *reinterpret_cast<const float4*>(lb_lds + kb * 32 + 8 * jg + 4 * hf);
-      }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = -__builtin_huge_valf();
+      // the tile's largest logit in log2 units: the scale is positive, so it
+      // is the scale times the largest accumulator
+      float sx = -__builtin_huge_valf();
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
+      for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const float bb[4] = {lbr[kb][jg].x, lbr[kb][jg].y, lbr[kb][jg].z, lbr[kb][jg].w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float t = __builtin_fmaf(S[kb][qb][4 * jg + r], cscale, bb[r]);
-            S[kb][qb][4 * jg + r] = t;
-            mx = fmaxf(mx, t);
-          }
-        }
-      }
+        for (int r = 0; r < 16; ++r) sx = fmaxf(sx, S[kb][qb][r]);
+      float mx = sx * cscale;
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const bool need = mx > mrun[qb] + 8.0f;
       if (__ballot(need)) {
@@ -463,7 +470,8 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            pf[qb][i] = (__bf16)__builtin_amdgcn_exp2f(S[kb][qb][8 * kk + i] - mrun[qb]);
+            pf[qb][i] = (__bf16)__builtin_amdgcn_exp2f(
+                __builtin_fmaf(S[kb][qb][8 * kk + i], cscale, -mrun[qb]));
           // row sum of the same bf16-rounded weights the MFMA multiplies
           float ls = lrun[qb];
 #pragma unroll
@@ -538,6 +546,20 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   }
 }
 
+// lbc = lb / (scale * log2(e)) over every head's shift rows (-inf stays -inf).
+__global__ __launch_bounds__(256) void scale_shift_kernel(const float* __restrict__ src,
+                                                          float* __restrict__ dst, int64_t n,
+                                                          float cscale) {
+  const int64_t n4 = n / 4;
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+  float4* d4 = reinterpret_cast<float4*>(dst);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 v = s4[i];
+    d4[i] = make_float4(v.x / cscale, v.y / cscale, v.z / cscale, v.w / cscale);
+  }
+}
+
 template <int D, int BN, int WAVES, int QB, int NBUF>
 hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                             hipStream_t s) {
@@ -545,6 +567,13 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
   const int qtiles = (a.Nq + C::BM - 1) / C::BM;
   const int blocks = dm.H * qtiles;
   if (blocks == 0) return hipSuccess;
+  {
+    // rows per head are a multiple of 128 (Bp), so n is a multiple of 4
+    const int64_t n = (int64_t)dm.H * (a.n_reg > 0 ? dm.R : 1) * dm.Bp;
+    const int64_t b = std::min<int64_t>((n / 4 + 255) / 256, 2048);
+    hipLaunchKernelGGL(scale_shift_kernel, dim3((unsigned)b), dim3(256), 0, s,
+                       a.n_reg > 0 ? c.rope_lb : c.lb, c.lbc, n, a.scale * kLog2e);
+  }
   if (a.n_reg > 0)
     hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, true>),
                        dim3(blocks), dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);

@@ -143,10 +143,13 @@ struct CacheDev {
   int32_t* hist;          // [H][B][R]
   void* rope_k;           // bf16 [H][R*Bp][d]
   float* rope_lb;         // [H][R*Bp]
+  // the shifts of the last attention call divided by its logit scale
+  // (scale * log2(e)): [H][Bp], or [H][R*Bp] for the M-degree regions
+  float* lbc;
 };
 
 struct Layout {
-  size_t off[32];
+  size_t off[40];
   size_t total;
 };
 
