@@ -131,7 +131,8 @@ struct CacheDev {
   int32_t* group_slot; // [H][B] slot of each merge group
   int4* items;         // [H][B] the frame's work items of the apply kernel: merge groups
                        // {slot, first member in group_tok, members, leader token},
-                       // then inserts {slot, -1, 1, token}
+                       // then inserts {slot, -1, 1, token}, y = -2 when the
+                       // slot was evicted in this frame
   int32_t* plan;       // [H][kPlanStride]
   // AnnSA: slot codes under the AnnSA hyperplanes and their bucket index
   uint32_t* annsa_codes;  // [H][4][B]

@@ -58,9 +58,10 @@ __device__ V block_excl_scan(V v, V* s_scan, V& total) {
 }
 
 struct PlanShared {
+  uint32_t red_m[2][kPlanWaves];  // per-wave (min, count of min), two buffers
+  int red_c[2][kPlanWaves];
   int digit, krem;
   int refused;  // fewer evictable slots than needed: the frame changes nothing
-  unsigned long long evicted_count;
 };
 
 // Three counts per token packed in one 64-bit scan: group leaders (bits
@@ -146,15 +147,81 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   const int need = max(0, m - (B - n_live));
   if (tid == 0) ps.refused = 0;
   if (need > 0) {
-    if (tid == 0) {
-      ps.krem = need;
-      ps.evicted_count = 0ull;
-    }
+    if (tid == 0) ps.krem = need;
     __syncthreads();
+    // Each thread owns a contiguous run [s_lo, s_hi) of the live slots.  Its
+    // slots' keys are read once into registers: the last-update frame of a
+    // slot not merged into in this frame (every such frame is <= f-1), else
+    // ~0u.  All passes below work on these registers.
+    constexpr int kPerS = (FASTAR_MAX_BUDGET + kPlanThreads - 1) / kPlanThreads;
+    const int per_s = (n_live + kPlanThreads - 1) / kPlanThreads;
+    const int s_lo = min(n_live, tid * per_s), s_hi = min(n_live, s_lo + per_s);
     const int32_t* last = c.last + (int64_t)h * B;
-    auto eligible = [&](int s) { return owner[s] == kNoOwner; };
-    // radix select of the need-th smallest `last` among eligible live slots
-    // (every eligible slot was last updated before frame f, so last <= f-1)
+    uint32_t key[kPerS];
+#pragma unroll
+    for (int k = 0; k < kPerS; ++k) {
+      const int sx = min(s_lo + k, B - 1);
+      const int32_t ow = owner[sx];
+      const int32_t lv = last[sx];
+      key[k] = (s_lo + k < s_hi && ow == kNoOwner) ? (uint32_t)lv : 0xffffffffu;
+    }
+    // The need-th smallest key among the eligible slots (the cut-off frame)
+    // and how many slots with exactly that key to evict.  Eviction takes the
+    // oldest frames first, and those hold few distinct values: walk them
+    // upward, one block-wide (min, count of min) reduction each.  If eight
+    // values do not cover `need`, a radix select over the rest finishes.
+    uint32_t cut = 0u;
+    int take_eq = 0;
+    bool found = false;
+    {
+      int krem = need;
+      uint32_t lo = 0u;  // keys below lo are already counted
+      for (int step = 0; step < 8 && !found; ++step) {
+        uint32_t mv = 0xffffffffu;
+#pragma unroll
+        for (int k = 0; k < kPerS; ++k)
+          if (key[k] >= lo) mv = min(mv, key[k]);
+        int cv = 0;
+#pragma unroll
+        for (int k = 0; k < kPerS; ++k) cv += key[k] == mv && mv != 0xffffffffu;
+        // (min, count of min) over the wave, then over the waves
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t m2 = (uint32_t)__shfl_xor((int)mv, o, 64);
+          const int c2 = __shfl_xor(cv, o, 64);
+          const uint32_t mn = min(mv, m2);
+          cv = (mv == mn ? cv : 0) + (m2 == mn ? c2 : 0);
+          mv = mn;
+        }
+        uint32_t* rm = ps.red_m[step & 1];
+        int* rc = ps.red_c[step & 1];
+        if ((tid & 63) == 0) {
+          rm[tid >> 6] = mv;
+          rc[tid >> 6] = cv;
+        }
+        __syncthreads();
+        mv = 0xffffffffu;
+        cv = 0;
+#pragma unroll
+        for (int w = 0; w < kPlanWaves; ++w) mv = min(mv, rm[w]);
+#pragma unroll
+        for (int w = 0; w < kPlanWaves; ++w) cv += rm[w] == mv ? rc[w] : 0;
+        if (mv == 0xffffffffu) break;  // fewer eligible slots than needed
+        if (cv >= krem) {
+          cut = mv;
+          take_eq = krem;
+          found = true;
+        } else {
+          krem -= cv;
+          lo = mv + 1u;
+        }
+      }
+      if (tid == 0) ps.krem = found ? take_eq : need;
+      __syncthreads();
+    }
+    if (!found) {
+    // radix select of the need-th smallest key among the eligible slots,
+    // 8 bits at a time from the top (digits above f-1's skipped)
     uint32_t prefix = 0u;
     const uint32_t maxv = (uint32_t)(f - 1);
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -162,44 +229,69 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
       for (int q = tid; q < 256; q += kPlanThreads) hist[q] = 0;
       __syncthreads();
       const uint64_t hi_mask = ~((1ull << (shift + 8)) - 1ull);
-      for (int s = tid; s < n_live; s += kPlanThreads) {
-        if (!eligible(s)) continue;
-        const uint32_t lv = (uint32_t)last[s];
-        if (((uint64_t)lv & hi_mask) != ((uint64_t)prefix & hi_mask)) continue;
-        atomicAdd(&hist[(lv >> shift) & 255u], 1);
+#pragma unroll
+      for (int k = 0; k < kPerS; ++k) {
+        const uint32_t lv = key[k];
+        if (lv != 0xffffffffu && ((uint64_t)lv & hi_mask) == ((uint64_t)prefix & hi_mask))
+          atomicAdd(&hist[(lv >> shift) & 255u], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, dg = 0;
+      // the digit holding the krem-th smallest key: lane l of wave 0 scans
+      // bins 4l .. 4l+3, a wave prefix sum gives each lane its base count
+      if (tid < 64) {
         const int kr = ps.krem;
-        for (dg = 0; dg < 256; ++dg) {
-          if (cum + hist[dg] >= kr) break;
-          cum += hist[dg];
+        const int h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2],
+                  h3 = hist[4 * tid + 3];
+        const int tot = h0 + h1 + h2 + h3;
+        int incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o, 64);
+          if (tid >= o) incl += y;
         }
-        ps.digit = dg;
-        ps.krem = kr - cum;
+        const int base = incl - tot;
+        if (base < kr && kr <= incl) {
+          int cum = base, dg = 4 * tid;
+          if (cum + h0 < kr) {
+            cum += h0;
+            ++dg;
+            if (cum + h1 < kr) {
+              cum += h1;
+              ++dg;
+              if (cum + h2 < kr) {
+                cum += h2;
+                ++dg;
+              }
+            }
+          }
+          ps.digit = dg;
+          ps.krem = kr - cum;
+        }
+        if (tid == 63 && incl < kr) {  // fewer eligible slots than needed
+          ps.digit = 256;
+          ps.krem = kr - incl;
+        }
       }
       __syncthreads();
       prefix |= (uint32_t)ps.digit << shift;
       __syncthreads();
     }
-    const uint32_t cut = prefix;      // the need-th smallest `last`
-    const int take_eq = ps.krem;      // how many slots with last == cut to evict
-    const int per_s = (n_live + kPlanThreads - 1) / kPlanThreads;
-    const int s_lo = min(n_live, tid * per_s), s_hi = min(n_live, s_lo + per_s);
+    cut = prefix;          // the need-th smallest `last`
+    take_eq = ps.krem;     // how many slots with last == cut to evict
+    }
     // rank of each slot among the eligible ones with last == cut
     int eq = 0;
-    for (int s = s_lo; s < s_hi; ++s) eq += eligible(s) && (uint32_t)last[s] == cut;
+#pragma unroll
+    for (int k = 0; k < kPerS; ++k) eq += key[k] == cut;
     int eq_total = 0;
     const int eq_base = block_excl_scan<int>(eq, s_scan, eq_total);
     int evc = 0;
     {
       int er = eq_base;
-      for (int s = s_lo; s < s_hi; ++s) {
-        if (!eligible(s)) continue;
-        const uint32_t lv = (uint32_t)last[s];
-        if (lv < cut) ++evc;
-        else if (lv == cut) evc += (er++ < take_eq);
+#pragma unroll
+      for (int k = 0; k < kPerS; ++k) {
+        if (key[k] < cut) ++evc;
+        else if (key[k] == cut) evc += (er++ < take_eq);
       }
     }
     int ev_total = 0;
@@ -210,21 +302,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
     if (ev_total < need) {
       if (tid == 0) ps.refused = 1;
     } else {
+      // (the tokens the evicted slots held are tallied by the apply step,
+      // which reads each slot's count before its insert overwrites it)
       int er = eq_base;
-      unsigned long long tok = 0ull;
-      const int32_t* count = c.count + (int64_t)h * B;
-      for (int s = s_lo; s < s_hi; ++s) {
-        if (!eligible(s)) continue;
-        const uint32_t lv = (uint32_t)last[s];
+#pragma unroll
+      for (int k = 0; k < kPerS; ++k) {
         bool ev = false;
-        if (lv < cut) ev = true;
-        else if (lv == cut) ev = (er++ < take_eq);
-        if (ev) {
-          ev_list[ep++] = s;
-          tok += (unsigned long long)count[s];
-        }
+        if (key[k] < cut) ev = true;
+        else if (key[k] == cut) ev = (er++ < take_eq);
+        if (ev) ev_list[ep++] = s_lo + k;
       }
-      if (tok) atomicAdd(&ps.evicted_count, tok);
     }
   }
   __syncthreads();
@@ -263,7 +350,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   for (int q = tid; q < m; q += kPlanThreads) {
     const int tok = ins_list[q];
     const int slot = q < need ? ev_list[q] : n_live + (q - need);
-    items[n_groups + q] = make_int4(slot, -1, 1, tok);
+    // y = -2 marks an insert into an evicted slot (its old count is tallied)
+    items[n_groups + q] = make_int4(slot, q < need ? -2 : -1, 1, tok);
     if (want_out) {
       const int64_t o = (int64_t)h * a.out_ld + a.out_col0 + tok;
       if (a.slot_out) a.slot_out[o] = slot;
@@ -281,7 +369,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   }
   if (tid == 0) {
     c.n_live[h] = n_live + m - need;
-    if (need > 0) c.evicted_tokens[h] += (int64_t)ps.evicted_count;
     int64_t* cn = c.counters + (int64_t)h * kNumCounters;
     cn[kCntTokens] += T;
     cn[kCntMerged] += M;
@@ -501,6 +588,9 @@ __global__ __launch_bounds__(kApplyThreads, FASTAR_APPLY_OCC) void apply_kernel(
     store_mirror_vec<T, E>(kmir + mrow, xk);  // inputs are storage-exact: copies
     store_mirror_vec<T, E>(vmir + mrow, xv);
     if (gl == 0) {
+      if (it.y == -2)  // the evicted group's tokens, an order-free integer sum
+        atomicAdd(reinterpret_cast<unsigned long long*>(c.evicted_tokens + h),
+                  (unsigned long long)c.count[(int64_t)h * B + s]);
       c.count[(int64_t)h * B + s] = 1;
       c.last[(int64_t)h * B + s] = f;
       c.lb[(int64_t)h * Bp + s] = 0.0f;

@@ -1,21 +1,54 @@
 """Host transcription of the merge planner's eviction select (CPU only).
 
-The planning kernel picks the slots to evict with a radix select on each slot's
-last-update frame (8-bit digits, most significant first, digits above the
-largest possible value frame - 1 skipped), then breaks ties on the cut-off
-frame by slot id.  This file replays those steps in Python, digit by digit as
-the kernel takes them, and checks them against the eviction rule itself
-(smallest (last, slot) among the slots not merged into this frame), and that
-the kernel's guard fires — fewer slots found than needed — for the states the
-host now refuses to import (a last-update frame at or after the frame counter).
+The planning kernel finds the cut-off frame of the eviction by walking the
+distinct last-update frames of the eligible slots upward (a block-wide minimum
+and its count per step, up to eight steps), and falls back to a radix select
+(8-bit digits, most significant first, digits above the largest possible value
+frame - 1 skipped) when eight values do not cover the need; ties on the cut-off
+frame go by slot id.  This file replays those steps in Python as the kernel
+takes them, checks them against the eviction rule itself (smallest
+(last, slot) among the slots not merged into this frame), and checks that the
+kernel's guard fires — fewer slots found than needed — for the states the host
+refuses to import (a last-update frame at or after the frame counter).
 """
 
 import numpy as np
 import pytest
 
 
-def kernel_select(last, eligible, n_live, need, f):
+def _take(last, eligible, n_live, cut, take_eq):
+    out, taken = [], 0
+    for s in range(n_live):
+        if not eligible[s]:
+            continue
+        lv = int(last[s]) & 0xFFFFFFFF
+        if lv < cut:
+            out.append(s)
+        elif lv == cut and taken < take_eq:
+            out.append(s)
+            taken += 1
+    return out
+
+
+def kernel_select(last, eligible, n_live, need, f, walk_steps=8):
     """The planner's select; returns the evicted slots in ascending order."""
+    keys = [int(last[s]) & 0xFFFFFFFF for s in range(n_live) if eligible[s]]
+    krem, lo = need, 0
+    for _ in range(walk_steps):
+        above = [k for k in keys if k >= lo]
+        if not above:
+            break
+        mv = min(above)
+        cv = sum(1 for k in keys if k == mv)
+        if cv >= krem:
+            return _take(last, eligible, n_live, mv, krem)
+        krem -= cv
+        lo = mv + 1
+    return radix_select(last, eligible, n_live, need, f)
+
+
+def radix_select(last, eligible, n_live, need, f):
+    """The planner's fallback: radix select on 8-bit digits."""
     krem, prefix, maxv = need, 0, (f - 1) & 0xFFFFFFFF
     for shift in (24, 16, 8, 0):
         if shift > 0 and (maxv >> shift) == 0:
@@ -37,17 +70,7 @@ def kernel_select(last, eligible, n_live, need, f):
             dg += 1
         krem -= cum
         prefix |= dg << shift
-    cut, take_eq, taken, out = prefix, krem, 0, []
-    for s in range(n_live):
-        if not eligible[s]:
-            continue
-        lv = int(last[s]) & 0xFFFFFFFF
-        if lv < cut:
-            out.append(s)
-        elif lv == cut and taken < take_eq:
-            out.append(s)
-            taken += 1
-    return out
+    return _take(last, eligible, n_live, prefix, krem)
 
 
 def rule_select(last, eligible, n_live, need):
@@ -67,9 +90,10 @@ def test_select_is_the_lru_rule_on_valid_states(seed):
     if n_el == 0:
         return
     need = int(rng.integers(1, n_el + 1))
-    got = kernel_select(last, eligible, n_live, need, f)
-    assert got == rule_select(last, eligible, n_live, need)
-    assert len(got) == need
+    want = rule_select(last, eligible, n_live, need)
+    for steps in (8, 0, 2):   # the kernel's walk, the radix path alone, a short walk
+        got = kernel_select(last, eligible, n_live, need, f, walk_steps=steps)
+        assert got == want and len(got) == need
 
 
 def test_guard_fires_on_last_update_frames_from_the_future():
@@ -80,12 +104,21 @@ def test_guard_fires_on_last_update_frames_from_the_future():
     n_live, f, need = 400, 1, 100
     last = np.arange(600, 1000)
     eligible = np.ones(n_live, dtype=bool)
-    got = kernel_select(last, eligible, n_live, need, f)
-    assert len(got) < need
+    for steps in (8, 0):
+        assert len(kernel_select(last, eligible, n_live, need, f, walk_steps=steps)) < need
 
 
 def test_guard_fires_when_too_few_slots_are_eligible():
     last = np.zeros(10, dtype=np.int64)
     eligible = np.zeros(10, dtype=bool)
     eligible[:3] = True
-    assert len(kernel_select(last, eligible, 10, 5, 4)) == 3
+    for steps in (8, 0):
+        assert len(kernel_select(last, eligible, 10, 5, 4, walk_steps=steps)) == 3
+
+
+def test_walk_covers_many_distinct_frames_through_the_fallback():
+    # the need spans 20 distinct frames: more than the walk's eight steps
+    last = np.repeat(np.arange(20), 5)
+    eligible = np.ones(100, dtype=bool)
+    got = kernel_select(last, eligible, 100, 97, 21)
+    assert got == rule_select(last, eligible, 100, 97)

@@ -976,3 +976,42 @@ def test_import_without_frame_keeps_the_frame_counter():
     st = cache.export_state()
     cache.import_state({"codes": st["codes"]})
     assert cache.stats()["frame"] == frame
+
+
+@pytest.mark.parametrize("tokens", [30, 97])   # 30: evictions span 6 frames; 97: all 20
+def test_eviction_across_many_last_update_frames(tokens):
+    """Eviction when the evicted slots span several last-update frames: 100
+    live slots updated at frames 0..19 (5 each, scattered over the slot ids),
+    then a frame of fresh keys that all insert.  The planner walks the
+    distinct frames upward for a few of them and falls back to a radix
+    select beyond; decisions and state are checked against the oracle."""
+    from oracle import HeadCache
+    w = WORKLOADS["tiny"].with_(heads=2, budget=100, tokens_per_frame=tokens)
+    rng = np.random.default_rng(70 + tokens)
+    planes = DriftStream(w).planes()
+    orc = TempCacheOracle.for_workload(w, planes)
+    for hc in orc.heads:
+        hc.n_live = 100
+        hc.K_m[:] = rng.standard_normal((100, w.head_dim)).astype(np.float32)
+        hc.V_m[:] = rng.standard_normal((100, w.head_dim)).astype(np.float32)
+        hc.k_hat[:] = hc.K_m
+        hc.v_hat[:] = hc.V_m
+        hc.count[:] = rng.integers(1, 4, size=100)
+        hc.last[:] = rng.permutation(np.repeat(np.arange(20), 5))
+        hc.codes[:] = hc.hash(hc.k_hat)
+        hc.frame = 20
+        hc._rebuild_buckets()
+    cache = _cache_for(w, planes)
+    cache.import_state(oracle_state_for_import(orc, w.dtype))
+    K = rng.standard_normal((w.heads, tokens, w.head_dim)).astype(np.float32)
+    V = rng.standard_normal((w.heads, tokens, w.head_dim)).astype(np.float32)
+    res = orc.process_frame(K, V)
+    assert all(not r.merged.any() and len(r.evicted) == tokens for r in res)
+    slot_out = torch.empty((w.heads, tokens), dtype=torch.int32, device="cuda")
+    cache.match_merge(to_device(K, w.dtype), to_device(V, w.dtype), tokens, 1, slot_out=slot_out)
+    torch.cuda.synchronize()
+    so = slot_out.cpu().numpy()
+    for h in range(w.heads):
+        np.testing.assert_array_equal(so[h], res[h].slot)
+    compare_state(cache.export_state(), orc, w.dtype)
+    assert cache.stats()["refused_frames"] == 0
