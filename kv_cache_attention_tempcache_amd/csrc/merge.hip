@@ -69,12 +69,15 @@ struct PlanShared {
 constexpr int kLeadShift = 42, kMemShift = 21;
 constexpr uint64_t kField = (1ull << 21) - 1;
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c, MergeArgs a) {
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c, MergeArgs a,
+                                                           int stage_keys) {
   extern __shared__ __attribute__((aligned(16))) int32_t sm[];
   const int T = a.T, B = dm.B;
   int32_t* dec_s = sm;                 // [T] merge target of each token, -1 = insert
   int32_t* ins_list = dec_s + T;       // [T] inserting tokens, ascending
   int32_t* ev_list = ins_list + T;     // [T] evicted slots, ascending
+  int32_t* lead_s = ev_list + T;       // [T] group size if the token leads its group, else 0
+  uint32_t* keys_s = reinterpret_cast<uint32_t*>(lead_s + T);  // [B] eviction keys, if staged
   __shared__ uint64_t s_scan64[kPlanWaves];
   __shared__ int s_scan[kPlanWaves];
   __shared__ int hist[256];
@@ -85,13 +88,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   const int n_live = c.n_live[h];
   int32_t* owner = c.owner + (int64_t)h * B;
   int32_t* gsize = c.gsize + (int64_t)h * B;
-  for (int i = tid; i < T; i += kPlanThreads) dec_s[i] = c.dec[(int64_t)h * B + i];
+  // 0. per token (strided over the threads, every load of a thread issued
+  //    together): its merge target, and whether it leads the target's group
+  //    (the lowest merging token, recorded by the match step) with the group
+  //    size, or 0.
+  constexpr int kPerT = (FASTAR_MAX_TOKENS_PER_FRAME + kPlanThreads - 1) / kPlanThreads;
+  {
+    int dv[kPerT], ow[kPerT], gs[kPerT];
+#pragma unroll
+    for (int k = 0; k < kPerT; ++k) {
+      const int i = tid + k * kPlanThreads;
+      dv[k] = i < T ? c.dec[(int64_t)h * B + i] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kPerT; ++k) {
+      const int sx = dv[k] < 0 ? 0 : dv[k];
+      ow[k] = owner[sx];
+      gs[k] = gsize[sx];
+    }
+#pragma unroll
+    for (int k = 0; k < kPerT; ++k) {
+      const int i = tid + k * kPlanThreads;
+      if (i >= T) continue;
+      dec_s[i] = dv[k];
+      lead_s[i] = (dv[k] >= 0 && ow[k] == i) ? gs[k] : 0;
+    }
+  }
   __syncthreads();
 
   // 1. per token: leader of a merge group (its group size), or insert.  A
   //    thread's tokens are few (T <= FASTAR_MAX_TOKENS_PER_FRAME): their
   //    leader flags and group sizes stay in registers for the passes below.
-  constexpr int kPerT = (FASTAR_MAX_TOKENS_PER_FRAME + kPlanThreads - 1) / kPlanThreads;
   const int per_t = (T + kPlanThreads - 1) / kPlanThreads;
   const int t_lo = min(T, tid * per_t), t_hi = min(T, t_lo + per_t);
   int lead_size[kPerT];  // group size if token t_lo+k leads its group, else 0
@@ -101,12 +128,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
     const int i = t_lo + k;
     lead_size[k] = 0;
     if (i >= t_hi) continue;
-    const int s = dec_s[i];
-    if (s < 0) {
+    if (dec_s[i] < 0) {
       mine += 1;
-    } else if (owner[s] == i) {
-      lead_size[k] = gsize[s];
-      mine += (1ull << kLeadShift) | ((uint64_t)lead_size[k] << kMemShift);
+    } else {
+      lead_size[k] = lead_s[i];
+      if (lead_size[k]) mine += (1ull << kLeadShift) | ((uint64_t)lead_size[k] << kMemShift);
     }
   }
   uint64_t tot = 0;
@@ -158,12 +184,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
     const int s_lo = min(n_live, tid * per_s), s_hi = min(n_live, s_lo + per_s);
     const int32_t* last = c.last + (int64_t)h * B;
     uint32_t key[kPerS];
+    if (stage_keys) {
+      // coalesced: thread tid reads slots tid, tid + 1024, ... into LDS, four
+      // slots' loads in flight at a time; then each thread takes its run
+      for (int s0 = tid; s0 < n_live; s0 += 4 * kPlanThreads) {
+        int32_t ow[4], lv[4];
 #pragma unroll
-    for (int k = 0; k < kPerS; ++k) {
-      const int sx = min(s_lo + k, B - 1);
-      const int32_t ow = owner[sx];
-      const int32_t lv = last[sx];
-      key[k] = (s_lo + k < s_hi && ow == kNoOwner) ? (uint32_t)lv : 0xffffffffu;
+        for (int u = 0; u < 4; ++u) {
+          const int sx = min(s0 + u * kPlanThreads, n_live - 1);
+          ow[u] = owner[sx];
+          lv[u] = last[sx];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int sx = s0 + u * kPlanThreads;
+          if (sx < n_live) keys_s[sx] = ow[u] == kNoOwner ? (uint32_t)lv[u] : 0xffffffffu;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kPerS; ++k)
+        key[k] = s_lo + k < s_hi ? keys_s[s_lo + k] : 0xffffffffu;
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPerS; ++k) {
+        const int sx = min(s_lo + k, B - 1);
+        const int32_t ow = owner[sx];
+        const int32_t lv = last[sx];
+        key[k] = (s_lo + k < s_hi && ow == kNoOwner) ? (uint32_t)lv : 0xffffffffu;
+      }
     }
     // The need-th smallest key among the eligible slots (the cut-off frame)
     // and how many slots with exactly that key to evict.  Eviction takes the
@@ -669,13 +718,18 @@ __global__ __launch_bounds__(256) void finalize_kernel(Dims dm, CacheDev c) {
 }  // namespace
 
 hipError_t launch_plan(const Dims& dm, const CacheDev& c, const MergeArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)a.T * 3 * 4;  // 96 KiB at FASTAR_MAX_TOKENS_PER_FRAME
+  // four per-token lists (128 KiB at FASTAR_MAX_TOKENS_PER_FRAME), and the
+  // eviction keys of every slot staged in LDS when they fit beside them
+  const size_t lists = (size_t)a.T * 4 * 4;
+  const size_t keys = (size_t)dm.B * 4;
+  const int stage = lists + keys <= 144 * 1024 ? 1 : 0;
+  const size_t lds = lists + (stage ? keys : 0);
   if (lds > 64 * 1024) {  // beyond the default dynamic LDS limit of a launch
     hipError_t e = hipFuncSetAttribute((const void*)plan_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(dm.H), dim3(kPlanThreads), lds, s, dm, c, a);
+  hipLaunchKernelGGL(plan_kernel, dim3(dm.H), dim3(kPlanThreads), lds, s, dm, c, a, stage);
   return hipGetLastError();
 }
 
