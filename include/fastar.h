@@ -352,6 +352,30 @@ fastar_status fastar_attend_subset(const void* q_dev, int64_t q_stride_h, int64_
                                    void* o_dev, int64_t o_stride_h, int64_t o_stride_n,
                                    void* stream);
 
+/* The AnnCA step in two launches (section 2B "Mecanismo": latent queries and
+ * prompt keys share one hashed space; per frame, only the prompt tokens that
+ * share a bucket with at least one of the frame's queries are attended).
+ * First the queries are hashed into q_codes_dev (uint32 [H][L][F*Nf], written
+ * exactly as fastar_hash writes them, under q_planes_dev [L][b][128] bf16);
+ * then one attention launch has every workgroup build its frame's bucket
+ * bitmaps from those codes, keep prompt row j iff p_codes_dev[(h*L + t)*Np + j]
+ * (uint32, e.g. from fastar_hash of the prompt keys) equals a query's code of
+ * table t for some t, and attend each query of the frame over the kept rows
+ * only (no logit bias); a frame that keeps nothing gets zero outputs.  The
+ * outputs equal fastar_hash of the queries, fastar_annca_select and
+ * fastar_attend_subset, without the selection buffers and the select launch.
+ * bf16 only, d = 128, 1 <= L <= 4, 0 <= b <= 16, Np <= 4096; q_dev, k_dev,
+ * v_dev, o_dev and strides as fastar_attend_subset (frame g's queries are rows
+ * [g*Nf, (g+1)*Nf) of head h); scale > 0, or 0 for 1/sqrt(d).  q_codes_dev is
+ * caller-owned and holds the query codes on return. */
+fastar_status fastar_annca_attend(const void* q_dev, int64_t q_stride_h, int64_t q_stride_n,
+                                  const void* q_planes_dev, int32_t L, int32_t b,
+                                  uint32_t* q_codes_dev, const uint32_t* p_codes_dev,
+                                  const void* k_dev, const void* v_dev,
+                                  int64_t kv_stride_h, int64_t kv_stride_n, int32_t Nf, int32_t F,
+                                  int32_t Np, int32_t H, int32_t d, float scale, void* o_dev,
+                                  int64_t o_stride_h, int64_t o_stride_n, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the AnnCA
  * step of fastar_annca_select followed by fastar_attend_subset, with the

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     Cache,
     CacheConfig,
     FastarError,
+    annca_attend,
     annca_attend_static,
     annca_select,
     attend_subset,

@@ -101,6 +101,9 @@ _SIGS = {
     "fastar_attend_subset": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _I64, _I64, _VP, _VP,
                                             _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _F, _VP,
                                             _I64, _I64, _VP]),
+    "fastar_annca_attend": (ctypes.c_int, [_VP, _I64, _I64, _VP, _I32, _I32, _VP, _VP, _VP,
+                                           _VP, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _F,
+                                           _VP, _I64, _I64, _VP]),
     "fastar_annca_attend_static": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _I64, _I64,
                                                   _VP, _I32, _I32, _I32, _I32, _I32, _I32,
                                                   ctypes.c_int, _F, _VP, _I64, _I64, _VP]),
@@ -570,3 +573,40 @@ def annca_attend_static(q: torch.Tensor, q_codes: torch.Tensor, k: torch.Tensor,
         k.stride(1), _ptr(p_codes), NQ // frames, frames, Np, H, d, L, dt, float(scale),
         _ptr(out), out.stride(0), out.stride(1), _stream(stream)))
     return out
+
+
+def annca_attend(q: torch.Tensor, q_planes: torch.Tensor, tables: int, bits: int,
+                 p_codes: torch.Tensor, k: torch.Tensor, v: torch.Tensor, frames: int,
+                 scale: float = 0.0, out: torch.Tensor | None = None,
+                 q_codes: torch.Tensor | None = None, stream=None):
+    """The AnnCA step in two launches: hash the queries into q_codes ([H][L][NQ]
+    int32, allocated when not given), then per frame keep the prompt rows that
+    share a bucket with its queries and attend over the kept rows, selection in
+    the attention kernel's prologue (bf16, d = 128)."""
+    _require(q, "q", torch.bfloat16)
+    _require(k, "k", torch.bfloat16)
+    _require(v, "v", torch.bfloat16)
+    _require(q_planes, "q_planes", torch.bfloat16)
+    _require(p_codes, "p_codes", torch.int32)
+    H, NQ, d = q.shape
+    Np = k.shape[1]
+    if k.shape != v.shape or k.stride() != v.stride() or NQ % frames:
+        raise ValueError("bad shapes")
+    if tuple(p_codes.shape) != (H, tables, Np) or not p_codes.is_contiguous():
+        raise ValueError("p_codes must be contiguous [H][L][Np]")
+    if not q_planes.is_contiguous() or q_planes.numel() != tables * bits * d:
+        raise ValueError("q_planes must be contiguous [L][b][d]")
+    if out is None:
+        out = torch.empty_like(q)
+    if q_codes is None:
+        q_codes = torch.empty((H, tables, NQ), dtype=torch.int32, device=q.device)
+    _require(q_codes, "q_codes", torch.int32)
+    if tuple(q_codes.shape) != (H, tables, NQ) or not q_codes.is_contiguous():
+        raise ValueError("q_codes must be contiguous [H][L][NQ]")
+    _check(library().fastar_annca_attend(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(q_planes), tables, bits, _ptr(q_codes),
+        _ptr(p_codes), _ptr(k), _ptr(v), k.stride(0), k.stride(1), NQ // frames, frames, Np, H, d,
+        float(scale),
+        _ptr(out), out.stride(0), out.stride(1), _stream(stream)))
+    return out
+

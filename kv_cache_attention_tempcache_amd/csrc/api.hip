@@ -919,6 +919,73 @@ fastar_status fastar_attend_subset(const void* q_dev, int64_t q_stride_h, int64_
   return ok();
 }
 
+fastar_status fastar_annca_attend(const void* q_dev, int64_t q_stride_h, int64_t q_stride_n,
+                                  const void* q_planes_dev, int32_t L, int32_t b,
+                                  uint32_t* q_codes_dev, const uint32_t* p_codes_dev,
+                                  const void* k_dev, const void* v_dev,
+                                  int64_t kv_stride_h, int64_t kv_stride_n, int32_t Nf, int32_t F,
+                                  int32_t Np, int32_t H, int32_t d, float scale, void* o_dev,
+                                  int64_t o_stride_h, int64_t o_stride_n, void* stream) {
+  FASTAR_REQUIRE(d == 128, "the fused AnnCA step needs d = 128");
+  FASTAR_REQUIRE(H >= 1 && F >= 1, "H and F must be >= 1");
+  FASTAR_REQUIRE(L >= 1 && L <= 4 && b >= 0 && b <= 16, "the fused AnnCA step takes 1..4 tables "
+                                                         "of 0..16 bits");
+  FASTAR_REQUIRE(Nf >= 0 && Nf <= FASTAR_MAX_ANNCA_QUERIES_PER_FRAME, "Nf out of range");
+  FASTAR_REQUIRE(Np >= 1 && Np <= 4096, "the fused AnnCA step takes 1..4096 prompt tokens");
+  FASTAR_REQUIRE(std::isfinite(scale) && scale >= 0.0f,
+                 "scale must be finite and >= 0 (0 selects 1/sqrt(d))");
+  if (Nf == 0) return ok();
+  FASTAR_REQUIRE(q_dev && k_dev && v_dev && o_dev && q_codes_dev && p_codes_dev, "NULL pointer");
+  FASTAR_REQUIRE(q_planes_dev != nullptr || b == 0, "q_planes is NULL");
+  FASTAR_REQUIRE(aligned(q_dev, 16) && aligned(k_dev, 16) && aligned(v_dev, 16) &&
+                     aligned(o_dev, 16) && aligned(q_planes_dev, 16) &&
+                     aligned(q_codes_dev, 4) && aligned(p_codes_dev, 4),
+                 "q, k, v, o and the hyperplanes must be 16-byte aligned, codes 4-byte aligned");
+  FASTAR_REQUIRE(q_stride_h % 8 == 0 && q_stride_n % 8 == 0 && kv_stride_h % 8 == 0 &&
+                     kv_stride_n % 8 == 0 && o_stride_h % 8 == 0 && o_stride_n % 8 == 0 &&
+                     q_stride_n >= d && kv_stride_n >= d && o_stride_n >= d,
+                 "strides must be multiples of 16 bytes");
+  AttendArgs a{};
+  a.q = q_dev;
+  a.sq_h = q_stride_h;
+  a.sq_n = q_stride_n;
+  a.k = k_dev;
+  a.v = v_dev;
+  a.sk_h = kv_stride_h;
+  a.sk_n = kv_stride_n;
+  a.n_keys_const = Np;
+  a.o = o_dev;
+  a.so_h = o_stride_h;
+  a.so_n = o_stride_n;
+  a.H = H;
+  a.d = d;
+  a.Nseg = Nf;
+  a.F = F;
+  a.scale = scale == 0.0f ? 1.0f / std::sqrt((float)d) : scale;
+  a.q_codes = q_codes_dev;
+  a.p_codes = p_codes_dev;
+  a.sel_L = L;
+  // the queries' codes, as fastar_hash computes them, then selection and
+  // attention in one launch
+  HashArgs ha{};
+  ha.x = q_dev;
+  ha.sx_h = q_stride_h;
+  ha.sx_n = q_stride_n;
+  ha.H = H;
+  ha.N = F * Nf;
+  ha.d = d;
+  ha.L = L;
+  ha.b = b;
+  ha.planes = q_planes_dev;
+  ha.codes = q_codes_dev;
+  ha.codes_ld = (int64_t)F * Nf;
+  ha.codes_col0 = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FASTAR_HIP(launch_hash_bf16(ha, s));
+  FASTAR_HIP(launch_annca_fused(a, s));
+  return ok();
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

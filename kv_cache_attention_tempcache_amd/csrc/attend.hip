@@ -183,6 +183,90 @@ struct CCfg {
   }
 };
 
+// AnnCA selection by one workgroup of 512 threads for frame g of head h (FAST-AR
+// summary, section 2B "Mecanismo": a prompt token is kept for a frame iff it
+// shares a bucket with at least one of the frame's queries).  Every code of
+// the frame's queries sets a bit of its table's 2^16-bit LDS bitmap; each
+// prompt code tests its bit; the kept rows are compacted into `sel` in
+// ascending order.  Uses the ring buffers' LDS before any copy is issued:
+// bitmaps in `bmb`, keep flags in `kf`.  Returns the kept count
+// (block-uniform).
+__device__ int annca_select_in_block(const AttendArgs& sa, int h, int g, uint8_t* kf,
+                                     uint8_t* bmb, int32_t* sel) {
+  constexpr int kThreads = 512, kWaves = kThreads / 64;
+  __shared__ int s_cnt[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = sa.sel_L, Np = sa.n_keys_const, Nf = sa.Nseg;
+  uint32_t* bm = reinterpret_cast<uint32_t*>(bmb);  // [L][2048]
+  for (int i = tid; i < L * 512; i += kThreads) reinterpret_cast<uint4*>(bm)[i] = uint4{0, 0, 0, 0};
+  // the frame's codes: table t holds Nf consecutive words per head row.  A
+  // thread requests up to kPer codes of every table before its first bitmap
+  // update, so the loads are in flight together.
+  constexpr int kPer = 4;
+  const int64_t nq = (int64_t)sa.F * Nf;
+  const uint32_t* qc = sa.q_codes + (int64_t)h * L * nq + (int64_t)g * Nf;
+  // the prompt codes of row tid are requested now too (the first pass of the
+  // test below uses them)
+  const uint32_t* pc = sa.p_codes + (int64_t)h * L * Np;
+  uint32_t pc0[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pc0[t] = t < L && tid < Np ? pc[(int64_t)t * Np + tid] : 0xffffffffu;
+  __syncthreads();
+  for (int r0 = 0; r0 < Nf; r0 += kPer * kThreads) {
+    uint32_t cv[4][kPer];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int r = r0 + u * kThreads + tid;
+        cv[t][u] = t < L && r < Nf ? qc[(int64_t)t * nq + r] : 0xffffffffu;
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        if (cv[t][u] < 65536u) atomicOr(&bm[t * 2048 + (cv[t][u] >> 5)], 1u << (cv[t][u] & 31u));
+  }
+  __syncthreads();
+  // prompt codes test their bits
+  for (int j = tid; j < Np; j += kThreads) {
+    uint32_t code[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      code[t] = j == tid ? pc0[t] : t < L ? pc[(int64_t)t * Np + j] : 0xffffffffu;
+    uint32_t hit = 0u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      hit |= code[t] >> 16 ? 0u : (bm[t * 2048 + (code[t] >> 5)] >> (code[t] & 31u)) & 1u;
+    kf[j] = (uint8_t)hit;
+  }
+  __syncthreads();
+  // kept ids in ascending order: each thread a contiguous run, a block scan
+  const int per = (Np + kThreads - 1) / kThreads;
+  const int lo = min(Np, tid * per), hi = min(Np, lo + per);
+  int cnt = 0;
+  for (int j = lo; j < hi; ++j) cnt += kf[j];
+  int x = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_cnt[wave] = x;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    base += w < wave ? s_cnt[w] : 0;
+    total += s_cnt[w];
+  }
+  int pos = base + x - cnt;
+  for (int j = lo; j < hi; ++j)
+    if (kf[j]) sel[pos++] = j;
+  __syncthreads();
+  return total;
+}
+
 // QB blocks of 32 queries per wave: every K or V fragment read from LDS feeds
 // QB MFMAs, which is what keeps the kernel below the LDS bandwidth (one 1 KiB
 // operand per 32x32x16 MFMA would need all 128 B/clk of a CU's LDS).
@@ -191,11 +275,13 @@ struct CCfg {
 // queries attends over rows of arbitrary [H][N][d] key and value arrays with
 // no bias: all sa.n_keys_const rows, or the first n_keys[h][g] rows of the
 // segment's gather list sa.sel, staged in LDS at the start.
-template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET, bool RAW, bool REG>
+template <int D, int BN, int WAVES, int QB, int NBUF, bool SUBSET, bool RAW, bool REG,
+          bool SEL = false>
 __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kernel(
     Dims dm, CacheDev c, CacheAttendArgs a, AttendArgs sa, int qtiles) {
   using C = CCfg<D, BN, WAVES, QB>;
   static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  static_assert(!SEL || (SUBSET && NBUF == 4 && D == 128), "selection in the kernel");
   extern __shared__ int32_t sel_lds[];  // SUBSET with a gather list
   // A ring of NBUF distinct LDS objects: tile it is read from one while the
   // copies of tiles it+1 .. it+NBUF-1 are in flight into the others.  Distinct
@@ -223,14 +309,32 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   }
   // queries, outputs, key/value rows of this block
   const int Np = SUBSET ? sa.n_keys_const : 0;  // rows of the subset arrays
-  const int nkeys = SUBSET ? (sa.n_keys ? min(max(sa.n_keys[h * sa.F + g], 0), Np) : Np)
-                           : c.n_live[h];
   const float cscale = (SUBSET ? sa.scale : a.scale) * kLog2e;
   const int nq = SUBSET ? sa.Nseg : a.Nq;
   const int64_t sq_n = SUBSET ? sa.sq_n : a.sq_n, so_n = SUBSET ? sa.so_n : a.so_n;
   const uint16_t* qbase =
       SUBSET ? static_cast<const uint16_t*>(sa.q) + (int64_t)h * sa.sq_h + (int64_t)g * sa.Nseg * sa.sq_n
              : static_cast<const uint16_t*>(a.q) + (int64_t)h * a.sq_h;
+  // queries of this wave: qi = qt*BM + wave*32*QB + qb*32 + m (requested
+  // first, so that their latency overlaps the selection below)
+  bf16x8_t Qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qt * C::BM + (wave * QB + qb) * 32 + m;
+    const bool qok = qi < nq;
+    const uint16_t* qp = qbase + (int64_t)(qok ? qi : 0) * sq_n + hf * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
+      if (!qok) v = bf16x8_t{};
+      Qf[qb][ks] = v;
+    }
+  }
+  int nkeys_sel = 0;
+  if constexpr (SEL) nkeys_sel = annca_select_in_block(sa, h, g, buf1, buf3, sel_lds);
+  const int nkeys = SEL      ? nkeys_sel
+                    : SUBSET ? (sa.n_keys ? min(max(sa.n_keys[h * sa.F + g], 0), Np) : Np)
+                             : c.n_live[h];
   uint16_t* obase =
       SUBSET ? static_cast<uint16_t*>(sa.o) + (int64_t)h * sa.so_h + (int64_t)g * sa.Nseg * sa.so_n
              : static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h;
@@ -263,8 +367,8 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   const uint8_t* xkg = nx ? static_cast<const uint8_t*>(a.xk) + (int64_t)h * a.sx_h * 2 : nullptr;
   const uint8_t* xvg = nx ? static_cast<const uint8_t*>(a.xv) + (int64_t)h * a.sx_h * 2 : nullptr;
   const int64_t xrs = SUBSET ? 0 : a.sx_n * 2;  // bytes between raw rows
-  const bool gather = SUBSET && sa.sel != nullptr;  // block-uniform
-  if (gather) {
+  const bool gather = SEL || (SUBSET && sa.sel != nullptr);  // block-uniform
+  if (gather && !SEL) {
     const int32_t* sel = sa.sel + (int64_t)(h * sa.F + g) * sa.sel_ld;
     for (int i = tid; i < nkeys; i += C::kThreads) sel_lds[i] = min(max(sel[i], 0), Np - 1);
     __syncthreads();
@@ -340,20 +444,6 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     }
   };
 
-  // queries of this wave: qi = qt*BM + wave*32*QB + qb*32 + m
-  bf16x8_t Qf[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qt * C::BM + (wave * QB + qb) * 32 + m;
-    const bool qok = qi < nq;
-    const uint16_t* qp = qbase + (int64_t)(qok ? qi : 0) * sq_n + hf * (D / 2);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 8);
-      if (!qok) v = bf16x8_t{};
-      Qf[qb][ks] = v;
-    }
-  }
   // Transposing V reads: within each 16-lane group, source lane j reads 4
   // features (8 bytes) of key row 4*hf + j/4 at feature 16*(group%2) + 4*(j%4)
   // of a 32-feature block; lane i then holds 4 consecutive keys of feature
@@ -587,7 +677,7 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
 }
 
 // Subsets: 8 waves x 32 queries per workgroup per (head, segment); a gather
-// list is staged in LDS (up to 4 bytes per prompt row) beside a 2-deep ring.
+// list is staged in LDS (4 bytes per prompt row) beside the ring.
 template <int D, int NBUF>
 hipError_t launch_subset_cfg(const AttendArgs& a, hipStream_t s) {
   using C = CCfg<D, 64, 8, 1>;
@@ -606,10 +696,29 @@ hipError_t launch_subset_cfg(const AttendArgs& a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_annca_fused(const AttendArgs& a, hipStream_t s) {
+  using C = CCfg<128, 64, 8, 1>;
+  if (a.d != 128) return hipErrorInvalidValue;
+  const int qtiles = (a.Nseg + C::BM - 1) / C::BM;
+  const int blocks = a.H * a.F * qtiles;
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = (size_t)a.n_keys_const * 4;
+  auto kern = attend_cache_kernel<128, 64, 8, 1, 4, true, false, false, true>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(C::kThreads), lds, s, Dims{}, CacheDev{},
+                     CacheAttendArgs{}, a, qtiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
   if (a.count != nullptr) return hipErrorInvalidValue;  // no count bias on subsets
-  if (a.d == 128) return a.sel ? launch_subset_cfg<128, 2>(a, s) : launch_subset_cfg<128, 4>(a, s);
-  return a.sel ? launch_subset_cfg<64, 2>(a, s) : launch_subset_cfg<64, 4>(a, s);
+  // a gather list of up to 4096 prompt rows (16 KiB) fits beside the 4-deep
+  // ring; longer lists take the 2-deep one
+  const bool deep = a.sel == nullptr || a.n_keys_const <= 4096;
+  if (a.d == 128) return deep ? launch_subset_cfg<128, 4>(a, s) : launch_subset_cfg<128, 2>(a, s);
+  return deep ? launch_subset_cfg<64, 4>(a, s) : launch_subset_cfg<64, 2>(a, s);
 }
 
 #ifndef FASTAR_CACHE_NBUF

@@ -276,8 +276,18 @@ struct AttendArgs {
   const void* xv;
   int64_t sx_h, sx_n;
   int n_x;
+  // AnnCA selection inside the attention kernel (bf16, d = 128): query i of
+  // head h has code q_codes[(h*sel_L + t)*F*Nseg + i] in table t (codes
+  // < 2^16, sel_L <= 4), and a key row j is kept for frame g iff
+  // p_codes[(h*sel_L + t)*n_keys_const + j] equals the code of some query of
+  // the frame in some table t; sel and n_keys are unused
+  const uint32_t* q_codes;
+  const uint32_t* p_codes;
+  int sel_L;
 };
 hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s);
+// Subset attention with the AnnCA selection in its prologue (AttendArgs.q_codes).
+hipError_t launch_annca_fused(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s);
 
 // Key projection with SimHash codes in its epilogue: k = x W^T for N tokens,

@@ -1015,3 +1015,50 @@ def test_eviction_across_many_last_update_frames(tokens):
         np.testing.assert_array_equal(so[h], res[h].slot)
     compare_state(cache.export_state(), orc, w.dtype)
     assert cache.stats()["refused_frames"] == 0
+
+
+@pytest.mark.parametrize("heads,qpf,frames,bits", [(2, 300, 3, 16), (3, 77, 2, 12), (12, 1560, 3, 16),
+                                                   (2, 64, 1, 0)])
+def test_fused_annca_equals_hash_select_and_subset_attention(heads, qpf, frames, bits):
+    """Hashing the queries and then one attention launch that selects in its
+    prologue gives the three-launch path's output bit for bit (same codes, same
+    kept lists, same attention kernel) and leaves the hash entry's codes in
+    q_codes; on two sampled heads it is also within the bf16 bound of the
+    oracle's sparse attention.  bits = 0 keeps every prompt row."""
+    cp = ClusterPrompt(heads=heads, queries_per_frame=qpf, frames=frames, bits=bits)
+    planes = cp.planes()
+    q = to_device(cp.Q, "bf16")
+    kp, vp = to_device(cp.Kp, "bf16"), to_device(cp.Vp, "bf16")
+    pl = _planes_dev(planes, "bf16") if bits else torch.zeros(0, dtype=torch.bfloat16, device="cuda")
+    qc = fa.hash_codes(q, pl, cp.tables, cp.bits)
+    pc = fa.hash_codes(kp, pl, cp.tables, cp.bits)
+    sel, cnt = fa.annca_select(qc, pc, frames)
+    ref = fa.attend_subset(q, kp, vp, frames, sel, cnt)
+    qc_fused = torch.full_like(qc, -1)
+    got = fa.annca_attend(q, pl, cp.tables, cp.bits, pc, kp, vp, frames, q_codes=qc_fused)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.equal(qc_fused, qc)
+    if bits == 0:
+        assert (cnt.cpu().numpy() == cp.prompt_tokens).all()
+    gq, gp = qc.cpu().numpy().view(np.uint32), pc.cpu().numpy().view(np.uint32)
+    out = got.float().cpu().numpy()
+    for h in (0, heads - 1):
+        for g in range(frames):
+            rows = slice(g * qpf, (g + 1) * qpf)
+            r = oannca.annca_frame(cp.Q[h, rows], cp.Kp[h], cp.Vp[h], planes,
+                                   codes_q=np.ascontiguousarray(gq[h][:, rows].T),
+                                   codes_p=np.ascontiguousarray(gp[h].T))
+            assert np.abs(out[h, rows] - r["o_sparse"]).max() <= 2e-2
+
+
+def test_fused_annca_frame_keeping_nothing_gives_zeros():
+    cp = ClusterPrompt(heads=2, queries_per_frame=100, frames=2)
+    q = to_device(cp.Q, "bf16")
+    kp, vp = to_device(cp.Kp, "bf16"), to_device(cp.Vp, "bf16")
+    pl = _planes_dev(cp.planes(), "bf16")
+    # prompt codes wider than 16 bits match no 16-bit query code
+    pc = torch.full((2, cp.tables, cp.prompt_tokens), 1 << 20, dtype=torch.int32, device="cuda")
+    got = fa.annca_attend(q, pl, cp.tables, cp.bits, pc, kp, vp, 2)
+    torch.cuda.synchronize()
+    assert (got == 0).all()
