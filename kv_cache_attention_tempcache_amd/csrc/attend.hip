@@ -18,7 +18,8 @@
 //     exactly the k-order the accumulator produced them; A = 8 keys of one
 //     feature, gathered from row-major V in LDS by transposing LDS reads.
 //   K, V (and log2-count) tiles of 64 keys move HBM -> LDS with direct-to-LDS
-//     loads into a ring of buffers, several tiles ahead of the one in use.
+//     loads into a ring of buffers, several tiles ahead of the one in use
+//     (slot tiles as buffer loads: scalar tile offset, fixed lane offsets).
 //   Blocks are renumbered so each XCD (blocks are dealt round-robin over the 8
 //     XCDs) gets a contiguous range of (head, query tile) and shares its L2.
 // f32 path (small fp32 workloads): one thread per query, fp32 online softmax.
@@ -267,6 +268,18 @@ __device__ int annca_select_in_block(const AttendArgs& sa, int h, int g, uint8_t
   return total;
 }
 
+// One 16-byte-per-lane direct-to-LDS copy through a buffer load: `base` and
+// `bytes` describe the rows as a buffer resource (descriptor word 3: raw
+// 32-bit data, no swizzle), `soff` is the tile's byte offset (a scalar) and
+// `voff` the lane's fixed byte offset inside the tile, so a copy needs no
+// vector address arithmetic.
+__device__ __forceinline__ void copy16_lds(const uint8_t* base, int bytes, uint32_t voff, int soff,
+                                           lds_void_t* dst) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
 // QB blocks of 32 queries per wave: every K or V fragment read from LDS feeds
 // QB MFMAs, which is what keeps the kernel below the LDS bandwidth (one 1 KiB
 // operand per 32x32x16 MFMA would need all 128 B/clk of a CU's LDS).
@@ -374,8 +387,9 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     __syncthreads();
   }
 
-  // Copy addresses: a wave-uniform tile base plus per-lane byte offsets that
-  // do not change from tile to tile, so issuing a copy costs no vector math.
+  // Copy addresses: a wave-uniform tile offset plus per-lane byte offsets that
+  // do not change from tile to tile, so issuing a slot tile's copy costs no
+  // vector math.
   // Wave w copies the 1 KiB chunks w, w + WAVES, ... of the K and V tiles; LDS
   // position (row, chunk) receives global chunk chunk ^ swz(row).
   // In a subset, a lane's source row is looked up per tile instead (rows past
@@ -393,6 +407,9 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     koff[j] = (uint32_t)(rb + ((slot ^ C::kswz(row)) << 4));
     voff[j] = (uint32_t)(rb + ((slot ^ C::vswz(row)) << 4));
   }
+  // the head's K (and region) rows and V rows, as buffer sizes for the copies
+  const int kbytes = SUBSET ? 0 : (REG ? dm.R * dm.Bp : dm.Bp) * C::kRowBytes;
+  const int vbytes = SUBSET ? 0 : dm.Bp * C::kRowBytes;
   auto issue = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
     const bool raw = RAW && k0 >= ntc * BN;  // block-uniform
     // REG: tile k0/BN is tile u of region r; K and shift rows r*Bp + u*BN, V rows u*BN
@@ -407,6 +424,14 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
       const int i = wave + j * WAVES;
+      if constexpr (!SUBSET) {
+        if (!raw) {  // slot tiles: scalar tile offset, fixed lane offsets
+          copy16_lds(kg, kbytes, koff[j], kr * C::kRowBytes, (lds_void_t*)(buf + i * 1024));
+          copy16_lds(vg, vbytes, voff[j], vr * C::kRowBytes,
+                     (lds_void_t*)(buf + C::kKBytes + i * 1024));
+          continue;
+        }
+      }
       const uint8_t* ks;
       const uint8_t* vs;
       if constexpr (SUBSET) {
@@ -570,6 +595,10 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
             ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
           }
           lrun[qb] = ls;
+          // keep the sum beside the conversions, while the packed weights are
+          // still in registers (else it sinks into the next tile and some
+          // weights are converted again)
+          asm volatile("" : "+v"(lrun[qb]));
         }
         // A operand: feature db*32 + m, keys kb*32 + kk*16 + {4*hf..4*hf+3}
         // then {8+4*hf..8+4*hf+3}, the key order of the P fragment
