@@ -517,10 +517,9 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
 
   // One key tile: read `cur`, issue the copy of tile it+NBUF-1 into `nxt`
   // (the buffer read in the previous step).
-  auto step = [&](const uint8_t* cur, uint8_t* nxt, int it, int nt) __attribute__((always_inline)) {
+  auto compute = [&](const uint8_t* cur) __attribute__((always_inline)) {
     const uint8_t* vt_lds = cur + C::kKBytes;
     const float* lb_lds = reinterpret_cast<const float*>(cur + C::kKBytes + C::kVBytes);
-    if (it + NBUF - 1 < nt) issue((it + NBUF - 1) * BN, nxt);
 
     // The accumulators start at the tile's shifts (already divided by the
     // logit scale): the rows of lane (m, hf) are 8*jg + 4*hf + 0..3 of each
@@ -617,29 +616,56 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
         }
       }
     }
+  };
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int it, int nt) __attribute__((always_inline)) {
+    if (it + NBUF - 1 < nt) issue((it + NBUF - 1) * BN, nxt);
+    compute(cur);
     // Tile it+1 must have landed; the copies of tiles it+2 .. it+NBUF-1
     // stay in flight.
     wait_barrier(min(nt - 1, it + NBUF - 1) - (it + 1));
   };
 
   const int nt = REG ? a.n_reg * ntc : ntc + (nx + BN - 1) / BN;
+  if constexpr (NBUF == 4) {
+    // One barrier per two tiles: tiles it, it+1 are read while the copies of
+    // it+2, it+3 land; after the barrier (every wave is done with it, it+1)
+    // their buffers receive it+4, it+5.  Measured slightly faster than a
+    // barrier per tile (0.5-1.3 % in same-process comparisons).
+    issue(0, buf0);
+    if (1 < nt) issue(BN, buf1);
+    if (2 < nt) issue(2 * BN, buf2);
+    if (3 < nt) issue(3 * BN, buf3);
+    wait_barrier(max(min(nt, 4) - 2, 0));
+    for (int it = 0; it < nt; it += 4) {
+      compute(buf0);
+      if (it + 1 < nt) compute(buf1);
+      if (it + 2 < nt) {
+        wait_barrier(0);
+        if (it + 4 < nt) issue((it + 4) * BN, buf0);
+        if (it + 5 < nt) issue((it + 5) * BN, buf1);
+        compute(buf2);
+        if (it + 3 < nt) compute(buf3);
+        if (it + 4 < nt) {
+          wait_barrier(0);
+          if (it + 6 < nt) issue((it + 6) * BN, buf2);
+          if (it + 7 < nt) issue((it + 7) * BN, buf3);
+        }
+      }
+    }
+  } else {
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u)
-    if (u < nt) issue(u * BN, u == 0 ? buf0 : u == 1 ? buf1 : u == 2 ? buf2 : buf3);
-  wait_barrier(min(nt, NBUF - 1) - 1);
-  for (int it = 0; it < nt; it += NBUF) {
-    if (NBUF == 2) {
-      step(buf0, buf1, it, nt);
-      if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
-    } else if (NBUF == 3) {
-      step(buf0, buf2, it, nt);
-      if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
-      if (it + 2 < nt) step(buf2, buf1, it + 2, nt);
-    } else {
-      step(buf0, buf3, it, nt);
-      if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
-      if (it + 2 < nt) step(buf2, buf1, it + 2, nt);
-      if (it + 3 < nt) step(buf3, buf2, it + 3, nt);
+    for (int u = 0; u < NBUF - 1; ++u)
+      if (u < nt) issue(u * BN, u == 0 ? buf0 : u == 1 ? buf1 : buf2);
+    wait_barrier(min(nt, NBUF - 1) - 1);
+    for (int it = 0; it < nt; it += NBUF) {
+      if (NBUF == 2) {
+        step(buf0, buf1, it, nt);
+        if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
+      } else {
+        step(buf0, buf2, it, nt);
+        if (it + 1 < nt) step(buf1, buf0, it + 1, nt);
+        if (it + 2 < nt) step(buf2, buf1, it + 2, nt);
+      }
     }
   }
 
