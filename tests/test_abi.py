@@ -98,3 +98,32 @@ def test_static_annca_refuses_sizes_beyond_its_array_on_host():
     st = lib.fastar_annca_attend_static(None, 0, 0, None, None, None, 0, 0, None, 1, 64, 16384, 2,
                                         128, 4, 1, 0.0, None, 0, 0, None)
     assert st == 3
+
+
+def test_two_launch_annca_refuses_bad_arguments_on_host():
+    """fastar_annca_attend checks sizes, pointers and alignment before any HIP
+    call; a frame with no queries is a no-op that succeeds."""
+    lib = fa.library()
+    fake = ctypes.c_void_p(4096)  # never dereferenced: every call below is refused
+
+    def call(q=fake, L=4, b=16, qc=fake, pc=fake, k=fake, v=fake, Nf=64, F=2, Np=512, H=2, d=128,
+             scale=0.0, o=fake, stride=128):
+        return lib.fastar_annca_attend(q, stride, stride, fake, L, b, qc, pc, k, v, stride, stride,
+                                       Nf, F, Np, H, d, scale, o, stride, stride, None)
+
+    assert call(d=64) == 1                       # d = 128 only
+    assert call(L=5) == 1                        # 1..4 tables
+    assert call(L=0) == 1
+    assert call(b=17) == 1                       # codes of at most 16 bits
+    assert call(Np=4097) == 1                    # the gather list must fit beside the ring
+    assert call(Np=0) == 1
+    assert call(H=0) == 1
+    assert call(Nf=4097) == 1                    # FASTAR_MAX_ANNCA_QUERIES_PER_FRAME
+    assert call(scale=-1.0) == 1
+    assert call(scale=float("nan")) == 1
+    assert call(qc=None) == 1                    # the query codes buffer is required
+    assert call(o=None) == 1
+    assert call(q=ctypes.c_void_p(4096 + 8)) == 1  # 16-byte alignment
+    assert call(stride=100) == 1                 # strides in whole 16-byte units
+    assert "stride" in lib.fastar_last_error().decode()
+    assert call(Nf=0) == 0                       # nothing to do
