@@ -1062,3 +1062,28 @@ def test_fused_annca_frame_keeping_nothing_gives_zeros():
     got = fa.annca_attend(q, pl, cp.tables, cp.bits, pc, kp, vp, 2)
     torch.cuda.synchronize()
     assert (got == 0).all()
+
+
+def test_two_launch_annca_with_strided_rows():
+    """Queries, keys, values and outputs as row-strided views (each row the
+    first 128 of 256 features, heads 2 rows apart): the hash and the attention
+    launches read the same strides; the result equals the contiguous call."""
+    cp = ClusterPrompt(heads=3, queries_per_frame=200, frames=2)
+    pl = _planes_dev(cp.planes(), "bf16")
+    q = to_device(cp.Q, "bf16")
+    kp, vp = to_device(cp.Kp, "bf16"), to_device(cp.Vp, "bf16")
+    pc = fa.hash_codes(kp, pl, cp.tables, cp.bits)
+    ref = fa.annca_attend(q, pl, cp.tables, cp.bits, pc, kp, vp, 2)
+
+    def wide(x):  # [H][N][d] -> view of a [H][N][2d] buffer, first d features
+        buf = torch.zeros((x.shape[0], x.shape[1], 2 * x.shape[2]), dtype=x.dtype, device=x.device)
+        buf[:, :, :x.shape[2]] = x
+        return buf[:, :, :x.shape[2]]
+
+    qs, ks, vs = wide(q), wide(kp), wide(vp)
+    out = torch.full((3, q.shape[1], 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    got = fa.annca_attend(qs, pl, cp.tables, cp.bits, pc, ks, vs, 2, out=out[:, :, :128])
+    torch.cuda.synchronize()
+    assert qs.stride(1) == 256 and ks.stride(1) == 256
+    assert torch.equal(got, ref)
+    assert (out[:, :, 128:] == 7.0).all()  # nothing written past each row's 128 features
