@@ -669,13 +669,23 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     }
   }
 
+  // The output tile goes through LDS, so that global stores write whole rows:
+  // each wave normalises its 32*QB rows into its own region of the ring (free
+  // once every wave has left the key loop), 16-byte chunk c of row r at
+  // c ^ (r mod chunks), then stores 16 bytes per lane with a row's chunks in
+  // consecutive lanes.
+  constexpr int kOChunks = D / 8;              // 16-byte chunks per row
+  constexpr int kORow = D * 2;                 // bytes per output row
+  constexpr int kOWave = 32 * QB * kORow;
+  static_assert(4 * kOWave <= C::kBuf && WAVES <= 8, "four waves' tiles per ring buffer");
+  __syncthreads();
+  uint8_t* ost = (wave < 4 ? buf0 : buf1) + (wave & 3) * kOWave;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qt * C::BM + (wave * QB + qb) * 32 + m;
     const float lt = lrun[qb] + __shfl_xor(lrun[qb], 32);
-    if (qi >= nq) continue;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    uint16_t* op = obase + (int64_t)qi * so_n;
+    const int r = qb * 32 + m;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -684,10 +694,21 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
                             (f32_to_bf16_bits(O[db][qb][4 * jg + 1] * inv) << 16);
         const uint32_t w1 = f32_to_bf16_bits(O[db][qb][4 * jg + 2] * inv) |
                             (f32_to_bf16_bits(O[db][qb][4 * jg + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + db * 32 + 8 * jg + 4 * hf) = make_uint2(w0, w1);
+        const int cs = (db * 4 + jg) ^ (r & (kOChunks - 1));
+        *reinterpret_cast<uint2*>(ost + r * kORow + cs * 16 + hf * 8) = make_uint2(w0, w1);
       }
-    if (lse_row && hf == 0)
+    if (lse_row && hf == 0 && qi < nq)
       lse_row[qi] = lt > 0.0f ? (mrun[qb] + __log2f(lt)) * kLn2 : -__builtin_huge_valf();
+  }
+  constexpr int kORowsPer = 64 / kOChunks;     // rows per wave-wide store
+  const int cc = lane % kOChunks;
+#pragma unroll
+  for (int i = 0; i < 32 * QB / kORowsPer; ++i) {
+    const int r = i * kORowsPer + lane / kOChunks;
+    const int qi = qt * C::BM + wave * QB * 32 + r;
+    const uint4 v =
+        *reinterpret_cast<const uint4*>(ost + r * kORow + ((cc ^ (r & (kOChunks - 1))) << 4));
+    if (qi < nq) *reinterpret_cast<uint4*>(obase + (int64_t)qi * so_n + cc * 8) = v;
   }
 }
 
