@@ -236,8 +236,12 @@ fastar_status fastar_project_keys(fastar_cache_t cache, const void* x_dev, int64
  * lse_dev: optional float [H][Nq],
  * natural-log partition function.  An empty cache gives zero outputs and
  * lse = -inf.  The call writes the slots' log-count shifts divided by the
- * scale into the cache's workspace before attending (a few bytes per slot), so
- * attention calls on one cache must not overlap. */
+ * scale into the cache's workspace before attending (a few bytes per slot),
+ * and, on bf16 caches when the last round of workgroups would leave a
+ * quarter or more of the GPU idle, the partial results of (head, query tile)
+ * pairs whose key tiles it splits in four; so attention calls on one cache
+ * must not overlap.  A split pair's outputs differ from the unsplit ones by
+ * summation order only (within bf16 rounding). */
 fastar_status fastar_attend(fastar_cache_t cache, const void* q_dev, int64_t stride_h,
                             int64_t stride_n, int32_t Nq, float scale, void* o_dev,
                             int64_t o_stride_h, int64_t o_stride_n, float* lse_dev, void* stream);

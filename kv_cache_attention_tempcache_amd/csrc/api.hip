@@ -111,7 +111,8 @@ enum Region {
   kPlanes, kPlanesFrag, kKMaster, kVMaster, kKMirror, kVMirror, kLb, kCount, kLast, kHist, kCodes,
   kIdxOff, kIdxSlot, kNLive, kEvicted, kCounters, kOwner, kGsize, kFrame, kStateEnd = kFrame,
   kBestSlot, kBestCos, kDec, kFrameCodes, kGroupTok, kGroupSlot, kItems,
-  kPlan, kAnnsaCodes, kAnnsaOff, kAnnsaEnt, kRopeK, kRopeLb, kLbc, kNumRegions
+  kPlan, kAnnsaCodes, kAnnsaOff, kAnnsaEnt, kRopeK, kRopeLb, kLbc, kAttnPart, kAttnMl,
+  kNumRegions
 };
 static_assert(kNumRegions + 1 <= (int)(sizeof(Layout::off) / sizeof(size_t)),
               "Layout::off holds every region's offset and the total");
@@ -190,6 +191,11 @@ Layout make_layout(const Dims& dm) {
   sizes[kRopeK] = e == 2 ? H * (size_t)dm.R * Bp * d * 2 : 0;
   sizes[kRopeLb] = e == 2 ? H * (size_t)dm.R * Bp * 4 : 0;
   sizes[kLbc] = e == 2 ? H * (size_t)std::max(dm.R, 1) * Bp * 4 : 0;
+  // partial results of split attention workgroups (bf16 caches): the tail of
+  // at most attn_split_pairs (head, query tile) pairs, four quarters each
+  const size_t P = e == 2 ? (size_t)attn_split_pairs(dm) : 0, bm = attn_query_tile(dm);
+  sizes[kAttnPart] = P * 4 * bm * d * 4;
+  sizes[kAttnMl] = P * 4 * bm * 8;
   size_t off = 0;
   for (int r = 0; r < kNumRegions; ++r) {
     L.off[r] = off;
@@ -237,6 +243,9 @@ CacheDev carve(void* base, const Dims& dm) {
   c.rope_k = b + L.off[kRopeK];
   c.rope_lb = reinterpret_cast<float*>(b + L.off[kRopeLb]);
   c.lbc = reinterpret_cast<float*>(b + L.off[kLbc]);
+  c.attn_part = reinterpret_cast<float*>(b + L.off[kAttnPart]);
+  c.attn_ml = reinterpret_cast<float2*>(b + L.off[kAttnMl]);
+  c.attn_pairs = dm.elem == 2 ? attn_split_pairs(dm) : 0;
   return c;
 }
 

@@ -304,18 +304,32 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   __shared__ __attribute__((aligned(16))) uint8_t buf1[C::kBuf];
   __shared__ __attribute__((aligned(16))) uint8_t buf2[NBUF >= 3 ? C::kBuf : 16];
   __shared__ __attribute__((aligned(16))) uint8_t buf3[NBUF == 4 ? C::kBuf : 16];
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform by construction: keeps the barrier paths below scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31, hf = lane >> 5;
   int h, g, qt;
+  // part >= 0: this workgroup attends key-tile quarter `part` of the split
+  // pair sp (pair a.nfull + sp); the whole pairs take the first a.nfull
+  // workgroup ids, so they are dispatched first, and the quarters fill the
+  // last round.  Each range is renumbered for the XCDs on its own.
+  int part = -1, sp = 0;
   if constexpr (SUBSET) {
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int per_head = sa.F * qtiles;
     h = lid / per_head;
     g = (lid - h * per_head) / qtiles;
     qt = lid - h * per_head - g * qtiles;
   } else {
+    int lid;
+    if ((int)blockIdx.x < a.nfull) {
+      lid = xcd_remap(blockIdx.x, a.nfull);
+    } else {
+      const int q4 = xcd_remap(blockIdx.x - a.nfull, gridDim.x - a.nfull);
+      sp = q4 >> 2;
+      part = q4 & 3;
+      lid = a.nfull + sp;
+    }
     h = lid / qtiles;
     g = 0;
     qt = lid - h * qtiles;
@@ -617,45 +631,48 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
       }
     }
   };
+  const int nt_all = REG ? a.n_reg * ntc : ntc + (nx + BN - 1) / BN;
+  // key tiles [tb, tb + nt) of this workgroup (a quarter may be empty)
+  const int tb = part < 0 ? 0 : part * nt_all / 4;
+  const int nt = part < 0 ? nt_all : (part + 1) * nt_all / 4 - tb;
   auto step = [&](const uint8_t* cur, uint8_t* nxt, int it, int nt) __attribute__((always_inline)) {
-    if (it + NBUF - 1 < nt) issue((it + NBUF - 1) * BN, nxt);
+    if (it + NBUF - 1 < nt) issue((tb + it + NBUF - 1) * BN, nxt);
     compute(cur);
     // Tile it+1 must have landed; the copies of tiles it+2 .. it+NBUF-1
     // stay in flight.
     wait_barrier(min(nt - 1, it + NBUF - 1) - (it + 1));
   };
 
-  const int nt = REG ? a.n_reg * ntc : ntc + (nx + BN - 1) / BN;
   if constexpr (NBUF == 4) {
     // One barrier per two tiles: tiles it, it+1 are read while the copies of
     // it+2, it+3 land; after the barrier (every wave is done with it, it+1)
     // their buffers receive it+4, it+5.  Measured slightly faster than a
     // barrier per tile (0.5-1.3 % in same-process comparisons).
-    issue(0, buf0);
-    if (1 < nt) issue(BN, buf1);
-    if (2 < nt) issue(2 * BN, buf2);
-    if (3 < nt) issue(3 * BN, buf3);
+    if (0 < nt) issue(tb * BN, buf0);
+    if (1 < nt) issue((tb + 1) * BN, buf1);
+    if (2 < nt) issue((tb + 2) * BN, buf2);
+    if (3 < nt) issue((tb + 3) * BN, buf3);
     wait_barrier(max(min(nt, 4) - 2, 0));
     for (int it = 0; it < nt; it += 4) {
       compute(buf0);
       if (it + 1 < nt) compute(buf1);
       if (it + 2 < nt) {
         wait_barrier(0);
-        if (it + 4 < nt) issue((it + 4) * BN, buf0);
-        if (it + 5 < nt) issue((it + 5) * BN, buf1);
+        if (it + 4 < nt) issue((tb + it + 4) * BN, buf0);
+        if (it + 5 < nt) issue((tb + it + 5) * BN, buf1);
         compute(buf2);
         if (it + 3 < nt) compute(buf3);
         if (it + 4 < nt) {
           wait_barrier(0);
-          if (it + 6 < nt) issue((it + 6) * BN, buf2);
-          if (it + 7 < nt) issue((it + 7) * BN, buf3);
+          if (it + 6 < nt) issue((tb + it + 6) * BN, buf2);
+          if (it + 7 < nt) issue((tb + it + 7) * BN, buf3);
         }
       }
     }
   } else {
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u)
-      if (u < nt) issue(u * BN, u == 0 ? buf0 : u == 1 ? buf1 : buf2);
+      if (u < nt) issue((tb + u) * BN, u == 0 ? buf0 : u == 1 ? buf1 : buf2);
     wait_barrier(min(nt, NBUF - 1) - 1);
     for (int it = 0; it < nt; it += NBUF) {
       if (NBUF == 2) {
@@ -669,6 +686,26 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     }
   }
 
+  if constexpr (!SUBSET) {
+    if (part >= 0) {  // block-uniform: a quarter's unnormalised result
+      const int64_t base = ((int64_t)sp * 4 + part) * C::BM;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int r = (wave * QB + qb) * 32 + m;
+        const float lt = lrun[qb] + __shfl_xor(lrun[qb], 32);
+        float* po = c.attn_part + (base + r) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg)
+            *reinterpret_cast<float4*>(po + db * 32 + 8 * jg + 4 * hf) =
+                make_float4(O[db][qb][4 * jg], O[db][qb][4 * jg + 1], O[db][qb][4 * jg + 2],
+                            O[db][qb][4 * jg + 3]);
+        if (hf == 0) c.attn_ml[base + r] = make_float2(mrun[qb], lt);
+      }
+      return;
+    }
+  }
   // The output tile goes through LDS, so that global stores write whole rows:
   // each wave normalises its 32*QB rows into its own region of the ring (free
   // once every wave has left the key loop), 16-byte chunk c of row r at
@@ -712,6 +749,68 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   }
 }
 
+// The four quarters of each split (head, query tile): per query row, the
+// parts' running maxima m_p (log2 units) and sums l_p give the common max m
+// and weights 2^(m_p - m); o = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p,
+// rounded to bf16 like the unsplit epilogue; a part that saw no key weight
+// (l_p = 0) adds nothing.  Threads own 4 features of one row.
+template <int D>
+__global__ __launch_bounds__(256) void attend_combine_kernel(CacheDev c, CacheAttendArgs a,
+                                                             int qtiles, int bm) {
+  constexpr int kT = D / 4, kRows = 256 / kT;
+  const int sp = blockIdx.y;
+  const int r = blockIdx.x * kRows + (int)threadIdx.x / kT;
+  const int f = ((int)threadIdx.x % kT) * 4;
+  if (r >= bm) return;
+  const int pair = a.nfull + sp, h = pair / qtiles, qt = pair - h * qtiles;
+  const int qi = qt * bm + r;
+  if (qi >= a.Nq) return;
+  const int64_t base = (int64_t)sp * 4 * bm + r;
+  float2 ml[4];
+  float mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    ml[p] = c.attn_ml[base + (int64_t)p * bm];
+    if (ml[p].y > 0.0f) mx = fmaxf(mx, ml[p].x);
+  }
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float l = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if (!(ml[p].y > 0.0f)) continue;
+    const float w = __builtin_amdgcn_exp2f(ml[p].x - mx);
+    const float4 o = *reinterpret_cast<const float4*>(c.attn_part + (base + (int64_t)p * bm) * D + f);
+    l = __builtin_fmaf(ml[p].y, w, l);
+    acc.x = __builtin_fmaf(o.x, w, acc.x);
+    acc.y = __builtin_fmaf(o.y, w, acc.y);
+    acc.z = __builtin_fmaf(o.z, w, acc.z);
+    acc.w = __builtin_fmaf(o.w, w, acc.w);
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const uint32_t w0 = f32_to_bf16_bits(acc.x * inv) | (f32_to_bf16_bits(acc.y * inv) << 16);
+  const uint32_t w1 = f32_to_bf16_bits(acc.z * inv) | (f32_to_bf16_bits(acc.w * inv) << 16);
+  uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t)h * a.so_h + (int64_t)qi * a.so_n + f;
+  *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
+  if (a.lse && f == 0)
+    a.lse[(int64_t)h * a.Nq + qi] = l > 0.0f ? (mx + __log2f(l)) * kLn2 : -__builtin_huge_valf();
+}
+
+// Compute units of the current device (a split pays only when the last round
+// of workgroups leaves CUs idle).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 // lbc = lb / (scale * log2(e)) over every head's shift rows (-inf stays -inf).
 __global__ __launch_bounds__(256) void scale_shift_kernel(const float* __restrict__ src,
                                                           float* __restrict__ dst, int64_t n,
@@ -731,8 +830,20 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
                             hipStream_t s) {
   using C = CCfg<D, BN, WAVES, QB>;
   const int qtiles = (a.Nq + C::BM - 1) / C::BM;
-  const int blocks = dm.H * qtiles;
-  if (blocks == 0) return hipSuccess;
+  const int pairs = dm.H * qtiles;
+  if (pairs == 0) return hipSuccess;
+  // The last round of workgroups: when it would leave a quarter or more of
+  // the CUs idle, its r pairs run as 4r workgroups of a quarter of the key
+  // tiles each (not for the M-degree regions, whose later tiles can be wholly
+  // masked), and a combine kernel merges the quarters.  Caches of at least 16
+  // key tiles only.
+  const int cus = device_cus();
+  const int r = pairs % cus;
+  const bool split = a.n_reg == 0 && r > 0 && 4 * r <= 3 * cus && r <= c.attn_pairs &&
+                     C::BM == attn_query_tile(dm) && dm.B >= 16 * BN;
+  CacheAttendArgs aa = a;
+  aa.nfull = split ? pairs - r : pairs;
+  const int blocks = split ? pairs - r + 4 * r : pairs;
   {
     // rows per head are a multiple of 128 (Bp), so n is a multiple of 4
     const int64_t n = (int64_t)dm.H * (a.n_reg > 0 ? dm.R : 1) * dm.Bp;
@@ -742,13 +853,18 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
   }
   if (a.n_reg > 0)
     hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, true>),
-                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
+                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
   else if (a.n_x > 0)
     hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, true, false>),
-                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
+                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
   else
     hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, false>),
-                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, a, AttendArgs{}, qtiles);
+                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
+  if (split) {
+    constexpr int kRows = 256 / (D / 4);
+    hipLaunchKernelGGL(attend_combine_kernel<D>, dim3((C::BM + kRows - 1) / kRows, r), dim3(256),
+                       0, s, c, aa, qtiles, C::BM);
+  }
   return hipGetLastError();
 }
 

@@ -98,6 +98,14 @@ struct Dims {
   int R;         // frames of each slot's most recent members kept (0: none)
 };
 
+// Queries per workgroup of the bf16 attention over the cache: 8 waves of 32
+// at d = 128, 4 waves of 32 at d = 64.
+inline int attn_query_tile(const Dims& dm) { return dm.d == 128 ? 256 : 128; }
+// (head, query tile) pairs whose key tiles the attention may split in four
+// (the last, partial round of workgroups): at most three quarters of the
+// GPU's 256 CUs, and 8 per head for small caches.
+inline int attn_split_pairs(const Dims& dm) { return dm.H * 8 < 192 ? dm.H * 8 : 192; }
+
 // Device pointers into one cache's workspace.
 struct CacheDev {
   void* planes;        // SimHash: [L][b][d]; PQ: codebooks [L][M][2^(b/M)][d/M]; storage dtype
@@ -147,6 +155,12 @@ struct CacheDev {
   // the shifts of the last attention call divided by its logit scale
   // (scale * log2(e)): [H][Bp], or [H][R*Bp] for the M-degree regions
   float* lbc;
+  // partial results of attention workgroups that cover a quarter of a
+  // (head, query tile)'s key tiles: unnormalised outputs [P][4][BM][d] fp32
+  // and (running max in log2 units, sum) [P][4][BM], P = attn_pairs
+  float* attn_part;
+  float2* attn_ml;
+  int attn_pairs;
 };
 
 struct Layout {
@@ -230,6 +244,9 @@ struct CacheAttendArgs {
   // n_reg > 0: keys and log2 shifts from c.rope_k / c.rope_lb, n_reg regions
   // of Bp rows per head; region r's row s pairs with the V mirror row s
   int n_reg;
+  // set by the launcher: (head, query tile) pairs [0, nfull) run whole, the
+  // rest as four workgroups of a quarter of the key tiles each
+  int nfull;
 };
 // The M-degree regions: rotated keys of each live slot's m most recent
 // members' frames and their log2(count/m') shifts (-inf past m' or n_live).

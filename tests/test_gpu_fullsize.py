@@ -326,7 +326,7 @@ def test_dit13b_pq_full_size_sampled_head():
     assert err <= 2e-2
 
 
-@pytest.mark.parametrize("name,heads", [("dit1.3b", [2, 9]), ("dit14b", [31])])
+@pytest.mark.parametrize("name,heads", [("dit1.3b", [2, 9]), ("dit14b", [31, 38])])
 def test_headline_path_hashes_inside_the_chunk_call(name, heads):
     """The benchmark's own path at full size: after the prefill, the timed
     chunk goes into one 3-frame match_merge that hashes the keys itself.  On
