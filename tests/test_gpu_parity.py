@@ -1087,3 +1087,43 @@ def test_two_launch_annca_with_strided_rows():
     assert qs.stride(1) == 256 and ks.stride(1) == 256
     assert torch.equal(got, ref)
     assert (out[:, :, 128:] == 7.0).all()  # nothing written past each row's 128 features
+
+
+@pytest.mark.parametrize("nq", [300, 1, 2000])
+def test_tail_split_changes_only_the_summation_order(nq):
+    """A launch whose (head, query tile) pairs all fit in the last round runs
+    them as key-tile quarters plus a combine; a 1023-slot cache (below 16 key
+    tiles) never splits.  The same imported state in both: outputs within
+    bf16 rounding of each other and of the oracle, log-partitions within
+    1e-3 relative.  (Quarters with no key tile, when a head holds fewer than
+    four, are covered by the one-frame cases of test_attend_matches_oracle.)"""
+    w = WORKLOADS["dit1.3b"].with_(heads=3, tokens_per_frame=220, budget=1024, seed=57)
+    st = DriftStream(w)
+    planes = st.planes()
+    orc = TempCacheOracle.for_workload(w, planes)
+    for _ in range(4):
+        K, V, _, _ = st.next_frame()
+        orc.process_frame(K, V)
+    q = np.random.default_rng(5).standard_normal((w.heads, nq, w.head_dim)).astype(np.float32)
+    q = round_to_storage(q, "bf16")
+    state = oracle_state_for_import(orc, w.dtype)
+    outs = {}
+    # at most 880 slots are live, so the 1023-slot cache takes the same state
+    # with the slot axis (the last of codes, the second of the others) cut
+    small = dict(state)
+    for k in ("k_master", "v_master", "k_mirror", "v_mirror", "count", "last"):
+        small[k] = state[k][:, :1023]
+    small["codes"] = state["codes"][:, :, :1023]
+    for budget, st_b in ((1024, state), (1023, small)):
+        cache = _cache_for(w.with_(budget=budget), planes)
+        cache.import_state(st_b)
+        lse = torch.empty((w.heads, nq), dtype=torch.float32, device="cuda")
+        outs[budget] = (cache.attend(to_device(q, "bf16"), lse=lse), lse)
+    torch.cuda.synchronize()
+    (o_split, l_split), (o_whole, l_whole) = outs[1024], outs[1023]
+    O_ref, lse_ref = orc.attend(q)
+    assert (o_split.float() - o_whole.float()).abs().max().item() <= 8e-3
+    assert np.abs(o_split.float().cpu().numpy() - O_ref).max() <= TOL["bf16"]
+    lim = 1e-3 * max(1.0, np.abs(lse_ref).max())
+    assert np.abs(l_split.cpu().numpy() - lse_ref).max() <= lim
+    assert (l_split - l_whole).abs().max().item() <= lim
