@@ -255,9 +255,12 @@ CALIB_BYTES = 1 << 30   # plain device copy used to scale the HBM counters
 
 
 def _attend_src_hash() -> str:
+    """Hash of the attention source's code: // comments and blank lines are
+    left out, so a comment edit keeps a traffic record valid."""
     import hashlib
-    with open(ATTEND_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(ATTEND_SRC, encoding="utf-8") as f:
+        code = [ln.split("//", 1)[0].rstrip() for ln in f]
+    return hashlib.sha256("\n".join(ln for ln in code if ln).encode()).hexdigest()[:16]
 
 
 def _traffic_path(workload: str, out_dir: str | None = None) -> str:

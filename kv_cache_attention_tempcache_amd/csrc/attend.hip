@@ -22,6 +22,10 @@
 //     (slot tiles as buffer loads: scalar tile offset, fixed lane offsets).
 //   Blocks are renumbered so each XCD (blocks are dealt round-robin over the 8
 //     XCDs) gets a contiguous range of (head, query tile) and shares its L2.
+//   The normalised output tile leaves through LDS as whole rows.  When the
+//     grid's last round of workgroups would leave a quarter or more of the
+//     CUs idle, its (head, query tile) pairs run as four key-tile quarters
+//     each, and a combine kernel merges the quarters' partial results.
 // f32 path (small fp32 workloads): one thread per query, fp32 online softmax.
 #include <algorithm>
 

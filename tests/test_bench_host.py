@@ -36,3 +36,16 @@ def test_step_roofline_of_the_13b_step():
     total = sum(r["bound_us"].values())
     assert abs(r["bound_us_total"] - total) < 0.02
     assert abs(r["frac"] - r["bound_us_total"] / 343.0) < 1e-3
+
+
+def test_traffic_record_survives_comment_edits_only(tmp_path, monkeypatch):
+    """The attention source hash that keys a traffic record ignores // comments
+    and blank lines, and changes with any code edit."""
+    src = tmp_path / "attend.hip"
+    monkeypatch.setattr(bench, "ATTEND_SRC", str(src))
+    src.write_text("int f(int x) {\n  return x + 1;  // add one\n}\n")
+    h0 = bench._attend_src_hash()
+    src.write_text("// a new header line\nint f(int x) {\n\n  return x + 1;  // plus one\n}\n")
+    assert bench._attend_src_hash() == h0
+    src.write_text("int f(int x) {\n  return x + 2;  // add one\n}\n")
+    assert bench._attend_src_hash() != h0
