@@ -7,65 +7,80 @@
 // The candidates of a query are found through a bucket index of the slots
 // (one CSR per table, built by the index kernel over the slots' codes), never
 // by comparing all query x slot pairs: the work follows the shared pairs.  A
-// group of 16 lanes owns one query, as in the match step: for every table it
-// reads its bucket 16 entries at a time, keeps the entries whose code equals
-// the query's and that no earlier table already shares (a slot found in
-// table t is dropped if its code of some table t' < t equals the query's),
-// and runs an online softmax over the kept slots, several slot rows in flight
-// at a time.  Every lane holds d/16 features of the query, of the running
-// output and of each slot row; dot products are summed over the 16 lanes by
-// DPP row rotations in binary32.
+// group of G lanes owns one query (8 for 2-byte rows, 16 for 4-byte ones), as
+// in the match step.  Every table's bucket bounds and first 16 entries load
+// up front; the entries whose code equals the query's are listed, each slot
+// once, and an online softmax then runs over the list with several slot rows
+// in flight.  A query whose list overflows takes a plain second pass instead:
+// bucket by bucket, a slot found in table t is dropped if its code of some
+// table t' < t equals the query's, and the list is consumed whenever it
+// fills.  Both passes take every shared slot exactly once.  Every lane holds
+// d/G features of the query, of the running output and of each slot row;
+// dot products are summed over the G lanes by DPP moves in binary32.
 #include "common.hpp"
+
+#include <cmath>
 
 namespace fastar {
 namespace {
 
-constexpr int kGroup = 16;     // lanes per query
-constexpr int kMaxList = 8;    // slots listed before their rows are read
-constexpr int kBatch = 4;      // slot rows in flight together
+constexpr int kCap = 32;   // slots listed before their rows are read
+constexpr int kPass = 16;  // bucket entries read per pass of a group
 
-template <int R>
-__device__ __forceinline__ float row_rotate_f(float x) {
+template <int CTRL>
+__device__ __forceinline__ float dpp_move_f(float x) {
   return __int_as_float(
-      __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x120 + R, 0xf, 0xf, false));
+      __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-// Sum over the 16 lanes of a DPP row; every lane ends with the same value.
+// Sum over a query's G lanes (aligned groups of 8 or 16 inside a DPP row);
+// each step adds the partner's mirror-image partial sum, so every lane ends
+// with the same value.
+template <int G>
 __device__ __forceinline__ float group_sum_f(float x) {
-  x += row_rotate_f<8>(x);
-  x += row_rotate_f<4>(x);
-  x += row_rotate_f<2>(x);
-  x += row_rotate_f<1>(x);
+  static_assert(G == 8 || G == 16, "a query's lanes lie inside one DPP row");
+  if constexpr (G == 16) {
+    x += dpp_move_f<0x128>(x);  // rotations by 8, 4, 2, 1 within the row
+    x += dpp_move_f<0x124>(x);
+    x += dpp_move_f<0x122>(x);
+    x += dpp_move_f<0x121>(x);
+  } else {
+    x += dpp_move_f<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp_move_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    x += dpp_move_f<0x141>(x);  // row_half_mirror: the other quad
+  }
   return x;
 }
 
+// E elements of one row as loaded: 2-byte elements as packed pairs, 4-byte
+// ones as words; elem() widens element q.
 template <typename T, int E>
-__device__ __forceinline__ void load_feats(const T* p, float (&v)[E]) {
-  if constexpr (sizeof(T) == 2) {
-    if constexpr (E == 8) {
-      const uint4 u = *reinterpret_cast<const uint4*>(p);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+struct Feats {
+  static constexpr int W = sizeof(T) == 2 ? E / 2 : E;
+  uint32_t w[W];
+};
+
+template <typename T, int E>
+__device__ __forceinline__ void load_feats(const T* p, Feats<T, E>& f) {
+  constexpr int W = Feats<T, E>::W;
+  if constexpr (W % 4 == 0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] = __uint_as_float(w[k] << 16);
-        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-      }
-    } else {
-      const uint2 u = *reinterpret_cast<const uint2*>(p);
-      v[0] = __uint_as_float(u.x << 16);
-      v[1] = __uint_as_float(u.x & 0xffff0000u);
-      v[2] = __uint_as_float(u.y << 16);
-      v[3] = __uint_as_float(u.y & 0xffff0000u);
+    for (int c = 0; c < W / 4; ++c) {
+      const uint4 u = reinterpret_cast<const uint4*>(p)[c];
+      f.w[4 * c] = u.x; f.w[4 * c + 1] = u.y; f.w[4 * c + 2] = u.z; f.w[4 * c + 3] = u.w;
     }
   } else {
-#pragma unroll
-    for (int k = 0; k < E; k += 4) {
-      const float4 f = *reinterpret_cast<const float4*>(p + k);
-      v[k] = f.x;
-      v[k + 1] = f.y;
-      v[k + 2] = f.z;
-      v[k + 3] = f.w;
-    }
+    static_assert(W == 2, "row slices are 8 bytes or a multiple of 16");
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    f.w[0] = u.x; f.w[1] = u.y;
   }
+}
+
+template <typename T, int E>
+__device__ __forceinline__ float elem(const Feats<T, E>& f, int q) {
+  if constexpr (sizeof(T) == 2)
+    return __uint_as_float((q & 1) ? (f.w[q >> 1] & 0xffff0000u) : (f.w[q >> 1] << 16));
+  else
+    return __uint_as_float(f.w[q]);
 }
 
 template <typename T, int E>
@@ -75,8 +90,13 @@ __device__ __forceinline__ void store_feats(T* p, const float (&v)[E]) {
 #pragma unroll
     for (int k = 0; k < E / 2; ++k)
       w[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
-    if constexpr (E == 8) *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-    else *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    if constexpr (E % 8 == 0) {
+#pragma unroll
+      for (int c = 0; c < E / 8; ++c)
+        reinterpret_cast<uint4*>(p)[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+    } else {
+      *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < E; k += 4)
@@ -85,18 +105,23 @@ __device__ __forceinline__ void store_feats(T* p, const float (&v)[E]) {
 }
 
 // c.codes / c.idx_off / c.idx_ent point at the AnnSA slot codes and their
-// bucket index; dm.L is the number of AnnSA tables.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void annsa_kernel(Dims dm, CacheDev c, AnnsaArgs a) {
-  constexpr int E = D / kGroup;
+// bucket index; dm.L is the number of AnnSA tables (at most 4).
+// G lanes per query; kBatch slot rows in flight together; OCC waves per SIMD;
+// kLong: lists expected longer than kCap go straight to the plain pass.
+template <typename T, int D, int G, int kBatch, int OCC, bool kLong>
+__global__ __launch_bounds__(256, OCC) void annsa_kernel(Dims dm, CacheDev c, AnnsaArgs a) {
+  constexpr int E = D / G;
+  constexpr int kF = kPass / G;  // entries per lane in a pass
   const int h = blockIdx.y;
-  const int i = blockIdx.x * (256 / kGroup) + (threadIdx.x / kGroup);
-  const int gl = threadIdx.x & (kGroup - 1);
-  if (i >= a.Nq) return;  // all 16 lanes of a group leave together
+  const int i = blockIdx.x * (256 / G) + (threadIdx.x / G);
+  const int gl = threadIdx.x & (G - 1);
+  if (i >= a.Nq) return;  // all G lanes of a group leave together
   const int L = dm.L, B = dm.B, NB = dm.NB, nb_bits = dm.nb_bits;
 
-  float qv[E];
-  load_feats<T, E>(static_cast<const T*>(a.q) + (int64_t)h * a.sq_h + (int64_t)i * a.sq_n + gl * E, qv);
+  // independent loads first: the query row, its codes, every table's bucket
+  // bounds and first kPass entries
+  Feats<T, E> qf;
+  load_feats<T, E>(static_cast<const T*>(a.q) + (int64_t)h * a.sq_h + (int64_t)i * a.sq_n + gl * E, qf);
   uint32_t qc[4];
   int beg[4], end[4];
 #pragma unroll
@@ -109,6 +134,15 @@ __global__ __launch_bounds__(256) void annsa_kernel(Dims dm, CacheDev c, AnnsaAr
       end[t] = off[1];
     }
   }
+  uint2 first[4][kF];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < kF; ++u) {
+      const int p = beg[t] + gl + G * u;
+      first[t][u] = (!kLong && t < L && p < end[t]) ? c.idx_ent[((int64_t)h * L + t) * B + p]
+                                                    : make_uint2(0u, 0u);
+    }
   const float cscale = a.scale * 1.4426950408889634f;  // logits in log2 units
   const T* keys = static_cast<const T*>(c.k_mirror) + (int64_t)h * dm.Bp * D;
   const T* vals = static_cast<const T*>(c.v_mirror) + (int64_t)h * dm.Bp * D;
@@ -121,9 +155,13 @@ __global__ __launch_bounds__(256) void annsa_kernel(Dims dm, CacheDev c, AnnsaAr
 
   // online softmax over list[0..n): the rows of a batch load before any of
   // its arithmetic
-  auto consume = [&](const int (&list)[kMaxList], int n) __attribute__((always_inline)) {
+  auto consume = [&](const int* list, int n) __attribute__((always_inline)) {
     for (int b0 = 0; b0 < n; b0 += kBatch) {
-      float kv[kBatch][E], vv[kBatch][E], lbs[kBatch];
+      // the query is widened per batch instead of being held as E floats
+#pragma unroll
+      for (int q = 0; q < Feats<T, E>::W; ++q) asm volatile("" : "+v"(qf.w[q]));
+      Feats<T, E> kv[kBatch], vv[kBatch];
+      float lbs[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int s = list[min(b0 + u, n - 1)];
@@ -136,44 +174,101 @@ __global__ __launch_bounds__(256) void annsa_kernel(Dims dm, CacheDev c, AnnsaAr
         if (b0 + u >= n) break;
         float dot = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) dot = __builtin_fmaf(qv[e], kv[u][e], dot);
-        dot = group_sum_f(dot);
+        for (int e = 0; e < E; ++e) dot = __builtin_fmaf(elem(qf, e), elem(kv[u], e), dot);
+        dot = group_sum_f<G>(dot);
         const float z = __builtin_fmaf(dot, cscale, lbs[u]);
         const float mn = fmaxf(m, z);
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         const float p = __builtin_amdgcn_exp2f(z - mn);
         l = __builtin_fmaf(l, alpha, p);
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(o[e], alpha, p * vv[u][e]);
+        for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf(o[e], alpha, p * elem(vv[u], e));
         m = mn;
       }
     }
   };
 
-  int list[kMaxList];
+  // The query's list lives in LDS (every lane of the group writes the same
+  // ids, so each lane reads back its own writes).
+  __shared__ int s_list[256 / G][kCap];
+  int* list = s_list[threadIdx.x / G];
   int n = 0;
-  const int gbase = threadIdx.x & 63 & ~(kGroup - 1);
+  bool full = kLong;
+  const int gbase = threadIdx.x & 63 & ~(G - 1);
+  constexpr uint32_t gmask = (1u << G) - 1u;
+  // lists the matching entries of one pass (kF per lane) of table t, each
+  // slot once; a full list stops the listing
+  auto list_pass = [&](const uint2 (&e)[kF], int p0, int t) __attribute__((always_inline)) {
+    uint32_t mask = 0;
+#pragma unroll
+    for (int u = 0; u < kF; ++u) {
+      const bool ok = p0 + gl + G * u < end[t] && e[u].y == qc[t];
+      mask |= ((uint32_t)(__ballot(ok) >> gbase) & gmask) << (G * u);
+    }
+    while (mask) {
+      const int j = __builtin_ctz(mask);
+      mask &= mask - 1;
+      const int uj = j / G;  // the same in every lane of the group
+      int v = (int)e[0].x;
+#pragma unroll
+      for (int u = 1; u < kF; ++u)
+        if (uj == u) v = (int)e[u].x;
+      const int sl = __shfl(v, j % G, G);
+      bool dup = false;
+      for (int k = 0; k < n; ++k) dup |= list[k] == sl;
+      if (dup) continue;
+      if (n == kCap) {
+        full = true;
+        break;
+      }
+      list[n++] = sl;
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (!kLong && t < L) list_pass(first[t], beg[t], t);
+  // buckets longer than one pass (rare)
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    if (t >= L) break;
+    if (kLong || t >= L) break;
     const uint2* ent = c.idx_ent + ((int64_t)h * L + t) * B;
-    for (int p0 = beg[t]; p0 < end[t]; p0 += kGroup) {
-      const int p = p0 + gl;
-      const uint2 e = p < end[t] ? ent[p] : make_uint2(0u, 0u);
-      bool ok = p < end[t] && e.y == qc[t];
-      // a slot sharing an earlier table's bucket was already taken there
+    for (int p0 = beg[t] + kPass; p0 < end[t] && !full; p0 += kPass) {
+      uint2 e[kF];
 #pragma unroll
-      for (int t2 = 0; t2 < t; ++t2)
-        if (ok) ok = scodes[(int64_t)t2 * B + e.x] != qc[t2];
-      uint32_t mask = (uint32_t)(__ballot(ok) >> gbase) & 0xffffu;
-      while (mask) {
-        const int j = __builtin_ctz(mask);
-        mask &= mask - 1;
-        if (n == kMaxList) {
-          consume(list, n);
-          n = 0;
+      for (int u = 0; u < kF; ++u) {
+        const int p = p0 + gl + G * u;
+        e[u] = p < end[t] ? ent[p] : make_uint2(0u, 0u);
+      }
+      list_pass(e, p0, t);
+    }
+  }
+  if (full) {
+    // more than kCap shared slots: bucket by bucket, the slot codes of
+    // earlier tables decide whether a slot was taken there, and the list is
+    // consumed whenever it fills (the code and bucket bounds are read again
+    // rather than kept live)
+    n = 0;
+    for (int t = 0; t < L; ++t) {
+      const uint32_t code = a.q_codes[((int64_t)h * L + t) * a.Nq + i];
+      const int32_t* off = c.idx_off + ((int64_t)h * L + t) * (NB + 1) + bucket_of(code, nb_bits);
+      const int b0 = off[0], b1 = off[1];
+      const uint2* ent = c.idx_ent + ((int64_t)h * L + t) * B;
+      for (int p0 = b0; p0 < b1; p0 += G) {
+        const int p = p0 + gl;
+        const uint2 e = p < b1 ? ent[p] : make_uint2(0u, 0u);
+        bool ok = p < b1 && e.y == code;
+        for (int t2 = 0; t2 < t; ++t2)
+          if (ok) ok = scodes[(int64_t)t2 * B + e.x] != a.q_codes[((int64_t)h * L + t2) * a.Nq + i];
+        uint32_t mask = (uint32_t)(__ballot(ok) >> gbase) & gmask;
+        while (mask) {
+          const int j = __builtin_ctz(mask);
+          mask &= mask - 1;
+          if (n == kCap) {
+            consume(list, n);
+            n = 0;
+          }
+          list[n++] = __shfl((int)e.x, j, G);
         }
-        list[n++] = __shfl((int)e.x, j, kGroup);
       }
     }
   }
@@ -190,17 +285,27 @@ __global__ __launch_bounds__(256) void annsa_kernel(Dims dm, CacheDev c, AnnsaAr
 
 }  // namespace
 
+template <typename T, int G, int kBatch, int OCC, bool kLong>
+hipError_t launch_annsa_cfg(const Dims& dm, const CacheDev& c, const AnnsaArgs& a, hipStream_t s) {
+  const dim3 grid((a.Nq + 256 / G - 1) / (256 / G), dm.H);
+  if (dm.d == 128) hipLaunchKernelGGL((annsa_kernel<T, 128, G, kBatch, OCC, kLong>), grid, dim3(256), 0, s, dm, c, a);
+  else hipLaunchKernelGGL((annsa_kernel<T, 64, G, kBatch, OCC, kLong>), grid, dim3(256), 0, s, dm, c, a);
+  return hipGetLastError();
+}
+
+// dm.b: the AnnSA code bits.  Short lists (few random collisions expected:
+// L * budget * 2^-b <= 16) take the listing pass with 8 lanes per query and
+// one row in flight, so 7 waves of 8 queries fit each SIMD; long lists take
+// the plain pass with 16 lanes and four rows in flight, since their time is
+// the chain of row loads per query.  4-byte rows take 16 lanes either way.
 hipError_t launch_annsa(const Dims& dm, const CacheDev& c, const AnnsaArgs& a, hipStream_t s) {
   if (a.Nq == 0) return hipSuccess;
-  const dim3 grid((a.Nq + 15) / 16, dm.H);
-  if (dm.elem == 2) {
-    if (dm.d == 128) hipLaunchKernelGGL((annsa_kernel<uint16_t, 128>), grid, dim3(256), 0, s, dm, c, a);
-    else hipLaunchKernelGGL((annsa_kernel<uint16_t, 64>), grid, dim3(256), 0, s, dm, c, a);
-  } else {
-    if (dm.d == 128) hipLaunchKernelGGL((annsa_kernel<float, 128>), grid, dim3(256), 0, s, dm, c, a);
-    else hipLaunchKernelGGL((annsa_kernel<float, 64>), grid, dim3(256), 0, s, dm, c, a);
-  }
-  return hipGetLastError();
+  const bool long_lists = (double)dm.L * dm.B * std::ldexp(1.0, -dm.b) > 16.0;
+  if (dm.elem == 2)
+    return long_lists ? launch_annsa_cfg<uint16_t, 16, 4, 4, true>(dm, c, a, s)
+                      : launch_annsa_cfg<uint16_t, 8, 1, 7, false>(dm, c, a, s);
+  return long_lists ? launch_annsa_cfg<float, 16, 4, 4, true>(dm, c, a, s)
+                    : launch_annsa_cfg<float, 16, 2, 5, false>(dm, c, a, s);
 }
 
 }  // namespace fastar

@@ -30,6 +30,7 @@ struct fastar_cache_s {
   uint64_t version = 0;
   uint64_t annsa_version = ~0ull;
   int annsa_L = 0;
+  int annsa_b = 0;  // bits of those codes
 };
 
 namespace {
@@ -527,6 +528,7 @@ fastar_status fastar_cache_hash_slots(fastar_cache_t c, const void* planes_dev, 
                                 hipMemcpyDeviceToDevice, s));
   c->annsa_version = c->version;
   c->annsa_L = L;
+  c->annsa_b = b;
   return ok();
 }
 
@@ -559,6 +561,7 @@ fastar_status fastar_annsa_attend(fastar_cache_t c, const void* q_dev, int64_t s
               o_stride_n, lse_dev};
   Dims da = dm;
   da.L = L;
+  da.b = c->annsa_b;
   CacheDev ca = c->dev;
   ca.codes = c->dev.annsa_codes;
   ca.idx_off = c->dev.annsa_off;

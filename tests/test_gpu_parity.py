@@ -907,6 +907,24 @@ def test_annsa_all_shared_equals_attend():
     assert diff <= 1e-2
 
 
+def test_annsa_overflowing_short_lists_equal_attend():
+    """16-bit codes (a short expected list per query) with zero hyperplanes:
+    every slot's code is 0, so a query with code 0 shares every slot and its
+    list overflows into the second pass; the result is the dense step."""
+    w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=300, budget=2048, seed=61), 4)
+    H, Nq = w.heads, Q.shape[1]
+    q = to_device(Q, w.dtype)
+    dense = cache.attend(q)
+    cache.hash_slots(torch.zeros((1, 16, w.head_dim), dtype=torch.bfloat16, device="cuda"), 1, 16)
+    sparse = cache.annsa_attend(q, _codes_dev(np.zeros((H, 1, Nq))))
+    torch.cuda.synchronize()
+    diff = (sparse.float() - dense.float()).abs().max().item()
+    print(f"annsa 16-bit all-shared vs attend: max-abs {diff:.3e}")
+    # two bf16 outputs of different summation orders (binary32 online softmax
+    # against bf16 MFMA weights): the attention output bound applies
+    assert diff <= TOL["bf16"]
+
+
 def test_annsa_nothing_shared_gives_zeros():
     w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=100, budget=512, seed=57), 3)
     H, Nq = w.heads, Q.shape[1]
