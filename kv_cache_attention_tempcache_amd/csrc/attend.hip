@@ -42,6 +42,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
+// The values of lanes l and l ^ 32 in every lane, lower half's first:
+// v_permlane32_swap exchanges the two 32-lane halves in the VALU, without the
+// LDS round trip of a lane shuffle.
+__device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  lo = __int_as_float(r[0]);
+  hi = __int_as_float(r[1]);
+}
+
 // Logit shifts of a raw-token key tile of 64 rows: 64 zeros, then 64 -inf.
 // A tile with r rows left reads its 64 shifts from entry 64 - r on, so rows
 // past the chunk get -inf by the same LDS copy that brings slot tiles their
@@ -580,7 +589,11 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
 #pragma unroll
         for (int r = 0; r < 16; ++r) sx = fmaxf(sx, S[kb][qb][r]);
       float mx = sx * cscale;
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      {
+        float lo, hi;
+        half_pair(mx, lo, hi);
+        mx = fmaxf(lo, hi);
+      }
       const bool need = mx > mrun[qb] + 8.0f;
       if (__ballot(need)) {
         const float mnew = need ? mx : mrun[qb];
@@ -597,6 +610,9 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        // A operand: feature db*32 + m, keys kb*32 + kk*16 + {4*hf..4*hf+3}
+        // then {8+4*hf..8+4*hf+3}, the key order of the P fragment
+        const uint8_t* vrow = vt_lds + (kb * 32 + kk * 16) * C::kRowBytes;
         bf16x8_t pf[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -617,9 +633,6 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
           // weights are converted again)
           asm volatile("" : "+v"(lrun[qb]));
         }
-        // A operand: feature db*32 + m, keys kb*32 + kk*16 + {4*hf..4*hf+3}
-        // then {8+4*hf..8+4*hf+3}, the key order of the P fragment
-        const uint8_t* vrow = vt_lds + (kb * 32 + kk * 16) * C::kRowBytes;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -696,7 +709,9 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int r = (wave * QB + qb) * 32 + m;
-        const float lt = lrun[qb] + __shfl_xor(lrun[qb], 32);
+        float llo, lhi;
+        half_pair(lrun[qb], llo, lhi);
+        const float lt = llo + lhi;
         float* po = c.attn_part + (base + r) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -724,7 +739,9 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qt * C::BM + (wave * QB + qb) * 32 + m;
-    const float lt = lrun[qb] + __shfl_xor(lrun[qb], 32);
+    float llo, lhi;
+    half_pair(lrun[qb], llo, lhi);
+    const float lt = llo + lhi;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int r = qb * 32 + m;
 #pragma unroll
