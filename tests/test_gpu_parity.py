@@ -833,11 +833,15 @@ def _slot_codes(cache, orc, pl, L, b):
     return per_head, amb
 
 
-@pytest.mark.parametrize("L,b,seed", [(4, 6, 50), (4, 12, 51), (1, 4, 52), (3, 8, 53), (2, 16, 54)])
-def test_annsa_matches_oracle(L, b, seed):
+@pytest.mark.parametrize("L,b,seed,d", [(4, 6, 50, 128), (4, 12, 51, 128), (1, 4, 52, 128),
+                                        (3, 8, 53, 128), (2, 16, 54, 128), (3, 12, 62, 64),
+                                        (2, 16, 63, 64)])
+def test_annsa_matches_oracle(L, b, seed, d):
     """Outputs within the bf16 bound; queries that share no bucket exactly zero
-    with lse = -inf."""
-    w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=300, budget=2048, seed=seed), 5)
+    with lse = -inf.  Short expected lists (12 and 16 bits) take the listing
+    pass, long ones the plain pass; d = 64 rows are 8 features per lane."""
+    w, orc, cache, Q = _annsa_cache(dict(heads=2, tokens_per_frame=300, budget=2048, head_dim=d,
+                                         seed=seed), 5)
     pl = _annsa_planes(L, b, w.head_dim, seed)
     H, Nq = w.heads, Q.shape[1]
     cks, amb = _slot_codes(cache, orc, pl, L, b)
