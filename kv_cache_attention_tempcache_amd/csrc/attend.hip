@@ -41,6 +41,12 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+// Half of the waves (one per SIMD) issue a tile's copies; the other half
+// starts its QK^T right after each barrier, so the two waves of a SIMD run
+// their MFMA and softmax phases offset from each other.
+#ifndef FASTAR_ATTN_IW_DIV
+#define FASTAR_ATTN_IW_DIV 2
+#endif
 
 // The values of lanes l and l ^ 32 in every lane, lower half's first:
 // v_permlane32_swap exchanges the two 32-lane halves in the VALU, without the
@@ -185,7 +191,7 @@ struct CCfg {
   static constexpr int kBuf = kKBytes + kVBytes + BN * 4;
   static constexpr int kKInstr = kKBytes / 1024;  // wave-wide 1 KiB direct loads per tile
   static_assert(kKBytes % 1024 == 0 && kBuf % 16 == 0, "tile shape");
-  static_assert(kKInstr % WAVES == 0, "every wave issues the same number of copies");
+  static_assert(kKInstr % WAVES == 0, "the copies divide evenly among the waves");
   // LDS chunk permutations (XOR on the 16-byte chunk index of a row).  K: a
   // wave reads one chunk of 32 consecutive rows.  V: a half-wave reads 4
   // chunks (32 features) of 4 consecutive rows, which this spreads over all
@@ -417,16 +423,19 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   // Copy addresses: a wave-uniform tile offset plus per-lane byte offsets that
   // do not change from tile to tile, so issuing a slot tile's copy costs no
   // vector math.
-  // Wave w copies the 1 KiB chunks w, w + WAVES, ... of the K and V tiles; LDS
-  // position (row, chunk) receives global chunk chunk ^ swz(row).
+  // The first IW waves issue the copies: wave w copies the 1 KiB chunks w,
+  // w + IW, ... of the K and V tiles; LDS position (row, chunk) receives
+  // global chunk chunk ^ swz(row).
   // In a subset, a lane's source row is looked up per tile instead (rows past
   // the kept count read row 0 and are masked by their bias).
-  constexpr int kPerWave = C::kKInstr / WAVES;
+  constexpr int IW = WAVES / FASTAR_ATTN_IW_DIV;  // waves that issue the copies
+  constexpr int kPerWave = C::kKInstr / IW;
+  const bool iw = wave < IW;  // wave-uniform
   uint32_t koff[kPerWave], voff[kPerWave];
   int rrow[kPerWave];
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
-    const int off = (wave + j * WAVES) * 1024 + lane * 16;
+    const int off = (wave % IW + j * IW) * 1024 + lane * 16;
     const int row = off / C::kRowBytes;
     const int slot = (off - row * C::kRowBytes) >> 4;
     rrow[j] = row;
@@ -450,7 +459,8 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     const uint8_t* vt = vg + (SUBSET || raw ? 0 : (int64_t)vr * C::kRowBytes);
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
-      const int i = wave + j * WAVES;
+      if (!iw) break;
+      const int i = wave + j * IW;
       if constexpr (!SUBSET) {
         if (!raw) {  // slot tiles: scalar tile offset, fixed lane offsets
           copy16_lds(kg, kbytes, koff[j], kr * C::kRowBytes, (lds_void_t*)(buf + i * 1024));
@@ -490,7 +500,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     }
 #pragma unroll
     for (int i = 0; i < (BN + 63) / 64; ++i) {
-      if (wave == (WAVES - 1 - i) % WAVES && i * 64 + lane < BN)
+      if (wave == (IW - 1 - i) % IW && i * 64 + lane < BN)
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(lsrc + i * 64 + (uint32_t)lane),
                                          (lds_void_t*)(buf + C::kKBytes + C::kVBytes + i * 256), 4, 0, 0);
     }
@@ -521,10 +531,11 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     for (int db = 0; db < D / 32; ++db) O[db][qb] = f32x16_t{};
   }
 
-  // Copies this wave issues per tile: K and V chunks, plus the bias row for
-  // the last wave(s).
-  constexpr int kCopies = 2 * C::kKInstr / WAVES;
-  const bool lb_wave = wave >= WAVES - (BN + 63) / 64;
+  // Copies an issuing wave makes per tile: K and V chunks, plus the bias row
+  // for the last issuing wave(s).  The others have none in flight, so their
+  // waits below pass at once and the barrier orders them after the copies.
+  constexpr int kCopies = 2 * C::kKInstr / IW;
+  const bool lb_wave = iw && wave >= IW - (BN + 63) / 64;
 
   // Wait until at most n tiles' copies issued by this wave are in flight
   // (every older tile has landed), finish this wave's LDS reads, then meet
