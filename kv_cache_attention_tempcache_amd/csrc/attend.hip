@@ -43,9 +43,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // Half of the waves (one per SIMD) issue a tile's copies; the other half
 // starts its QK^T right after each barrier, so the two waves of a SIMD run
-// their MFMA and softmax phases offset from each other.
+// their MFMA and softmax phases offset from each other.  The AnnCA launch
+// that selects in its prologue attends over a few tiles only, and there all
+// waves issue (its start-up copies are then spread over twice the waves).
 #ifndef FASTAR_ATTN_IW_DIV
 #define FASTAR_ATTN_IW_DIV 2
+#endif
+#ifndef FASTAR_ATTN_IW_DIV_SEL
+#define FASTAR_ATTN_IW_DIV_SEL 1
 #endif
 
 // The values of lanes l and l ^ 32 in every lane, lower half's first:
@@ -428,7 +433,7 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   // global chunk chunk ^ swz(row).
   // In a subset, a lane's source row is looked up per tile instead (rows past
   // the kept count read row 0 and are masked by their bias).
-  constexpr int IW = WAVES / FASTAR_ATTN_IW_DIV;  // waves that issue the copies
+  constexpr int IW = SEL ? WAVES / FASTAR_ATTN_IW_DIV_SEL : WAVES / FASTAR_ATTN_IW_DIV;  // waves that issue the copies
   constexpr int kPerWave = C::kKInstr / IW;
   const bool iw = wave < IW;  // wave-uniform
   uint32_t koff[kPerWave], voff[kPerWave];
