@@ -7,7 +7,8 @@
 //   S^T = K Q^T on the 32x32x16 bf16 MFMA: A = a K tile row block from LDS,
 //     B = the wave's queries, held in registers for the whole key loop.  The
 //     accumulator gives each lane one query column and 16 key rows, so the
-//     running max and sum stay in the lane (plus one exchange with lane^32).
+//     running max and sum stay in the lane (plus one exchange with lane^32,
+//     a VALU permute).
 //   logits in log2 units: t = s * scale * log2(e) + log2(count), computed as
 //     (s + log2(count) / (scale * log2(e))) * scale * log2(e): the accumulators
 //     start at the divided shift, and each weight is one FMA and one exp2
@@ -20,6 +21,8 @@
 //   K, V (and log2-count) tiles of 64 keys move HBM -> LDS with direct-to-LDS
 //     loads into a ring of buffers, several tiles ahead of the one in use
 //     (slot tiles as buffer loads: scalar tile offset, fixed lane offsets).
+//     One wave per SIMD issues them; the other starts its QK^T right after
+//     each barrier, so the two run their MFMA and softmax phases offset.
 //   Blocks are renumbered so each XCD (blocks are dealt round-robin over the 8
 //     XCDs) gets a contiguous range of (head, query tile) and shares its L2.
 //   The normalised output tile leaves through LDS as whole rows.  When the
