@@ -52,6 +52,9 @@ constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 #ifndef FASTAR_ATTN_IW_DIV
 #define FASTAR_ATTN_IW_DIV 2
 #endif
+#ifndef FASTAR_ATTN_SKIPW
+#define FASTAR_ATTN_SKIPW 1
+#endif
 #ifndef FASTAR_ATTN_IW_DIV_SEL
 #define FASTAR_ATTN_IW_DIV_SEL 1
 #endif
@@ -671,9 +674,13 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
   // key tiles [tb, tb + nt) of this workgroup (a quarter may be empty)
   const int tb = part < 0 ? 0 : part * nt_all / 4;
   const int nt = part < 0 ? nt_all : (part + 1) * nt_all / 4 - tb;
+  // A wave whose queries all lie past the last one (the last query tile of a
+  // head) still issues its copies and meets every barrier, but skips the
+  // MFMA and softmax work, leaving its SIMD to the other wave there.
+  const bool wq = FASTAR_ATTN_SKIPW == 0 || qt * C::BM + wave * QB * 32 < nq;  // wave-uniform
   auto step = [&](const uint8_t* cur, uint8_t* nxt, int it, int nt) __attribute__((always_inline)) {
     if (it + NBUF - 1 < nt) issue((tb + it + NBUF - 1) * BN, nxt);
-    compute(cur);
+    if (wq) compute(cur);
     // Tile it+1 must have landed; the copies of tiles it+2 .. it+NBUF-1
     // stay in flight.
     wait_barrier(min(nt - 1, it + NBUF - 1) - (it + 1));
@@ -690,14 +697,18 @@ __global__ __launch_bounds__(WAVES * 64, QB == 1 ? 2 : 1) void attend_cache_kern
     if (3 < nt) issue((tb + 3) * BN, buf3);
     wait_barrier(max(min(nt, 4) - 2, 0));
     for (int it = 0; it < nt; it += 4) {
-      compute(buf0);
-      if (it + 1 < nt) compute(buf1);
+      if (wq) {
+        compute(buf0);
+        if (it + 1 < nt) compute(buf1);
+      }
       if (it + 2 < nt) {
         wait_barrier(0);
         if (it + 4 < nt) issue((tb + it + 4) * BN, buf0);
         if (it + 5 < nt) issue((tb + it + 5) * BN, buf1);
-        compute(buf2);
-        if (it + 3 < nt) compute(buf3);
+        if (wq) {
+          compute(buf2);
+          if (it + 3 < nt) compute(buf3);
+        }
         if (it + 4 < nt) {
           wait_barrier(0);
           if (it + 6 < nt) issue((tb + it + 6) * BN, buf2);
