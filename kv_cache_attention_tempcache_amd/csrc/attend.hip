@@ -23,6 +23,8 @@
 //     (slot tiles as buffer loads: scalar tile offset, fixed lane offsets).
 //     One wave per SIMD issues them; the other starts its QK^T right after
 //     each barrier, so the two run their MFMA and softmax phases offset.
+//     In a head's last query tile, waves that hold only padding queries
+//     still issue copies and meet the barriers but skip the tile work.
 //   Blocks are renumbered so each XCD (blocks are dealt round-robin over the 8
 //     XCDs) gets a contiguous range of (head, query tile) and shares its L2.
 //   The normalised output tile leaves through LDS as whole rows.  When the
