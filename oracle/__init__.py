@@ -15,7 +15,8 @@ token counts, hand-derived worked examples under ``tests/golden/``.
 Parity unpinned: the approximation quality of merging *non-identical* keys
 (the pages give only end-to-end video metrics for it), the LRU eviction order
 and the rollout generator, which are readings of silent passages and are
-checked only through invariants.
+checked through invariants (a hand-derived worked example pins the eviction
+order to its reading, which the pages themselves do not fix).
 """
 
 from .tempcache import (  # noqa: F401
