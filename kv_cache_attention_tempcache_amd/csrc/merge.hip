@@ -69,6 +69,12 @@ struct PlanShared {
 constexpr int kLeadShift = 42, kMemShift = 21;
 constexpr uint64_t kField = (1ull << 21) - 1;
 
+#ifndef FASTAR_PLAN_PREFETCH
+#define FASTAR_PLAN_PREFETCH 1
+#endif
+typedef __attribute__((address_space(3))) void plan_lds_t;
+typedef __attribute__((address_space(1))) void plan_gbl_t;
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c, MergeArgs a,
                                                            int stage_keys) {
   extern __shared__ __attribute__((aligned(16))) int32_t sm[];
@@ -88,6 +94,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
   const int n_live = c.n_live[h];
   int32_t* owner = c.owner + (int64_t)h * B;
   int32_t* gsize = c.gsize + (int64_t)h * B;
+#if FASTAR_PLAN_PREFETCH
+  // Eviction is possible only if the frame's tokens can outnumber the free
+  // slots.  Then the live slots' last-update frames are copied into LDS
+  // (direct-to-LDS loads, 64 slots per wave instruction) while the token
+  // passes below run; the slots merged into in this frame are masked out of
+  // that copy afterwards, from the tokens' targets.
+  const bool prefetch = stage_keys && n_live + T > B;  // block-uniform
+  if (prefetch) {
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), ln = tid & 63;
+    const int32_t* lastp = c.last + (int64_t)h * B;
+    for (int c0 = wv * 64; c0 < n_live; c0 += kPlanThreads)
+      if (c0 + ln < n_live)
+        __builtin_amdgcn_global_load_lds((plan_gbl_t*)(lastp + c0 + ln),
+                                         (plan_lds_t*)(keys_s + c0), 4, 0, 0);
+  }
+#endif
   // 0. per token (strided over the threads, every load of a thread issued
   //    together): its merge target, and whether it leads the target's group
   //    (the lowest merging token, recorded by the match step) with the group
@@ -184,6 +206,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
     const int s_lo = min(n_live, tid * per_s), s_hi = min(n_live, s_lo + per_s);
     const int32_t* last = c.last + (int64_t)h * B;
     uint32_t key[kPerS];
+#if FASTAR_PLAN_PREFETCH
+    if (stage_keys) {
+      // every wave's copies have landed (prefetch holds: need > 0 implies
+      // n_live + T > B); then the slots merged into lose eligibility
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      for (int i = tid; i < T; i += kPlanThreads) {
+        const int s = dec_s[i];
+        if (s >= 0) keys_s[s] = 0xffffffffu;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kPerS; ++k)
+        key[k] = s_lo + k < s_hi ? keys_s[s_lo + k] : 0xffffffffu;
+    } else
+#else
     if (stage_keys) {
       // coalesced: thread tid reads slots tid, tid + 1024, ... into LDS, four
       // slots' loads in flight at a time; then each thread takes its run
@@ -205,7 +243,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
 #pragma unroll
       for (int k = 0; k < kPerS; ++k)
         key[k] = s_lo + k < s_hi ? keys_s[s_lo + k] : 0xffffffffu;
-    } else {
+    } else
+#endif
+    {
 #pragma unroll
       for (int k = 0; k < kPerS; ++k) {
         const int sx = min(s_lo + k, B - 1);
@@ -363,6 +403,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims dm, CacheDev c,
       }
     }
   }
+#if FASTAR_PLAN_PREFETCH
+  // no LDS copy may still be in flight when the block ends
+  if (prefetch) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
   __syncthreads();
 
   // 4. reset the per-slot bookkeeping for the next frame (leaders own it)
