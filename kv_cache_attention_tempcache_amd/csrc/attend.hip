@@ -888,12 +888,12 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
   // The last round of workgroups: when it would leave a quarter or more of
   // the CUs idle, its r pairs run as 4r workgroups of a quarter of the key
   // tiles each (not for the M-degree regions, whose later tiles can be wholly
-  // masked), and a combine kernel merges the quarters.  Caches of at least 16
-  // key tiles only.
+  // masked), and a combine kernel merges the quarters.  Caches of at least
+  // 1024 slots only.
   const int cus = device_cus();
   const int r = pairs % cus;
   const bool split = a.n_reg == 0 && r > 0 && 4 * r <= 3 * cus && r <= c.attn_pairs &&
-                     C::BM == attn_query_tile(dm) && dm.B >= 16 * BN;
+                     C::BM == attn_query_tile(dm) && dm.B >= 1024;
   CacheAttendArgs aa = a;
   aa.nfull = split ? pairs - r : pairs;
   const int blocks = split ? pairs - r + 4 * r : pairs;
@@ -904,15 +904,23 @@ hipError_t launch_cache_cfg(const Dims& dm, const CacheDev& c, const CacheAttend
     hipLaunchKernelGGL(scale_shift_kernel, dim3((unsigned)b), dim3(256), 0, s,
                        a.n_reg > 0 ? c.rope_lb : c.lb, c.lbc, n, a.scale * kLog2e);
   }
-  if (a.n_reg > 0)
-    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, true>),
-                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
-  else if (a.n_x > 0)
-    hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, true, false>),
-                       dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
-  else
+  if constexpr (BN == kRawTile) {
+    if (a.n_reg > 0)
+      hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, true>),
+                         dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
+    else if (a.n_x > 0)
+      hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, true, false>),
+                         dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
+    else
+      hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, false>),
+                         dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
+  } else {
+    // wider key tiles serve the plain step only (the launcher routes the
+    // chunk tiles and the regions to 64-key tiles)
+    if (a.n_reg > 0 || a.n_x > 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attend_cache_kernel<D, BN, WAVES, QB, NBUF, false, false, false>),
                        dim3(blocks), dim3(C::kThreads), 0, s, dm, c, aa, AttendArgs{}, qtiles);
+  }
   if (split) {
     constexpr int kRows = 256 / (D / 4);
     hipLaunchKernelGGL(attend_combine_kernel<D>, dim3((C::BM + kRows - 1) / kRows, r), dim3(256),
@@ -966,6 +974,17 @@ hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
   return deep ? launch_subset_cfg<64, 4>(a, s) : launch_subset_cfg<64, 2>(a, s);
 }
 
+// The plain step (slots only) takes 128-key tiles in a ring of two; the
+// step with the chunk's raw tokens and the M-degree regions take 64-key
+// tiles in a ring of four (their constant shift rows cover 64 keys).  At the
+// 14B layer the 128-key tiles measured 1-2 % faster in same-process A/B runs:
+// one max exchange, one rescale test and one tile's bookkeeping per 128 keys.
+#ifndef FASTAR_PLAIN_BN
+#define FASTAR_PLAIN_BN 128
+#endif
+#ifndef FASTAR_PLAIN_NBUF
+#define FASTAR_PLAIN_NBUF 2
+#endif
 #ifndef FASTAR_CACHE_NBUF
 #define FASTAR_CACHE_NBUF 4
 #endif
@@ -982,6 +1001,8 @@ hipError_t launch_attend_bf16(const AttendArgs& a, hipStream_t s) {
 hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const CacheAttendArgs& a,
                                     hipStream_t s) {
   constexpr int BN = FASTAR_CACHE_BN, W = FASTAR_CACHE_WAVES, QB = FASTAR_CACHE_QB;
+  if (dm.d == 128 && a.n_reg == 0 && a.n_x == 0)
+    return launch_cache_cfg<128, FASTAR_PLAIN_BN, W, QB, FASTAR_PLAIN_NBUF>(dm, c, a, s);
   if (dm.d == 128) return launch_cache_cfg<128, BN, W, QB, FASTAR_CACHE_NBUF>(dm, c, a, s);
   return launch_cache_cfg<64, 64, 4, 1, FASTAR_CACHE_NBUF>(dm, c, a, s);
 }
