@@ -18,9 +18,10 @@
 //   O^T += V^T P^T: B = the probabilities, converted to bf16 in registers in
 //     exactly the k-order the accumulator produced them; A = 8 keys of one
 //     feature, gathered from row-major V in LDS by transposing LDS reads.
-//   K, V (and log2-count) tiles of 64 keys move HBM -> LDS with direct-to-LDS
-//     loads into a ring of buffers, several tiles ahead of the one in use
-//     (slot tiles as buffer loads: scalar tile offset, fixed lane offsets).
+//   K, V (and log2-count) tiles move HBM -> LDS with direct-to-LDS loads into
+//     a ring of buffers ahead of the tile in use (slot tiles as buffer loads:
+//     scalar tile offset, fixed lane offsets): 128-key tiles in a ring of two
+//     for the plain step, 64-key tiles in a ring of four for the others.
 //     One wave per SIMD issues them; the other starts its QK^T right after
 //     each barrier, so the two run their MFMA and softmax phases offset.
 //     In a head's last query tile, waves that hold only padding queries
