@@ -32,7 +32,8 @@
 //     grid's last round of workgroups would leave a quarter or more of the
 //     CUs idle, its (head, query tile) pairs run as four key-tile quarters
 //     each, and a combine kernel merges the quarters' partial results.
-// f32 path (small fp32 workloads): one thread per query, fp32 online softmax.
+// f32 path (small fp32 workloads): one thread per query and key part (four
+// parts of every fourth 16-key tile), fp32 online softmax, parts merged in LDS.
 #include <algorithm>
 
 #include "common.hpp"
@@ -87,18 +88,32 @@ constexpr RawShifts make_raw_shifts() {
 __device__ const RawShifts raw_shifts = make_raw_shifts();
 
 
+// One thread per query and key part: the 64 queries of a block are shared by
+// its 4 waves, wave p taking key tiles p, p+4, ...; each keeps its own running
+// max, sum and output, and the parts are merged through LDS at the end.
+constexpr int kF32Parts = 4;
+constexpr int kF32Tile = 16;
+template <int D>
+constexpr size_t attend_f32_lds_bytes() {
+  const size_t tiles = (size_t)kF32Parts * (2 * kF32Tile * D + kF32Tile);
+  const size_t parts = (size_t)2 * 64 * (D + 2);
+  return 4 * (tiles > parts ? tiles : parts);
+}
+
 template <int D, bool GATHER>
-__global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles) {
-  constexpr int KT = 32;
-  __shared__ float Ks[KT][D];
-  __shared__ float Vs[KT][D];
-  __shared__ float lbs[KT];
+__global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a, int qtiles) {
+  constexpr int KT = kF32Tile, P = kF32Parts;
+  extern __shared__ __attribute__((aligned(16))) float f32_lds[];
+  const int tid = threadIdx.x, qq = tid & 63;
+  const int part = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  float* Ks = f32_lds + part * (2 * KT * D + KT);
+  float* Vs = Ks + KT * D;
+  float* lbs = Vs + KT * D;
   const int per_head = a.F * qtiles;
   const int h = blockIdx.x / per_head;
   const int g = (blockIdx.x - h * per_head) / qtiles;
   const int qt = blockIdx.x - h * per_head - g * qtiles;
-  const int tid = threadIdx.x;
-  const int qi = qt * 64 + tid;
+  const int qi = qt * 64 + qq;
   const bool ok = qi < a.Nseg;
   const int nkeys = a.n_keys ? a.n_keys[h * a.F + g] : a.n_keys_const;
   const float cscale = a.scale * kLog2e;
@@ -120,54 +135,129 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a, int qtiles
     o[e] = 0.0f;
   }
   float mrun = -__builtin_huge_valf(), l = 0.0f;
-  for (int k0 = 0; k0 < ntot; k0 += KT) {
-    for (int idx = tid; idx < KT * D; idx += 64) {
-      const int r = idx / D, e = idx % D;
-      const int key = k0 + r;
-      float kx = 0.0f, vx = 0.0f;
-      if (key < nkeys) {
-        const int src = GATHER ? sel[key] : key;
-        kx = kbase[(int64_t)src * a.sk_n + e];
-        vx = vbase[(int64_t)src * a.sk_n + e];
-      } else if (key < ntot) {
-        kx = xkb[(int64_t)(key - nkeys) * a.sx_n + e];
-        vx = xvb[(int64_t)(key - nkeys) * a.sx_n + e];
+  const int ntiles = (ntot + KT - 1) / KT;
+  for (int t0 = 0; t0 < ntiles; t0 += P) {  // block-uniform
+    const int tile = t0 + part;
+    const int k0 = tile * KT;
+    if (tile < ntiles) {
+      // eight elements of K and of V per lane in flight before their stores
+      constexpr int kBatch = 8;
+      static_assert((KT * D / 64) % kBatch == 0, "tile elements per lane");
+#pragma unroll
+      for (int i0 = 0; i0 < KT * D / 64; i0 += kBatch) {
+        float kx[kBatch], vx[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int idx = qq + 64 * (i0 + u);
+          const int r = idx / D, e = idx % D;
+          const int key = k0 + r;
+          kx[u] = 0.0f;
+          vx[u] = 0.0f;
+          if (key < nkeys) {
+            const int src = GATHER ? sel[key] : key;
+            kx[u] = kbase[(int64_t)src * a.sk_n + e];
+            vx[u] = vbase[(int64_t)src * a.sk_n + e];
+          } else if (key < ntot) {
+            kx[u] = xkb[(int64_t)(key - nkeys) * a.sx_n + e];
+            vx[u] = xvb[(int64_t)(key - nkeys) * a.sx_n + e];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          Ks[qq + 64 * (i0 + u)] = kx[u];
+          Vs[qq + 64 * (i0 + u)] = vx[u];
+        }
       }
-      Ks[r][e] = kx;
-      Vs[r][e] = vx;
-    }
-    if (tid < KT) {
-      const int key = k0 + tid;
-      float lbv = -__builtin_huge_valf();
-      if (key < nkeys) {
-        const int src = GATHER ? sel[key] : key;
-        lbv = cnt ? log2f((float)cnt[src]) : 0.0f;
-      } else if (key < ntot) {
-        lbv = 0.0f;
+      if (qq < KT) {
+        const int key = k0 + qq;
+        float lbv = -__builtin_huge_valf();
+        if (key < nkeys) {
+          const int src = GATHER ? sel[key] : key;
+          lbv = cnt ? log2f((float)cnt[src]) : 0.0f;
+        } else if (key < ntot) {
+          lbv = 0.0f;
+        }
+        lbs[qq] = lbv;
       }
-      lbs[tid] = lbv;
     }
     __syncthreads();
-    const int nr = min(KT, ntot - k0);
-    for (int r = 0; r < nr; ++r) {
-      float dot = 0.0f;
+    const int nr = tile < ntiles ? min(KT, ntot - k0) : 0;
+    // keys in groups of four: four independent dot products, one rescale
+    // test per group.  Tile rows past the last key hold zero rows and a -inf
+    // shift, so they add nothing (the group's first key is real, which makes
+    // the running max finite before any weight is formed).
+    for (int r0 = 0; r0 < nr; r0 += 4) {
+      float t4[4];
 #pragma unroll
-      for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qv[e], Ks[r][e], dot);
-      const float t = dot * cscale + lbs[r];
-      if (t > mrun) {
-        const float alpha = exp2f(mrun - t);
+      for (int j = 0; j < 4; ++j) {
+        const float4* kr = reinterpret_cast<const float4*>(Ks + (r0 + j) * D);
+        float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int e4 = 0; e4 < D / 4; ++e4) {
+          const float4 kv = kr[e4];
+          d4[0] = __builtin_fmaf(qv[4 * e4 + 0], kv.x, d4[0]);
+          d4[1] = __builtin_fmaf(qv[4 * e4 + 1], kv.y, d4[1]);
+          d4[2] = __builtin_fmaf(qv[4 * e4 + 2], kv.z, d4[2]);
+          d4[3] = __builtin_fmaf(qv[4 * e4 + 3], kv.w, d4[3]);
+        }
+        t4[j] = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * cscale + lbs[r0 + j];
+      }
+      const float tm = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+      if (tm > mrun) {
+        const float alpha = exp2f(mrun - tm);
         l *= alpha;
 #pragma unroll
         for (int e = 0; e < D; ++e) o[e] *= alpha;
-        mrun = t;
+        mrun = tm;
       }
-      const float p = exp2f(t - mrun);
-      l += p;
+      float p4[4];
 #pragma unroll
-      for (int e = 0; e < D; ++e) o[e] = __builtin_fmaf(p, Vs[r][e], o[e]);
+      for (int j = 0; j < 4; ++j) {
+        p4[j] = exp2f(t4[j] - mrun);
+        l += p4[j];
+      }
+#pragma unroll
+      for (int e4 = 0; e4 < D / 4; ++e4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 vv = reinterpret_cast<const float4*>(Vs + (r0 + j) * D)[e4];
+          o[4 * e4 + 0] = __builtin_fmaf(p4[j], vv.x, o[4 * e4 + 0]);
+          o[4 * e4 + 1] = __builtin_fmaf(p4[j], vv.y, o[4 * e4 + 1]);
+          o[4 * e4 + 2] = __builtin_fmaf(p4[j], vv.z, o[4 * e4 + 2]);
+          o[4 * e4 + 3] = __builtin_fmaf(p4[j], vv.w, o[4 * e4 + 3]);
+        }
+      }
     }
     __syncthreads();
   }
+  // merge the parts: parts 2 and 3 hand over to 0 and 1, then 1 to 0.  A
+  // part that saw no key (running max -inf) adds nothing.
+  auto absorb = [&](const float* src) __attribute__((always_inline)) {
+    const float m2 = src[qq * (D + 2)], l2 = src[qq * (D + 2) + 1];
+    const float m = fmaxf(mrun, m2);
+    if (m == -__builtin_huge_valf()) return;
+    const float w1 = exp2f(mrun - m), w2 = exp2f(m2 - m);
+    l = l * w1 + l2 * w2;
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[e] = o[e] * w1 + src[qq * (D + 2) + 2 + e] * w2;
+    mrun = m;
+  };
+  auto hand_over = [&](float* dst) __attribute__((always_inline)) {
+    dst[qq * (D + 2)] = mrun;
+    dst[qq * (D + 2) + 1] = l;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dst[qq * (D + 2) + 2 + e] = o[e];
+  };
+  float* R0 = f32_lds;
+  float* R1 = f32_lds + 64 * (D + 2);
+  if (part >= 2) hand_over(part == 2 ? R0 : R1);
+  __syncthreads();
+  if (part < 2) absorb(part == 0 ? R0 : R1);
+  __syncthreads();
+  if (part == 1) hand_over(R0);
+  __syncthreads();
+  if (part != 0) return;
+  absorb(R0);
   if (!ok) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   float* op = static_cast<float*>(a.o) + (int64_t)h * a.so_h + (int64_t)(g * a.Nseg + qi) * a.so_n;
@@ -1008,19 +1098,29 @@ hipError_t launch_attend_cache_bf16(const Dims& dm, const CacheDev& c, const Cac
   return launch_cache_cfg<64, 64, 4, 1, FASTAR_CACHE_NBUF>(dm, c, a, s);
 }
 
+template <int D, bool GATHER>
+hipError_t launch_attend_f32_cfg(const AttendArgs& a, int qtiles, int blocks, hipStream_t s) {
+  constexpr size_t lds = attend_f32_lds_bytes<D>();
+  auto kern = attend_f32_kernel<D, GATHER>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kF32Parts), lds, s, a, qtiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s) {
   const int qtiles = (a.Nseg + 63) / 64;
   const int blocks = a.H * a.F * qtiles;
   if (blocks == 0) return hipSuccess;
   const bool gather = a.sel != nullptr;
-  if (a.d == 128) {
-    if (gather) hipLaunchKernelGGL((attend_f32_kernel<128, true>), dim3(blocks), dim3(64), 0, s, a, qtiles);
-    else hipLaunchKernelGGL((attend_f32_kernel<128, false>), dim3(blocks), dim3(64), 0, s, a, qtiles);
-  } else {
-    if (gather) hipLaunchKernelGGL((attend_f32_kernel<64, true>), dim3(blocks), dim3(64), 0, s, a, qtiles);
-    else hipLaunchKernelGGL((attend_f32_kernel<64, false>), dim3(blocks), dim3(64), 0, s, a, qtiles);
-  }
-  return hipGetLastError();
+  if (a.d == 128)
+    return gather ? launch_attend_f32_cfg<128, true>(a, qtiles, blocks, s)
+                  : launch_attend_f32_cfg<128, false>(a, qtiles, blocks, s);
+  return gather ? launch_attend_f32_cfg<64, true>(a, qtiles, blocks, s)
+                : launch_attend_f32_cfg<64, false>(a, qtiles, blocks, s);
 }
 
 }  // namespace fastar

@@ -15,7 +15,8 @@
 // plane order.  Rows past the end and padding planes are read clamped to valid
 // memory and never stored.
 //
-// f32 path: one thread per (row, table), products and sums in float64.
+// f32 path: 32 lanes per (row, table), one plane per lane, products and sums
+// in float64.
 #include "common.hpp"
 
 namespace fastar {
@@ -140,28 +141,44 @@ __global__ __launch_bounds__(kHashThreads) void hash_bf16_kernel(HashArgs a, int
   }
 }
 
+// 32 lanes per (head, table, row): lane j projects onto plane j of the table
+// (a sequential float64 sum over the features, as one thread per row would),
+// and a wave ballot packs the bits of the wave's two rows.
 template <int D>
 __global__ __launch_bounds__(256) void hash_f32_kernel(HashArgs a, int64_t total) {
   const float* planes = static_cast<const float*>(a.planes);
   const float* xbase = static_cast<const float*>(a.x);
-  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int t = (int)(idx % a.L);
-    const int64_t rest = idx / a.L;
-    const int r = (int)(rest % a.N);
-    const int h = (int)(rest / a.N);
-    const int nrows = a.rows ? a.n_rows[(int64_t)h * a.n_rows_stride] : a.N;
-    if (r >= nrows) continue;
-    const int64_t xrow = a.rows ? (int64_t)a.rows[(int64_t)h * a.rows_ld + r] : (int64_t)r;
-    const float* xp = xbase + (int64_t)h * a.sx_h + xrow * a.sx_n;
-    uint32_t code = 0u;
-    for (int j = 0; j < a.b; ++j) {
+  const int j = threadIdx.x & 31;
+  // every thread of a block runs the same iterations (the ballot needs the
+  // whole wave)
+  for (int64_t base = blockIdx.x * (int64_t)blockDim.x; base < total * 32;
+       base += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t item = (base + threadIdx.x) >> 5;  // (h, t, r), r fastest
+    bool valid = item < total;
+    int h = 0, t = 0, r = 0;
+    int64_t xrow = 0;
+    if (valid) {
+      r = (int)(item % a.N);
+      const int64_t ht = item / a.N;
+      t = (int)(ht % a.L);
+      h = (int)(ht / a.L);
+      const int nrows = a.rows ? a.n_rows[(int64_t)h * a.n_rows_stride] : a.N;
+      valid = r < nrows;
+      if (valid) xrow = a.rows ? (int64_t)a.rows[(int64_t)h * a.rows_ld + r] : (int64_t)r;
+    }
+    bool bit = false;
+    if (valid && j < a.b) {
+      const float* xp = xbase + (int64_t)h * a.sx_h + xrow * a.sx_n;
       const float* rp = planes + ((int64_t)t * a.b + j) * D;
       double acc = 0.0;
       for (int k = 0; k < D; ++k) acc += (double)xp[k] * (double)rp[k];
-      if (acc > 0.0) code |= 1u << j;
+      bit = acc > 0.0;
     }
-    a.codes[((int64_t)h * a.L + t) * a.codes_ld + a.codes_col0 + xrow] = code;
+    const uint64_t bits = __ballot(bit);
+    if (valid && j == 0) {
+      const uint32_t code = (uint32_t)(bits >> (threadIdx.x & 32));
+      a.codes[((int64_t)h * a.L + t) * a.codes_ld + a.codes_col0 + xrow] = code;
+    }
   }
 }
 
@@ -188,9 +205,9 @@ hipError_t launch_hash_bf16(const HashArgs& a, hipStream_t s) {
 
 hipError_t launch_hash_f32(const HashArgs& a, hipStream_t s) {
   if (a.M > 0) return launch_pq(a, false, s);
-  const int64_t total = (int64_t)a.H * a.N * a.L;
+  const int64_t total = (int64_t)a.H * a.N * a.L;  // (head, table, row) items, 32 lanes each
   if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
+  int64_t blocks = (total * 32 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (a.d == 128)
     hipLaunchKernelGGL(hash_f32_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a, total);
