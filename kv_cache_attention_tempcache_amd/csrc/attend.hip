@@ -32,8 +32,9 @@
 //     grid's last round of workgroups would leave a quarter or more of the
 //     CUs idle, its (head, query tile) pairs run as four key-tile quarters
 //     each, and a combine kernel merges the quarters' partial results.
-// f32 path (small fp32 workloads): one thread per query and key part (four
-// parts of every fourth 16-key tile), fp32 online softmax, parts merged in LDS.
+// f32 path (small fp32 workloads): sixteen key parts per query (four waves on
+// every fourth 16-key tile, four lanes per query inside a tile), fp32 online
+// softmax, parts merged by lane exchanges and through LDS.
 #include <algorithm>
 
 #include "common.hpp"
@@ -88,15 +89,18 @@ constexpr RawShifts make_raw_shifts() {
 __device__ const RawShifts raw_shifts = make_raw_shifts();
 
 
-// One thread per query and key part: the 64 queries of a block are shared by
-// its 4 waves, wave p taking key tiles p, p+4, ...; each keeps its own running
-// max, sum and output, and the parts are merged through LDS at the end.
-constexpr int kF32Parts = 4;
+// Sixteen key parts per query: the 16 queries of a block are shared by its 4
+// waves, wave p taking key tiles p, p+4, ..., and inside a wave the four lanes
+// of a query take one key of every four of the tile; each part keeps its own
+// running max, sum and output, merged by lane exchanges and then through LDS.
+constexpr int kF32Parts = 4;     // waves per block, one key tile each per round
+constexpr int kF32Queries = 16;  // queries per block (lanes qq, qq+16, qq+32, qq+48)
+constexpr int kF32Subparts = 64 / kF32Queries;
 constexpr int kF32Tile = 16;
 template <int D>
 constexpr size_t attend_f32_lds_bytes() {
   const size_t tiles = (size_t)kF32Parts * (2 * kF32Tile * D + kF32Tile);
-  const size_t parts = (size_t)2 * 64 * (D + 2);
+  const size_t parts = (size_t)2 * kF32Queries * (D + 2);
   return 4 * (tiles > parts ? tiles : parts);
 }
 
@@ -104,7 +108,8 @@ template <int D, bool GATHER>
 __global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a, int qtiles) {
   constexpr int KT = kF32Tile, P = kF32Parts;
   extern __shared__ __attribute__((aligned(16))) float f32_lds[];
-  const int tid = threadIdx.x, qq = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int qq = lane & (kF32Queries - 1), sub = lane / kF32Queries;  // query, key sub-part
   const int part = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   float* Ks = f32_lds + part * (2 * KT * D + KT);
   float* Vs = Ks + KT * D;
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a
   const int h = blockIdx.x / per_head;
   const int g = (blockIdx.x - h * per_head) / qtiles;
   const int qt = blockIdx.x - h * per_head - g * qtiles;
-  const int qi = qt * 64 + qq;
+  const int qi = qt * kF32Queries + qq;
   const bool ok = qi < a.Nseg;
   const int nkeys = a.n_keys ? a.n_keys[h * a.F + g] : a.n_keys_const;
   const float cscale = a.scale * kLog2e;
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a
         float kx[kBatch], vx[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          const int idx = qq + 64 * (i0 + u);
+          const int idx = lane + 64 * (i0 + u);
           const int r = idx / D, e = idx % D;
           const int key = k0 + r;
           kx[u] = 0.0f;
@@ -164,12 +169,12 @@ __global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          Ks[qq + 64 * (i0 + u)] = kx[u];
-          Vs[qq + 64 * (i0 + u)] = vx[u];
+          Ks[lane + 64 * (i0 + u)] = kx[u];
+          Vs[lane + 64 * (i0 + u)] = vx[u];
         }
       }
-      if (qq < KT) {
-        const int key = k0 + qq;
+      if (lane < KT) {
+        const int key = k0 + lane;
         float lbv = -__builtin_huge_valf();
         if (key < nkeys) {
           const int src = GATHER ? sel[key] : key;
@@ -177,20 +182,21 @@ __global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a
         } else if (key < ntot) {
           lbv = 0.0f;
         }
-        lbs[qq] = lbv;
+        lbs[lane] = lbv;
       }
     }
     __syncthreads();
     const int nr = tile < ntiles ? min(KT, ntot - k0) : 0;
-    // keys in groups of four: four independent dot products, one rescale
-    // test per group.  Tile rows past the last key hold zero rows and a -inf
-    // shift, so they add nothing (the group's first key is real, which makes
-    // the running max finite before any weight is formed).
-    for (int r0 = 0; r0 < nr; r0 += 4) {
+    // this lane's keys of the tile: sub, sub + 4, sub + 8, sub + 12, scored
+    // together with one rescale test.  Tile rows past the last key hold zero
+    // rows and a -inf shift, so they add nothing; key `sub` is real whenever
+    // sub < nr, which makes the running max finite before any weight.
+    static_assert(KT == 4 * kF32Subparts, "four keys per lane and tile");
+    if (sub < nr) {
       float t4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4* kr = reinterpret_cast<const float4*>(Ks + (r0 + j) * D);
+        const float4* kr = reinterpret_cast<const float4*>(Ks + (sub + kF32Subparts * j) * D);
         float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int e4 = 0; e4 < D / 4; ++e4) {
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a
           d4[2] = __builtin_fmaf(qv[4 * e4 + 2], kv.z, d4[2]);
           d4[3] = __builtin_fmaf(qv[4 * e4 + 3], kv.w, d4[3]);
         }
-        t4[j] = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * cscale + lbs[r0 + j];
+        t4[j] = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * cscale + lbs[sub + kF32Subparts * j];
       }
       const float tm = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
       if (tm > mrun) {
@@ -220,7 +226,8 @@ __global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a
       for (int e4 = 0; e4 < D / 4; ++e4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float4 vv = reinterpret_cast<const float4*>(Vs + (r0 + j) * D)[e4];
+          const float4 vv =
+              reinterpret_cast<const float4*>(Vs + (sub + kF32Subparts * j) * D)[e4];
           o[4 * e4 + 0] = __builtin_fmaf(p4[j], vv.x, o[4 * e4 + 0]);
           o[4 * e4 + 1] = __builtin_fmaf(p4[j], vv.y, o[4 * e4 + 1]);
           o[4 * e4 + 2] = __builtin_fmaf(p4[j], vv.z, o[4 * e4 + 2]);
@@ -230,33 +237,48 @@ __global__ __launch_bounds__(64 * kF32Parts) void attend_f32_kernel(AttendArgs a
     }
     __syncthreads();
   }
-  // merge the parts: parts 2 and 3 hand over to 0 and 1, then 1 to 0.  A
-  // part that saw no key (running max -inf) adds nothing.
-  auto absorb = [&](const float* src) __attribute__((always_inline)) {
-    const float m2 = src[qq * (D + 2)], l2 = src[qq * (D + 2) + 1];
+  // merge the parts: a part that saw no key (running max -inf) adds nothing.
+  // First the four sub-parts of each query inside a wave (lanes qq, qq+16,
+  // qq+32, qq+48, by two lane exchanges), then the waves: 2 and 3 hand over to
+  // 0 and 1 through LDS, then 1 to 0.
+  auto merge_with = [&](float m2, float l2, const float* o2, int o2_stride)
+      __attribute__((always_inline)) {
     const float m = fmaxf(mrun, m2);
     if (m == -__builtin_huge_valf()) return;
     const float w1 = exp2f(mrun - m), w2 = exp2f(m2 - m);
     l = l * w1 + l2 * w2;
 #pragma unroll
-    for (int e = 0; e < D; ++e) o[e] = o[e] * w1 + src[qq * (D + 2) + 2 + e] * w2;
+    for (int e = 0; e < D; ++e) o[e] = o[e] * w1 + o2[e * o2_stride] * w2;
     mrun = m;
   };
-  auto hand_over = [&](float* dst) __attribute__((always_inline)) {
-    dst[qq * (D + 2)] = mrun;
-    dst[qq * (D + 2) + 1] = l;
 #pragma unroll
-    for (int e = 0; e < D; ++e) dst[qq * (D + 2) + 2 + e] = o[e];
+  for (int x = kF32Queries; x < 64; x <<= 1) {
+    float o2[D];
+#pragma unroll
+    for (int e = 0; e < D; ++e) o2[e] = __shfl_xor(o[e], x);
+    const float m2 = __shfl_xor(mrun, x), l2 = __shfl_xor(l, x);
+    merge_with(m2, l2, o2, 1);
+  }
+  constexpr int kRow = D + 2;
+  auto hand_over = [&](float* dst) __attribute__((always_inline)) {
+    if (sub != 0) return;  // the four sub-part lanes of a query now agree
+    dst[qq * kRow] = mrun;
+    dst[qq * kRow + 1] = l;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dst[qq * kRow + 2 + e] = o[e];
+  };
+  auto absorb = [&](const float* src) __attribute__((always_inline)) {
+    merge_with(src[qq * kRow], src[qq * kRow + 1], src + qq * kRow + 2, 1);
   };
   float* R0 = f32_lds;
-  float* R1 = f32_lds + 64 * (D + 2);
+  float* R1 = f32_lds + kF32Queries * kRow;
   if (part >= 2) hand_over(part == 2 ? R0 : R1);
   __syncthreads();
   if (part < 2) absorb(part == 0 ? R0 : R1);
   __syncthreads();
   if (part == 1) hand_over(R0);
   __syncthreads();
-  if (part != 0) return;
+  if (part != 0 || sub != 0) return;
   absorb(R0);
   if (!ok) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
@@ -1112,7 +1134,7 @@ hipError_t launch_attend_f32_cfg(const AttendArgs& a, int qtiles, int blocks, hi
 }
 
 hipError_t launch_attend_f32(const AttendArgs& a, hipStream_t s) {
-  const int qtiles = (a.Nseg + 63) / 64;
+  const int qtiles = (a.Nseg + kF32Queries - 1) / kF32Queries;
   const int blocks = a.H * a.F * qtiles;
   if (blocks == 0) return hipSuccess;
   const bool gather = a.sel != nullptr;
