@@ -16,7 +16,7 @@ the 1.3B-layer step, the tiny fp32 step, the 240-frame rollout's per-chunk
 latency and memory, and the chunk's hash bits against the CPU oracle.
 
 Prints one JSON line (rank 0).  Other workloads (`--workload`): dit1.3b,
-dit1.3b_pq, rollout, annca, annsa, denoise, project, rope.
+dit1.3b_pq, rollout, annca, annsa, denoise, project, rope, tiny.
 """
 
 from __future__ import annotations
@@ -46,7 +46,7 @@ def _parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dit14b",
                    choices=["dit1.3b", "dit1.3b_pq", "dit14b", "rollout", "annca", "annsa",
-                            "denoise", "project", "rope"])
+                            "denoise", "project", "rope", "tiny"])
     p.add_argument("--annsa-bits", type=int, default=16, help="bits per table of the AnnSA buckets")
     p.add_argument("--denoise-steps", type=int, default=4, help="denoising steps per chunk")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -445,6 +445,8 @@ def main():
         return project(args, fa, torch)
     if args.workload == "rope":
         return rope(args, fa, torch)
+    if args.workload == "tiny":
+        return tiny(args, fa, torch)
 
     return step_line(args, fa, torch, WORKLOADS[args.workload])
 
@@ -1237,6 +1239,22 @@ def rope(args, fa, torch):
             lambda: orope.mdegree_attend(q, kh, vh, cnt, fr, 4, d_t), (cq.shape[1] // 10) / H,
             "query tokens/s", f"M-degree attention (m = 4) of {cq.shape[1] // 10} queries (every "
             f"10th) of one head over {S} slots, shapes of the GPU workload", scale=1.0 / H)
+    print(json.dumps(line), flush=True)
+
+
+def tiny(args, fa, torch):
+    """The tiny fp32 step alone (one frame merged, then its 64 queries attend),
+    eager and as one replayed HIP graph; latency-bound, so no roofline."""
+    r = _tiny_step(args, fa, torch, reps=max(args.steps, 20))
+    line = {
+        "metric": "query tokens/s per tiny fp32 step (merge of one frame, then its queries attend)",
+        "value": 64 / (r["us_median"] / 1e6), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": r["reps"], "warmup": 0, "ms_per_step": r["us_median"] / 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded drift-model frames)",
+        "config": {"workload": r["workload"]},
+        "detail": r,
+    }
     print(json.dumps(line), flush=True)
 
 
